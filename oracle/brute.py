@@ -1,0 +1,109 @@
+"""Pure-Python brute force for tiny inputs (test infrastructure only).
+
+An independent formulation of each step of the AdaFuse pre-gated projection
+(technical summary §2.A pre-gating, §2.B SGMM / decoding procedure), used to
+pin oracle/reference.py.  It uses no NumPy arithmetic: plain loops over Python
+numbers.  With integer-valued inputs every result is an exact integer.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from typing import List, Sequence, Tuple
+
+
+def _tolist(a):
+    return a.tolist() if hasattr(a, "tolist") else a
+
+
+def logits(x, Wg) -> List[List[float]]:
+    """l[t][e] = sum over i of x[t][i] * Wg[i][e], summed in index order."""
+    x, Wg = _tolist(x), _tolist(Wg)
+    T, d = len(x), len(Wg)
+    E = len(Wg[0]) if d else 0
+    out = []
+    for t in range(T):
+        row = []
+        for e in range(E):
+            s = 0
+            for i in range(d):
+                s += x[t][i] * Wg[i][e]
+            row.append(s)
+        out.append(row)
+    return out
+
+
+def topk(l_row: Sequence[float], k: int) -> List[int]:
+    """The unique k-subset S whose every member outranks every non-member.
+
+    Rank order: higher logit first; between equal logits the lower index
+    first.  Found by enumerating all k-subsets (E small), then listed best
+    first.
+    """
+    E = len(l_row)
+
+    def beats(a, b):
+        return l_row[a] > l_row[b] or (l_row[a] == l_row[b] and a < b)
+
+    found = []
+    for S in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in S]
+        if all(beats(a, b) for a in S for b in rest):
+            found.append(S)
+    assert len(found) == 1, "rank order is total, so exactly one subset dominates"
+    S = list(found[0])
+    # order the members: a member's place = number of members that beat it
+    placed = [None] * k
+    for a in S:
+        placed[sum(1 for b in S if b != a and beats(b, a))] = a
+    return placed
+
+
+def gates(l_row: Sequence[float], chosen: Sequence[int]) -> List[float]:
+    """Softmax over the chosen logits (math.exp; no shift needed at test sizes)."""
+    w = [math.exp(l_row[e]) for e in chosen]
+    s = sum(w)
+    return [v / s for v in w]
+
+
+def segments(idx, E: int) -> Tuple[List[int], List[int]]:
+    """For each adapter in turn, scan all pairs in order and collect those that chose it."""
+    idx = _tolist(idx)
+    T = len(idx)
+    k = len(idx[0]) if T else 0
+    perm, offsets = [], [0]
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if idx[t][j] == e:
+                    perm.append(t * k + j)
+        offsets.append(len(perm))
+    return offsets, perm
+
+
+def projection(x, W0, A, B, idx, gate) -> List[List[float]]:
+    """y[t][o] = sum_i W0[o][i] x[t][i] + sum_j g[t][j] sum_c B[e][o][c] sum_i A[e][c][i] x[t][i]."""
+    x, W0, A, B, idx, gate = map(_tolist, (x, W0, A, B, idx, gate))
+    T = len(x)
+    d_out, d_in = len(W0), len(W0[0])
+    k = len(idx[0]) if T else 0
+    y = []
+    for t in range(T):
+        row = []
+        for o in range(d_out):
+            s = 0
+            for i in range(d_in):
+                s += W0[o][i] * x[t][i]
+            for j in range(k):
+                e = idx[t][j]
+                r = len(A[e])
+                delta = 0
+                for c in range(r):
+                    u = 0
+                    for i in range(d_in):
+                        u += A[e][c][i] * x[t][i]
+                    delta += B[e][o][c] * u
+                s += gate[t][j] * delta
+            row.append(s)
+        y.append(row)
+    return y
