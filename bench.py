@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the pre-gated fused multi-adapter projection step on one MI355X.
+
+A step is the whole hot path once over one batch (AdaFuse technical summary
+§2.A-§2.B): router pre-gating (rp_pregate), segmentation (rp_segment) and
+every projection group in dependency order (rp_sgmm_fused for q|k|v, then o,
+and for the MLP workloads gate|up, then down).  Weights and inputs are seeded
+synthetic data already resident in HBM; weight copies are rotated so repeated
+steps stream from HBM rather than the on-chip caches.  The step is captured
+in one HIP graph per weight copy and replayed.
+
+Prints one JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "fused adapter-projection tokens/s + achieved HBM GB/s (% peak), 4096-d decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rank_pregate_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_src_sha") != kernel_source_hash():
+        log(f"traffic counters in {path} predate the current kernels; reporting null")
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    """The CPU oracle on the same workload, timed on this host (a reported baseline only)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from rank_pregate_amd import datagen
+
+    # inputs drawn outside the timed region (bf16 bit patterns, as uploaded)
+    xr, Wg = datagen.router_input(wl), datagen.router_weight(wl)
+    groups = []
+    for g in wl.groups:
+        xg = datagen.layer_input(wl, 0, g.x_name)
+        groups.append((xg, [datagen.proj_weights(wl, 0, g, p) for p in g.projs]))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        idx, gate, _ = oracle.pregate(oracle.widen(xr, wl.dtype), oracle.widen(Wg, wl.dtype), wl.k)
+        oracle.segment(idx, wl.E)
+        for xg, ws in groups:
+            x64 = oracle.widen(xg, wl.dtype)
+            for w in ws:
+                oracle.sgmm(x64, oracle.widen(w.W0, wl.dtype), oracle.widen(w.A, wl.dtype),
+                            oracle.widen(w.B, wl.dtype), idx, gate)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": wl.T * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full {wl.name} step(s) of the fp64 NumPy oracle (T={wl.T}, layer 0, all groups), "
+                      f"{el:.1f} s, widening of bf16 inputs included, input generation excluded; "
+                      f"host {platform.processor() or platform.machine()}, "
+                      f"{len(os.sched_getaffinity(0))} cores available"}
+
+
+def calibrate():
+    """Known-traffic kernels: a 1 GiB copy (reads 1 GiB, writes 1 GiB) for scaling the
+    FETCH_SIZE / WRITE_SIZE counters, and a 4 GiB stream read for the achievable read bandwidth."""
+    import torch
+
+    import rank_pregate_amd as rp
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
+    sink = torch.empty(1024, dtype=torch.float32, device=dev)
+    out = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: rp.copy(dst, src), 2 << 30),
+                             ("stream_read_4GiB", lambda: rp.stream_read(big, sink), 4 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n = 10
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        out[name] = {"avg_us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log(f"[calibrate] {name}: {us:.1f} us, {nbytes / (us * 1e-6) / 1e9:,.0f} GB/s")
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_qkvo")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies rotated per step (0: auto)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of the step: time the plain copy and stream-read kernels (known traffic) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_pregate_amd as rp
+    from rank_pregate_amd import datagen
+    from rank_pregate_amd.workload import DeviceWorkload
+
+    rp.lib()  # fail loudly if the HIP library is missing
+    if args.calibrate:
+        calibrate()
+        return
+    wl = datagen.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    copies = args.copies
+    if copies <= 0:
+        # keep the rotated weight set well above the 256 MB last-level cache
+        per_copy = sum(g.d_in * g.d_out * len(g.projs) for g in wl.groups) * wl.layers * (2 if wl.dtype == "bf16" else 4)
+        copies = max(1, min(16, -(-1_200_000_000 // per_copy)))
+    log(f"[bench] workload {wl.name}: {wl.description}; weight copies {copies}")
+    t_gen = time.perf_counter()
+    dw = DeviceWorkload(wl, dev, copies=copies)
+    log(f"[bench] data generated and uploaded in {time.perf_counter() - t_gen:.1f} s")
+
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dw.step()
+        stream.synchronize()
+        n_touched = int((torch.diff(dw.seg_offsets) > 0).sum().item())
+
+        if args.no_graph:
+            def run(i):
+                dw.route()
+                dw.project(i % copies)
+        else:
+            graphs = []
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    dw.route()
+                    dw.project(c)
+                graphs.append(g)
+
+            def run(i):
+                graphs[i % copies].replay()
+
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+        # the dominant call (first projection group, the widest), bracketed with
+        # events on the stream it is launched on, eager, over its own timed loop
+        g0 = wl.groups[0]
+        layer = dw.layers[0]
+        xg = dw.inputs[(layer, g0.x_name)]
+        evs = []
+        for i in range(args.steps):
+            W = dw.weights[i % copies]
+            projs = [(W[(layer, p)].W0, W[(layer, p)].A, W[(layer, p)].B, dw.outputs[(layer, p)]) for p in g0.projs]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rp.sgmm_fused(projs, xg, wl.E, wl.r, wl.k, dw.sel_idx, dw.sel_gate, dw.seg_offsets, dw.pair_perm,
+                          ws=dw.ws)
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+        # base-only (k = 0) step for the adapter overhead
+        for i in range(3):
+            dw.project(i % copies, k=0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nb = max(10, args.steps // 4)
+        for i in range(nb):
+            dw.project(i % copies, k=0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        base_ms = e0.elapsed_time(e1) / nb
+
+    step_bytes = dw.algorithmic_bytes(n_touched)
+    step_flops = dw.algorithmic_flops()
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = wl.T / (ms_per_step * 1e-3)
+    bpe = 2 if wl.dtype == "bf16" else 4
+    dom_bytes = sum(g0.d_out * g0.d_in * bpe + n_touched * wl.r * (g0.d_in + g0.d_out) * bpe + wl.T * g0.d_out * bpe
+                    for _ in g0.projs) + wl.T * g0.d_in * bpe
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, {tokens_per_s:,.0f} tokens/s, algorithmic {step_bytes / 1e6:.1f} MB "
+        f"-> {gbs:,.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); {step_flops / (ms_per_step * 1e-3) / 1e12:.1f} "
+        f"TFLOP/s; touched adapters {n_touched}/{wl.E}")
+    log(f"[bench] dominant call rp_sgmm_fused({'|'.join(g0.projs)}): {dom_ms * 1e3:.1f} us for {dom_bytes / 1e6:.1f} MB "
+        f"-> {dom_gbs:,.0f} GB/s")
+    log(f"[bench] base-only (k=0) projections {base_ms * 1e3:.1f} us per step (eager)")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "r": wl.r, "k": wl.k,
+                   "layers": wl.layers, "groups": [g.name for g in wl.groups], "weight_copies": copies,
+                   "graph": not args.no_graph, "achieved_GBps": round(gbs, 1),
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "algorithmic_bytes_per_step": step_bytes, "touched_adapters": n_touched},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("sgmm_" + g0.name, wl.name),
+                     "kernel": f"rp_sgmm_fused({'|'.join(g0.projs)})", "avg_launch_us": round(dom_ms * 1e3, 2),
+                     "bytes_per_launch": dom_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

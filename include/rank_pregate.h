@@ -1,0 +1,165 @@
+/*
+ * rank_pregate.h -- C ABI of the pre-gated multi-adapter low-rank projection
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (AdaFuse, "Accelerating Dynamic Adapter Inference via
+ * Token-Level Pre-Gating and Fused Kernel Optimization", technical summary §2):
+ *
+ *   rp_pregate    -- §2.A token-level pre-gating and §2.B decoding steps 1-2: a
+ *                    light linear router scores every token once and keeps its
+ *                    top-k adapters; the choice then holds for every layer.
+ *   rp_segment    -- groups the (token, slot) pairs by adapter, giving the
+ *                    segments the segmented gather matrix multiply runs over.
+ *   rp_sgmm_fused -- §2.B SGMM and decoding step 3: base projection plus the
+ *                    gated low-rank deltas of the chosen adapters, in one pass:
+ *                       y[t] = W0 x[t] + sum_j g[t,j] B_e (A_e x[t]),  e = idx[t,j]
+ *                    for up to four projections that share x and the gate.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     allocates no device memory and keeps no state besides a per-device
+ *     property cache and a thread-local error message.
+ *   - Matrices are row-major.  Sizes and leading dimensions count elements.
+ *   - Work is queued on `stream` (0 = the null stream) and returns at once;
+ *     results are valid once the stream is synchronised or ordered after.
+ *   - Argument checks happen on the host, before any launch; a failing check
+ *     returns a non-OK status, launches nothing and records a message readable
+ *     through rp_last_error().  No C++ exception crosses this boundary.
+ *   - Calls are thread-safe on distinct streams with distinct workspaces.
+ *   - Inputs must be finite; behaviour on NaN or Inf is unspecified.
+ */
+#ifndef RANK_PREGATE_H
+#define RANK_PREGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RP_ABI_VERSION 1
+#define RP_MAX_K 8          /* largest top-k */
+#define RP_MAX_E 1024       /* largest adapter count */
+#define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call */
+
+typedef enum {
+  RP_OK = 0,
+  RP_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, size or count out of range */
+  RP_ERR_UNSUPPORTED = 2,   /* well-formed but outside what the kernels implement */
+  RP_ERR_WORKSPACE = 3,     /* workspace missing, misaligned or too small */
+  RP_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} rp_status;
+
+typedef enum { RP_F32 = 0, RP_BF16 = 1 } rp_dtype;
+
+/* One adapted projection (one linear layer with its adapter bank).
+ *   W0 [d_out, d_in]     backbone weight, dense (leading dimension d_in)
+ *   A  [E, r, d_in]      adapter down-projections, dense, one block per adapter
+ *   B  [E, d_out, r]     adapter up-projections, dense, one block per adapter
+ *   y  [T, d_out]        output, leading dimension ld_y (>= d_out)
+ * All four have the call's dtype.  y must not alias any input. */
+typedef struct {
+  const void* W0;
+  const void* A;
+  const void* B;
+  void* y;
+  int64_t d_out;
+  int64_t ld_y;
+} rp_proj;
+
+/* Token-level pre-gating (AdaFuse §2.A; §2.B decoding steps 1-2).
+ *
+ *   logits[t,e] = sum_i x[t,i] * Wg[i,e]            fp32 accumulation
+ *   topk_idx[t,0..k-1]  = the k adapters with the largest logits, best first;
+ *                         an exact tie goes to the lower adapter index
+ *   topk_gate[t,j]      = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) over the k
+ *                         chosen logits (softmax over the selection; 1.0 when k=1)
+ *
+ *   x       [T, d_in], leading dimension ld_x, dtype dt
+ *   Wg      [d_in, E], dense, dtype dt
+ *   topk_idx  int32 [T, k], dense          (output)
+ *   topk_gate fp32  [T, k], dense          (output)
+ *   logits_or_null  fp32 [T, E], dense, or NULL to skip (output)
+ *
+ * The sum over i runs in the same order for every adapter column, so equal
+ * router columns give bit-equal logits and the tie rule is exact.
+ * Limits: 1 <= k <= min(E, RP_MAX_K), 1 <= E <= RP_MAX_E, d_in >= 1 and a
+ * multiple of 8 (bf16) or 4 (fp32); x, Wg 16-byte aligned, ld_x*sizeof(dt) a
+ * multiple of 16; T = 0 is a no-op. */
+rp_status rp_pregate(const void* x, int64_t T, int64_t d_in, int64_t ld_x, const void* Wg, int64_t E,
+                     int32_t k, rp_dtype dt, int32_t* topk_idx, float* topk_gate, float* logits_or_null,
+                     hipStream_t stream);
+
+/* Segmentation: group the pairs p = t*k + j by adapter (the segments of the
+ * segmented gather matrix multiply, AdaFuse §2.B).
+ *
+ *   seg_offsets int32 [E+1] (output): segment e is pair_perm[seg_offsets[e] ..
+ *                                     seg_offsets[e+1]); seg_offsets[0] = 0
+ *   pair_perm   int32 [T*k] (output): pair ids grouped by ascending adapter and,
+ *                                     inside a segment, by ascending pair id
+ *   ws          device workspace of at least rp_segment_workspace_size() bytes,
+ *               4-byte aligned; its first int32 receives the number of pairs
+ *               whose index was outside [0, E).  Such pairs are left out of
+ *               every segment (seg_offsets[E] counts only the valid pairs) and
+ *               the tail of pair_perm is then left unwritten.
+ * Runs as one workgroup.  Limits: 0 <= k <= RP_MAX_K, 1 <= E <= RP_MAX_E,
+ * T*k < 2^31.  T = 0 or k = 0 writes all-zero offsets. */
+rp_status rp_segment(const int32_t* topk_idx, int64_t T, int32_t k, int64_t E, int32_t* seg_offsets,
+                     int32_t* pair_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t rp_segment_workspace_size(int64_t T, int32_t k, int64_t E);
+
+/* Fused pre-gated SGMM (AdaFuse §2.B): for each of the n_proj projections,
+ *
+ *   y[t,:] = W0 x[t,:] + sum_{j<k} topk_gate[t,j] * B_e (A_e x[t,:]),  e = topk_idx[t,j]
+ *
+ * with fp32 accumulation and one rounding to dt on the final store.  The
+ * adapter work follows the segments of rp_segment (each chosen adapter's A
+ * and B are read once per output tile).  k = 0 computes the base projection
+ * only (topk_*, seg_offsets, pair_perm may then be NULL).
+ *
+ *   projs      host array of n_proj (1..RP_MAX_PROJ) descriptors sharing x and
+ *              the gate, e.g. q|k|v or gate|up (the descriptor array itself is
+ *              read during the call and not kept)
+ *   x          [T, d_in], leading dimension ld_x
+ *   topk_idx, topk_gate, seg_offsets, pair_perm   as produced above
+ *   ws         device workspace of at least rp_sgmm_workspace_size() bytes,
+ *              256-byte aligned.  Its first 64 KiB hold arrival counters that
+ *              must be zero before the first call (zero-fill the buffer once);
+ *              every call that completes leaves them zero again, so one
+ *              workspace serves calls of any shape in sequence.  Calls that may
+ *              overlap in time need distinct workspaces.
+ * Limits: r in {8,16,32,64,128}; 0 <= k <= min(E, RP_MAX_K); 1 <= E <=
+ * RP_MAX_E; d_in a multiple of 8 (bf16) / 4 (fp32); d_out a multiple of 8;
+ * all matrix pointers 16-byte aligned and ld_x*sizeof(dt), ld_y*sizeof(dt)
+ * multiples of 16; T = 0 is a no-op. */
+rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                        int64_t ld_x, int64_t E, int64_t r, int32_t k, const int32_t* topk_idx,
+                        const float* topk_gate, const int32_t* seg_offsets, const int32_t* pair_perm,
+                        rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes rp_sgmm_fused needs for these sizes; sum_d_out is the sum of
+ * the projections' d_out.  Returns 0 for sizes the call would reject. */
+size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t sum_d_out, int64_t E,
+                              int64_t r, int32_t k, rp_dtype dt);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* rp_last_error(void);
+
+/* RP_ABI_VERSION of the built library. */
+int rp_abi_version(void);
+
+/* ---- measurement helpers (not part of the method) ------------------------
+ * rp_util_stream_read: reads n_bytes (multiple of 16, 16-byte aligned) from
+ * src with coalesced 16-byte loads and writes one fp32 checksum per workgroup
+ * to sink[0..1023]; gives the achievable HBM read bandwidth of the device.
+ * rp_util_copy: copies n_bytes (multiple of 16, both 16-byte aligned) from src
+ * to dst; a kernel of known traffic for scaling hardware byte counters. */
+rp_status rp_util_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t stream);
+rp_status rp_util_copy(void* dst, const void* src, size_t n_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RANK_PREGATE_H */

@@ -1,0 +1,243 @@
+"""rank_pregate_amd -- pre-gated multi-adapter low-rank projection on MI355X (gfx950).
+
+Thin Python binding of librank_pregate.so (include/rank_pregate.h).  The
+functions here only marshal torch tensors into pointers, sizes and the
+current HIP stream; every step runs in the library's HIP kernels.  There is
+no CPU fallback: if the library is not built, every call raises.
+
+    pregate(x, Wg, k)                    -> topk_idx, topk_gate      (rp_pregate)
+    segment(topk_idx, E)                 -> seg_offsets, pair_perm   (rp_segment)
+    sgmm_fused(projs, x, E, r, ...)      -> list of y                (rp_sgmm_fused)
+
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librank_pregate.so")
+
+RP_OK, RP_ERR_INVALID_ARG, RP_ERR_UNSUPPORTED, RP_ERR_WORKSPACE, RP_ERR_HIP = range(5)
+RP_F32, RP_BF16 = 0, 1
+RP_MAX_K, RP_MAX_E, RP_MAX_PROJ = 8, 1024, 4
+
+_STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3: "RP_ERR_WORKSPACE",
+                 4: "RP_ERR_HIP"}
+
+EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
+            "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+
+
+class RankPregateError(RuntimeError):
+    def __init__(self, where: str, status: int, message: str):
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class RpProj(ctypes.Structure):
+    _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("d_out", ctypes.c_int64), ("ld_y", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_pregate_amd.build` "
+                           "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.rp_pregate.argtypes = [vp, i64, i64, i64, vp, i64, i32, ctypes.c_int, vp, vp, vp, vp]
+    L.rp_segment.argtypes = [vp, i64, i32, i64, vp, vp, vp, sz, vp]
+    L.rp_segment_workspace_size.argtypes = [i64, i32, i64]
+    L.rp_segment_workspace_size.restype = sz
+    L.rp_sgmm_fused.argtypes = [ctypes.POINTER(RpProj), i32, vp, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp,
+                                ctypes.c_int, vp, sz, vp]
+    L.rp_sgmm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32, ctypes.c_int]
+    L.rp_sgmm_workspace_size.restype = sz
+    L.rp_last_error.argtypes = []
+    L.rp_last_error.restype = ctypes.c_char_p
+    L.rp_abi_version.argtypes = []
+    L.rp_abi_version.restype = ctypes.c_int
+    L.rp_util_stream_read.argtypes = [vp, sz, vp, vp]
+    L.rp_util_copy.argtypes = [vp, vp, sz, vp]
+    for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_util_stream_read", "rp_util_copy"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().rp_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib().rp_abi_version()
+
+
+def _check(status: int, where: str) -> None:
+    if status != RP_OK:
+        raise RankPregateError(where, status, last_error())
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RP_BF16
+    if t.dtype == torch.float32:
+        return RP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rows(t, name: str) -> int:
+    """Leading dimension of a row-major 2-D view (unit stride along columns)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major tensor with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def pregate(x, Wg, k: int, topk_idx=None, topk_gate=None, logits=None, stream=None):
+    """rp_pregate on torch tensors: x [T, d_in], Wg [d_in, E] (dense), same dtype, on one GPU.
+
+    Returns (topk_idx int32 [T, k], topk_gate float32 [T, k]); `logits`
+    (float32 [T, E]) is filled when given.
+    """
+    torch = _torch()
+    T, d_in = x.shape
+    E = Wg.shape[1]
+    if Wg.dtype != x.dtype or not Wg.is_contiguous() or Wg.shape[0] != d_in:
+        raise ValueError("Wg must be a dense [d_in, E] tensor of x's dtype")
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    st = lib().rp_pregate(_ptr(x), T, d_in, _rows(x, "x"), _ptr(Wg), E, k, _dtype_code(x), _ptr(topk_idx),
+                          _ptr(topk_gate), _ptr(logits), _stream(stream, x.device))
+    _check(st, "rp_pregate")
+    return topk_idx, topk_gate
+
+
+def segment_workspace_size(T: int, k: int, E: int) -> int:
+    return lib().rp_segment_workspace_size(T, k, E)
+
+
+def segment(topk_idx, E: int, seg_offsets=None, pair_perm=None, ws=None, stream=None):
+    """rp_segment on torch tensors.  Returns (seg_offsets int32 [E+1], pair_perm int32 [T*k])."""
+    torch = _torch()
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if seg_offsets is None:
+        seg_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pair_perm is None:
+        pair_perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    nbytes = segment_workspace_size(T, k, E)
+    if ws is None:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    st = lib().rp_segment(_ptr(topk_idx), T, k, E, _ptr(seg_offsets), _ptr(pair_perm), _ptr(ws), ws.numel(),
+                          _stream(stream, dev))
+    _check(st, "rp_segment")
+    return seg_offsets, pair_perm
+
+
+def sgmm_workspace_size(n_proj: int, T: int, d_in: int, sum_d_out: int, E: int, r: int, k: int,
+                        dtype_code: int) -> int:
+    return lib().rp_sgmm_workspace_size(n_proj, T, d_in, sum_d_out, E, r, k, dtype_code)
+
+
+class Workspace:
+    """A zero-initialised device buffer reused across rp_sgmm_fused calls on one stream.
+
+    The library leaves the counter words zero after every completed call, so a
+    buffer only has to be zeroed when it is (re)allocated.
+    """
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        key = str(device)
+        b = self._buf.get(key)
+        if b is None or b.numel() < nbytes:
+            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._buf[key] = b
+        return b
+
+
+_default_ws = Workspace()
+
+
+def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None, topk_gate=None, seg_offsets=None,
+               pair_perm=None, ws=None, stream=None) -> List:
+    """rp_sgmm_fused on torch tensors.
+
+    projs: up to four tuples (W0 [d_out, d_in], A [E, r, d_in], B [E, d_out, r], y [T, d_out] or None);
+    outputs that are None are allocated.  Returns the list of y tensors.
+    """
+    torch = _torch()
+    T, d_in = x.shape
+    dt = _dtype_code(x)
+    arr = (RpProj * len(projs))()
+    ys = []
+    sum_d_out = 0
+    for i, pr in enumerate(projs):
+        W0, A, B = pr[0], pr[1], pr[2]
+        y = pr[3] if len(pr) > 3 else None
+        d_out = W0.shape[0]
+        for name, t in (("W0", W0), ("A", A), ("B", B)):
+            if t is not None and (t.dtype != x.dtype or not t.is_contiguous()):
+                raise ValueError(f"projection {i}: {name} must be dense with x's dtype")
+        if y is None:
+            y = torch.empty((T, d_out), dtype=x.dtype, device=x.device)
+        ys.append(y)
+        arr[i] = RpProj(_ptr(W0), _ptr(A), _ptr(B), _ptr(y), d_out, _rows(y, "y"))
+        sum_d_out += d_out
+    if ws is None:
+        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), x.device)
+    st = lib().rp_sgmm_fused(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), E, r, k, _ptr(topk_idx),
+                             _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(),
+                             _stream(stream, x.device))
+    _check(st, "rp_sgmm_fused")
+    return ys
+
+
+def stream_read(src, sink, stream=None) -> None:
+    """rp_util_stream_read over the bytes of tensor `src`; `sink` is a float32 tensor of >= 1024 elements."""
+    st = lib().rp_util_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                   _stream(stream, src.device))
+    _check(st, "rp_util_stream_read")
+
+
+def copy(dst, src, stream=None) -> None:
+    st = lib().rp_util_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream, src.device))
+    _check(st, "rp_util_copy")
+
+
+# the C names, for callers that mirror the header
+rp_pregate, rp_segment, rp_sgmm_fused = pregate, segment, sgmm_fused

@@ -1,0 +1,254 @@
+// C ABI of the library: argument validation, launch planning and dispatch.
+// Every check runs on the host before anything is queued; no exception leaves
+// this file.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/rank_pregate.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rp_status fail(rp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rp_status hip_fail(const char* where, hipError_t e) {
+  return fail(RP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dsize(rp_dtype dt) { return dt == RP_BF16 ? 2 : 4; }
+
+bool valid_dtype(rp_dtype dt) { return dt == RP_F32 || dt == RP_BF16; }
+
+// Compute units of the current device, cached per device id.
+int cu_count(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return 0;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return 0;
+}
+
+constexpr int64_t kIntMax = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+const char* rp_last_error(void) { return g_last_error.c_str(); }
+
+int rp_abi_version(void) { return RP_ABI_VERSION; }
+
+rp_status rp_pregate(const void* x, int64_t T, int64_t d_in, int64_t ld_x, const void* Wg, int64_t E, int32_t k,
+                     rp_dtype dt, int32_t* topk_idx, float* topk_gate, float* logits_or_null, hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "rp_pregate: unknown dtype %d", (int)dt);
+  if (T < 0 || T > kIntMax) return fail(RP_ERR_INVALID_ARG, "rp_pregate: T=%lld out of range", (long long)T);
+  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "rp_pregate: E=%lld not in [1, %d]", (long long)E, RP_MAX_E);
+  if (k < 1 || k > RP_MAX_K || k > E)
+    return fail(RP_ERR_INVALID_ARG, "rp_pregate: k=%d not in [1, min(E, %d)]", k, RP_MAX_K);
+  const int64_t vec = dt == RP_BF16 ? 8 : 4;
+  if (d_in < 1 || d_in % vec != 0 || d_in > kIntMax)
+    return fail(RP_ERR_INVALID_ARG, "rp_pregate: d_in=%lld must be a positive multiple of %lld", (long long)d_in,
+                (long long)vec);
+  if (ld_x < d_in || (ld_x * (int64_t)dsize(dt)) % 16 != 0 || ld_x > kIntMax)
+    return fail(RP_ERR_INVALID_ARG, "rp_pregate: ld_x=%lld must be >= d_in with ld_x*elem a multiple of 16 bytes",
+                (long long)ld_x);
+  if (T * E > (int64_t)1 << 40) return fail(RP_ERR_INVALID_ARG, "rp_pregate: T*E too large");
+  if (T == 0) return RP_OK;
+  if (!x || !Wg || !topk_idx || !topk_gate) return fail(RP_ERR_INVALID_ARG, "rp_pregate: null pointer");
+  if (!aligned(x, 16) || !aligned(Wg, 16)) return fail(RP_ERR_INVALID_ARG, "rp_pregate: x and Wg must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(topk_gate, 4) || (logits_or_null && !aligned(logits_or_null, 4)))
+    return fail(RP_ERR_INVALID_ARG, "rp_pregate: outputs must be 4-byte aligned");
+  rp::PregateArgs a;
+  a.x = x;
+  a.T = (int)T;
+  a.d_in = (int)d_in;
+  a.ld_x = (int)ld_x;
+  a.Wg = Wg;
+  a.E = (int)E;
+  a.k = k;
+  a.dt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.logits = logits_or_null;
+  hipError_t e = rp::launch_pregate(a, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_pregate launch", e);
+}
+
+size_t rp_segment_workspace_size(int64_t T, int32_t k, int64_t E) {
+  (void)T;
+  (void)k;
+  (void)E;
+  return 256;
+}
+
+rp_status rp_segment(const int32_t* topk_idx, int64_t T, int32_t k, int64_t E, int32_t* seg_offsets,
+                     int32_t* pair_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (T < 0 || k < 0 || k > RP_MAX_K) return fail(RP_ERR_INVALID_ARG, "rp_segment: T=%lld / k=%d out of range", (long long)T, k);
+  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "rp_segment: E=%lld not in [1, %d]", (long long)E, RP_MAX_E);
+  if (T * (int64_t)k > kIntMax) return fail(RP_ERR_INVALID_ARG, "rp_segment: T*k must be < 2^31");
+  if (!seg_offsets || !ws) return fail(RP_ERR_INVALID_ARG, "rp_segment: null pointer");
+  if (T * k > 0 && (!topk_idx || !pair_perm)) return fail(RP_ERR_INVALID_ARG, "rp_segment: null pointer");
+  if (!aligned(seg_offsets, 4) || (topk_idx && !aligned(topk_idx, 4)) || (pair_perm && !aligned(pair_perm, 4)))
+    return fail(RP_ERR_INVALID_ARG, "rp_segment: pointers must be 4-byte aligned");
+  if (!aligned(ws, 4)) return fail(RP_ERR_WORKSPACE, "rp_segment: workspace must be 4-byte aligned");
+  if (ws_bytes < rp_segment_workspace_size(T, k, E))
+    return fail(RP_ERR_WORKSPACE, "rp_segment: workspace %zu bytes, need %zu", ws_bytes, rp_segment_workspace_size(T, k, E));
+  rp::SegmentArgs a;
+  a.topk_idx = topk_idx;
+  a.n_pairs = (int)(T * k);
+  a.k = k;
+  a.E = (int)E;
+  a.seg_offsets = seg_offsets;
+  a.pair_perm = pair_perm;
+  a.err_count = static_cast<int*>(ws);
+  hipError_t e = rp::launch_segment(a, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_segment launch", e);
+}
+
+size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t sum_d_out, int64_t E, int64_t r,
+                              int32_t k, rp_dtype dt) {
+  if (!valid_dtype(dt) || n_proj < 1 || n_proj > RP_MAX_PROJ || T < 0 || T > kIntMax || d_in < 1 || sum_d_out < 1 ||
+      E < 1 || E > RP_MAX_E || k < 0 || k > RP_MAX_K || k > E)
+    return 0;
+  if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128)) return 0;
+  if (T * k * r * n_proj > ((int64_t)1 << 34)) return 0;
+  return rp::sgmm_workspace_upper_bound(dt == RP_BF16 ? rp::kBF16 : rp::kF32, n_proj, (int)T, (int)d_in,
+                                        (long long)sum_d_out, (int)E, (int)r, k);
+}
+
+rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in, int64_t ld_x,
+                        int64_t E, int64_t r, int32_t k, const int32_t* topk_idx, const float* topk_gate,
+                        const int32_t* seg_offsets, const int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: unknown dtype %d", (int)dt);
+  if (!projs || n_proj < 1 || n_proj > RP_MAX_PROJ)
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: n_proj=%d not in [1, %d]", n_proj, RP_MAX_PROJ);
+  if (T < 0 || T > kIntMax) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: T=%lld out of range", (long long)T);
+  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: E=%lld not in [1, %d]", (long long)E, RP_MAX_E);
+  if (k < 0 || k > RP_MAX_K || k > E)
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k=%d not in [0, min(E, %d)]", k, RP_MAX_K);
+  if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128))
+    return fail(RP_ERR_UNSUPPORTED, "rp_sgmm_fused: rank r=%lld not in {8,16,32,64,128}", (long long)r);
+  const int64_t es = (int64_t)dsize(dt);
+  const int64_t vec = dt == RP_BF16 ? 8 : 4;
+  if (d_in < 1 || d_in % vec != 0 || d_in > kIntMax)
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: d_in=%lld must be a positive multiple of %lld", (long long)d_in,
+                (long long)vec);
+  if (ld_x < d_in || (ld_x * es) % 16 != 0 || ld_x > kIntMax)
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: ld_x=%lld must be >= d_in with ld_x*elem a multiple of 16 bytes",
+                (long long)ld_x);
+  if (T * k * r * n_proj > ((int64_t)1 << 34)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: T*k*r too large");
+  int d_out[RP_MAX_PROJ];
+  int64_t sum_d_out = 0;
+  for (int p = 0; p < n_proj; ++p) {
+    const rp_proj& q = projs[p];
+    if (q.d_out < 8 || q.d_out % 8 != 0 || q.d_out > kIntMax)
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: d_out=%lld must be a positive multiple of 8", p,
+                  (long long)q.d_out);
+    if (q.ld_y < q.d_out || (q.ld_y * es) % 16 != 0 || q.ld_y > kIntMax)
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: ld_y=%lld must be >= d_out with ld_y*elem a "
+                  "multiple of 16 bytes", p, (long long)q.ld_y);
+    if (T > 0 && (!q.W0 || !q.y || (k > 0 && (!q.A || !q.B))))
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: null pointer", p);
+    if (!aligned(q.W0, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.y, 16))
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: W0, A, B, y must be 16-byte aligned", p);
+    if ((int64_t)q.d_out * d_in > ((int64_t)1 << 40) || E * r * std::max<int64_t>(d_in, q.d_out) > ((int64_t)1 << 40))
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d too large", p);
+    d_out[p] = (int)q.d_out;
+    sum_d_out += q.d_out;
+  }
+  if (T == 0) return RP_OK;
+  if (!x || !aligned(x, 16)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: x must be non-null and 16-byte aligned");
+  if (k > 0 && (!topk_idx || !topk_gate || !seg_offsets || !pair_perm))
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k>0 needs topk_idx, topk_gate, seg_offsets and pair_perm");
+  if (!ws) return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: null workspace");
+  if (!aligned(ws, 256)) return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: workspace must be 256-byte aligned");
+  int n_cu = 0;
+  if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "rp_sgmm_fused: cannot query the current device");
+  const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
+  const rp::SgmmPlan plan = rp::plan_sgmm(rdt, n_proj, d_out, (int)T, (int)d_in, (int)E, (int)r, k, n_cu);
+  if (ws_bytes < plan.bytes)
+    return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: workspace %zu bytes, need %zu (rp_sgmm_workspace_size)", ws_bytes,
+                plan.bytes);
+
+  rp::SgmmArgs a{};
+  int tile = 0;
+  for (int p = 0; p < RP_MAX_PROJ; ++p) {
+    const int q = p < n_proj ? p : n_proj - 1;  // unused slots repeat the last projection
+    a.proj[p].W0 = projs[q].W0;
+    a.proj[p].A = projs[q].A;
+    a.proj[p].B = projs[q].B;
+    a.proj[p].y = projs[q].y;
+    a.proj[p].d_out = (int)projs[q].d_out;
+    a.proj[p].ld_y = (int)projs[q].ld_y;
+    a.proj[p].tile_begin = tile;
+    if (p < n_proj) tile += (d_out[p] + plan.tile_rows - 1) / plan.tile_rows;
+  }
+  a.n_proj = n_proj;
+  a.x = x;
+  a.T = (int)T;
+  a.d_in = (int)d_in;
+  a.ld_x = (int)ld_x;
+  a.E = (int)E;
+  a.r = (int)r;
+  a.k = k;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.seg_offsets = seg_offsets;
+  a.pair_perm = pair_perm;
+  char* w = static_cast<char*>(ws);
+  a.counters = reinterpret_cast<int*>(w + plan.off_counters);
+  a.u = reinterpret_cast<float*>(w + plan.off_u);
+  a.partial = reinterpret_cast<float*>(w + plan.off_partial);
+  a.n_tiles = plan.n_tiles;
+  a.S = plan.S;
+  hipError_t e = rp::launch_sgmm(a, plan, rdt, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_sgmm_fused launch", e);
+}
+
+rp_status rp_util_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t stream) {
+  g_last_error.clear();
+  if (!src || !sink || !aligned(src, 16) || n_bytes % 16 != 0 || n_bytes == 0)
+    return fail(RP_ERR_INVALID_ARG, "rp_util_stream_read: need non-null 16-byte aligned src and n_bytes %% 16 == 0");
+  hipError_t e = rp::launch_stream_read(src, n_bytes, sink, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_util_stream_read launch", e);
+}
+
+rp_status rp_util_copy(void* dst, const void* src, size_t n_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || n_bytes % 16 != 0 || n_bytes == 0)
+    return fail(RP_ERR_INVALID_ARG, "rp_util_copy: need non-null 16-byte aligned buffers and n_bytes %% 16 == 0");
+  hipError_t e = rp::launch_copy(dst, src, n_bytes, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_util_copy launch", e);
+}
+
+}  // extern "C"

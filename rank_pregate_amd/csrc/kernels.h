@@ -1,0 +1,83 @@
+// Host-side launch interface between the C ABI layer (api.cpp) and the kernels.
+// Everything here has already been validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rp {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+struct PregateArgs {
+  const void* x;
+  int T, d_in, ld_x;
+  const void* Wg;
+  int E, k;
+  Dtype dt;
+  int* topk_idx;
+  float* topk_gate;
+  float* logits;  // may be null
+};
+hipError_t launch_pregate(const PregateArgs& a, hipStream_t s);
+
+struct SegmentArgs {
+  const int* topk_idx;
+  int n_pairs;  // T * k
+  int k;
+  int E;
+  int* seg_offsets;
+  int* pair_perm;
+  int* err_count;  // first word of the workspace
+};
+hipError_t launch_segment(const SegmentArgs& a, hipStream_t s);
+
+constexpr int kMaxProj = 4;
+
+struct ProjDesc {
+  const void* W0;
+  const void* A;
+  const void* B;
+  void* y;
+  int d_out;
+  int ld_y;
+  int tile_begin;  // first output-row tile of this projection in the packed row space
+};
+
+struct SgmmArgs {
+  ProjDesc proj[kMaxProj];
+  int n_proj;
+  const void* x;
+  int T, d_in, ld_x;
+  int E, r, k;
+  const int* topk_idx;
+  const float* topk_gate;
+  const int* seg_offsets;
+  const int* pair_perm;
+  // workspace views
+  float* u;          // [n_proj][T*k][r] gated rank-r intermediates
+  float* partial;    // split-K partial tiles (decode path)
+  int* counters;     // per output tile arrival counters (decode path)
+  int n_tiles;       // output-row tiles over all projections
+  int S;             // K splits per output tile (decode path)
+};
+
+// Which kernel family serves a call, and the workspace it needs.
+struct SgmmPlan {
+  int path;          // 0: fp32 VALU, 1: bf16 decode (T <= 256), 2: bf16 prefill
+  int tile_rows;     // output rows per tile
+  int n_tiles;
+  int S;
+  int t_pad;         // tokens padded to the decode tile width
+  size_t off_u, off_partial, off_counters, bytes;
+};
+SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu);
+size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
+                                  int k);
+hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);
+
+hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t n_bytes, hipStream_t s);
+
+}  // namespace rp

@@ -1,0 +1,157 @@
+"""Device-resident synthetic workloads and the pre-gated decode/prefill step.
+
+A step is the whole hot path once (AdaFuse technical summary §2.A-§2.B):
+route the router input once (rp_pregate), group pairs by adapter
+(rp_segment), then every projection group of every layer in dependency order
+(q|k|v -> o -> gate|up -> down), each one rp_sgmm_fused call.  The same
+gate and segments serve every layer.
+
+Inputs come from rank_pregate_amd.datagen (seeded); weights are uploaded
+once and stay resident in HBM.  `copies` > 1 keeps several copies of the
+weights and rotates through them step by step, so repeated steps do not hit
+the on-chip caches.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+from . import datagen
+from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
+from . import sgmm_workspace_size, segment_workspace_size, RP_BF16, RP_F32
+
+
+def to_device(a: np.ndarray, dtype: str, device):
+    """Upload a datagen array: uint16 bf16 bits -> torch.bfloat16, float32 -> torch.float32."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+        return t.view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    """Download: torch.bfloat16 -> uint16 bits, float32 -> float32."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+@dataclasses.dataclass
+class DevProj:
+    W0: object
+    A: object
+    B: object
+
+
+class DeviceWorkload:
+    def __init__(self, wl: datagen.Workload, device="cuda:0", layers: Optional[List[int]] = None,
+                 b_scale: float = 0.1, copies: int = 1):
+        import torch
+        self.wl = wl
+        self.device = torch.device(device)
+        self.layers = list(range(wl.layers)) if layers is None else list(layers)
+        self.copies = copies
+        dt = wl.dtype
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        self.code = RP_BF16 if dt == "bf16" else RP_F32
+        up = lambda a: to_device(a, dt, self.device)  # noqa: E731
+        self.x_router = up(datagen.router_input(wl))
+        self.Wg = up(datagen.router_weight(wl))
+        # per layer: inputs by name and weights by projection (copy 0)
+        self.inputs: Dict[Tuple[int, str], object] = {}
+        self.weights: List[Dict[Tuple[int, str], DevProj]] = [dict()]
+        for l in self.layers:
+            for g in wl.groups:
+                if (l, g.x_name) not in self.inputs:
+                    self.inputs[(l, g.x_name)] = up(datagen.layer_input(wl, l, g.x_name))
+                for p in g.projs:
+                    w = datagen.proj_weights(wl, l, g, p, b_scale=b_scale)
+                    self.weights[0][(l, p)] = DevProj(up(w.W0), up(w.A), up(w.B))
+                    del w
+        for c in range(1, copies):
+            self.weights.append({key: DevProj(v.W0.clone(), v.A.clone(), v.B.clone())
+                                 for key, v in self.weights[0].items()})
+        T, k, E = wl.T, wl.k, wl.E
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=self.device)
+        self.topk_gate = torch.empty((T, k), dtype=torch.float32, device=self.device)
+        self.seg_offsets = torch.empty(E + 1, dtype=torch.int32, device=self.device)
+        self.pair_perm = torch.empty(max(1, T * k), dtype=torch.int32, device=self.device)
+        self.seg_ws = torch.zeros(segment_workspace_size(T, k, E), dtype=torch.uint8, device=self.device)
+        # the choice the projections use: the router's, or a forced (Zipf) one
+        self.sel_idx, self.sel_gate = self.topk_idx, self.topk_gate
+        if wl.assignment == "zipf":
+            fi, fg = datagen.zipf_assignment(wl)
+            self.sel_idx = torch.from_numpy(fi).to(self.device)
+            self.sel_gate = torch.from_numpy(fg).to(self.device)
+        self.outputs: Dict[Tuple[int, str], object] = {}
+        ws_bytes = 0
+        for g in wl.groups:
+            ws_bytes = max(ws_bytes, sgmm_workspace_size(len(g.projs), T, g.d_in, g.d_out * len(g.projs), E,
+                                                         wl.r, k, self.code))
+            for l in self.layers:
+                for p in g.projs:
+                    self.outputs[(l, p)] = torch.empty((T, g.d_out), dtype=tdt, device=self.device)
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.step_count = 0
+
+    # -- the hot path --------------------------------------------------------
+    def route(self, stream=None):
+        wl = self.wl
+        # with a forced assignment the router still runs (its cost stays in the
+        # step) but the segments follow the forced choice
+        rp_pregate(self.x_router, self.Wg, wl.k, self.topk_idx, self.topk_gate, stream=stream)
+        rp_segment(self.sel_idx, wl.E, self.seg_offsets, self.pair_perm, ws=self.seg_ws, stream=stream)
+
+    def project(self, copy: int = 0, k: Optional[int] = None, stream=None):
+        wl = self.wl
+        kk = wl.k if k is None else k
+        W = self.weights[copy]
+        for l in self.layers:
+            for g in wl.groups:
+                x = self.inputs[(l, g.x_name)]
+                projs = [(W[(l, p)].W0, W[(l, p)].A, W[(l, p)].B, self.outputs[(l, p)]) for p in g.projs]
+                rp_sgmm_fused(projs, x, wl.E, wl.r, kk, self.sel_idx, self.sel_gate, self.seg_offsets,
+                              self.pair_perm, ws=self.ws, stream=stream)
+
+    def step(self, stream=None):
+        self.route(stream)
+        self.project(self.step_count % self.copies, stream=stream)
+        self.step_count += 1
+
+    # -- accounting ------------------------------------------------------------
+    def algorithmic_bytes(self, n_touched: int, k: Optional[int] = None) -> int:
+        """Bytes the method must move per step: every W0 once, the touched
+        adapters' A and B once, each distinct input and every output once, the
+        router weight, and the small routing arrays."""
+        wl = self.wl
+        kk = wl.k if k is None else k
+        bpe = 2 if wl.dtype == "bf16" else 4
+        b = 0
+        for l in self.layers:
+            names = set()
+            for g in wl.groups:
+                for _ in g.projs:
+                    b += g.d_out * g.d_in * bpe
+                    if kk > 0:
+                        b += n_touched * wl.r * (g.d_in + g.d_out) * bpe
+                    b += wl.T * g.d_out * bpe
+                if g.x_name not in names:
+                    names.add(g.x_name)
+                    b += wl.T * g.d_in * bpe
+        b += wl.d * wl.E * bpe + wl.T * wl.d * bpe  # router weight and router input
+        b += wl.T * wl.k * 8 + (wl.E + 1) * 4 + wl.T * wl.k * 4  # idx, gate, offsets, perm
+        return b
+
+    def algorithmic_flops(self, k: Optional[int] = None) -> int:
+        wl = self.wl
+        kk = wl.k if k is None else k
+        f = 2 * wl.T * wl.d * wl.E
+        for _ in self.layers:
+            for g in wl.groups:
+                for _ in g.projs:
+                    f += 2 * wl.T * g.d_in * g.d_out + 2 * wl.T * kk * wl.r * (g.d_in + g.d_out)
+        return f

@@ -64,6 +64,6 @@ def make(name, seed, T, d_in, d_out, E, r, k, dtype, integer_range, tie_cols=Non
 if __name__ == "__main__":
     make("exact_int_top1_bf16", 1, T=8, d_in=32, d_out=24, E=4, r=8, k=1, dtype="bf16",
          integer_range=2, tie_cols=(1, 3))
-    make("exact_int_top1_f32", 2, T=10, d_in=24, d_out=40, E=5, r=4, k=1, dtype="f32",
+    make("exact_int_top1_f32", 2, T=10, d_in=24, d_out=40, E=5, r=8, k=1, dtype="f32",
          integer_range=3, tie_cols=(0, 4))
-    make("top2_bf16", 3, T=6, d_in=16, d_out=20, E=6, r=4, k=2, dtype="bf16", integer_range=None)
+    make("top2_bf16", 3, T=6, d_in=16, d_out=24, E=6, r=8, k=2, dtype="bf16", integer_range=None)

@@ -1,0 +1,155 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_pregate_amd as rp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rank_pregate.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rp.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = rp.lib()
+    names = _declared()
+    assert set(names) == set(rp.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert rp.abi_version() == 1
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(rp, "_lib", None)
+    monkeypatch.setattr(rp, "LIB_PATH", "/nonexistent/librank_pregate.so")
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        rp.lib()
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+def _pregate(**kw):
+    a = dict(x=FAKE, T=4, d_in=64, ld_x=64, Wg=FAKE, E=8, k=2, dt=rp.RP_BF16, idx=FAKE, gate=FAKE, logits=None,
+             stream=None)
+    a.update(kw)
+    return rp.lib().rp_pregate(a["x"], a["T"], a["d_in"], a["ld_x"], a["Wg"], a["E"], a["k"], a["dt"], a["idx"],
+                               a["gate"], a["logits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), rp.RP_ERR_INVALID_ARG),
+    (dict(k=9, E=16), rp.RP_ERR_INVALID_ARG),
+    (dict(k=3, E=2), rp.RP_ERR_INVALID_ARG),
+    (dict(E=0), rp.RP_ERR_INVALID_ARG),
+    (dict(E=1025), rp.RP_ERR_INVALID_ARG),
+    (dict(T=-1), rp.RP_ERR_INVALID_ARG),
+    (dict(d_in=60, ld_x=64), rp.RP_ERR_INVALID_ARG),
+    (dict(ld_x=60), rp.RP_ERR_INVALID_ARG),
+    (dict(x=None), rp.RP_ERR_INVALID_ARG),
+    (dict(Wg=FAKE + 8), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),
+    (dict(dt=7), rp.RP_ERR_INVALID_ARG),
+])
+def test_pregate_rejects(kw, status):
+    assert _pregate(**kw) == status
+    assert rp.last_error()
+
+
+def test_pregate_T0_is_noop():
+    assert _pregate(T=0, x=None, idx=None, gate=None) == rp.RP_OK
+
+
+def _segment(**kw):
+    a = dict(idx=FAKE, T=4, k=2, E=8, off=FAKE, perm=FAKE, ws=FAKE, ws_bytes=256)
+    a.update(kw)
+    return rp.lib().rp_segment(a["idx"], a["T"], a["k"], a["E"], a["off"], a["perm"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9), rp.RP_ERR_INVALID_ARG),
+    (dict(E=0), rp.RP_ERR_INVALID_ARG),
+    (dict(off=None), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),
+    (dict(ws=None), rp.RP_ERR_INVALID_ARG),
+    (dict(ws_bytes=3), rp.RP_ERR_WORKSPACE),
+    (dict(off=FAKE + 2), rp.RP_ERR_INVALID_ARG),
+])
+def test_segment_rejects(kw, status):
+    assert _segment(**kw) == status
+
+
+def _sgmm(projs=None, **kw):
+    a = dict(n_proj=1, x=FAKE, T=32, d_in=256, ld_x=256, E=8, r=16, k=2, idx=FAKE, gate=FAKE, off=FAKE, perm=FAKE,
+             dt=rp.RP_BF16, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    if projs is None:
+        projs = [rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128)]
+    arr = (rp.RpProj * max(1, len(projs)))(*projs)
+    return rp.lib().rp_sgmm_fused(arr, a["n_proj"], a["x"], a["T"], a["d_in"], a["ld_x"], a["E"], a["r"], a["k"],
+                                  a["idx"], a["gate"], a["off"], a["perm"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_proj=0), rp.RP_ERR_INVALID_ARG),
+    (dict(n_proj=5), rp.RP_ERR_INVALID_ARG),
+    (dict(r=12), rp.RP_ERR_UNSUPPORTED),
+    (dict(r=256), rp.RP_ERR_UNSUPPORTED),
+    (dict(k=9), rp.RP_ERR_INVALID_ARG),
+    (dict(k=3, E=2), rp.RP_ERR_INVALID_ARG),
+    (dict(E=2000), rp.RP_ERR_INVALID_ARG),
+    (dict(d_in=100, ld_x=104), rp.RP_ERR_INVALID_ARG),
+    (dict(ld_x=200), rp.RP_ERR_INVALID_ARG),
+    (dict(x=FAKE + 4), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),
+    (dict(ws=None), rp.RP_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), rp.RP_ERR_WORKSPACE),
+    (dict(T=-5), rp.RP_ERR_INVALID_ARG),
+])
+def test_sgmm_rejects(kw, status):
+    assert _sgmm(**kw) == status
+    assert rp.last_error()
+
+
+@pytest.mark.parametrize("proj,status", [
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 100, 104), rp.RP_ERR_INVALID_ARG),   # d_out % 8
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 120), rp.RP_ERR_INVALID_ARG),   # ld_y < d_out
+    (rp.RpProj(None, FAKE, FAKE, FAKE, 128, 128), rp.RP_ERR_INVALID_ARG),   # null W0
+    (rp.RpProj(FAKE, FAKE + 2, FAKE, FAKE, 128, 128), rp.RP_ERR_INVALID_ARG),  # misaligned A
+])
+def test_sgmm_rejects_projection(proj, status):
+    assert _sgmm(projs=[proj]) == status
+
+
+def test_sgmm_T0_is_noop():
+    assert _sgmm(T=0, x=None, ws=None) == rp.RP_OK
+
+
+def test_sgmm_k0_needs_no_adapter_buffers_in_validation():
+    # k = 0 with null routing buffers passes validation up to the workspace check
+    assert _sgmm(k=0, idx=None, gate=None, off=None, perm=None, ws=None) == rp.RP_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    L = rp.lib()
+    assert L.rp_segment_workspace_size(32, 2, 8) >= 4
+    b = L.rp_sgmm_workspace_size(3, 32, 4096, 3 * 4096, 8, 16, 2, rp.RP_BF16)
+    assert b >= 3 * 32 * 2 * 16 * 4 and b % 256 == 0
+    assert L.rp_sgmm_workspace_size(3, 32, 4096, 3 * 4096, 8, 12, 2, rp.RP_BF16) == 0
+    assert L.rp_sgmm_workspace_size(0, 32, 4096, 4096, 8, 16, 2, rp.RP_BF16) == 0
+    # prefill sizes need no split-K partials: only the rank-r intermediates
+    big = L.rp_sgmm_workspace_size(2, 4096, 4096, 22016, 32, 64, 1, rp.RP_BF16)
+    assert big >= 2 * 4096 * 64 * 4

@@ -1,0 +1,412 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (AdaFuse technical summary §2.A-§2.B defines what is computed):
+  * topk_idx, seg_offsets, pair_perm: bit-exact (ties to the lowest index).
+    The router decides in fp32 on both sides; a token whose two competing
+    logits lie within the fp32 accumulation bound of each other may choose
+    either way and is reported (the seeded workloads have none).
+  * topk_gate: |dg| <= 1e-5 (fp32 softmax of logits carrying the fp32
+    accumulation error; 0.25 * logit error + a few ulp).
+  * y, fp32: max|y - ref| <= 1e-4 max|ref| and |y - ref| <= 1e-4 |ref| where
+    |ref| >= 1e-2 max|ref|.
+  * y, bf16: max|y - ref| <= 2e-2 max|ref| (per projection output).
+  * exact-integer inputs: bit-exact.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from rank_pregate_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rank_pregate_amd as rp  # noqa: E402
+from rank_pregate_amd.workload import DeviceWorkload, to_device, to_host  # noqa: E402
+
+DEV = torch.device("cuda:0")
+EPS32 = 2.0 ** -24
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def widen(a, dt):
+    return oracle.widen(a, dt)
+
+
+def dl_widen(t, dt):
+    return widen(to_host(t), dt)
+
+
+def logit_bound(x64, Wg64):
+    """Worst-case fp32 accumulation error of the router sum (d terms)."""
+    d = x64.shape[1]
+    return 1.01 * d * EPS32 * (np.abs(x64) @ np.abs(Wg64)) + 1e-30
+
+
+def check_y(y_dev, ref, dt, what=""):
+    got = dl_widen(y_dev, dt)
+    m = np.abs(ref).max()
+    err = np.abs(got - ref)
+    if dt == "bf16":
+        assert err.max() <= 2e-2 * m, f"{what}: max err {err.max():.3e} > 2e-2*{m:.3e}"
+    else:
+        assert err.max() <= 1e-4 * m, f"{what}: max err {err.max():.3e} > 1e-4*{m:.3e}"
+        big = np.abs(ref) >= 1e-2 * m
+        rel = err[big] / np.abs(ref[big])
+        assert rel.max() <= 1e-4, f"{what}: max rel err {rel.max():.3e}"
+    return err.max() / m
+
+
+def compare_routing(idx_dev, gate_dev, logits_dev, x64, Wg64, k):
+    """Oracle pre-gate vs device; returns the mask of tokens that agree."""
+    idx_ref, gate_ref, l_ref = oracle.pregate(x64, Wg64, k)
+    bound = logit_bound(x64, Wg64)
+    if logits_dev is not None:
+        l_dev = logits_dev.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(l_dev - l_ref) <= bound), "router logits outside the fp32 accumulation bound"
+    idx = idx_dev.cpu().numpy()
+    same = np.all(idx == idx_ref, axis=1)
+    # near ties: the k-th and (k+1)-th logits closer than twice the bound
+    srt = np.sort(l_ref, axis=1)[:, ::-1]
+    E = l_ref.shape[1]
+    near = np.zeros(len(idx), bool)
+    if k < E:
+        kth = np.take_along_axis(l_ref, idx_ref[:, k - 1:k].astype(np.int64), 1)[:, 0]
+        gap = kth - srt[:, k]
+        bmax = bound.max(axis=1)
+        near = gap <= 2 * bmax
+    for t in np.nonzero(~same)[0]:
+        assert near[t], f"token {t}: idx {idx[t]} vs oracle {idx_ref[t]} with a clear margin"
+        # the device's choice must be a valid top-k within the bound
+        chosen = l_ref[t, idx[t]]
+        rest = np.delete(l_ref[t], idx[t])
+        assert chosen.min() >= rest.max() - 2 * bound[t].max()
+    if (~same).any():
+        say(f"near-tie tokens choosing differently: {int((~same).sum())}")
+    g = gate_dev.cpu().numpy().astype(np.float64)
+    assert np.abs(g[same] - gate_ref[same]).max(initial=0) <= 1e-5
+    return same, idx_ref, gate_ref
+
+
+# --------------------------------------------------------------------------- pre-gating
+
+@pytest.mark.parametrize("name", datagen.WORKLOAD_ORDER)
+def test_pregate_workload(name):
+    say("pregate", name)
+    wl = datagen.WORKLOADS[name]
+    x, Wg = datagen.router_input(wl), datagen.router_weight(wl)
+    xd, Wgd = to_device(x, wl.dtype, DEV), to_device(Wg, wl.dtype, DEV)
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=DEV)
+    idx, gate = rp.pregate(xd, Wgd, wl.k, logits=logits)
+    torch.cuda.synchronize()
+    same, _, _ = compare_routing(idx, gate, logits, widen(x, wl.dtype), widen(Wg, wl.dtype), wl.k)
+    assert same.all(), "seeded workloads are chosen free of near ties"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d,E,k", [(7, 64, 6, 2), (65, 128, 200, 3), (16, 256, 1024, 8), (3, 32, 1, 1)])
+def test_pregate_exact_ties(dt, T, d, E, k):
+    """Integer inputs give exact logits; duplicated router columns tie exactly -> lowest index."""
+    say("pregate ties", dt, T, d, E, k)
+    rng = np.random.default_rng(T * 1000 + E)
+    x = rng.integers(-2, 3, (T, d)).astype(np.float32)
+    Wg = rng.integers(-2, 3, (d, E)).astype(np.float32)
+    if E >= 4:
+        Wg[:, E - 1] = Wg[:, 0]
+        Wg[:, E // 2] = Wg[:, 1]
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a)
+    xd, Wgd = to_device(conv(x), dt, DEV), to_device(conv(Wg), dt, DEV)
+    idx, gate = rp.pregate(xd, Wgd, k)
+    torch.cuda.synchronize()
+    idx_ref, gate_ref, _ = oracle.pregate(x.astype(np.float64), Wg.astype(np.float64), k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.abs(gate.cpu().numpy() - gate_ref).max() <= 1e-6
+
+
+# --------------------------------------------------------------------------- segmentation
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (32, 2, 8), (64, 1, 4), (256, 2, 256), (4096, 1, 32),
+                                   (300, 3, 1024), (5000, 8, 64), (17, 2, 1000), (0, 2, 8), (20, 0, 8)])
+def test_segment(T, k, E):
+    say("segment", T, k, E)
+    idx = datagen.uniform_indices(T + 7 * k + E, T, E, k) if k > 0 else np.zeros((T, 0), np.int32)
+    if T >= 10 and E > 4 and k > 0:
+        idx[: T // 2, 0] = 3  # a big segment plus many empty ones
+        for t in range(T // 2):
+            if k > 1 and 3 in idx[t, 1:]:
+                idx[t, 1:][idx[t, 1:] == 3] = 4 if idx[t, 0] != 4 else 5
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    idx_d = torch.from_numpy(idx).to(DEV) if idx.size else torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    off, perm = rp.segment(idx_d, E)
+    torch.cuda.synchronize()
+    off_ref, perm_ref = oracle.segment(idx, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), off_ref)
+    if T * k:
+        np.testing.assert_array_equal(perm.cpu().numpy()[: T * k], perm_ref)
+
+
+def test_segment_counts_out_of_range():
+    say("segment out-of-range")
+    idx = np.array([[0, 5], [9, 1], [-1, 2], [3, 4]], np.int32)
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    off, perm = rp.segment(torch.from_numpy(idx).to(DEV), 6, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    valid = [(p, e) for p, e in enumerate(idx.ravel().tolist()) if 0 <= e < 6]
+    want_perm = [p for e in range(6) for p, ee in valid if ee == e]
+    assert off.cpu().numpy()[-1] == len(valid)
+    assert perm.cpu().numpy()[: len(valid)].tolist() == want_perm
+
+
+# --------------------------------------------------------------------------- fused projection
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+@pytest.mark.parametrize("name", ["exact_int_top1_bf16.json", "exact_int_top1_f32.json", "top2_bf16.json"])
+def test_golden_end_to_end(name):
+    """Golden fixtures (expected values by brute force): router, segments and projection."""
+    say("golden", name)
+    g = _golden(name)
+    dt = g["dtype"]
+    npdt = np.uint16 if dt == "bf16" else np.float32
+    inp = {n: np.array(g["inputs"][n], dtype=npdt) for n in ("x", "Wg", "W0", "A", "B")}
+    dev = {n: to_device(v, dt, DEV) for n, v in inp.items()}
+    idx, gate = rp.pregate(dev["x"], dev["Wg"], g["k"])
+    off, perm = rp.segment(idx, g["E"])
+    (y,) = rp.sgmm_fused([(dev["W0"], dev["A"], dev["B"])], dev["x"], g["E"], g["r"], g["k"], idx, gate, off, perm)
+    torch.cuda.synchronize()
+    exp = g["expected"]
+    assert idx.cpu().numpy().tolist() == exp["topk_idx"]
+    assert off.cpu().numpy().tolist() == exp["seg_offsets"]
+    assert perm.cpu().numpy()[: g["T"] * g["k"]].tolist() == exp["pair_perm"]
+    ref = np.array(exp["y"], dtype=np.float64)
+    if g["exact"]:
+        if dt == "bf16":
+            want = datagen.f32_to_bf16_bits(ref.astype(np.float32))  # exact ints, rounded once
+            np.testing.assert_array_equal(to_host(y), want)
+        else:
+            np.testing.assert_array_equal(to_host(y).astype(np.float64), ref)
+    else:
+        check_y(y, ref, dt, name)
+
+
+def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B=False, idx=None, gate=None):
+    """Random single-group case through route-free inputs; returns max error ratio."""
+    rng = np.random.default_rng(seed)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    projs, hw = [], []
+    for d_out in d_outs:
+        W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        B = np.zeros((E, d_out, r), np.float32) if zero_B else \
+            rng.standard_normal((E, d_out, r), dtype=np.float32) * np.float32(b_scale / np.sqrt(r))
+        B = conv(B)
+        hw.append((W0, A, B))
+        projs.append((to_device(W0, dt, DEV), to_device(A, dt, DEV), to_device(B, dt, DEV)))
+    if idx is None:
+        idx = datagen.uniform_indices(seed, T, E, k)
+    if gate is None:
+        gate = datagen.random_gates(seed, T, k)
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
+    gate_d = torch.from_numpy(np.ascontiguousarray(gate, np.float32)).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    xd = to_device(x, dt, DEV)
+    ys = rp.sgmm_fused(projs, xd, E, r, k, idx_d, gate_d, off, perm)
+    torch.cuda.synchronize()
+    x64 = widen(x, dt)
+    worst = 0.0
+    for (W0, A, B), y in zip(hw, ys):
+        ref = oracle.sgmm(x64, widen(W0, dt), widen(A, dt), widen(B, dt), idx, gate.astype(np.float64))
+        worst = max(worst, check_y(y, ref, dt, f"T={T} d_in={d_in} d_out={W0.shape[0]}"))
+    return worst, ys
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (1, 64, [64], 4, 8, 1),            # single token
+    (33, 72, [200], 5, 16, 2),         # ragged T, d_in % 16 == 8, d_out not a tile multiple
+    (64, 256, [128, 96], 16, 8, 2),    # two projections, different widths
+    (100, 128, [64, 64, 64], 9, 32, 3),
+    (256, 512, [256], 256, 16, 2),     # many adapters, 1-3 tokens per segment
+    (257, 256, [136], 7, 64, 1),       # first prefill size, ragged
+    (300, 264, [128, 40], 12, 128, 2),  # prefill, k=2, r=128
+    (1000, 512, [512], 32, 64, 1),
+])
+def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
+    say("projection", dt, T, d_in, d_outs, E, r, k)
+    _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed=T + d_in + E)
+
+
+@pytest.mark.parametrize("T", [32, 300])
+def test_projection_zero_B_is_base(T):
+    say("zero B", T)
+    _, ys = _run_projection_case(T, 256, [128], 8, 16, 2, "bf16", seed=5, zero_B=True)
+    _, ys0 = _run_projection_case(T, 256, [128], 8, 16, 0, "bf16", seed=5)
+    assert torch.equal(ys[0], ys0[0]), "B = 0 must reproduce the base projection bit for bit"
+
+
+@pytest.mark.parametrize("T", [48, 512])
+def test_projection_single_adapter_merged(T):
+    """Every token on one adapter with gate 1: equals x (W0 + B A)^T (merged weight formed on the host)."""
+    say("merged weight", T)
+    d_in, d_out, E, r = 128, 96, 3, 16
+    idx = np.full((T, 1), 2, np.int32)
+    gate = np.ones((T, 1), np.float32)
+    rng = np.random.default_rng(11)
+    conv = datagen.f32_to_bf16_bits
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) * np.float32(0.1))
+    A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) * np.float32(0.1))
+    B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) * np.float32(0.3))
+    dv = [to_device(a, "bf16", DEV) for a in (x, W0, A, B)]
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    (y,) = rp.sgmm_fused([(dv[1], dv[2], dv[3])], dv[0], E, r, 1, idx_d, gate_d, off, perm)
+    torch.cuda.synchronize()
+    x64, W64, A64, B64 = (widen(a, "bf16") for a in (x, W0, A, B))
+    merged = W64 + B64[2] @ A64[2]
+    check_y(y, x64 @ merged.T, "bf16", "merged")
+
+
+@pytest.mark.parametrize("T", [64, 512])
+def test_token_permutation(T):
+    say("token permutation", T)
+    rng = np.random.default_rng(3)
+    p = rng.permutation(T)
+    d_in, d_out, E, r, k = 256, 128, 8, 16, 2
+    idx = datagen.uniform_indices(1, T, E, k)
+    gate = datagen.random_gates(1, T, k)
+    conv = datagen.f32_to_bf16_bits
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(16))
+    A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(16))
+    B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) / np.float32(4))
+    W = [to_device(a, "bf16", DEV) for a in (W0, A, B)]
+
+    def run(xx, ii, gg):
+        ii_d, gg_d = torch.from_numpy(np.ascontiguousarray(ii)).to(DEV), torch.from_numpy(np.ascontiguousarray(gg)).to(DEV)
+        off, perm = rp.segment(ii_d, E)
+        (y,) = rp.sgmm_fused([tuple(W)], to_device(np.ascontiguousarray(xx), "bf16", DEV), E, r, k, ii_d, gg_d, off, perm)
+        torch.cuda.synchronize()
+        return y
+
+    y = run(x, idx, gate)
+    yp = run(x[p], idx[p], gate[p])
+    ref = oracle.sgmm(widen(x, "bf16"), widen(W0, "bf16"), widen(A, "bf16"), widen(B, "bf16"), idx, gate.astype(np.float64))
+    check_y(yp, ref[p], "bf16", "permuted")
+    bit = np.array_equal(to_host(yp), to_host(y)[p])
+    say(f"permuted output bit-identical: {bit}")
+
+
+def test_adapter_sensitivity():
+    """B without the 0.1 factor: a wrong adapter or gate could not hide under the bf16 tolerance."""
+    say("adapter sensitivity")
+    T, d, E, r, k = 32, 4096, 8, 16, 2
+    idx = datagen.uniform_indices(9, T, E, k)
+    gate = datagen.random_gates(9, T, k)
+    worst, ys = _run_projection_case(T, d, [d], E, r, k, "bf16", seed=9, b_scale=1.0, idx=idx, gate=gate)
+    assert worst < 2e-2
+    # the oracle with the two slots' gates swapped differs from the device output beyond the tolerance
+    rng = np.random.default_rng(9)
+    x = datagen.f32_to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    W0 = datagen.f32_to_bf16_bits(rng.standard_normal((d, d), dtype=np.float32) / np.float32(np.sqrt(d)))
+    A = datagen.f32_to_bf16_bits(rng.standard_normal((E, r, d), dtype=np.float32) / np.float32(np.sqrt(d)))
+    B = datagen.f32_to_bf16_bits(rng.standard_normal((E, d, r), dtype=np.float32) * np.float32(1.0 / np.sqrt(r)))
+    wrong = oracle.sgmm(widen(x, "bf16"), widen(W0, "bf16"), widen(A, "bf16"), widen(B, "bf16"), idx,
+                        gate[:, ::-1].astype(np.float64))
+    got = dl_widen(ys[0], "bf16")
+    assert np.abs(got - wrong).max() > 2e-2 * np.abs(wrong).max()
+
+
+def test_determinism_repeat():
+    say("determinism")
+    wl = datagen.WORKLOADS["decode_qkvo"]
+    dw = DeviceWorkload(wl, DEV)
+    outs = []
+    for _ in range(10):
+        dw.step()
+        torch.cuda.synchronize()
+        outs.append({key: to_host(v).copy() for key, v in dw.outputs.items()})
+    for o in outs[1:]:
+        for key in o:
+            assert np.array_equal(o[key], outs[0][key]), key
+
+
+# --------------------------------------------------------------------------- the workloads end to end
+
+def _oracle_routing(wl):
+    x64 = widen(datagen.router_input(wl), wl.dtype)
+    Wg64 = widen(datagen.router_weight(wl), wl.dtype)
+    if wl.assignment == "zipf":
+        idx, gate = datagen.zipf_assignment(wl)
+        return idx, gate.astype(np.float64)
+    idx, gate, _ = oracle.pregate(x64, Wg64, wl.k)
+    return idx, gate
+
+
+@pytest.mark.parametrize("name,layers,tokens", [
+    ("toy_f32", None, None),
+    ("decode_qkvo", None, None),
+    ("decode_many_adapters", None, None),
+    ("prefill_mlp", None, "sample"),
+    ("decode_32layer", [0, 15, 31], None),
+])
+def test_workload_end_to_end(name, layers, tokens):
+    """Full-size workloads in the launch configuration the bench times.  The
+    32-layer step is checked on three of its layers (each layer is the same
+    four launches on its own seeded weights)."""
+    wl = datagen.WORKLOADS[name]
+    say("workload", name, "generating + uploading")
+    dw = DeviceWorkload(wl, DEV, layers=layers)
+    dw.step()
+    torch.cuda.synchronize()
+    say("workload", name, "ran; checking")
+    idx_ref, gate_ref = _oracle_routing(wl)
+    if wl.assignment == "router":
+        same, _, _ = compare_routing(dw.topk_idx, dw.topk_gate, None, widen(datagen.router_input(wl), wl.dtype),
+                                     widen(datagen.router_weight(wl), wl.dtype), wl.k)
+        assert same.all()
+    off_ref, perm_ref = oracle.segment(idx_ref, wl.E)
+    np.testing.assert_array_equal(dw.seg_offsets.cpu().numpy(), off_ref)
+    np.testing.assert_array_equal(dw.pair_perm.cpu().numpy()[: wl.T * wl.k], perm_ref)
+    check_layers = dw.layers
+    if tokens == "sample":
+        rng = np.random.default_rng(0)
+        # every segment's first and last token plus a random sample
+        toks = set(rng.choice(wl.T, 96, replace=False).tolist())
+        for e in range(wl.E):
+            if off_ref[e + 1] > off_ref[e]:
+                toks.add(int(perm_ref[off_ref[e]]) // wl.k)
+                toks.add(int(perm_ref[off_ref[e + 1] - 1]) // wl.k)
+        toks = sorted(toks)
+    else:
+        toks = None
+    for l in check_layers:
+        for g in wl.groups:
+            x64 = widen(datagen.layer_input(wl, l, g.x_name), wl.dtype)
+            for p in g.projs:
+                w = datagen.proj_weights(wl, l, g, p)
+                ref = oracle.sgmm(x64, widen(w.W0, wl.dtype), widen(w.A, wl.dtype), widen(w.B, wl.dtype),
+                                  idx_ref, gate_ref, tokens=toks)
+                y = dw.outputs[(l, p)]
+                if toks is not None:
+                    y = y[torch.tensor(toks, device=DEV)]
+                r = check_y(y, ref, wl.dtype, f"{name} layer {l} {p}")
+                say(f"{name} L{l} {p}: max|err|/max|ref| = {r:.2e}")
