@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librank_pregate.so")
 
-SOURCES = ["api.cpp", "pregate.hip", "segment.hip", "sgmm.hip", "util.hip"]
+SOURCES = ["api.cpp", "pregate.hip", "segment.hip", "sgmm_plan.cpp", "sgmm_decode.hip", "sgmm_prefill.hip",
+           "sgmm_f32.hip", "util.hip"]
 ARCH = "gfx950"
 
 

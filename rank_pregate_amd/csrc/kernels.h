@@ -58,21 +58,26 @@ struct SgmmArgs {
   // workspace views
   float* u;          // [n_proj][T*k][r] gated rank-r intermediates
   float* partial;    // split-K partial tiles (decode path)
-  int* counters;     // per output tile arrival counters (decode path)
+  int* counters;     // reserved counter region: control words, then per-tile arrival counters
   int n_tiles;       // output-row tiles over all projections
   int S;             // K splits per output tile (decode path)
 };
 
 // Which kernel family serves a call, and the workspace it needs.
 struct SgmmPlan {
-  int path;          // 0: fp32 VALU, 1: bf16 decode (T <= 256), 2: bf16 prefill
+  int path;          // 0: fp32 VALU, 1: bf16 decode (T <= 64), 2: bf16 prefill
   int tile_rows;     // output rows per tile
   int n_tiles;
   int S;
-  int t_pad;         // tokens padded to the decode tile width
+  int t_pad;         // tokens padded to the decode token tiles
   size_t off_u, off_partial, off_counters, bytes;
 };
 SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu);
+int decode_mt(int T);       // 16-token tiles of the decode kernel
+int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
+hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
+hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
+hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
                                   int k);
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);

@@ -1,0 +1,178 @@
+// Device helpers shared by the fused SGMM kernels (decode and prefill).
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace rp {
+
+// Control words at the start of the workspace's reserved counter region.
+enum CtlWord { kCtlTicket = 0, kCtlShrinkDone = 1, kCtlFinished = 2, kCtlWaitOverflow = 3, kCtlTiles = 16 };
+
+// Projection that owns output-row tile `tile` of the packed row space.
+__device__ __forceinline__ int proj_of_tile(const SgmmArgs& a, int tile) {
+  int p = 0;
+  if (a.n_proj > 1 && tile >= a.proj[1].tile_begin) p = 1;
+  if (a.n_proj > 2 && tile >= a.proj[2].tile_begin) p = 2;
+  if (a.n_proj > 3 && tile >= a.proj[3].tile_begin) p = 3;
+  return p;
+}
+
+// Field-wise select of projection p's descriptor (keeps the kernel argument
+// block out of private memory).
+template <typename F>
+__device__ __forceinline__ F pick4(int p, F f0, F f1, F f2, F f3) {
+  return p == 0 ? f0 : p == 1 ? f1 : p == 2 ? f2 : f3;
+}
+#define RP_PICK(a, p, field) pick4(p, a.proj[0].field, a.proj[1].field, a.proj[2].field, a.proj[3].field)
+
+__device__ __forceinline__ ProjDesc proj_at(const SgmmArgs& a, int p) {
+  ProjDesc d;
+  d.W0 = RP_PICK(a, p, W0);
+  d.A = RP_PICK(a, p, A);
+  d.B = RP_PICK(a, p, B);
+  d.y = RP_PICK(a, p, y);
+  d.d_out = RP_PICK(a, p, d_out);
+  d.ld_y = RP_PICK(a, p, ld_y);
+  d.tile_begin = RP_PICK(a, p, tile_begin);
+  return d;
+}
+
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : zero4(); }
+
+// The slot j with idx[t, j] == e, or -1.
+__device__ __forceinline__ int match_slot(const int* idx, int t, int k, int e) {
+  int js = -1;
+  for (int j = 0; j < k; ++j)
+    if (idx[t * k + j] == e) js = j;
+  return js;
+}
+
+// Gated u row chunk [c, c+8) of pair p as hi/lo bf16 operands (zero if !ok).
+__device__ __forceinline__ void u_operand(const float* u, int r, int p, int c, bool ok, uint4& hi, uint4& lo) {
+  float v[8];
+  if (ok) {
+    const float4 a = *reinterpret_cast<const float4*>(u + (size_t)p * r + c);
+    const float4 b = *reinterpret_cast<const float4*>(u + (size_t)p * r + c + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  split_hi_lo(v, hi, lo);
+}
+
+// Shrink chunks are numbered segment by segment, ceil(n_e / nch) per segment.
+// Run by one full wave; returns (segment, chunk) or segment -1 past the end.
+__device__ __forceinline__ void locate_chunk(const SgmmArgs& a, int unit, int nch, int lane, int* seg,
+                                             int* chunk) {
+  int carry = 0, fe = -1, fc = 0;
+  for (int e0 = 0; e0 < a.E; e0 += 64) {
+    const int e = e0 + lane;
+    const int n = (e < a.E) ? (a.seg_offsets[e + 1] - a.seg_offsets[e]) : 0;
+    const int c = (n + nch - 1) / nch;
+    const int incl = wave_inclusive_scan(c, lane);
+    const int excl = carry + incl - c;
+    const uint64_t m = __ballot(c > 0 && unit >= excl && unit < excl + c);
+    if (m) {
+      const int src = __ffsll((unsigned long long)m) - 1;
+      fe = e0 + src;
+      fc = unit - __shfl(excl, src, 64);
+      break;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  *seg = fe;
+  *chunk = fc;
+}
+
+// One shrink unit: u[p, :] = g_p * A_e x_t for the pairs p of chunk `chunk`
+// (16*NCT pairs) of segment e, with bf16 MFMA 16x16x32 (A_e rows as M, pairs
+// as N).  WAVES waves split d_in; their partial sums are added in wave order in
+// LDS (`red`: MTR*NCT*4*64 floats), so the result does not depend on timing.
+// Must be called by all WAVES*64 threads of the workgroup.
+template <int MTR, int NCT, int WAVES, int U>
+__device__ __forceinline__ void shrink_unit(const SgmmArgs& a, int proj, int e, int chunk, float* red) {
+  constexpr int NCH = 16 * NCT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ProjDesc pd = proj_at(a, proj);
+  const int slot0 = a.seg_offsets[e] + chunk * NCH;
+  const int slot_end = min(a.seg_offsets[e + 1], slot0 + NCH);
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const bf16_t* Ae = static_cast<const bf16_t*>(pd.A) + (size_t)e * a.r * a.d_in;
+  const int lr = lane & 15, kg = lane >> 4;
+
+  const bf16_t* xp[NCT];
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt) {
+    const int slot = min(slot0 + nt * 16 + lr, slot_end - 1);
+    xp[nt] = x + (size_t)(a.pair_perm[slot] / a.k) * a.ld_x;
+  }
+  const bf16_t* ap[MTR];
+  bool aok[MTR];
+#pragma unroll
+  for (int mt = 0; mt < MTR; ++mt) {
+    const int c = mt * 16 + lr;
+    aok[mt] = c < a.r;
+    ap[mt] = Ae + (size_t)min(c, a.r - 1) * a.d_in;
+  }
+
+  const int nsteps = (a.d_in + 31) >> 5;
+  const int sb = nsteps * wave / WAVES, se = nsteps * (wave + 1) / WAVES;
+  f32x4_t acc[MTR][NCT];
+#pragma unroll
+  for (int mt = 0; mt < MTR; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NCT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = sb; s < se; s += U) {
+    uint4 av[U][MTR], bv[U][NCT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s + u) * 32 + kg * 8;
+      const bool ok = (s + u < se) && (k < a.d_in);
+      const int kc = min(k, a.d_in - 8);
+#pragma unroll
+      for (int mt = 0; mt < MTR; ++mt) av[u][mt] = sel4(ok && aok[mt], ld16(ap[mt] + kc));
+#pragma unroll
+      for (int nt = 0; nt < NCT; ++nt) bv[u][nt] = sel4(ok, ld16(xp[nt] + kc));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MTR; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) acc[mt][nt] = mfma16(av[u][mt], bv[u][nt], acc[mt][nt]);
+  }
+
+  // fixed-order sum over waves (wave 0 first), accumulated in LDS
+  for (int w = 0; w < WAVES; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mt = 0; mt < MTR; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float* dst = red + ((mt * NCT + nt) * 4 + v) * 64 + lane;
+            *dst = (w == 0) ? acc[mt][nt][v] : *dst + acc[mt][nt][v];
+          }
+    }
+    __syncthreads();
+  }
+
+  // D layout: lane -> pair lane%16, rank row 4*(lane/16)+v
+  float* u_out = a.u + (size_t)proj * a.T * a.k * a.r;
+  for (int q = tid; q < MTR * NCT * 4 * 64; q += WAVES * 64) {
+    const int l = q & 63, f = q >> 6;
+    const int v = f & 3, nt = (f >> 2) % NCT, mt = (f >> 2) / NCT;
+    const int slot = slot0 + nt * 16 + (l & 15);
+    const int c = mt * 16 + 4 * (l >> 4) + v;
+    if (slot < slot_end && c < a.r) {
+      const int p = a.pair_perm[slot];
+      u_out[(size_t)p * a.r + c] = a.topk_gate[p] * red[q];
+    }
+  }
+}
+
+}  // namespace rp
