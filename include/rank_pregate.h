@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 1
+#define RP_ABI_VERSION 2
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
 #define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call */
@@ -54,12 +54,22 @@ typedef enum {
 
 typedef enum { RP_F32 = 0, RP_BF16 = 1 } rp_dtype;
 
+/* Storage order of a backbone weight W0.
+ *   RP_W0_ROWS   dense row-major [d_out, d_in]
+ *   RP_W0_TILED  the order rp_pack_w0 writes (bf16 only): blocks of 16 rows x 32
+ *                columns, block (rb, cb) at element offset (rb * d_in/32 + cb) * 512;
+ *                inside a block, 64 groups of 8 consecutive columns, group g
+ *                holding row 16*rb + g%16, columns 32*cb + 8*(g/16) .. +7.
+ *                Each decode wave then streams one contiguous run of memory. */
+typedef enum { RP_W0_ROWS = 0, RP_W0_TILED = 1 } rp_w0_layout;
+
 /* One adapted projection (one linear layer with its adapter bank).
- *   W0 [d_out, d_in]     backbone weight, dense (leading dimension d_in)
+ *   W0 [d_out, d_in]     backbone weight, in the storage order w0_layout names
  *   A  [E, r, d_in]      adapter down-projections, dense, one block per adapter
  *   B  [E, d_out, r]     adapter up-projections, dense, one block per adapter
  *   y  [T, d_out]        output, leading dimension ld_y (>= d_out)
- * All four have the call's dtype.  y must not alias any input. */
+ * All four have the call's dtype.  y must not alias any input.
+ * RP_W0_TILED needs bf16, d_out % 16 == 0 and d_in % 32 == 0; reserved must be 0. */
 typedef struct {
   const void* W0;
   const void* A;
@@ -67,6 +77,8 @@ typedef struct {
   void* y;
   int64_t d_out;
   int64_t ld_y;
+  int32_t w0_layout;
+  int32_t reserved;
 } rp_proj;
 
 /* Token-level pre-gating (AdaFuse §2.A; §2.B decoding steps 1-2).
@@ -138,6 +150,11 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
                         int64_t ld_x, int64_t E, int64_t r, int32_t k, const int32_t* topk_idx,
                         const float* topk_gate, const int32_t* seg_offsets, const int32_t* pair_perm,
                         rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Repack a dense row-major bf16 W0 [d_out, d_in] into RP_W0_TILED order (a
+ * one-time weight preparation; the result serves every later call).
+ * d_out % 16 == 0, d_in % 32 == 0, src and dst 16-byte aligned and disjoint. */
+rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream);
 
 /* Workspace bytes rp_sgmm_fused needs for these sizes; sum_d_out is the sum of
  * the projections' d_out.  Returns 0 for sizes the call would reject. */

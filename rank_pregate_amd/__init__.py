@@ -28,7 +28,8 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
                  4: "RP_ERR_HIP"}
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
-            "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+            "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
 class RankPregateError(RuntimeError):
@@ -39,7 +40,8 @@ class RankPregateError(RuntimeError):
 
 class RpProj(ctypes.Structure):
     _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("d_out", ctypes.c_int64), ("ld_y", ctypes.c_int64)]
+                ("d_out", ctypes.c_int64), ("ld_y", ctypes.c_int64), ("w0_layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,9 +69,10 @@ def lib() -> ctypes.CDLL:
     L.rp_last_error.restype = ctypes.c_char_p
     L.rp_abi_version.argtypes = []
     L.rp_abi_version.restype = ctypes.c_int
+    L.rp_pack_w0.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
     L.rp_util_stream_read.argtypes = [vp, sz, vp, vp]
     L.rp_util_copy.argtypes = [vp, vp, sz, vp]
-    for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_util_stream_read", "rp_util_copy"):
+    for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_pack_w0", "rp_util_stream_read", "rp_util_copy"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -197,8 +200,9 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
                pair_perm=None, ws=None, stream=None) -> List:
     """rp_sgmm_fused on torch tensors.
 
-    projs: up to four tuples (W0 [d_out, d_in], A [E, r, d_in], B [E, d_out, r], y [T, d_out] or None);
-    outputs that are None are allocated.  Returns the list of y tensors.
+    projs: up to four tuples (W0, A [E, r, d_in], B [E, d_out, r], y [T, d_out] or None); W0 is either
+    a dense [d_out, d_in] tensor or the 4-D tensor pack_w0 returns (tiled order).  Outputs that are
+    None are allocated.  Returns the list of y tensors.
     """
     torch = _torch()
     T, d_in = x.shape
@@ -209,14 +213,16 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
     for i, pr in enumerate(projs):
         W0, A, B = pr[0], pr[1], pr[2]
         y = pr[3] if len(pr) > 3 else None
-        d_out = W0.shape[0]
+        tiled = W0.dim() == 4
+        d_out = W0.shape[0] * 16 if tiled else W0.shape[0]
         for name, t in (("W0", W0), ("A", A), ("B", B)):
             if t is not None and (t.dtype != x.dtype or not t.is_contiguous()):
                 raise ValueError(f"projection {i}: {name} must be dense with x's dtype")
         if y is None:
             y = torch.empty((T, d_out), dtype=x.dtype, device=x.device)
         ys.append(y)
-        arr[i] = RpProj(_ptr(W0), _ptr(A), _ptr(B), _ptr(y), d_out, _rows(y, "y"))
+        arr[i] = RpProj(_ptr(W0), _ptr(A), _ptr(B), _ptr(y), d_out, _rows(y, "y"),
+                        RP_W0_TILED if tiled else RP_W0_ROWS, 0)
         sum_d_out += d_out
     if ws is None:
         ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), x.device)
@@ -225,6 +231,20 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
                              _stream(stream, x.device))
     _check(st, "rp_sgmm_fused")
     return ys
+
+
+def pack_w0(W0, out=None, stream=None):
+    """rp_pack_w0: repack a dense bf16 W0 [d_out, d_in] into the tiled order.
+
+    Returns a [d_out/16, d_in/32, 64, 8] tensor (the shape marks the layout for sgmm_fused).
+    """
+    torch = _torch()
+    d_out, d_in = W0.shape
+    if out is None:
+        out = torch.empty((d_out // 16, d_in // 32, 64, 8), dtype=W0.dtype, device=W0.device)
+    st = lib().rp_pack_w0(_ptr(W0), _ptr(out), d_out, d_in, _dtype_code(W0), _stream(stream, W0.device))
+    _check(st, "rp_pack_w0")
+    return out
 
 
 def stream_read(src, sink, stream=None) -> None:

@@ -183,6 +183,12 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
       return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: W0, A, B, y must be 16-byte aligned", p);
     if ((int64_t)q.d_out * d_in > ((int64_t)1 << 40) || E * r * std::max<int64_t>(d_in, q.d_out) > ((int64_t)1 << 40))
       return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d too large", p);
+    if (q.reserved != 0 || (q.w0_layout != RP_W0_ROWS && q.w0_layout != RP_W0_TILED))
+      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: unknown w0_layout %d / reserved %d", p,
+                  q.w0_layout, q.reserved);
+    if (q.w0_layout == RP_W0_TILED && (dt != RP_BF16 || q.d_out % 16 != 0 || d_in % 32 != 0))
+      return fail(RP_ERR_UNSUPPORTED, "rp_sgmm_fused: projection %d: the tiled W0 layout needs bf16, d_out %% 16 == 0 "
+                  "and d_in %% 32 == 0", p);
     d_out[p] = (int)q.d_out;
     sum_d_out += q.d_out;
   }
@@ -211,6 +217,7 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
     a.proj[p].d_out = (int)projs[q].d_out;
     a.proj[p].ld_y = (int)projs[q].ld_y;
     a.proj[p].tile_begin = tile;
+    a.proj[p].tiled = projs[q].w0_layout == RP_W0_TILED;
     if (p < n_proj) tile += (d_out[p] + plan.tile_rows - 1) / plan.tile_rows;
   }
   a.n_proj = n_proj;
@@ -233,6 +240,23 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
   a.S = plan.S;
   hipError_t e = rp::launch_sgmm(a, plan, rdt, stream);
   return e == hipSuccess ? RP_OK : hip_fail("rp_sgmm_fused launch", e);
+}
+
+rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream) {
+  g_last_error.clear();
+  if (dt != RP_BF16) return fail(RP_ERR_UNSUPPORTED, "rp_pack_w0: the tiled layout is bf16 only");
+  if (d_out < 16 || d_in < 32 || d_out % 16 != 0 || d_in % 32 != 0 || d_out * d_in > ((int64_t)1 << 40))
+    return fail(RP_ERR_INVALID_ARG, "rp_pack_w0: need d_out %% 16 == 0 and d_in %% 32 == 0 (got %lld x %lld)",
+                (long long)d_out, (long long)d_in);
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16))
+    return fail(RP_ERR_INVALID_ARG, "rp_pack_w0: src and dst must be non-null and 16-byte aligned");
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  const int64_t bytes = d_out * d_in * 2;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RP_ERR_INVALID_ARG, "rp_pack_w0: src and dst overlap");
+  if (d_out > kIntMax || d_in > kIntMax) return fail(RP_ERR_INVALID_ARG, "rp_pack_w0: sizes too large");
+  hipError_t e = rp::launch_pack_w0(src, dst, (int)d_out, (int)d_in, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_pack_w0 launch", e);
 }
 
 rp_status rp_util_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t stream) {

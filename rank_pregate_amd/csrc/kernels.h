@@ -43,6 +43,7 @@ struct ProjDesc {
   int d_out;
   int ld_y;
   int tile_begin;  // first output-row tile of this projection in the packed row space
+  int tiled;       // W0 in the 16x32-block order of rp_pack_w0
 };
 
 struct SgmmArgs {
@@ -82,6 +83,7 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
                                   int k);
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);
 
+hipError_t launch_pack_w0(const void* src, void* dst, int d_out, int d_in, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t n_bytes, hipStream_t s);
 

@@ -35,6 +35,7 @@ __device__ __forceinline__ ProjDesc proj_at(const SgmmArgs& a, int p) {
   d.d_out = RP_PICK(a, p, d_out);
   d.ld_y = RP_PICK(a, p, ld_y);
   d.tile_begin = RP_PICK(a, p, tile_begin);
+  d.tiled = RP_PICK(a, p, tiled);
   return d;
 }
 

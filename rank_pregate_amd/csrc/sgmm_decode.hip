@@ -138,21 +138,19 @@ __device__ void shrink_item(const SgmmArgs& a, int proj, int unit, float* red, i
 // ---------------------------------------------------------------------------
 // base item
 // ---------------------------------------------------------------------------
+// Per-wave wait for the shrink units of this launch (uniform across the wave).
 __device__ __forceinline__ void wait_shrink(int* ctl, int n_shrink) {
-  if (threadIdx.x == 0) {
-    int spins = 0;
-    while (__hip_atomic_load(&ctl[kCtlShrinkDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_shrink) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
-        atomicOr(&ctl[kCtlWaitOverflow], 1);
-        break;
-      }
+  int spins = 0;
+  while (__hip_atomic_load(&ctl[kCtlShrinkDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_shrink) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      if ((threadIdx.x & 63) == 0) atomicOr(&ctl[kCtlWaitOverflow], 1);
+      break;
     }
   }
-  __syncthreads();
 }
 
-template <int MT>
+template <int MT, bool TILED>
 __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int n_shrink, int* s_flag) {
   constexpr int TP = 16 * MT;
   constexpr int XCH = TP * kKC / 8 / kThreads;  // 16-byte x pieces per thread per chunk
@@ -164,7 +162,10 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
   const int lr = lane & 15, kg = lane >> 4;
   const int row = min(row0 + lr, pd.d_out - 1);
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
-  const bf16_t* wrow = static_cast<const bf16_t*>(pd.W0) + (size_t)row * a.d_in + kg * 8;
+  // row-major: this lane's row at column 8*kg; tiled: this wave's run of 1 KB blocks
+  const bf16_t* wrow = TILED
+      ? static_cast<const bf16_t*>(pd.W0) + (size_t)(row0 / 16) * (a.d_in / 32) * 512 + lane * 8
+      : static_cast<const bf16_t*>(pd.W0) + (size_t)row * a.d_in + kg * 8;
   const int nch = (a.d_in + kKC - 1) / kKC;
   const int cb = (int)((long long)nch * split / a.S), ce = (int)((long long)nch * (split + 1) / a.S);
 
@@ -172,13 +173,17 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // W0 k-step loads (clamped to the item's last chunk; masked past d_in)
+  // Loads in the loop are never masked (a select would force a wait right
+  // after the load): W0 addresses are clamped into the row, and whatever they
+  // read past d_in meets activations that store_x wrote as zero.
   auto load_w = [&](uint4 (&w)[kSteps], int c) {
     const int cc = min(c, ce - 1);
+    if (TILED) {
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int k = cc * kKC + st * 32;
-      w[st] = sel4(k + kg * 8 < a.d_in, ld16(wrow + min(k, a.d_in - 8 - kg * 8)));
+      for (int st = 0; st < kSteps; ++st) w[st] = ld16(wrow + (size_t)min(cc * kSteps + st, a.d_in / 32 - 1) * 512);
+    } else {
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) w[st] = ld16(wrow + min(cc * kKC + st * 32, a.d_in - 8 - kg * 8));
     }
   };
   auto load_x = [&](uint4 (&xr)[XCH], int c) {
@@ -187,16 +192,16 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
     for (int i = 0; i < XCH; ++i) {
       const int q = tid + i * kThreads;
       const int tok = q / (kKC / 8), kc = (q % (kKC / 8)) * 8;
-      const int k = cc * kKC + kc;
-      xr[i] = sel4(tok < a.T && k < a.d_in, ld16(x + (size_t)min(tok, a.T - 1) * a.ld_x + min(k, a.d_in - 8)));
+      xr[i] = ld16(x + (size_t)min(tok, a.T - 1) * a.ld_x + min(cc * kKC + kc, a.d_in - 8));
     }
   };
-  auto store_x = [&](const uint4 (&xr)[XCH], int buf) {
+  auto store_x = [&](const uint4 (&xr)[XCH], int buf, int c) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int q = tid + i * kThreads;
       const int tok = q / (kKC / 8), kc = (q % (kKC / 8)) * 8;
-      *reinterpret_cast<uint4*>(&xs[((size_t)buf * TP + tok) * kLD + kc]) = xr[i];
+      *reinterpret_cast<uint4*>(&xs[((size_t)buf * TP + tok) * kLD + kc]) =
+          sel4(tok < a.T && c < ce && c * kKC + kc < a.d_in, xr[i]);
     }
   };
   auto compute = [&](const uint4 (&w)[kSteps], int buf) {
@@ -209,14 +214,25 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
       }
   };
 
+  // the lane's tokens' choices (for the adapter deltas), read before the stream starts
+  int sel[MT][kMaxK];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = min(m * 16 + lr, a.T - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) sel[m][j] = (j < a.k && m * 16 + lr < a.T) ? a.topk_idx[t * a.k + j] : -1;
+  }
+
   if (cb < ce) {
     uint4 wA[kSteps], wB[kSteps], XA[XCH], XB[XCH];
     load_w(wA, cb);
     load_x(XA, cb);
     load_x(XB, cb + 1);
-    store_x(XA, 0);
+    store_x(XA, 0, cb);
     __syncthreads();
-    for (int c = cb; c < ce; c += 2) {
+    // chunk pairs, no exit between the two halves; an odd last chunk follows
+    int c = cb;
+    for (; c + 2 <= ce; c += 2) {
       // chunk c: x in LDS buffer 0, W0 in wA; XB holds chunk c+1
       __builtin_amdgcn_sched_barrier(0);
       load_w(wB, c + 1);
@@ -224,9 +240,8 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
       __builtin_amdgcn_sched_barrier(0);
       compute(wA, 0);
       __builtin_amdgcn_sched_barrier(0);
-      store_x(XB, 1);
+      store_x(XB, 1, c + 1);
       __syncthreads();
-      if (c + 1 >= ce) break;
       // chunk c+1: x in buffer 1, W0 in wB; XA holds chunk c+2
       __builtin_amdgcn_sched_barrier(0);
       load_w(wA, c + 2);
@@ -234,58 +249,88 @@ __device__ void base_item(const SgmmArgs& a, int item, bf16_t* xs, int* ctl, int
       __builtin_amdgcn_sched_barrier(0);
       compute(wB, 1);
       __builtin_amdgcn_sched_barrier(0);
-      store_x(XA, 0);
+      store_x(XA, 0, c + 2);
       __syncthreads();
     }
+    if (c < ce) compute(wA, 0);
   }
 
   // adapter deltas for this wave's 16 rows: adapters e = split, split + S, ...
+  // A lane's tokens chose at most k adapters, so it needs u only for its own
+  // (token, slot) pairs: those are loaded once, two slots per pass, right after
+  // the shrink units finish (one round trip of device-coherent loads), and the
+  // operand for adapter e is picked from them in registers.  The tokens'
+  // choices are read before the wait; B rows are loaded eight adapters at a
+  // time, together.
   if (a.k > 0) {
-    wait_shrink(ctl, n_shrink);
     const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
     const float* ub = a.u + (size_t)proj * a.T * a.k * a.r;
     const __amdgpu_buffer_rsrc_t ur = rsrc(ub, (uint32_t)((size_t)a.T * a.k * a.r * sizeof(float)));
-    // the lane's tokens' choices, kept in registers
-    int sel[MT][kMaxK];
+    constexpr uint32_t kOob = 0x80000000u;  // past any buffer: the load returns zero
+    constexpr int G = 8;                    // adapters per batch of B loads
+    wait_shrink(ctl, n_shrink);
+    for (int c0 = 0; c0 < a.r; c0 += 32) {
+      const int c = c0 + kg * 8;
+      const int cc = min(c, a.r - 8);
+      for (int jp = 0; jp < a.k; jp += 2) {
+        f32x4_t uu[MT][2][2];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = min(m * 16 + lr, a.T - 1);
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) sel[m][j] = (j < a.k && m * 16 + lr < a.T) ? a.topk_idx[t * a.k + j] : -1;
-    }
-    for (int e = split; e < a.E; e += a.S) {
-      int js[MT];
-      bool any = false;
+          for (int q = 0; q < 2; ++q) {
+            const int j = jp + q;
+            const bool ok = j < a.k && c < a.r && sel[m][min(j, kMaxK - 1)] >= 0;
+            const uint32_t off =
+                ok ? (uint32_t)((((size_t)(m * 16 + lr) * a.k + j) * a.r + cc) * sizeof(float)) : kOob;
+            uu[m][q][0] = ld_coh16(ur, off);
+            uu[m][q][1] = ld_coh16(ur, ok ? off + 16 : kOob);
+          }
+        for (int e0 = split; e0 < a.E; e0 += G * a.S) {
+          int js[G][MT];  // slot (jp or jp+1) of the lane's token that chose adapter e, else -1
+          bool any[G];
+          bool group = false;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        js[m] = -1;
+          for (int g = 0; g < G; ++g) {
+            const int e = e0 + g * a.S;
+            any[g] = false;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-          if (sel[m][j] == e) js[m] = j;
-        any |= __ballot(js[m] >= 0) != 0;
-      }
-      if (!any) continue;
-      const bf16_t* Be = Bm + ((size_t)e * pd.d_out + row) * a.r;
-      for (int c0 = 0; c0 < a.r; c0 += 32) {
-        const int c = c0 + kg * 8;
-        const bool cok = c < a.r;
-        const uint4 bo = sel4(cok, ld16(Be + min(c, a.r - 8)));
-        f32x4_t u0[MT], u1[MT];
+            for (int m = 0; m < MT; ++m) {
+              js[g][m] = -1;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int p = (m * 16 + lr) * a.k + max(js[m], 0);
-          const uint32_t off = (uint32_t)(((size_t)p * a.r + min(c, a.r - 8)) * sizeof(float));
-          const bool ok = cok && js[m] >= 0;
-          u0[m] = ok ? ld_coh16(ur, off) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          u1[m] = ok ? ld_coh16(ur, off + 16) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+              for (int q = 0; q < 2; ++q)
+                if (jp + q < kMaxK && sel[m][min(jp + q, kMaxK - 1)] == e) js[g][m] = q;
+              any[g] |= __ballot(js[g][m] >= 0) != 0;
+            }
+            group |= any[g];
+          }
+          if (!group) continue;
+          uint4 bo[G];
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          float v[8] = {u0[m][0], u0[m][1], u0[m][2], u0[m][3], u1[m][0], u1[m][1], u1[m][2], u1[m][3]};
-          uint4 hi, lo;
-          split_hi_lo(v, hi, lo);
-          acc[m] = mfma16(hi, bo, acc[m]);
-          acc[m] = mfma16(lo, bo, acc[m]);
+          for (int g = 0; g < G; ++g) {
+            const int e = min(e0 + g * a.S, a.E - 1);
+            bo[g] = ld16(Bm + ((size_t)e * pd.d_out + row) * a.r + cc);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (!any[g]) continue;
+            const uint4 b = sel4(c < a.r, bo[g]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              const int q = js[g][m];
+              float v[8];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                v[i] = q == 0 ? uu[m][0][0][i] : (q == 1 ? uu[m][1][0][i] : 0.f);
+                v[4 + i] = q == 0 ? uu[m][0][1][i] : (q == 1 ? uu[m][1][1][i] : 0.f);
+              }
+              uint4 hi, lo;
+              split_hi_lo(v, hi, lo);
+              acc[m] = mfma16(hi, b, acc[m]);
+              acc[m] = mfma16(lo, b, acc[m]);
+            }
+          }
         }
       }
     }
@@ -356,7 +401,12 @@ __global__ __launch_bounds__(kThreads) void decode_fused(SgmmArgs a, int units_p
     __syncthreads();
     if (tid == 0) atomicAdd(&ctl[kCtlShrinkDone], 1);
   } else {
-    base_item<MT>(a, item - n_shrink, reinterpret_cast<bf16_t*>(smem), ctl, n_shrink, &s_flag);
+    const int bi = item - n_shrink;
+    const int bp = proj_of_tile(a, bi / a.S);
+    if (RP_PICK(a, bp, tiled))
+      base_item<MT, true>(a, bi, reinterpret_cast<bf16_t*>(smem), ctl, n_shrink, &s_flag);
+    else
+      base_item<MT, false>(a, bi, reinterpret_cast<bf16_t*>(smem), ctl, n_shrink, &s_flag);
   }
   // the last workgroup to finish clears the launch's control words
   if (tid == 0) {

@@ -53,9 +53,13 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
   const bf16_t* W0 = static_cast<const bf16_t*>(pd.W0);
 
   // global -> LDS: 512 16-byte chunks per operand tile, two per thread each
+  // A (tokens): chunk q -> token row q/4, columns 8*(q%4).  B (W0 rows):
+  // row-major the same; tiled, chunk q is lane q%64 of 16-row block q/64, which
+  // holds row 16*(q/64) + (q%64)%16, columns 8*((q%64)/16).
   const bf16_t* gA[2];
   const bf16_t* gB[2];
-  int lrow[2], lk[2];
+  int lrow[2], lk[2], brow[2], bk[2];
+  const int nkb = a.d_in / 32;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = tid + i * 256;
@@ -63,7 +67,16 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
     lk[i] = (q & 3) * 8;
     const int pos = min(i0 + lrow[i], a.T - 1);
     gA[i] = x + (size_t)token_at(a, pos) * a.ld_x;
-    gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in;
+    if (pd.tiled) {
+      const int blk = min(row0 / 16 + q / 64, pd.d_out / 16 - 1);
+      brow[i] = (q / 64) * 16 + (q % 64) % 16;
+      bk[i] = ((q % 64) / 16) * 8;
+      gB[i] = W0 + (size_t)blk * nkb * 512 + (q % 64) * 8;
+    } else {
+      brow[i] = lrow[i];
+      bk[i] = lk[i];
+      gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in;
+    }
   }
   const int nk = (a.d_in + kPK - 1) / kPK;
   uint4 ra[2], rb[2];
@@ -74,14 +87,17 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
       const bool ok = k < a.d_in;
       const int kc = min(k, a.d_in - 8);
       ra[i] = sel4(ok, ld16(gA[i] + kc));
-      rb[i] = sel4(ok, ld16_stream(gB[i] + kc));
+      if (pd.tiled)
+        rb[i] = ld16(gB[i] + (size_t)min(kt, nkb - 1) * 512);  // d_in % 32 == 0: whole blocks
+      else
+        rb[i] = sel4(k < a.d_in, ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8)));
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][lrow[i]][lk[i]]) = rb[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = rb[i];
     }
   };
 

@@ -20,7 +20,7 @@ import numpy as np
 
 from . import datagen
 from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
-from . import sgmm_workspace_size, segment_workspace_size, RP_BF16, RP_F32
+from . import sgmm_workspace_size, segment_workspace_size, pack_w0, RP_BF16, RP_F32
 
 
 def to_device(a: np.ndarray, dtype: str, device):
@@ -49,7 +49,7 @@ class DevProj:
 
 class DeviceWorkload:
     def __init__(self, wl: datagen.Workload, device="cuda:0", layers: Optional[List[int]] = None,
-                 b_scale: float = 0.1, copies: int = 1):
+                 b_scale: float = 0.1, copies: int = 1, packed: bool = True):
         import torch
         self.wl = wl
         self.device = torch.device(device)
@@ -59,6 +59,9 @@ class DeviceWorkload:
         tdt = torch.bfloat16 if dt == "bf16" else torch.float32
         self.code = RP_BF16 if dt == "bf16" else RP_F32
         up = lambda a: to_device(a, dt, self.device)  # noqa: E731
+        # backbone weights in the tiled order the kernels stream fastest (one-time repack)
+        self.packed = packed and dt == "bf16" and all(g.d_out % 16 == 0 and g.d_in % 32 == 0 for g in wl.groups)
+        upw = (lambda a: pack_w0(up(a))) if self.packed else up
         self.x_router = up(datagen.router_input(wl))
         self.Wg = up(datagen.router_weight(wl))
         # per layer: inputs by name and weights by projection (copy 0)
@@ -70,7 +73,7 @@ class DeviceWorkload:
                     self.inputs[(l, g.x_name)] = up(datagen.layer_input(wl, l, g.x_name))
                 for p in g.projs:
                     w = datagen.proj_weights(wl, l, g, p, b_scale=b_scale)
-                    self.weights[0][(l, p)] = DevProj(up(w.W0), up(w.A), up(w.B))
+                    self.weights[0][(l, p)] = DevProj(upw(w.W0), up(w.A), up(w.B))
                     del w
         for c in range(1, copies):
             self.weights.append({key: DevProj(v.W0.clone(), v.A.clone(), v.B.clone())

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(rp.LIB_PATH), reason="library
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 1
+    assert rp.abi_version() == 2
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -97,7 +97,7 @@ def _sgmm(projs=None, **kw):
              dt=rp.RP_BF16, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     if projs is None:
-        projs = [rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128)]
+        projs = [rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 0)]
     arr = (rp.RpProj * max(1, len(projs)))(*projs)
     return rp.lib().rp_sgmm_fused(arr, a["n_proj"], a["x"], a["T"], a["d_in"], a["ld_x"], a["E"], a["r"], a["k"],
                                   a["idx"], a["gate"], a["off"], a["perm"], a["dt"], a["ws"], a["ws_bytes"], None)
@@ -125,13 +125,34 @@ def test_sgmm_rejects(kw, status):
 
 
 @pytest.mark.parametrize("proj,status", [
-    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 100, 104), rp.RP_ERR_INVALID_ARG),   # d_out % 8
-    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 120), rp.RP_ERR_INVALID_ARG),   # ld_y < d_out
-    (rp.RpProj(None, FAKE, FAKE, FAKE, 128, 128), rp.RP_ERR_INVALID_ARG),   # null W0
-    (rp.RpProj(FAKE, FAKE + 2, FAKE, FAKE, 128, 128), rp.RP_ERR_INVALID_ARG),  # misaligned A
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 100, 104, 0, 0), rp.RP_ERR_INVALID_ARG),   # d_out % 8
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 120, 0, 0), rp.RP_ERR_INVALID_ARG),   # ld_y < d_out
+    (rp.RpProj(None, FAKE, FAKE, FAKE, 128, 128, 0, 0), rp.RP_ERR_INVALID_ARG),   # null W0
+    (rp.RpProj(FAKE, FAKE + 2, FAKE, FAKE, 128, 128, 0, 0), rp.RP_ERR_INVALID_ARG),  # misaligned A
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 7, 0), rp.RP_ERR_INVALID_ARG),   # unknown layout
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 3), rp.RP_ERR_INVALID_ARG),   # reserved != 0
+    (rp.RpProj(FAKE, FAKE, FAKE, FAKE, 136, 136, 1, 0), rp.RP_ERR_UNSUPPORTED),   # tiled needs d_out % 16
 ])
 def test_sgmm_rejects_projection(proj, status):
     assert _sgmm(projs=[proj]) == status
+
+
+def test_sgmm_tiled_needs_bf16_and_d_in_multiple_of_32():
+    proj = rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 1, 0)
+    assert _sgmm(projs=[proj], dt=rp.RP_F32) == rp.RP_ERR_UNSUPPORTED
+    assert _sgmm(projs=[proj], d_in=264, ld_x=264) == rp.RP_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE + (1 << 24), 128, 256, 0), rp.RP_ERR_UNSUPPORTED),   # fp32
+    ((FAKE, FAKE + (1 << 24), 120, 256, 1), rp.RP_ERR_INVALID_ARG),   # d_out % 16
+    ((FAKE, FAKE + (1 << 24), 128, 200, 1), rp.RP_ERR_INVALID_ARG),   # d_in % 32
+    ((FAKE, FAKE + 1024, 128, 256, 1), rp.RP_ERR_INVALID_ARG),        # overlap
+    ((None, FAKE, 128, 256, 1), rp.RP_ERR_INVALID_ARG),
+])
+def test_pack_w0_rejects(args, status):
+    s, d, n, k, dt = args
+    assert rp.lib().rp_pack_w0(s, d, n, k, dt, None) == status
 
 
 def test_sgmm_T0_is_noop():

@@ -206,7 +206,26 @@ def test_golden_end_to_end(name):
         check_y(y, ref, dt, name)
 
 
-def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B=False, idx=None, gate=None):
+def test_pack_w0_layout():
+    """rp_pack_w0 writes the documented block order (checked against a NumPy permutation)."""
+    say("pack_w0")
+    rng = np.random.default_rng(4)
+    d_out, d_in = 48, 96
+    W = datagen.f32_to_bf16_bits(rng.standard_normal((d_out, d_in), dtype=np.float32))
+    packed = to_host(rp.pack_w0(to_device(W, "bf16", DEV))).reshape(-1)
+    want = np.empty(d_out * d_in, np.uint16)
+    o = 0
+    for rb in range(d_out // 16):
+        for cb in range(d_in // 32):
+            for g in range(64):
+                row, col = rb * 16 + g % 16, cb * 32 + (g // 16) * 8
+                want[o:o + 8] = W[row, col:col + 8]
+                o += 8
+    np.testing.assert_array_equal(packed, want)
+
+
+def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B=False, idx=None, gate=None,
+                         tiled=False):
     """Random single-group case through route-free inputs; returns max error ratio."""
     rng = np.random.default_rng(seed)
     conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
@@ -219,7 +238,8 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
             rng.standard_normal((E, d_out, r), dtype=np.float32) * np.float32(b_scale / np.sqrt(r))
         B = conv(B)
         hw.append((W0, A, B))
-        projs.append((to_device(W0, dt, DEV), to_device(A, dt, DEV), to_device(B, dt, DEV)))
+        W0d = to_device(W0, dt, DEV)
+        projs.append((rp.pack_w0(W0d) if tiled else W0d, to_device(A, dt, DEV), to_device(B, dt, DEV)))
     if idx is None:
         idx = datagen.uniform_indices(seed, T, E, k)
     if gate is None:
@@ -252,6 +272,19 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
 def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     say("projection", dt, T, d_in, d_outs, E, r, k)
     _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed=T + d_in + E)
+
+
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (1, 64, [64], 4, 8, 1),
+    (33, 96, [208], 5, 16, 2),          # 208 rows: last 32-row tile half full
+    (64, 256, [128, 96], 16, 8, 2),
+    (48, 4096, [4096], 8, 16, 2),
+    (100, 128, [64, 64, 64], 9, 32, 3),  # tiled order through the prefill path
+    (300, 256, [208, 48], 12, 64, 1),
+])
+def test_projection_tiled_w0(T, d_in, d_outs, E, r, k):
+    say("projection tiled", T, d_in, d_outs, E, r, k)
+    _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + 7 * d_in + E, tiled=True)
 
 
 @pytest.mark.parametrize("T", [32, 300])
