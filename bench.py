@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--workload", default="decode_qkvo")
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated per step (0: auto)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--separate-route", action="store_true",
+                    help="run rp_pregate and rp_segment as launches of their own instead of inside the first group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
@@ -171,17 +173,16 @@ def main():
         stream.synchronize()
         n_touched = int((torch.diff(dw.seg_offsets) > 0).sum().item())
 
+        fused = not args.separate_route and dw.can_fuse_route()
         if args.no_graph:
             def run(i):
-                dw.route()
-                dw.project(i % copies)
+                dw.run(i % copies, fused=fused)
         else:
             graphs = []
             for c in range(copies):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
-                    dw.route()
-                    dw.project(c)
+                    dw.run(c, fused=fused)
                 graphs.append(g)
 
             def run(i):
@@ -209,8 +210,12 @@ def main():
             projs = [(W[(layer, p)].W0, W[(layer, p)].A, W[(layer, p)].B, dw.outputs[(layer, p)]) for p in g0.projs]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            rp.sgmm_fused(projs, xg, wl.E, wl.r, wl.k, dw.sel_idx, dw.sel_gate, dw.seg_offsets, dw.pair_perm,
-                          ws=dw.ws)
+            if fused:
+                rp.route_sgmm_fused(projs, xg, dw.Wg, wl.E, wl.r, wl.k, dw.topk_idx, dw.topk_gate, dw.seg_offsets,
+                                    dw.pair_perm, ws=dw.ws)
+            else:
+                rp.sgmm_fused(projs, xg, wl.E, wl.r, wl.k, dw.sel_idx, dw.sel_gate, dw.seg_offsets, dw.pair_perm,
+                              ws=dw.ws)
             b.record(stream)
             evs.append((a, b))
         torch.cuda.synchronize()
@@ -236,11 +241,14 @@ def main():
     bpe = 2 if wl.dtype == "bf16" else 4
     dom_bytes = sum(g0.d_out * g0.d_in * bpe + n_touched * wl.r * (g0.d_in + g0.d_out) * bpe + wl.T * g0.d_out * bpe
                     for _ in g0.projs) + wl.T * g0.d_in * bpe
+    if fused:  # the launch also reads the router weight and writes the routing arrays
+        dom_bytes += wl.d * wl.E * bpe + wl.T * wl.k * 8 + (wl.E + 1) * 4 + wl.T * wl.k * 4
+    dom_name = f"rp_{'route_' if fused else ''}sgmm_fused({'|'.join(g0.projs)})"
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, {tokens_per_s:,.0f} tokens/s, algorithmic {step_bytes / 1e6:.1f} MB "
         f"-> {gbs:,.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); {step_flops / (ms_per_step * 1e-3) / 1e12:.1f} "
         f"TFLOP/s; touched adapters {n_touched}/{wl.E}")
-    log(f"[bench] dominant call rp_sgmm_fused({'|'.join(g0.projs)}): {dom_ms * 1e3:.1f} us for {dom_bytes / 1e6:.1f} MB "
+    log(f"[bench] dominant call {dom_name}: {dom_ms * 1e3:.1f} us for {dom_bytes / 1e6:.1f} MB "
         f"-> {dom_gbs:,.0f} GB/s")
     log(f"[bench] base-only (k=0) projections {base_ms * 1e3:.1f} us per step (eager)")
 
@@ -259,13 +267,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "r": wl.r, "k": wl.k,
                    "layers": wl.layers, "groups": [g.name for g in wl.groups], "weight_copies": copies,
-                   "graph": not args.no_graph, "achieved_GBps": round(gbs, 1),
+                   "graph": not args.no_graph, "route_fused": fused, "achieved_GBps": round(gbs, 1),
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                    "algorithmic_bytes_per_step": step_bytes, "touched_adapters": n_touched},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("sgmm_" + g0.name, wl.name),
-                     "kernel": f"rp_sgmm_fused({'|'.join(g0.projs)})", "avg_launch_us": round(dom_ms * 1e3, 2),
+                     "traffic": measured_traffic(("route_sgmm_" if fused else "sgmm_") + g0.name, wl.name),
+                     "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
                      "bytes_per_launch": dom_bytes},
     }
     if not args.no_cpu_baseline:

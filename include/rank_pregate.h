@@ -14,6 +14,9 @@
  *                    gated low-rank deltas of the chosen adapters, in one pass:
  *                       y[t] = W0 x[t] + sum_j g[t,j] B_e (A_e x[t]),  e = idx[t,j]
  *                    for up to four projections that share x and the gate.
+ *   rp_route_sgmm_fused -- the three steps above for the first adapted layer
+ *                    of a step, whose input is also the router input: one
+ *                    launch for decode shapes, so routing overlaps the weights.
  *
  * Conventions shared by every entry point
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -39,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 2
+#define RP_ABI_VERSION 3
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
 #define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call */
@@ -137,11 +140,12 @@ size_t rp_segment_workspace_size(int64_t T, int32_t k, int64_t E);
  *   x          [T, d_in], leading dimension ld_x
  *   topk_idx, topk_gate, seg_offsets, pair_perm   as produced above
  *   ws         device workspace of at least rp_sgmm_workspace_size() bytes,
- *              256-byte aligned.  Its first 64 KiB hold arrival counters that
- *              must be zero before the first call (zero-fill the buffer once);
- *              every call that completes leaves them zero again, so one
- *              workspace serves calls of any shape in sequence.  Calls that may
- *              overlap in time need distinct workspaces.
+ *              256-byte aligned.  Its first 64 KiB are a control region that
+ *              must be zero before the first call (zero-fill the buffer once)
+ *              and is then kept consistent by the calls themselves: do not
+ *              write it between calls.  One workspace serves calls of any
+ *              shape in sequence; calls that may overlap in time need distinct
+ *              workspaces.
  * Limits: r in {8,16,32,64,128}; 0 <= k <= min(E, RP_MAX_K); 1 <= E <=
  * RP_MAX_E; d_in a multiple of 8 (bf16) / 4 (fp32); d_out a multiple of 8;
  * all matrix pointers 16-byte aligned and ld_x*sizeof(dt), ld_y*sizeof(dt)
@@ -150,6 +154,29 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
                         int64_t ld_x, int64_t E, int64_t r, int32_t k, const int32_t* topk_idx,
                         const float* topk_gate, const int32_t* seg_offsets, const int32_t* pair_perm,
                         rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Pre-gating, segmentation and the fused SGMM in one call (AdaFuse §2.A-§2.B),
+ * for the first adapted projection group of a step: x is both the router input
+ * and the input of the projections.  Equivalent to
+ *
+ *   rp_pregate(x, T, d_in, ld_x, Wg, E, k, dt, topk_idx, topk_gate, NULL)
+ *   rp_segment(topk_idx, T, k, E, seg_offsets, pair_perm, ...)
+ *   rp_sgmm_fused(projs, n_proj, x, ..., topk_idx, topk_gate, seg_offsets, pair_perm, ...)
+ *
+ * with bit-identical routing outputs, which later groups of the same step then
+ * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 64) everything runs in
+ * one kernel launch whose router and segmentation finish while the backbone
+ * weights stream; other shapes issue the three launches in order.
+ *
+ *   Wg        [d_in, E], dense, dtype dt (the router weight)
+ *   topk_idx  int32 [T, k], topk_gate fp32 [T, k], seg_offsets int32 [E+1],
+ *   pair_perm int32 [T*k]  (outputs, as rp_pregate / rp_segment define them)
+ *   ws        as for rp_sgmm_fused, rp_sgmm_workspace_size() bytes
+ * Limits: those of rp_pregate and rp_sgmm_fused, and k >= 1. */
+rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                              int64_t ld_x, const void* Wg, int64_t E, int64_t r, int32_t k, rp_dtype dt,
+                              int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets, int32_t* pair_perm,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Repack a dense row-major bf16 W0 [d_out, d_in] into RP_W0_TILED order (a
  * one-time weight preparation; the result serves every later call).

@@ -28,7 +28,7 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
                  4: "RP_ERR_HIP"}
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
-            "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+            "rp_route_sgmm_fused", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.rp_segment_workspace_size.restype = sz
     L.rp_sgmm_fused.argtypes = [ctypes.POINTER(RpProj), i32, vp, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp,
                                 ctypes.c_int, vp, sz, vp]
+    L.rp_route_sgmm_fused.argtypes = [ctypes.POINTER(RpProj), i32, vp, i64, i64, i64, vp, i64, i64, i32,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
     L.rp_sgmm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32, ctypes.c_int]
     L.rp_sgmm_workspace_size.restype = sz
     L.rp_last_error.argtypes = []
@@ -176,8 +178,8 @@ def sgmm_workspace_size(n_proj: int, T: int, d_in: int, sum_d_out: int, E: int, 
 class Workspace:
     """A zero-initialised device buffer reused across rp_sgmm_fused calls on one stream.
 
-    The library leaves the counter words zero after every completed call, so a
-    buffer only has to be zeroed when it is (re)allocated.
+    The library keeps the buffer's control region consistent between calls, so
+    a buffer only has to be zeroed when it is (re)allocated.
     """
 
     def __init__(self):
@@ -196,17 +198,9 @@ class Workspace:
 _default_ws = Workspace()
 
 
-def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None, topk_gate=None, seg_offsets=None,
-               pair_perm=None, ws=None, stream=None) -> List:
-    """rp_sgmm_fused on torch tensors.
-
-    projs: up to four tuples (W0, A [E, r, d_in], B [E, d_out, r], y [T, d_out] or None); W0 is either
-    a dense [d_out, d_in] tensor or the 4-D tensor pack_w0 returns (tiled order).  Outputs that are
-    None are allocated.  Returns the list of y tensors.
-    """
+def _proj_array(projs: Sequence[Tuple], x):
     torch = _torch()
-    T, d_in = x.shape
-    dt = _dtype_code(x)
+    T = x.shape[0]
     arr = (RpProj * len(projs))()
     ys = []
     sum_d_out = 0
@@ -224,6 +218,50 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
         arr[i] = RpProj(_ptr(W0), _ptr(A), _ptr(B), _ptr(y), d_out, _rows(y, "y"),
                         RP_W0_TILED if tiled else RP_W0_ROWS, 0)
         sum_d_out += d_out
+    return arr, ys, sum_d_out
+
+
+def route_sgmm_fused(projs: Sequence[Tuple], x, Wg, E: int, r: int, k: int, topk_idx=None, topk_gate=None,
+                     seg_offsets=None, pair_perm=None, ws=None, stream=None):
+    """rp_route_sgmm_fused on torch tensors: router, segmentation and the projections of `projs` on x.
+
+    Returns (ys, topk_idx, topk_gate, seg_offsets, pair_perm); routing outputs that are None are allocated.
+    """
+    torch = _torch()
+    T, d_in = x.shape
+    dt = _dtype_code(x)
+    if Wg.dtype != x.dtype or not Wg.is_contiguous() or tuple(Wg.shape) != (d_in, E):
+        raise ValueError("Wg must be a dense [d_in, E] tensor with x's dtype")
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if seg_offsets is None:
+        seg_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pair_perm is None:
+        pair_perm = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
+    arr, ys, sum_d_out = _proj_array(projs, x)
+    if ws is None:
+        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), dev)
+    st = lib().rp_route_sgmm_fused(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), _ptr(Wg), E, r, k, dt,
+                                   _ptr(topk_idx), _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), _ptr(ws),
+                                   ws.numel(), _stream(stream, dev))
+    _check(st, "rp_route_sgmm_fused")
+    return ys, topk_idx, topk_gate, seg_offsets, pair_perm
+
+
+def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None, topk_gate=None, seg_offsets=None,
+               pair_perm=None, ws=None, stream=None) -> List:
+    """rp_sgmm_fused on torch tensors.
+
+    projs: up to four tuples (W0, A [E, r, d_in], B [E, d_out, r], y [T, d_out] or None); W0 is either
+    a dense [d_out, d_in] tensor or the 4-D tensor pack_w0 returns (tiled order).  Outputs that are
+    None are allocated.  Returns the list of y tensors.
+    """
+    T, d_in = x.shape
+    dt = _dtype_code(x)
+    arr, ys, sum_d_out = _proj_array(projs, x)
     if ws is None:
         ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), x.device)
     st = lib().rp_sgmm_fused(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), E, r, k, _ptr(topk_idx),
@@ -260,4 +298,4 @@ def copy(dst, src, stream=None) -> None:
 
 
 # the C names, for callers that mirror the header
-rp_pregate, rp_segment, rp_sgmm_fused = pregate, segment, sgmm_fused
+rp_pregate, rp_segment, rp_sgmm_fused, rp_route_sgmm_fused = pregate, segment, sgmm_fused, route_sgmm_fused

@@ -144,66 +144,73 @@ size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t s
                                         (long long)sum_d_out, (int)E, (int)r, k);
 }
 
-rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in, int64_t ld_x,
-                        int64_t E, int64_t r, int32_t k, const int32_t* topk_idx, const float* topk_gate,
-                        const int32_t* seg_offsets, const int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
-  g_last_error.clear();
-  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: unknown dtype %d", (int)dt);
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by rp_sgmm_fused and rp_route_sgmm_fused (no device calls).
+rp_status check_sgmm(const char* fn, const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                     int64_t ld_x, int64_t E, int64_t r, int32_t k, rp_dtype dt, void* ws) {
+  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   if (!projs || n_proj < 1 || n_proj > RP_MAX_PROJ)
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: n_proj=%d not in [1, %d]", n_proj, RP_MAX_PROJ);
-  if (T < 0 || T > kIntMax) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: T=%lld out of range", (long long)T);
-  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: E=%lld not in [1, %d]", (long long)E, RP_MAX_E);
+    return fail(RP_ERR_INVALID_ARG, "%s: n_proj=%d not in [1, %d]", fn, n_proj, RP_MAX_PROJ);
+  if (T < 0 || T > kIntMax) return fail(RP_ERR_INVALID_ARG, "%s: T=%lld out of range", fn, (long long)T);
+  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "%s: E=%lld not in [1, %d]", fn, (long long)E, RP_MAX_E);
   if (k < 0 || k > RP_MAX_K || k > E)
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k=%d not in [0, min(E, %d)]", k, RP_MAX_K);
+    return fail(RP_ERR_INVALID_ARG, "%s: k=%d not in [0, min(E, %d)]", fn, k, RP_MAX_K);
   if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128))
-    return fail(RP_ERR_UNSUPPORTED, "rp_sgmm_fused: rank r=%lld not in {8,16,32,64,128}", (long long)r);
+    return fail(RP_ERR_UNSUPPORTED, "%s: rank r=%lld not in {8,16,32,64,128}", fn, (long long)r);
   const int64_t es = (int64_t)dsize(dt);
   const int64_t vec = dt == RP_BF16 ? 8 : 4;
   if (d_in < 1 || d_in % vec != 0 || d_in > kIntMax)
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: d_in=%lld must be a positive multiple of %lld", (long long)d_in,
+    return fail(RP_ERR_INVALID_ARG, "%s: d_in=%lld must be a positive multiple of %lld", fn, (long long)d_in,
                 (long long)vec);
   if (ld_x < d_in || (ld_x * es) % 16 != 0 || ld_x > kIntMax)
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: ld_x=%lld must be >= d_in with ld_x*elem a multiple of 16 bytes",
+    return fail(RP_ERR_INVALID_ARG, "%s: ld_x=%lld must be >= d_in with ld_x*elem a multiple of 16 bytes", fn,
                 (long long)ld_x);
-  if (T * k * r * n_proj > ((int64_t)1 << 34)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: T*k*r too large");
-  int d_out[RP_MAX_PROJ];
-  int64_t sum_d_out = 0;
+  if (T * k * r * n_proj > ((int64_t)1 << 34)) return fail(RP_ERR_INVALID_ARG, "%s: T*k*r too large", fn);
   for (int p = 0; p < n_proj; ++p) {
     const rp_proj& q = projs[p];
     if (q.d_out < 8 || q.d_out % 8 != 0 || q.d_out > kIntMax)
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: d_out=%lld must be a positive multiple of 8", p,
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: d_out=%lld must be a positive multiple of 8", fn, p,
                   (long long)q.d_out);
     if (q.ld_y < q.d_out || (q.ld_y * es) % 16 != 0 || q.ld_y > kIntMax)
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: ld_y=%lld must be >= d_out with ld_y*elem a "
-                  "multiple of 16 bytes", p, (long long)q.ld_y);
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: ld_y=%lld must be >= d_out with ld_y*elem a "
+                  "multiple of 16 bytes", fn, p, (long long)q.ld_y);
     if (T > 0 && (!q.W0 || !q.y || (k > 0 && (!q.A || !q.B))))
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: null pointer", p);
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: null pointer", fn, p);
     if (!aligned(q.W0, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.y, 16))
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: W0, A, B, y must be 16-byte aligned", p);
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: W0, A, B, y must be 16-byte aligned", fn, p);
     if ((int64_t)q.d_out * d_in > ((int64_t)1 << 40) || E * r * std::max<int64_t>(d_in, q.d_out) > ((int64_t)1 << 40))
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d too large", p);
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d too large", fn, p);
     if (q.reserved != 0 || (q.w0_layout != RP_W0_ROWS && q.w0_layout != RP_W0_TILED))
-      return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: projection %d: unknown w0_layout %d / reserved %d", p,
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: unknown w0_layout %d / reserved %d", fn, p,
                   q.w0_layout, q.reserved);
     if (q.w0_layout == RP_W0_TILED && (dt != RP_BF16 || q.d_out % 16 != 0 || d_in % 32 != 0))
-      return fail(RP_ERR_UNSUPPORTED, "rp_sgmm_fused: projection %d: the tiled W0 layout needs bf16, d_out %% 16 == 0 "
-                  "and d_in %% 32 == 0", p);
-    d_out[p] = (int)q.d_out;
-    sum_d_out += q.d_out;
+      return fail(RP_ERR_UNSUPPORTED, "%s: projection %d: the tiled W0 layout needs bf16, d_out %% 16 == 0 "
+                  "and d_in %% 32 == 0", fn, p);
   }
   if (T == 0) return RP_OK;
-  if (!x || !aligned(x, 16)) return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: x must be non-null and 16-byte aligned");
-  if (k > 0 && (!topk_idx || !topk_gate || !seg_offsets || !pair_perm))
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k>0 needs topk_idx, topk_gate, seg_offsets and pair_perm");
-  if (!ws) return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: null workspace");
-  if (!aligned(ws, 256)) return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: workspace must be 256-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(RP_ERR_INVALID_ARG, "%s: x must be non-null and 16-byte aligned", fn);
+  if (!ws) return fail(RP_ERR_WORKSPACE, "%s: null workspace", fn);
+  if (!aligned(ws, 256)) return fail(RP_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  return RP_OK;
+}
+
+// Launch plan, workspace size check and kernel arguments (routing pointers
+// excepted) of a checked call.
+rp_status plan_sgmm_call(const char* fn, const rp_proj* projs, int32_t n_proj, const void* x, int64_t T,
+                         int64_t d_in, int64_t ld_x, int64_t E, int64_t r, int32_t k, rp_dtype dt, void* ws,
+                         size_t ws_bytes, bool fused_route, rp::SgmmArgs* out, rp::SgmmPlan* plan_out) {
+  int d_out[RP_MAX_PROJ];
+  for (int p = 0; p < n_proj; ++p) d_out[p] = (int)projs[p].d_out;
   int n_cu = 0;
-  if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "rp_sgmm_fused: cannot query the current device");
+  if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "%s: cannot query the current device", fn);
   const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
-  const rp::SgmmPlan plan = rp::plan_sgmm(rdt, n_proj, d_out, (int)T, (int)d_in, (int)E, (int)r, k, n_cu);
+  const rp::SgmmPlan plan =
+      rp::plan_sgmm(rdt, n_proj, d_out, (int)T, (int)d_in, (int)E, (int)r, k, n_cu, fused_route);
   if (ws_bytes < plan.bytes)
-    return fail(RP_ERR_WORKSPACE, "rp_sgmm_fused: workspace %zu bytes, need %zu (rp_sgmm_workspace_size)", ws_bytes,
+    return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu (rp_sgmm_workspace_size)", fn, ws_bytes,
                 plan.bytes);
 
   rp::SgmmArgs a{};
@@ -228,18 +235,100 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
   a.E = (int)E;
   a.r = (int)r;
   a.k = k;
-  a.topk_idx = topk_idx;
-  a.topk_gate = topk_gate;
-  a.seg_offsets = seg_offsets;
-  a.pair_perm = pair_perm;
   char* w = static_cast<char*>(ws);
   a.counters = reinterpret_cast<int*>(w + plan.off_counters);
   a.u = reinterpret_cast<float*>(w + plan.off_u);
   a.partial = reinterpret_cast<float*>(w + plan.off_partial);
   a.n_tiles = plan.n_tiles;
   a.S = plan.S;
-  hipError_t e = rp::launch_sgmm(a, plan, rdt, stream);
+  *out = a;
+  *plan_out = plan;
+  return RP_OK;
+}
+
+// Word of the workspace's control region that receives the count of
+// out-of-range router indices in a route-and-project call.
+constexpr size_t kSegErrWord = 64;
+
+}  // namespace
+
+extern "C" {
+
+rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in, int64_t ld_x,
+                        int64_t E, int64_t r, int32_t k, const int32_t* topk_idx, const float* topk_gate,
+                        const int32_t* seg_offsets, const int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_sgmm_fused";
+  rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws);
+  if (st != RP_OK || T == 0) return st;
+  if (k > 0 && (!topk_idx || !topk_gate || !seg_offsets || !pair_perm))
+    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k>0 needs topk_idx, topk_gate, seg_offsets and pair_perm");
+  rp::SgmmArgs a{};
+  rp::SgmmPlan plan{};
+  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, false, &a, &plan);
+  if (st != RP_OK) return st;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.seg_offsets = seg_offsets;
+  a.pair_perm = pair_perm;
+  hipError_t e = rp::launch_sgmm(a, plan, dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
   return e == hipSuccess ? RP_OK : hip_fail("rp_sgmm_fused launch", e);
+}
+
+rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                              int64_t ld_x, const void* Wg, int64_t E, int64_t r, int32_t k, rp_dtype dt,
+                              int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets, int32_t* pair_perm,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_route_sgmm_fused";
+  if (k < 1) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: k=%d, routing needs k >= 1", k);
+  rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws);
+  if (st != RP_OK || T == 0) return st;
+  if (!Wg || !aligned(Wg, 16)) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: Wg must be non-null and 16-byte aligned");
+  if (!topk_idx || !topk_gate || !seg_offsets || !pair_perm)
+    return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: null routing output");
+  if (!aligned(topk_idx, 4) || !aligned(topk_gate, 4) || !aligned(seg_offsets, 4) || !aligned(pair_perm, 4))
+    return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: routing outputs must be 4-byte aligned");
+  if (T * E > (int64_t)1 << 40) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: T*E too large");
+  rp::SgmmArgs a{};
+  rp::SgmmPlan plan{};
+  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, true, &a, &plan);
+  if (st != RP_OK) return st;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.seg_offsets = seg_offsets;
+  a.pair_perm = pair_perm;
+  rp::PregateArgs pg;
+  pg.x = x;
+  pg.T = (int)T;
+  pg.d_in = (int)d_in;
+  pg.ld_x = (int)ld_x;
+  pg.Wg = Wg;
+  pg.E = (int)E;
+  pg.k = k;
+  pg.dt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
+  pg.topk_idx = topk_idx;
+  pg.topk_gate = topk_gate;
+  pg.logits = nullptr;
+  rp::SegmentArgs sg;
+  sg.topk_idx = topk_idx;
+  sg.n_pairs = (int)(T * k);
+  sg.k = k;
+  sg.E = (int)E;
+  sg.seg_offsets = seg_offsets;
+  sg.pair_perm = pair_perm;
+  sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
+  hipError_t e;
+  if (plan.path == 1) {
+    e = rp::launch_route_sgmm(a, pg, sg, plan, stream);
+  } else {
+    // other shapes: the same three steps as separate launches on the stream
+    e = rp::launch_pregate(pg, stream);
+    if (e == hipSuccess) e = rp::launch_segment(sg, stream);
+    if (e == hipSuccess) e = rp::launch_sgmm(a, plan, pg.dt, stream);
+  }
+  return e == hipSuccess ? RP_OK : hip_fail("rp_route_sgmm_fused launch", e);
 }
 
 rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream) {

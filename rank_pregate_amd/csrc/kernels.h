@@ -59,9 +59,26 @@ struct SgmmArgs {
   // workspace views
   float* u;          // [n_proj][T*k][r] gated rank-r intermediates
   float* partial;    // split-K partial tiles (decode path)
-  int* counters;     // reserved counter region: control words, then per-tile arrival counters
+  int* counters;     // reserved counter region (decode path): epoch, control sets, split-K counters
   int n_tiles;       // output-row tiles over all projections
   int S;             // K splits per output tile (decode path)
+};
+
+// Extra launch constants of the decode kernel.  Items are numbered
+//   [0, n_route)                 router tiles (fused route-and-project launches)
+//   [n_route, n_pre)             the segmentation item (fused launches)
+//   [n_pre, n_pre + n_shrink)    shrink units, units_per_proj per projection
+//   [n_pre + n_shrink, n_items)  base items, n_tiles * S
+struct DecodeArgs {
+  int n_route, n_pre, n_shrink, n_items;
+  int units_per_proj;
+  int KP;         // K parts of a shrink unit (partial sums added in the expand)
+  int dense;      // 1: a shrink unit covers every token for one adapter; 0: one chunk of <= 16 pairs
+  int t_pad;      // tokens padded to whole 16-token tiles
+  int fused;      // routing runs inside the launch (router tiles + segmentation item)
+  PregateArgs pg; // fused: router arguments (outputs topk_idx, topk_gate)
+  SegmentArgs sg; // fused: segmentation arguments
+  int route_np, route_slice, route_vec, route_tt;  // fused: router tiling
 };
 
 // Which kernel family serves a call, and the workspace it needs.
@@ -71,17 +88,29 @@ struct SgmmPlan {
   int n_tiles;
   int S;
   int t_pad;         // tokens padded to the decode token tiles
+  int KP;            // decode: K parts per shrink unit
+  int dense;         // decode: shrink units over all tokens of one adapter
+  int units_per_proj;
+  int n_pre, n_route;  // decode: routing items of a fused launch
+  int n_items, grid;   // decode: work items and workgroups (grid <= resident capacity)
   size_t off_u, off_partial, off_counters, bytes;
 };
-SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu);
+// fused_route: the launch also runs the router and segmentation (decode path only)
+SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
+                   bool fused_route);
 int decode_mt(int T);       // 16-token tiles of the decode kernel
 int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
+int decode_resident_per_cu(int T, bool fused);  // workgroups of the decode kernel one CU holds at once
+int route_tile_tokens(int E);                   // tokens per router tile
 hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
                                   int k);
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);
+// Router, segmentation and projections in one decode launch (plan.path == 1, built with fused_route).
+hipError_t launch_route_sgmm(const SgmmArgs& a, const PregateArgs& pg, const SegmentArgs& sg, const SgmmPlan& plan,
+                             hipStream_t s);
 
 hipError_t launch_pack_w0(const void* src, void* dst, int d_out, int d_in, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);

@@ -91,7 +91,7 @@ __host__ __device__ inline int route_lds_floats(int E, int TT) { return 3 * TT *
 // order, so equal router columns give bit-equal logits.
 // NCBp <= 128 (E <= 1024).  Must be called by all kRouteThreads threads.
 template <typename Tin, int TT>
-__device__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem) {
+__device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem) {
   const int NCBp = rp_.NCBp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = min(TT, a.T - t0);
@@ -236,7 +236,7 @@ __device__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, f
 //      pairs in ascending id.
 // Out-of-range ids are counted into *err_count and left out.
 template <int NW>
-__device__ void segment_block(const SegmentArgs& a, int* hist, int* wave_tot, int* bad) {
+__device__ __forceinline__ void segment_block(const SegmentArgs& a, int* hist, int* wave_tot, int* bad) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, n = a.n_pairs;

@@ -6,8 +6,42 @@
 
 namespace rp {
 
-// Control words at the start of the workspace's reserved counter region.
-enum CtlWord { kCtlTicket = 0, kCtlShrinkDone = 1, kCtlFinished = 2, kCtlWaitOverflow = 3, kCtlTiles = 16 };
+// Layout of the workspace's reserved counter region (int32 words; words that
+// atomics hit from many workgroups sit on cache lines of their own).
+//   kCtlEpoch      decode launches completed on this workspace.  Launch n uses
+//                  control set n & 1; the last workgroup to arrive clears the
+//                  other set for launch n + 1 and then advances the epoch, so
+//                  no launch ends with a serialised "who finished last" count.
+//   kCtlWaitOverflow  sticky flag: a wait gave up after its spin limit.
+//   kCtlSegErr     out-of-range router indices seen by a fused launch's
+//                  segmentation (always 0 for indices the router wrote).
+//   kCtlTiles + t  split-K arrivals of output tile t; the tile's owner resets
+//                  its word after use.
+constexpr int kCtlEpoch = 0;
+constexpr int kCtlWaitOverflow = 32;
+constexpr int kCtlSegErr = 64;
+constexpr int kCtlSet0 = 1024;
+constexpr int kCtlSetStride = 1024;
+constexpr int kSetShrinkDone = 0;   // shrink units finished
+constexpr int kSetRouteDone = 32;   // router tiles finished
+constexpr int kSetSegDone = 64;     // segmentation finished
+constexpr int kSetArrive = 96;      // + 32 * (blockIdx % 8): workgroups that read the epoch
+constexpr int kSetArriveAll = 96 + 8 * 32;
+constexpr int kSetWords = kSetArriveAll + 32;
+constexpr int kCtlTiles = 4096;
+
+// Device-scope (sc1) loads of routing data another workgroup of the same
+// launch may have written; plain loads when it was written by an earlier launch.
+template <bool COH>
+__device__ __forceinline__ int ld_route(const int* p) {
+  if (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float ld_route(const float* p) {
+  if (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
 
 // Projection that owns output-row tile `tile` of the packed row space.
 __device__ __forceinline__ int proj_of_tile(const SgmmArgs& a, int tile) {
@@ -65,12 +99,13 @@ __device__ __forceinline__ void u_operand(const float* u, int r, int p, int c, b
 
 // Shrink chunks are numbered segment by segment, ceil(n_e / nch) per segment.
 // Run by one full wave; returns (segment, chunk) or segment -1 past the end.
+template <bool COH = false>
 __device__ __forceinline__ void locate_chunk(const SgmmArgs& a, int unit, int nch, int lane, int* seg,
                                              int* chunk) {
   int carry = 0, fe = -1, fc = 0;
   for (int e0 = 0; e0 < a.E; e0 += 64) {
     const int e = e0 + lane;
-    const int n = (e < a.E) ? (a.seg_offsets[e + 1] - a.seg_offsets[e]) : 0;
+    const int n = (e < a.E) ? (ld_route<COH>(&a.seg_offsets[e + 1]) - ld_route<COH>(&a.seg_offsets[e])) : 0;
     const int c = (n + nch - 1) / nch;
     const int incl = wave_inclusive_scan(c, lane);
     const int excl = carry + incl - c;

@@ -4,7 +4,9 @@ A step is the whole hot path once (AdaFuse technical summary §2.A-§2.B):
 route the router input once (rp_pregate), group pairs by adapter
 (rp_segment), then every projection group of every layer in dependency order
 (q|k|v -> o -> gate|up -> down), each one rp_sgmm_fused call.  The same
-gate and segments serve every layer.
+gate and segments serve every layer.  By default the routing runs inside the
+first group's launch (rp_route_sgmm_fused), since the router's input is that
+group's input.
 
 Inputs come from rank_pregate_amd.datagen (seeded); weights are uploaded
 once and stay resident in HBM.  `copies` > 1 keeps several copies of the
@@ -20,6 +22,7 @@ import numpy as np
 
 from . import datagen
 from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
+from . import route_sgmm_fused as rp_route_sgmm_fused
 from . import sgmm_workspace_size, segment_workspace_size, pack_w0, RP_BF16, RP_F32
 
 
@@ -109,20 +112,43 @@ class DeviceWorkload:
         rp_pregate(self.x_router, self.Wg, wl.k, self.topk_idx, self.topk_gate, stream=stream)
         rp_segment(self.sel_idx, wl.E, self.seg_offsets, self.pair_perm, ws=self.seg_ws, stream=stream)
 
-    def project(self, copy: int = 0, k: Optional[int] = None, stream=None):
+    def project(self, copy: int = 0, k: Optional[int] = None, stream=None, skip_first: bool = False):
         wl = self.wl
         kk = wl.k if k is None else k
         W = self.weights[copy]
+        first = True
         for l in self.layers:
             for g in wl.groups:
+                if first and skip_first:
+                    first = False
+                    continue
+                first = False
                 x = self.inputs[(l, g.x_name)]
                 projs = [(W[(l, p)].W0, W[(l, p)].A, W[(l, p)].B, self.outputs[(l, p)]) for p in g.projs]
                 rp_sgmm_fused(projs, x, wl.E, wl.r, kk, self.sel_idx, self.sel_gate, self.seg_offsets,
                               self.pair_perm, ws=self.ws, stream=stream)
 
-    def step(self, stream=None):
-        self.route(stream)
-        self.project(self.step_count % self.copies, stream=stream)
+    def can_fuse_route(self) -> bool:
+        """The router's input is layer 0's first group input and its choice is the one used."""
+        return self.layers[0] == 0 and self.sel_idx is self.topk_idx
+
+    def run(self, copy: int = 0, fused: bool = True, stream=None):
+        """One step: routing, then every projection group in order.  With `fused`, the router and the
+        segmentation run inside the first group's launch (rp_route_sgmm_fused)."""
+        wl = self.wl
+        if fused and self.can_fuse_route():
+            g = wl.groups[0]
+            W = self.weights[copy]
+            projs = [(W[(0, p)].W0, W[(0, p)].A, W[(0, p)].B, self.outputs[(0, p)]) for p in g.projs]
+            rp_route_sgmm_fused(projs, self.inputs[(0, g.x_name)], self.Wg, wl.E, wl.r, wl.k, self.topk_idx,
+                                self.topk_gate, self.seg_offsets, self.pair_perm, ws=self.ws, stream=stream)
+            self.project(copy, stream=stream, skip_first=True)
+        else:
+            self.route(stream)
+            self.project(copy, stream=stream)
+
+    def step(self, stream=None, fused: bool = True):
+        self.run(self.step_count % self.copies, fused=fused, stream=stream)
         self.step_count += 1
 
     # -- accounting ------------------------------------------------------------

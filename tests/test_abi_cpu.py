@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 2
+    assert rp.abi_version() == 3
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -174,3 +174,38 @@ def test_workspace_sizes():
     # prefill sizes need no split-K partials: only the rank-r intermediates
     big = L.rp_sgmm_workspace_size(2, 4096, 4096, 22016, 32, 64, 1, rp.RP_BF16)
     assert big >= 2 * 4096 * 64 * 4
+
+
+def _route(projs=None, **kw):
+    a = dict(n_proj=1, x=FAKE, T=32, d_in=256, ld_x=256, Wg=FAKE, E=8, r=16, k=2, dt=rp.RP_BF16, idx=FAKE,
+             gate=FAKE, off=FAKE, perm=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    if projs is None:
+        projs = [rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 0)]
+    arr = (rp.RpProj * max(1, len(projs)))(*projs)
+    return rp.lib().rp_route_sgmm_fused(arr, a["n_proj"], a["x"], a["T"], a["d_in"], a["ld_x"], a["Wg"], a["E"],
+                                        a["r"], a["k"], a["dt"], a["idx"], a["gate"], a["off"], a["perm"], a["ws"],
+                                        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), rp.RP_ERR_INVALID_ARG),           # routing needs k >= 1
+    (dict(k=9), rp.RP_ERR_INVALID_ARG),
+    (dict(E=0), rp.RP_ERR_INVALID_ARG),
+    (dict(r=12), rp.RP_ERR_UNSUPPORTED),
+    (dict(Wg=None), rp.RP_ERR_INVALID_ARG),
+    (dict(Wg=FAKE + 8), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),
+    (dict(perm=None), rp.RP_ERR_INVALID_ARG),
+    (dict(off=FAKE + 2), rp.RP_ERR_INVALID_ARG),
+    (dict(ws=None), rp.RP_ERR_WORKSPACE),
+    (dict(x=FAKE + 4), rp.RP_ERR_INVALID_ARG),
+    (dict(n_proj=5), rp.RP_ERR_INVALID_ARG),
+])
+def test_route_sgmm_rejects(kw, status):
+    assert _route(**kw) == status
+    assert rp.last_error()
+
+
+def test_route_sgmm_T0_is_noop():
+    assert _route(T=0, x=None, Wg=None, idx=None, gate=None, off=None, perm=None, ws=None) == rp.RP_OK

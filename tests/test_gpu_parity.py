@@ -225,7 +225,7 @@ def test_pack_w0_layout():
 
 
 def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B=False, idx=None, gate=None,
-                         tiled=False):
+                         tiled=False, ws=None):
     """Random single-group case through route-free inputs; returns max error ratio."""
     rng = np.random.default_rng(seed)
     conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
@@ -248,7 +248,7 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
     gate_d = torch.from_numpy(np.ascontiguousarray(gate, np.float32)).to(DEV)
     off, perm = rp.segment(idx_d, E)
     xd = to_device(x, dt, DEV)
-    ys = rp.sgmm_fused(projs, xd, E, r, k, idx_d, gate_d, off, perm)
+    ys = rp.sgmm_fused(projs, xd, E, r, k, idx_d, gate_d, off, perm, ws=ws)
     torch.cuda.synchronize()
     x64 = widen(x, dt)
     worst = 0.0
@@ -264,6 +264,8 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
     (33, 72, [200], 5, 16, 2),         # ragged T, d_in % 16 == 8, d_out not a tile multiple
     (64, 256, [128, 96], 16, 8, 2),    # two projections, different widths
     (100, 128, [64, 64, 64], 9, 32, 3),
+    (48, 256, [128], 100, 16, 2),      # decode, E > 32: shrink over segment chunks
+    (64, 4096, [4096], 16, 8, 2),      # decode, four token tiles, full width
     (256, 512, [256], 256, 16, 2),     # many adapters, 1-3 tokens per segment
     (257, 256, [136], 7, 64, 1),       # first prefill size, ragged
     (300, 264, [128, 40], 12, 128, 2),  # prefill, k=2, r=128
@@ -346,6 +348,75 @@ def test_token_permutation(T):
     check_y(yp, ref[p], "bf16", "permuted")
     bit = np.array_equal(to_host(yp), to_host(y)[p])
     say(f"permuted output bit-identical: {bit}")
+
+
+# --------------------------------------------------------------------------- routing inside the projection launch
+
+def _fused_case(T, d_in, d_outs, E, r, k, dt, seed, tiled=False, ws=None):
+    """rp_route_sgmm_fused against the separate calls (routing bit for bit) and the oracle (y)."""
+    rng = np.random.default_rng(seed)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    Wg = conv(rng.standard_normal((d_in, E), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    projs, hw = [], []
+    for d_out in d_outs:
+        W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) * np.float32(1.0 / np.sqrt(r)))
+        hw.append((W0, A, B))
+        W0d = to_device(W0, dt, DEV)
+        projs.append((rp.pack_w0(W0d) if tiled else W0d, to_device(A, dt, DEV), to_device(B, dt, DEV)))
+    xd, Wgd = to_device(x, dt, DEV), to_device(Wg, dt, DEV)
+    ys, idx, gate, off, perm = rp.route_sgmm_fused(projs, xd, Wgd, E, r, k, ws=ws)
+    idx2, gate2 = rp.pregate(xd, Wgd, k)
+    off2, perm2 = rp.segment(idx2, E)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "fused router indices differ from rp_pregate"
+    assert torch.equal(gate.view(torch.int32), gate2.view(torch.int32)), "fused gates differ from rp_pregate"
+    assert torch.equal(off, off2) and torch.equal(perm[: T * k], perm2[: T * k]), "fused segments differ"
+    x64, Wg64 = widen(x, dt), widen(Wg, dt)
+    same, idx_ref, gate_ref = compare_routing(idx, gate, None, x64, Wg64, k)
+    assert same.all(), "seeds are chosen free of near ties"
+    off_ref, perm_ref = oracle.segment(idx_ref, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), off_ref)
+    np.testing.assert_array_equal(perm.cpu().numpy()[: T * k], perm_ref)
+    worst = 0.0
+    for (W0, A, B), y in zip(hw, ys):
+        ref = oracle.sgmm(x64, widen(W0, dt), widen(A, dt), widen(B, dt), idx_ref, gate_ref)
+        worst = max(worst, check_y(y, ref, dt, f"fused T={T} d_in={d_in} d_out={W0.shape[0]} E={E}"))
+    return worst
+
+
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k,dt", [
+    (1, 64, [64], 4, 8, 1, "bf16"),                   # one token, one router tile
+    (17, 256, [96, 32], 40, 16, 2, "bf16"),           # E > 32: shrink over segment chunks
+    (32, 4096, [4096, 4096, 4096], 8, 16, 2, "bf16"),  # decode q|k|v shape
+    (64, 512, [256], 16, 8, 2, "bf16"),               # 64 tokens (four token tiles)
+    (48, 1024, [512], 1024, 32, 8, "bf16"),           # E = 1024: two-token router tiles, k = 8
+    (5, 128, [128], 3, 128, 3, "bf16"),               # r = 128
+    (100, 256, [128], 8, 16, 2, "bf16"),              # prefill shape: three launches
+    (16, 128, [64], 4, 8, 1, "f32"),                  # fp32: three launches
+])
+def test_route_fused(T, d_in, d_outs, E, r, k, dt):
+    say("route fused", T, d_in, d_outs, E, r, k, dt)
+    _fused_case(T, d_in, d_outs, E, r, k, dt, seed=31 + T + E)
+
+
+def test_route_fused_tiled():
+    say("route fused tiled")
+    _fused_case(32, 1024, [512, 256], 8, 16, 2, "bf16", seed=77, tiled=True)
+
+
+def test_workspace_shared_across_call_kinds():
+    """One workspace through a sequence of fused, separate and differently shaped calls: each
+    call starts from the control state the previous one left."""
+    say("workspace sequence")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    shapes = [(32, 512, [256, 128], 8, 16, 2), (9, 256, [64], 40, 8, 1), (64, 256, [128], 16, 32, 2)]
+    for rep in range(3):
+        for i, (T, d_in, d_outs, E, r, k) in enumerate(shapes):
+            _fused_case(T, d_in, d_outs, E, r, k, "bf16", seed=100 + i, ws=ws)
+            _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=200 + i, ws=ws)
 
 
 def test_adapter_sensitivity():
