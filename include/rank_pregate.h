@@ -164,7 +164,7 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
  *   rp_sgmm_fused(projs, n_proj, x, ..., topk_idx, topk_gate, seg_offsets, pair_perm, ...)
  *
  * with bit-identical routing outputs, which later groups of the same step then
- * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 64) everything runs in
+ * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 32) everything runs in
  * one kernel launch whose router and segmentation finish while the backbone
  * weights stream; other shapes issue the three launches in order.
  *

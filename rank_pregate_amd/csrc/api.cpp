@@ -293,7 +293,8 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
   if (T * E > (int64_t)1 << 40) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: T*E too large");
   rp::SgmmArgs a{};
   rp::SgmmPlan plan{};
-  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, true, &a, &plan);
+  const bool one_launch = dt == RP_BF16 && T <= 64 && rp::decode_fused_route_supported((int)T);
+  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, one_launch, &a, &plan);
   if (st != RP_OK) return st;
   a.topk_idx = topk_idx;
   a.topk_gate = topk_gate;
@@ -320,7 +321,7 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
   sg.pair_perm = pair_perm;
   sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
   hipError_t e;
-  if (plan.path == 1) {
+  if (one_launch && plan.path == 1) {
     e = rp::launch_route_sgmm(a, pg, sg, plan, stream);
   } else {
     // other shapes: the same three steps as separate launches on the stream

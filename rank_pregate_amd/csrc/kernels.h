@@ -71,9 +71,14 @@ struct SgmmArgs {
 //   [n_pre + n_shrink, n_items)  base items, n_tiles * S
 struct DecodeArgs {
   int n_route, n_pre, n_shrink, n_items;
-  int units_per_proj;
-  int KP;         // K parts of a shrink unit (partial sums added in the expand)
-  int dense;      // 1: a shrink unit covers every token for one adapter; 0: one chunk of <= 16 pairs
+  int units_per_proj;  // pair-chunk shrink units per projection (E > 32)
+  int KP;         // K parts of a pair-chunk shrink unit (partial sums added in the expand)
+  int dense;      // 1: the shrink runs as row tiles of the stacked A_e over every token (E <= 32);
+                  // 0: pair-chunk shrink units of <= 16 pairs of one segment
+  int atiles_per_proj, n_atiles, SA;  // dense: 32-row tiles of [A_0; ..; A_{E-1}] and their K splits
+  int shrink_target;                  // shrink_done count that means every u is written
+  float* partial_a;                   // dense: split-K partial tiles of the A tiles
+  unsigned int* route_tagged;         // fused: (index, tag, gate, tag) per (token, slot)
   int t_pad;      // tokens padded to whole 16-token tiles
   int fused;      // routing runs inside the launch (router tiles + segmentation item)
   PregateArgs pg; // fused: router arguments (outputs topk_idx, topk_gate)
@@ -88,9 +93,11 @@ struct SgmmPlan {
   int n_tiles;
   int S;
   int t_pad;         // tokens padded to the decode token tiles
-  int KP;            // decode: K parts per shrink unit
-  int dense;         // decode: shrink units over all tokens of one adapter
+  int KP;            // decode: K parts per pair-chunk shrink unit
+  int dense;         // decode: shrink as row tiles of the stacked A_e over all tokens
   int units_per_proj;
+  int atiles_per_proj, n_atiles, SA;
+  size_t off_partial_a, off_route;
   int n_pre, n_route;  // decode: routing items of a fused launch
   int n_items, grid;   // decode: work items and workgroups (grid <= resident capacity)
   size_t off_u, off_partial, off_counters, bytes;
@@ -101,7 +108,8 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
 int decode_mt(int T);       // 16-token tiles of the decode kernel
 int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
 int decode_resident_per_cu(int T, bool fused);  // workgroups of the decode kernel one CU holds at once
-int route_tile_tokens(int E);                   // tokens per router tile
+int fused_route_tile_tokens();                  // tokens per router tile of a fused decode launch
+bool decode_fused_route_supported(int T);       // routing can run inside a decode launch of T tokens
 hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);

@@ -31,7 +31,3 @@ hipError_t launch_pregate(const PregateArgs& a, hipStream_t s) {
 }
 
 }  // namespace rp
-
-namespace rp {
-int route_tile_tokens(int E) { return route_plan(E, 8, 2).TT; }
-}  // namespace rp

@@ -57,6 +57,37 @@ struct Vec8<float> {
   static __device__ __forceinline__ float one(const float* p) { return *p; }
 };
 
+// Eight consecutive elements as raw loaded data (unpacked to fp32 later).
+template <typename Tin>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+  typedef uint4 type;
+  static __device__ __forceinline__ type fetch(const bf16_t* p) { return ld16(p); }
+  static __device__ __forceinline__ void unpack(const type& q, float (&v)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+struct F32x8 {
+  float4 a, b;
+};
+template <>
+struct Raw8<float> {
+  typedef F32x8 type;
+  static __device__ __forceinline__ type fetch(const float* p) {
+    return F32x8{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+  }
+  static __device__ __forceinline__ void unpack(const type& q, float (&v)[8]) {
+    v[0] = q.a.x; v[1] = q.a.y; v[2] = q.a.z; v[3] = q.a.w; v[4] = q.b.x; v[5] = q.b.y; v[6] = q.b.z; v[7] = q.b.w;
+  }
+};
+constexpr int kRouteNB = 2;  // groups of 8 k per router load batch
+
 // (value, index) order of the router: larger logit first, lower index on ties.
 __device__ __forceinline__ bool route_better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -90,8 +121,11 @@ __host__ __device__ inline int route_lds_floats(int E, int TT) { return 3 * TT *
 // slices are combined with a fixed butterfly inside each wave and then in wave
 // order, so equal router columns give bit-equal logits.
 // NCBp <= 128 (E <= 1024).  Must be called by all kRouteThreads threads.
+// With `tagged` set, each (token, slot) result is also written as two tagged
+// 8-byte pairs (index, tag) and (gate bits, tag) for readers in the same launch.
 template <typename Tin, int TT>
-__device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem) {
+__device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem,
+                                           unsigned long long* tagged = nullptr, uint32_t tag = 0) {
   const int NCBp = rp_.NCBp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = min(TT, a.T - t0);
@@ -118,7 +152,37 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
     for (int t = 0; t < TT; ++t) xr[t] = x + (size_t)(t0 + min(t, nt - 1)) * a.ld_x;
     const int kb = ks * rp_.slice, ke = min(a.d_in, kb + rp_.slice);
     const int ke8 = kb + max(0, ke - kb) / 8 * 8;  // full groups of 8; fp32 rows may end in a group of 4
-    for (int k0 = kb; k0 < ke8; k0 += 8) {
+    int k0 = kb;
+    if (rp_.vec_cols && c0 + kRouteCB <= E) {
+      // batches of kRouteNB groups: every load of a batch is issued before its
+      // arithmetic, so a batch costs one memory round trip; the sums still run
+      // over k in ascending order
+      for (; k0 + 8 * kRouteNB <= ke8; k0 += 8 * kRouteNB) {
+        typename Raw8<Tin>::type xq[kRouteNB][TT], wq[kRouteNB][8];
+#pragma unroll
+        for (int b = 0; b < kRouteNB; ++b) {
+#pragma unroll
+          for (int t = 0; t < TT; ++t) xq[b][t] = Raw8<Tin>::fetch(xr[t] + k0 + 8 * b);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) wq[b][kk] = Raw8<Tin>::fetch(Wg + (size_t)(k0 + 8 * b + kk) * E + c0);
+        }
+#pragma unroll
+        for (int b = 0; b < kRouteNB; ++b) {
+          float xv[TT][8], wv[8][kRouteCB];
+#pragma unroll
+          for (int t = 0; t < TT; ++t) Raw8<Tin>::unpack(xq[b][t], xv[t]);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) Raw8<Tin>::unpack(wq[b][kk], wv[kk]);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+              for (int c = 0; c < kRouteCB; ++c) acc[t][c] = fmaf(xv[t][kk], wv[kk][c], acc[t][c]);
+        }
+      }
+    }
+    for (; k0 < ke8; k0 += 8) {
       float xv[TT][8];
 #pragma unroll
       for (int t = 0; t < TT; ++t) Vec8<Tin>::load(xr[t] + k0, xv[t]);
@@ -216,8 +280,15 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
         if (j == lane) { mine = z; mine_i = seli[j]; }
       }
       const size_t base = (size_t)(t0 + tt) * a.k;
+      const float g = mine / s;
       stc_i32(&a.topk_idx[base + lane], mine_i);
-      stc_f32(&a.topk_gate[base + lane], mine / s);
+      stc_f32(&a.topk_gate[base + lane], g);
+      if (tagged) {
+        const unsigned long long hi = (unsigned long long)tag << 32;
+        __hip_atomic_store(&tagged[(base + lane) * 2], hi | (uint32_t)mine_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&tagged[(base + lane) * 2 + 1], hi | __float_as_uint(g), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }

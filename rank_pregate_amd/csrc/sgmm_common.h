@@ -15,8 +15,6 @@ namespace rp {
 //   kCtlWaitOverflow  sticky flag: a wait gave up after its spin limit.
 //   kCtlSegErr     out-of-range router indices seen by a fused launch's
 //                  segmentation (always 0 for indices the router wrote).
-//   kCtlTiles + t  split-K arrivals of output tile t; the tile's owner resets
-//                  its word after use.
 constexpr int kCtlEpoch = 0;
 constexpr int kCtlWaitOverflow = 32;
 constexpr int kCtlSegErr = 64;
@@ -28,7 +26,6 @@ constexpr int kSetSegDone = 64;     // segmentation finished
 constexpr int kSetArrive = 96;      // + 32 * (blockIdx % 8): workgroups that read the epoch
 constexpr int kSetArriveAll = 96 + 8 * 32;
 constexpr int kSetWords = kSetArriveAll + 32;
-constexpr int kCtlTiles = 4096;
 
 // Device-scope (sc1) loads of routing data another workgroup of the same
 // launch may have written; plain loads when it was written by an earlier launch.

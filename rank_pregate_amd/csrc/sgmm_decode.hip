@@ -27,10 +27,11 @@
 // exceeds what the chip holds at once, so every wait ends: the smallest
 // unfinished item always has its workgroup running and nothing to wait for.
 //
-// Data crossing workgroups (routing results, u, split-K partial tiles) is
-// written and read with device-scope (sc1) accesses; a writer waits for its
-// stores before it bumps a counter, so no cache-wide fence is needed.  The
-// split-K partials of a tile are summed in split order by the tile's last
+// Data crossing workgroups is written and read with device-scope (sc1)
+// accesses, so no cache-wide fence is needed.  Routing results and pair-chunk
+// u are announced by counters (a writer waits for its stores first); dense u
+// and split-K partial tiles travel as tagged pairs that the reader validates.
+// The split-K partials of a tile are summed in split order by the tile's last
 // split, so the output does not depend on timing.
 #include "route_common.h"
 #include "sgmm_common.h"
@@ -46,6 +47,8 @@ constexpr int kKC = 256;             // K per LDS chunk
 constexpr int kSteps = kKC / 32;     // MFMA k-steps per chunk
 constexpr int kLD = kKC + 8;         // padded LDS row (elements)
 static_assert(kThreads == kRouteThreads, "router tiles run on the decode workgroup shape");
+constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
+constexpr int kMaxSplits = 8;         // K splits of a tile (the launch plan keeps S <= this)
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, CDNA
@@ -59,6 +62,41 @@ __device__ __forceinline__ void st_coh16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 }
 __device__ __forceinline__ f32x4_t ld_coh16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
+// Tagged hand-offs: a value crossing workgroups travels as an 8-byte pair
+// (fp32 bits, tag), where the tag names the launch that wrote it (a NaN bit
+// pattern carrying the low 20 bits of the workspace's launch epoch; finite
+// data never has it).  A reader loads the pairs directly and retries while
+// any tag is stale, so no separate "ready" counter costs it a round trip.
+// Each pair is written by one 8-byte-aligned piece of a store and checked on
+// its own, so a store seen half-done is simply retried.
+__device__ __forceinline__ uint32_t launch_tag(int ep) { return 0xFFF00000u | ((uint32_t)ep & 0xFFFFFu); }
+
+__device__ __forceinline__ void st_tagged4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v, uint32_t tag) {
+  const u32x4_v a = {__float_as_uint(v[0]), tag, __float_as_uint(v[1]), tag};
+  const u32x4_v b = {__float_as_uint(v[2]), tag, __float_as_uint(v[3]), tag};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, kSc1);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, kSc1);
+}
+
+// Four tagged values at byte offset off (32 bytes); true when all four carry `tag`.
+__device__ __forceinline__ bool ld_tagged4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t tag, f32x4_t& v) {
+  const u32x4_v a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+  const u32x4_v b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kSc1);
+  v = f32x4_t{__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(b.x), __uint_as_float(b.z)};
+  return a.y == tag && a.w == tag && b.y == tag && b.w == tag;
+}
+
+// Per-wave retry bookkeeping of a tagged read: true while it should go on.
+__device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins) {
+  if (__ballot(!lane_ok) == 0) return false;
+  __builtin_amdgcn_s_sleep(2);
+  if (++*spins > kSpinLimit) {
+    if ((threadIdx.x & 63) == 0) atomicOr(&ctl[kCtlWaitOverflow], 1);
+    return false;
+  }
+  return true;
 }
 
 template <int MT, bool FUSED>
@@ -100,48 +138,35 @@ __device__ __forceinline__ size_t upart_slots(const SgmmArgs& a, const DecodeArg
 }
 
 // ---------------------------------------------------------------------------
-// shrink units, 2 waves
+// pair-chunk shrink units, 2 waves
 // ---------------------------------------------------------------------------
-// One unit: rank rows of A_e (MTR tiles of 16) against NT tiles of 16 columns
-// (tokens when dense, pairs of one segment chunk otherwise) over K part kp;
-// the two waves split the part and are added in wave order.
-template <int MTR, int NT, bool DENSE, bool COH>
-__device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs& d, int proj, int unit, int kp, float* red,
-                            int* s_loc) {
-  constexpr int U = MTR * NT >= 8 ? 1 : 2;
+// One unit (adapters beyond the dense limit): rank rows of A_e (MTR tiles of
+// 16) against one chunk of <= 16 pairs of e's segment, over K part kp; the
+// two waves split the part and are added in wave order.  COH: the segments
+// were written by this launch.
+template <int MTR, bool COH>
+__device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs& d, int proj, int unit, int kp,
+                                            float* red, int* s_loc) {
+  // k-steps per batch: all loads of a batch are issued before its MFMAs, so a
+  // unit costs about one memory round trip per batch
+  constexpr int U = MTR <= 2 ? 8 : (MTR <= 8 ? 2 : 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int e, slot0 = 0, slot_end = 0;
-  if (DENSE) {
-    e = unit;
-    // adapters no token chose have no consumer (known before the launch only)
-    if (!COH && a.seg_offsets[e + 1] == a.seg_offsets[e]) return;
-  } else {
-    if (tid < 64) {
-      int ee, c;
-      locate_chunk<COH>(a, unit, 16, tid, &ee, &c);
-      if (tid == 0) { s_loc[0] = ee; s_loc[1] = c; }
-    }
-    __syncthreads();
-    e = s_loc[0];
-    if (e < 0) return;
-    slot0 = ld_route<COH>(&a.seg_offsets[e]) + s_loc[1] * 16;
-    slot_end = min(ld_route<COH>(&a.seg_offsets[e + 1]), slot0 + 16);
+  if (tid < 64) {
+    int ee, c;
+    locate_chunk<COH>(a, unit, 16, tid, &ee, &c);
+    if (tid == 0) { s_loc[0] = ee; s_loc[1] = c; }
   }
+  __syncthreads();
+  const int e = s_loc[0];
+  if (e < 0) return;
+  const int slot0 = ld_route<COH>(&a.seg_offsets[e]) + s_loc[1] * 16;
+  const int slot_end = min(ld_route<COH>(&a.seg_offsets[e + 1]), slot0 + 16);
 
   const ProjDesc pd = proj_at(a, proj);
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* Ae = static_cast<const bf16_t*>(pd.A) + (size_t)e * a.r * a.d_in;
   const int lr = lane & 15, kg = lane >> 4;
-  const bf16_t* xp[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int t;
-    if (DENSE)
-      t = min(nt * 16 + lr, a.T - 1);
-    else
-      t = ld_route<COH>(&a.pair_perm[min(slot0 + nt * 16 + lr, slot_end - 1)]) / a.k;
-    xp[nt] = x + (size_t)t * a.ld_x;
-  }
+  const bf16_t* xp = x + (size_t)(ld_route<COH>(&a.pair_perm[min(slot0 + lr, slot_end - 1)]) / a.k) * a.ld_x;
   const bf16_t* ap[MTR];
   bool aok[MTR];
 #pragma unroll
@@ -153,13 +178,11 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
   const int nsteps = (a.d_in + 31) >> 5;
   const int pb = nsteps * kp / d.KP, pe = nsteps * (kp + 1) / d.KP;
   const int sb = pb + (pe - pb) * wave / kWV, se = pb + (pe - pb) * (wave + 1) / kWV;
-  f32x4_t acc[MTR][NT];
+  f32x4_t acc[MTR];
 #pragma unroll
-  for (int mt = 0; mt < MTR; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MTR; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s = sb; s < se; s += U) {
-    uint4 av[U][MTR], bv[U][NT];
+    uint4 av[U][MTR], bv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = (s + u) * 32 + kg * 8;
@@ -167,50 +190,33 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
       const int kc = min(k, a.d_in - 8);
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) av[u][mt] = sel4(ok && aok[mt], ld16(ap[mt] + kc));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bv[u][nt] = sel4(ok, ld16(xp[nt] + kc));
+      bv[u] = sel4(ok, ld16(xp + kc));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MTR; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(av[u][mt], bv[u][nt], acc[mt][nt]);
+      for (int mt = 0; mt < MTR; ++mt) acc[mt] = mfma16(av[u][mt], bv[u], acc[mt]);
   }
-  // wave 0 + wave 1, in that order; D layout: lane -> column nt*16 + lane%16,
+  // wave 0 + wave 1, in that order; D layout: lane -> pair slot0 + lane%16,
   // rank rows mt*16 + 4*(lane/16) + 0..3
   if (wave == 1) {
 #pragma unroll
-    for (int mt = 0; mt < MTR; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f32x4_t*>(&red[((mt * NT + nt) * 64 + lane) * 4]) = acc[mt][nt];
+    for (int mt = 0; mt < MTR; ++mt) *reinterpret_cast<f32x4_t*>(&red[(mt * 64 + lane) * 4]) = acc[mt];
   }
   __syncthreads();
   if (wave == 0) {
     const size_t slots = upart_slots(a, d);
     const float* ub = a.u + ((size_t)proj * d.KP + kp) * slots * a.r;
     const __amdgpu_buffer_rsrc_t r = rsrc(ub, (uint32_t)(slots * a.r * sizeof(float)));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      int slot;
-      bool ok;
-      if (DENSE) {
-        const int t = nt * 16 + lr;
-        ok = t < a.T;
-        slot = e * d.t_pad + t;
-      } else {
-        const int s = slot0 + nt * 16 + lr;
-        ok = s < slot_end;
-        slot = ok ? ld_route<COH>(&a.pair_perm[s]) : 0;
-      }
-      if (!ok) continue;
+    const int s = slot0 + lr;
+    if (s < slot_end) {
+      const int p = ld_route<COH>(&a.pair_perm[s]);
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) {
         const int c = mt * 16 + 4 * kg;
         if (c < a.r) {
-          const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[((mt * NT + nt) * 64 + lane) * 4]);
-          st_coh16(r, (uint32_t)(((size_t)slot * a.r + c) * sizeof(float)), acc[mt][nt] + o);
+          const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[(mt * 64 + lane) * 4]);
+          st_coh16(r, (uint32_t)(((size_t)p * a.r + c) * sizeof(float)), acc[mt] + o);
         }
       }
     }
@@ -220,25 +226,39 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 // ---------------------------------------------------------------------------
 // base item
 // ---------------------------------------------------------------------------
-template <int MT, bool TILED, bool FUSED>
+// One output tile of 32 rows over one K split.  With ATILE the rows are
+// those of the stacked adapter down-projections [A_0; ..; A_{E-1}] of one
+// projection and the result is the rank-r intermediate u[e][t] (fp32, every
+// token) instead of y.  The last of a tile's S splits applies the adapter
+// deltas and sums the other splits' partial tiles; the operands of its first
+// expand pass are requested during its final chunk pair, so they arrive while
+// the last chunks compute.
+template <int MT, bool TILED, bool FUSED, bool ATILE>
 __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d, int bi, bf16_t* xs, int* ctl, int* s_ep,
-                          bool first, int ep_in, int* arrive_old, int* s_flag) {
+                          bool first, int ep_in, int* arrive_old) {
   constexpr int TP = 16 * MT;
   constexpr int XCH = TP * kKC / 8 / kThreads;  // 16-byte x pieces per thread per chunk
+  constexpr int G = 8;                          // adapters per batch of B loads
+  constexpr uint32_t kOob = 0x80000000u;        // past any buffer: a buffer load returns zero
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = bi / a.S, split = bi % a.S;
-  const int proj = proj_of_tile(a, tile);
+  const int S = ATILE ? d.SA : a.S;
+  const int tile = bi / S, split = bi % S;
+  const bool last = split == S - 1;
+  const bool expand = !ATILE && a.k > 0 && last;
+  const int proj = ATILE ? tile / d.atiles_per_proj : proj_of_tile(a, tile);
   const ProjDesc pd = proj_at(a, proj);
-  const int row0 = (tile - pd.tile_begin) * kTileRows + wave * 16;
+  const int n_rows = ATILE ? a.E * a.r : pd.d_out;
+  const int row0 = (ATILE ? tile % d.atiles_per_proj : tile - pd.tile_begin) * kTileRows + wave * 16;
   const int lr = lane & 15, kg = lane >> 4;
-  const int row = min(row0 + lr, pd.d_out - 1);
+  const int row = min(row0 + lr, n_rows - 1);
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
   // row-major: this lane's row at column 8*kg; tiled: this wave's run of 1 KB blocks
   const bf16_t* wrow = TILED
       ? static_cast<const bf16_t*>(pd.W0) + (size_t)(row0 / 16) * (a.d_in / 32) * 512 + lane * 8
-      : static_cast<const bf16_t*>(pd.W0) + (size_t)row * a.d_in + kg * 8;
+      : static_cast<const bf16_t*>(ATILE ? pd.A : pd.W0) + (size_t)row * a.d_in + kg * 8;
   const int nch = (a.d_in + kKC - 1) / kKC;
-  const int cb = (int)((long long)nch * split / a.S), ce = (int)((long long)nch * (split + 1) / a.S);
+  const int cb = (int)((long long)nch * split / S), ce = (int)((long long)nch * (split + 1) / S);
 
   f32x4_t acc[MT];
 #pragma unroll
@@ -285,16 +305,69 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       }
   };
 
-  // the lane's tokens' choices; known before the launch unless routing runs in it
+  // routing of the lane's tokens, slots 0..k-1: read before the stream when
+  // the registers allow (and this launch does not compute it), else after
+  constexpr bool kEarlyRoute = MT <= 2;
   int sel[MT][kMaxK];
-  if (!FUSED) {
+  float gate[MT][kMaxK];
+  auto read_route = [&]() {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = m * 16 + lr;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        const bool v = j < a.k && t < a.T;
+        sel[m][j] = v ? a.topk_idx[t * a.k + j] : -1;
+        gate[m][j] = v ? a.topk_gate[t * a.k + j] : 0.f;
+      }
+    }
+  };
+  if (!FUSED && expand && kEarlyRoute) read_route();
+
+  // operands of the first expand pass (rank columns 8*kg..+7, slots 0 and 1),
+  // requested in the final chunk pair
+  const int c_first = min(kg * 8, a.r - 8);
+  const __amdgpu_buffer_rsrc_t ru =
+      rsrc(reinterpret_cast<const char*>(a.u) + (size_t)proj * a.E * d.t_pad * a.r * 8,
+           (uint32_t)((size_t)a.E * d.t_pad * a.r * 8));
+  const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)a.T * a.k * 16));
+  constexpr bool kPrefetchU = MT <= 2;  // registers allow the u pairs to ride along too
+  uint4 bpf[G];                         // B rows of adapters 0..G-1, this lane's output row
+  u32x4_v upf[kPrefetchU ? MT : 1][2][4];  // dense u as tagged pairs (non-fused: the choices are known)
+  u32x4_v rpf[MT][2];                   // fused: tagged (index, gate) of the lane's tokens, slots 0 and 1
+  auto u_offset = [&](int m, int q, int c) -> uint32_t {
+    const int t = m * 16 + lr;
+    const bool ok = q < a.k && c < a.r && sel[m][min(q, kMaxK - 1)] >= 0;
+    return ok ? (uint32_t)((((size_t)sel[m][min(q, kMaxK - 1)] * d.t_pad + t) * a.r + c) * 8) : kOob;
+  };
+  auto load_u4 = [&](u32x4_v (&w)[4], uint32_t off) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off == kOob ? kOob : off + 16 * i, 0, kSc1);
+  };
+  auto load_route = [&](u32x4_v (&r)[MT][2], int j0) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int t = min(m * 16 + lr, a.T - 1);
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) sel[m][j] = (j < a.k && m * 16 + lr < a.T) ? a.topk_idx[t * a.k + j] : -1;
+      for (int q = 0; q < 2; ++q)
+        r[m][q] = __builtin_amdgcn_raw_buffer_load_b128(rt, j0 + q < a.k ? (uint32_t)((t * a.k + j0 + q) * 16) : kOob, 0,
+                                                         kSc1);
     }
-  }
+  };
+  auto prefetch = [&]() {
+    if (!expand || !kEarlyRoute) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) bpf[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + c_first);
+    if (FUSED) {
+      load_route(rpf, 0);
+    } else if (kPrefetchU && d.dense) {
+#pragma unroll
+      for (int m = 0; m < (kPrefetchU ? MT : 1); ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) load_u4(upf[m][q], u_offset(m, q, kg * 8));
+    }
+  };
 
   {
     uint4 wA[kSteps], wB[kSteps], XA[XCH], XB[XCH];
@@ -305,6 +378,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       *s_ep = ep_in;
       *arrive_old = arrive(ctl, ep_in);
     }
+    if (ce - cb < 2) prefetch();
     store_x(XA, 0, cb);
     __syncthreads();
     // chunk pairs, no exit between the two halves; an odd last chunk follows
@@ -314,6 +388,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       __builtin_amdgcn_sched_barrier(0);
       load_w(wB, c + 1);
       load_x(XA, c + 2);
+      if (c + 4 > ce) prefetch();
       __builtin_amdgcn_sched_barrier(0);
       compute(wA, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -333,61 +408,139 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   }
   const int ep = *s_ep;
   int* set = ctl_set(ctl, ep);
+  const uint32_t tag = launch_tag(ep);
 
-  // adapter deltas for this wave's 16 rows: adapters e = split, split + S, ...
-  // A lane's tokens chose at most k adapters, so it needs u only for its own
-  // (token, slot) pairs: their KP partials are loaded two slots per pass,
-  // summed in part order and scaled by the gate; the operand for adapter e is
-  // then picked in registers.  B rows are loaded eight adapters at a time.
-  if (a.k > 0) {
-    if (FUSED) wait_geq(ctl, &set[kSetRouteDone], d.n_route);
-    wait_geq(ctl, &set[kSetShrinkDone], d.n_shrink);
+  // adapter deltas for this wave's 16 rows.  A lane's tokens chose at most k
+  // adapters, so it needs u only for its own (token, slot) pairs, two slots
+  // per pass, scaled by the gate; the operand for adapter e is then picked in
+  // registers.  B rows are loaded eight adapters at a time.
+  if (expand) {
+    if (!FUSED && !kEarlyRoute) read_route();
     if (FUSED) {
+      // the routing this launch's router tiles wrote, validated by tag; slots
+      // 0 and 1 were requested in the final chunk pair, the rest go now
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int t = min(m * 16 + lr, a.T - 1);
+      for (int j0 = 0; j0 < kMaxK; j0 += 2) {
+        if (j0 >= a.k) break;
+        u32x4_v r[MT][2];
+        if (j0 == 0 && kEarlyRoute) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) r[m][0] = rpf[m][0], r[m][1] = rpf[m][1];
+        } else {
+          load_route(r, j0);
+        }
+        int spins = 0;
+        while (true) {
+          bool good = true;
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const bool v = j0 + q < a.k && m * 16 + lr < a.T;
+              sel[m][j0 + q] = v ? (int)r[m][q].x : -1;
+              gate[m][j0 + q] = v ? __uint_as_float(r[m][q].z) : 0.f;
+              if (v) good &= r[m][q].y == tag && r[m][q].w == tag;
+            }
+          if (!retry_tagged(ctl, good, &spins)) break;
+          load_route(r, j0);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
-          sel[m][j] = (j < a.k && m * 16 + lr < a.T) ? ld_route<true>(&a.topk_idx[t * a.k + j]) : -1;
-      }
+          if (j >= a.k) sel[m][j] = -1, gate[m][j] = 0.f;
     }
-    const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
+    if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone], d.shrink_target);
     const size_t slots = upart_slots(a, d);
-    const float* ub = a.u + (size_t)proj * d.KP * slots * a.r;
-    const __amdgpu_buffer_rsrc_t ur = rsrc(ub, (uint32_t)((size_t)d.KP * slots * a.r * sizeof(float)));
-    constexpr uint32_t kOob = 0x80000000u;  // past any buffer: the load returns zero
-    constexpr int G = 8;                    // adapters per batch of B loads
+    const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
+    const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
     for (int c0 = 0; c0 < a.r; c0 += 32) {
       const int c = c0 + kg * 8;
       const int cc = min(c, a.r - 8);
       for (int jp = 0; jp < a.k; jp += 2) {
         f32x4_t uu[MT][2][2];
+        if (d.dense) {
+          // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
+          // at a time (all their loads out before any is checked)
+          constexpr int MU = MT <= 2 ? MT : 2;
+#pragma unroll
+          for (int m0 = 0; m0 < MT; m0 += MU) {
+            u32x4_v w[MU][2][4];
+            uint32_t offv[MU][2];
+#pragma unroll
+            for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                offv[mm][q] = u_offset(m0 + mm, jp + q, c);
+                if (kPrefetchU && !FUSED && c0 == 0 && jp == 0) {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) w[mm][q][i] = upf[kPrefetchU ? m0 + mm : 0][q][i];
+                } else {
+                  load_u4(w[mm][q], offv[mm][q]);
+                }
+              }
+            int spins = 0;
+            while (true) {
+              bool good = true;
+#pragma unroll
+              for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                  for (int i = 0; i < 2; ++i) {
+                    const u32x4_v& lo4 = w[mm][q][2 * i];
+                    const u32x4_v& hi4 = w[mm][q][2 * i + 1];
+                    uu[m0 + mm][q][i] = f32x4_t{__uint_as_float(lo4.x), __uint_as_float(lo4.z), __uint_as_float(hi4.x),
+                                                __uint_as_float(hi4.z)};
+                    if (offv[mm][q] != kOob) good &= lo4.y == tag && lo4.w == tag && hi4.y == tag && hi4.w == tag;
+                  }
+              if (!retry_tagged(ctl, good, &spins)) break;
+#pragma unroll
+              for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) load_u4(w[mm][q], offv[mm][q]);
+            }
+          }
+        } else {
+          const uint32_t part = (uint32_t)(slots * a.r * sizeof(float));
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int t = m * 16 + lr, j = min(jp + q, kMaxK - 1);
+              const bool ok = jp + q < a.k && c < a.r && sel[m][j] >= 0;
+              const uint32_t off = ok ? (uint32_t)((((size_t)t * a.k + j) * a.r + cc) * sizeof(float)) : kOob;
+              uu[m][q][0] = ld_coh16(rp, off);
+              uu[m][q][1] = ld_coh16(rp, ok ? off + 16 : kOob);
+              for (int kp = 1; kp < d.KP; ++kp) {
+                uu[m][q][0] += ld_coh16(rp, ok ? off + kp * part : kOob);
+                uu[m][q][1] += ld_coh16(rp, ok ? off + kp * part + 16 : kOob);
+              }
+            }
+        }
+        // gated operands of the two slots, split once into (hi, lo) bf16 parts
+        uint4 uhi[MT][2], ulo[MT][2];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const int j = min(jp + q, kMaxK - 1);
-            const int t = m * 16 + lr;
-            const bool ok = jp + q < a.k && c < a.r && sel[m][j] >= 0;
-            const size_t slot = d.dense ? (size_t)max(sel[m][j], 0) * d.t_pad + t : (size_t)t * a.k + j;
-            const uint32_t off = ok ? (uint32_t)((slot * a.r + cc) * sizeof(float)) : kOob;
-            const uint32_t part = (uint32_t)(slots * a.r * sizeof(float));
-            f32x4_t s0 = ld_coh16(ur, off), s1 = ld_coh16(ur, ok ? off + 16 : kOob);
-            for (int kp = 1; kp < d.KP; ++kp) {
-              s0 += ld_coh16(ur, ok ? off + kp * part : kOob);
-              s1 += ld_coh16(ur, ok ? off + kp * part + 16 : kOob);
+            const float g = gate[m][min(jp + q, kMaxK - 1)];
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = g * uu[m][q][0][i];
+              v[4 + i] = g * uu[m][q][1][i];
             }
-            const float g = ok ? ld_route<FUSED>(&a.topk_gate[min(t, a.T - 1) * a.k + j]) : 0.f;
-            uu[m][q][0] = g * s0;
-            uu[m][q][1] = g * s1;
+            split_hi_lo(v, uhi[m][q], ulo[m][q]);
           }
-        for (int e0 = split; e0 < a.E; e0 += G * a.S) {
+        for (int e0 = 0; e0 < a.E; e0 += G) {
           int js[G][MT];  // slot (jp or jp+1) of the lane's token that chose adapter e, else -1
           bool any[G];
           bool group = false;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const int e = e0 + g * a.S;
+            const int e = e0 + g;
             any[g] = false;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -401,13 +554,14 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           }
           if (!group) continue;
           uint4 bo[G];
-          __builtin_amdgcn_sched_barrier(0);
+          if (kEarlyRoute && c0 == 0 && e0 == 0) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const int e = min(e0 + g * a.S, a.E - 1);
-            bo[g] = ld16(Bm + ((size_t)e * pd.d_out + row) * a.r + cc);
+            for (int g = 0; g < G; ++g) bo[g] = bpf[g];
+          } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+              bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             if (!any[g]) continue;
@@ -415,14 +569,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               const int q = js[g][m];
-              float v[8];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                v[i] = q == 0 ? uu[m][0][0][i] : (q == 1 ? uu[m][1][0][i] : 0.f);
-                v[4 + i] = q == 0 ? uu[m][0][1][i] : (q == 1 ? uu[m][1][1][i] : 0.f);
-              }
-              uint4 hi, lo;
-              split_hi_lo(v, hi, lo);
+              const uint4 hi = q == 0 ? uhi[m][0] : (q == 1 ? uhi[m][1] : zero4());
+              const uint4 lo = q == 0 ? ulo[m][0] : (q == 1 ? ulo[m][1] : zero4());
               acc[m] = mfma16(hi, b, acc[m]);
               acc[m] = mfma16(lo, b, acc[m]);
             }
@@ -432,35 +580,63 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     }
   }
 
-  if (a.S > 1) {
-    // split-K: splits 0..S-2 publish their partial tiles and count in; the
-    // last split waits for them and sums all S in split order
-    constexpr int kWaveBytes = MT * 64 * 16;
-    const size_t tile_bytes = (size_t)a.S * kWV * kWaveBytes;
-    const __amdgpu_buffer_rsrc_t pr = rsrc(reinterpret_cast<char*>(a.partial) + tile * tile_bytes, (uint32_t)tile_bytes);
-    int* tc = &ctl[kCtlTiles + tile];
-    if (split != a.S - 1) {
+  if (S > 1) {
+    // split-K: splits 0..S-2 publish their partial tiles as tagged pairs; the
+    // last split reads them as they land and sums all S in split order
+    constexpr int kWaveBytes = MT * 64 * 32;
+    const size_t tile_bytes = (size_t)S * kWV * kWaveBytes;
+    const __amdgpu_buffer_rsrc_t pr =
+        rsrc(reinterpret_cast<char*>(ATILE ? d.partial_a : a.partial) + tile * tile_bytes, (uint32_t)tile_bytes);
+    if (!last) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        st_coh16(pr, (uint32_t)((split * kWV + wave) * kWaveBytes + (m * 64 + lane) * 16), acc[m]);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(tc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_tagged4(pr, (uint32_t)((split * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32), acc[m], tag);
       return;
     }
-    wait_geq(ctl, tc, a.S - 1);
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(tc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // all S-1 partials are requested in one pass (retried whole while any tag
+    // is stale), then summed in split order
     f32x4_t tot[MT];
+    int spins = 0;
+    bool good;
+    do {
+      good = true;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) tot[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
+      for (int m = 0; m < MT; ++m) tot[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      constexpr int SU = MT <= 2 ? kMaxSplits : 2;  // splits whose loads go out together
+      for (int s0 = 0; s0 < S; s0 += SU) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        tot[m] += (s == split) ? acc[m] : ld_coh16(pr, (uint32_t)((s * kWV + wave) * kWaveBytes + (m * 64 + lane) * 16));
-    }
+        for (int i = 0; i < SU; ++i) {
+          const int s = s0 + i;
+          if (s >= S) break;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            f32x4_t part = acc[m];
+            if (s != split)
+              good &= ld_tagged4(pr, (uint32_t)((s * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32), tag, part);
+            tot[m] += part;
+          }
+        }
+      }
+    } while (retry_tagged(ctl, good, &spins));
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = tot[m];
+  }
+
+  if (ATILE) {
+    // u[proj][e][t][c] for row e*r + c, as tagged pairs (one 8-byte store each)
+    if (row0 + lr < n_rows) {
+      const int e = (row0 + lr) / a.r, c = (row0 + lr) % a.r;
+      unsigned long long* u = reinterpret_cast<unsigned long long*>(a.u) + (((size_t)proj * a.E + e) * d.t_pad) * a.r + c;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = m * 16 + 4 * kg + v;
+          const unsigned long long pair = ((unsigned long long)tag << 32) | __float_as_uint(acc[m][v]);
+          if (t < a.T) __hip_atomic_store(&u[(size_t)t * a.r], pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    return;
   }
 
   // store: lane -> output row row0 + lane%16; accumulator v -> token m*16 + 4*(lane/16) + v
@@ -482,7 +658,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 template <int MT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_kernel(SgmmArgs a, DecodeArgs d) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<MT, FUSED>()];
-  __shared__ int s_ep, s_loc[2], s_flag, s_wave_tot[2], s_bad;
+  __shared__ int s_ep, s_loc[2], s_wave_tot[2], s_bad;
   int* ctl = a.counters;
   const int tid = threadIdx.x;
   // the epoch is read once per workgroup; base items publish it after their
@@ -505,10 +681,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(SgmmArgs a, DecodeArgs
       int* set = ctl_set(ctl, s_ep);
       const RoutePlan rpl = route_plan(d.pg.E, d.pg.d_in, (int)sizeof(bf16_t));
       float* f = reinterpret_cast<float*>(smem);
-      if (rpl.TT == 4)
-        route_tile<bf16_t, 4>(d.pg, item * 4, rpl, f);
-      else
-        route_tile<bf16_t, 2>(d.pg, item * 2, rpl, f);
+      // two tokens per tile whatever E (the sums do not depend on the tile size)
+      route_tile<bf16_t, kFusedRouteTokens>(d.pg, item * kFusedRouteTokens, rpl, f,
+                                            reinterpret_cast<unsigned long long*>(d.route_tagged), launch_tag(s_ep));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) atomicAdd(&set[kSetRouteDone], 1);
@@ -519,26 +694,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(SgmmArgs a, DecodeArgs
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) atomicAdd(&set[kSetSegDone], 1);
+    } else if (item < n_base0 && d.dense) {
+      base_item<MT, false, FUSED, true>(a, d, item - d.n_pre, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first,
+                                        ep_in, &arrive_old);
+      first = false;
     } else if (item < n_base0) {
       int* set = ctl_set(ctl, s_ep);
       const int si = item - d.n_pre;
       const int proj = si / d.units_per_proj, w = si % d.units_per_proj;
       const int unit = w / d.KP, kp = w % d.KP;
       float* red = reinterpret_cast<float*>(smem);
-      if (d.dense) {
-        switch ((a.r + 15) >> 4) {
-          case 1: shrink_item<1, MT, true, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 2: shrink_item<2, MT, true, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 4: shrink_item<4, MT, true, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          default: shrink_item<8, MT, true, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-        }
-      } else {
+      {
         if (FUSED) wait_geq(ctl, &set[kSetSegDone], 1);
         switch ((a.r + 15) >> 4) {
-          case 1: shrink_item<1, 1, false, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 2: shrink_item<2, 1, false, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 4: shrink_item<4, 1, false, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          default: shrink_item<8, 1, false, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
+          case 1: shrink_item<1, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
+          case 2: shrink_item<2, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
+          case 4: shrink_item<4, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
+          default: shrink_item<8, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
         }
       }
       // the u stores are device-coherent; wait for them before counting this unit done
@@ -549,11 +721,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(SgmmArgs a, DecodeArgs
       const int bi = item - n_base0;
       const int bp = proj_of_tile(a, bi / a.S);
       if (RP_PICK(a, bp, tiled))
-        base_item<MT, true, FUSED>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in, &arrive_old,
-                                   &s_flag);
+        base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
+                                          &arrive_old);
       else
-        base_item<MT, false, FUSED>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in, &arrive_old,
-                                    &s_flag);
+        base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
+                                           &arrive_old);
       first = false;
     }
     __syncthreads();  // LDS is reused by the next item
@@ -589,13 +761,24 @@ int resident_per_cu() {
   return n;
 }
 
-template <bool FUSED>
-hipError_t launch_t(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan, hipStream_t s) {
+hipError_t launch_plain(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan, hipStream_t s) {
   const dim3 grid(plan.grid);
   switch (decode_mt(a.T)) {
-    case 1: decode_kernel<1, FUSED><<<grid, kThreads, 0, s>>>(a, d); break;
-    case 2: decode_kernel<2, FUSED><<<grid, kThreads, 0, s>>>(a, d); break;
-    default: decode_kernel<4, FUSED><<<grid, kThreads, 0, s>>>(a, d); break;
+    case 1: decode_kernel<1, false><<<grid, kThreads, 0, s>>>(a, d); break;
+    case 2: decode_kernel<2, false><<<grid, kThreads, 0, s>>>(a, d); break;
+    default: decode_kernel<4, false><<<grid, kThreads, 0, s>>>(a, d); break;
+  }
+  return hipGetLastError();
+}
+
+// Routing inside the launch is built for up to two token tiles (T <= 32);
+// larger decode batches route in launches of their own.
+hipError_t launch_fused(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan, hipStream_t s) {
+  const dim3 grid(plan.grid);
+  switch (decode_mt(a.T)) {
+    case 1: decode_kernel<1, true><<<grid, kThreads, 0, s>>>(a, d); break;
+    case 2: decode_kernel<2, true><<<grid, kThreads, 0, s>>>(a, d); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -605,21 +788,30 @@ hipError_t launch_t(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan
 int decode_mt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 int decode_chunk_k(int T) { (void)T; return kKC; }
 int decode_tile_rows() { return kTileRows; }
+int fused_route_tile_tokens() { return kFusedRouteTokens; }
 
 int decode_resident_per_cu(int T, bool fused) {
   switch (decode_mt(T)) {
     case 1: return fused ? resident_per_cu<1, true>() : resident_per_cu<1, false>();
     case 2: return fused ? resident_per_cu<2, true>() : resident_per_cu<2, false>();
-    default: return fused ? resident_per_cu<4, true>() : resident_per_cu<4, false>();
+    default: return resident_per_cu<4, false>();
   }
 }
+
+bool decode_fused_route_supported(int T) { return decode_mt(T) <= 2; }
 
 static DecodeArgs decode_args(const SgmmArgs& a, const SgmmPlan& plan) {
   DecodeArgs d{};
   d.n_route = plan.n_route;
   d.n_pre = plan.n_pre;
   d.units_per_proj = plan.units_per_proj;
-  d.n_shrink = plan.units_per_proj * a.n_proj;
+  d.atiles_per_proj = plan.atiles_per_proj;
+  d.n_atiles = plan.n_atiles;
+  d.SA = plan.SA;
+  d.n_shrink = plan.dense ? plan.n_atiles * plan.SA : plan.units_per_proj * a.n_proj;
+  d.shrink_target = d.n_shrink;  // pair-chunk units (dense u is tagged instead)
+  d.partial_a = a.partial + (plan.off_partial_a - plan.off_partial) / sizeof(float);
+  d.route_tagged = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(a.counters) + plan.off_route);
   d.n_items = plan.n_items;
   d.KP = plan.KP;
   d.dense = plan.dense;
@@ -630,7 +822,7 @@ static DecodeArgs decode_args(const SgmmArgs& a, const SgmmPlan& plan) {
 hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s) {
   DecodeArgs d = decode_args(a, plan);
   d.fused = 0;
-  return launch_t<false>(a, d, plan, s);
+  return launch_plain(a, d, plan, s);
 }
 
 hipError_t launch_route_sgmm(const SgmmArgs& a, const PregateArgs& pg, const SegmentArgs& sg, const SgmmPlan& plan,
@@ -639,7 +831,7 @@ hipError_t launch_route_sgmm(const SgmmArgs& a, const PregateArgs& pg, const Seg
   d.fused = 1;
   d.pg = pg;
   d.sg = sg;
-  return launch_t<true>(a, d, plan, s);
+  return launch_fused(a, d, plan, s);
 }
 
 }  // namespace rp

@@ -9,8 +9,6 @@ namespace rp {
 
 namespace {
 constexpr size_t kCounterBytes = 65536;  // reserved control region at the start of the workspace
-constexpr int kCtlTilesOffset = 4096;    // control words before the split-K tile counters
-constexpr int kMaxTileCounters = (int)(kCounterBytes / sizeof(int)) - kCtlTilesOffset;
 constexpr int kDecodeTileRows = 32;
 constexpr int kDecodeMaxT = 64;
 constexpr int kPrefillTileRows = 128;
@@ -18,7 +16,8 @@ constexpr int kF32TileRows = 64;
 constexpr int kDenseMaxE = 32;      // decode shrink covers every token per adapter up to this many adapters
 constexpr int kMaxSplits = 8;       // decode split-K
 constexpr int kMaxKParts = 8;       // decode shrink K parts
-constexpr int kShrinkPartBytes = 32768;  // target A bytes per decode shrink unit
+constexpr int kShrinkPartBytes = 16384;  // target A bytes per decode shrink unit
+constexpr int kItemsPerCu2 = 3;          // twice the backbone items per CU a decode launch aims for
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -31,15 +30,18 @@ int shrink_kparts(int d_in, int r) {
   return kp;
 }
 
+// dense u and split-K partials are (fp32, tag) pairs: 8 bytes per value
 size_t decode_u_bytes(int n_proj, int T, int E, int r, int k, int KP, bool dense) {
   const size_t t_pad = (size_t)16 * decode_mt(T);
-  const size_t slots = dense ? (size_t)E * t_pad : (size_t)T * k;
-  return (size_t)n_proj * KP * slots * r * sizeof(float);
+  if (dense) return (size_t)n_proj * E * t_pad * r * 8;
+  return (size_t)n_proj * KP * T * k * r * sizeof(float);
 }
 
 size_t decode_partial_bytes(int n_tiles, int S, int T) {
-  return S > 1 ? (size_t)n_tiles * S * 16 * decode_mt(T) * kDecodeTileRows * sizeof(float) : 0;
+  return S > 1 ? (size_t)n_tiles * S * 16 * decode_mt(T) * kDecodeTileRows * 8 : 0;
 }
+
+int a_tiles_per_proj(int E, int r) { return (E * r + kDecodeTileRows - 1) / kDecodeTileRows; }
 }  // namespace
 
 SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
@@ -64,16 +66,34 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
   // it can run together
   p.t_pad = 16 * decode_mt(T);
   p.dense = E <= kDenseMaxE;
-  p.KP = k > 0 ? shrink_kparts(d_in, r) : 1;
-  p.units_per_proj = k > 0 ? (p.dense ? E : E + (T * k + 15) / 16) * p.KP : 0;
-  p.n_route = fused_route ? (T + route_tile_tokens(E) - 1) / route_tile_tokens(E) : 0;
-  p.n_pre = fused_route ? p.n_route + 1 : 0;
-  const int n_shrink = p.units_per_proj * n_proj;
-  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
   const int nchunks = (d_in + decode_chunk_k(T) - 1) / decode_chunk_k(T);
   int s_max = std::max(1, std::min(kMaxSplits, nchunks / 2));
-  if (p.n_tiles > kMaxTileCounters) s_max = 1;
-  int S = (cap - p.n_pre - n_shrink) / p.n_tiles;
+  p.KP = 1;
+  p.units_per_proj = 0;
+  p.atiles_per_proj = p.n_atiles = 0;
+  p.SA = 1;
+  int n_shrink = 0;
+  if (k > 0 && p.dense) {
+    // the shrink as row tiles of [A_0; ..; A_{E-1}], split along K more finely
+    // than the backbone so its results are ready before the backbone's
+    p.atiles_per_proj = a_tiles_per_proj(E, r);
+    p.n_atiles = p.atiles_per_proj * n_proj;
+    p.SA = s_max;
+    n_shrink = p.n_atiles * p.SA;
+  } else if (k > 0) {
+    p.KP = shrink_kparts(d_in, r);
+    p.units_per_proj = (E + (T * k + 15) / 16) * p.KP;
+    n_shrink = p.units_per_proj * n_proj;
+  }
+  p.n_route = fused_route ? (T + fused_route_tile_tokens() - 1) / fused_route_tile_tokens() : 0;
+  p.n_pre = fused_route ? p.n_route + 1 : 0;
+  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
+
+  // about 1.5 backbone items per CU: enough loads in flight to saturate HBM,
+  // and no more (extra bytes in flight only queue, and every dependent round
+  // trip of the launch then waits behind them)
+  int S = (kItemsPerCu2 * n_cu / 2 + p.n_tiles / 2) / p.n_tiles;
+  S = std::min(S, (cap - p.n_pre - n_shrink) / p.n_tiles);
   if (const char* env = std::getenv("RP_DECODE_SPLITS")) {  // tuning override
     const int v = std::atoi(env);
     if (v > 0) S = v;
@@ -84,6 +104,10 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
   off = align256(off + decode_u_bytes(n_proj, T, E, r, k, p.KP, p.dense));
   p.off_partial = off;
   off = align256(off + decode_partial_bytes(p.n_tiles, p.S, T));
+  p.off_partial_a = off;
+  off = align256(off + decode_partial_bytes(p.n_atiles, p.SA, T));
+  p.off_route = off;  // fused launches: tagged routing results
+  if (fused_route) off = align256(off + (size_t)T * k * 16);
   p.bytes = off;
   return p;
 }
@@ -91,10 +115,13 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r, int k) {
   size_t b = kCounterBytes;
   if (dt == kBF16 && T <= kDecodeMaxT) {
-    const int KP = k > 0 ? shrink_kparts(d_in, r) : 1;
-    b = align256(b + decode_u_bytes(n_proj, T, E, r, k, KP, E <= kDenseMaxE));
+    const bool dense = E <= kDenseMaxE;
+    const int KP = (k > 0 && !dense) ? shrink_kparts(d_in, r) : 1;
+    b = align256(b + decode_u_bytes(n_proj, T, E, r, k, KP, dense));
     const int tiles = (int)(sum_d_out / kDecodeTileRows + n_proj);
     b = align256(b + decode_partial_bytes(tiles, kMaxSplits, T));
+    if (k > 0 && dense) b = align256(b + decode_partial_bytes(a_tiles_per_proj(E, r) * n_proj, kMaxSplits, T));
+    b = align256(b + (size_t)T * k * 16);
   } else {
     b = align256(b + (size_t)n_proj * T * k * r * sizeof(float));
   }
