@@ -43,16 +43,22 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the current kernels.
+
+    The summary is a text file of `key: value` lines; it names the kernel sources it was measured on."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
+    d = {}
     with open(path) as fh:
-        d = json.load(fh)
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                d[key.strip()] = val.strip()
     if d.get("kernel_src_sha") != kernel_source_hash():
         log(f"traffic counters in {path} predate the current kernels; reporting null")
         return None
-    return d.get("bytes_per_launch")
+    return int(d["bytes_per_launch"]) if "bytes_per_launch" in d else None
 
 
 def cpu_baseline(wl, seconds: float):
@@ -199,27 +205,47 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-        # the dominant call (first projection group, the widest), bracketed with
-        # events on the stream it is launched on, eager, over its own timed loop
+        # the dominant call (first projection group, the widest): one graph of
+        # that call alone on each weight copy in turn, replayed; events on the
+        # stream it is launched on bracket the replays
         g0 = wl.groups[0]
         layer = dw.layers[0]
         xg = dw.inputs[(layer, g0.x_name)]
-        evs = []
-        for i in range(args.steps):
-            W = dw.weights[i % copies]
+
+        def dominant(c):
+            W = dw.weights[c]
             projs = [(W[(layer, p)].W0, W[(layer, p)].A, W[(layer, p)].B, dw.outputs[(layer, p)]) for p in g0.projs]
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
             if fused:
                 rp.route_sgmm_fused(projs, xg, dw.Wg, wl.E, wl.r, wl.k, dw.topk_idx, dw.topk_gate, dw.seg_offsets,
                                     dw.pair_perm, ws=dw.ws)
             else:
                 rp.sgmm_fused(projs, xg, wl.E, wl.r, wl.k, dw.sel_idx, dw.sel_gate, dw.seg_offsets, dw.pair_perm,
                               ws=dw.ws)
+
+        reps = max(2, args.steps // copies)
+        if args.no_graph:
+            for c in range(copies):
+                dominant(c)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps * copies):
+                dominant(i % copies)
             b.record(stream)
-            evs.append((a, b))
+        else:
+            dg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(dg, stream=stream):
+                for c in range(copies):
+                    dominant(c)
+            dg.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                dg.replay()
+            b.record(stream)
         torch.cuda.synchronize()
-        dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        dom_ms = a.elapsed_time(b) / (reps * copies)
 
         # base-only (k = 0) step for the adapter overhead
         for i in range(3):
