@@ -22,12 +22,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even float -> bfloat16 (inputs are finite by contract).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 packed in one word (a in the low half), rounded to
+// nearest even by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+
+// Round-to-nearest-even float -> bfloat16 (inputs are finite by contract).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return static_cast<bf16_t>(f32x2_to_bf16x2(f, f) & 0xffffu); }
 
 // Eight packed bf16 (one 16-byte vector) as the MFMA operand type.
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -47,16 +52,16 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 // about 16 significant bits, so a bf16 MFMA on (hi, lo) keeps close to fp32
 // precision for the small rank-r operand.
 __device__ __forceinline__ void split_hi_lo(const float* v, uint4& hi, uint4& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bf16_t hb = f32_to_bf16(v[i]);
-    float rem = v[i] - bf16_to_f32(hb);
-    h[i] = hb;
-    l[i] = f32_to_bf16(rem);
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f32x2_to_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float r0 = v[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = v[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u);
+    l[i] = f32x2_to_bf16x2(r0, r1);
   }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {

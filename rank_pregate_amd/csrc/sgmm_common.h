@@ -72,24 +72,29 @@ __device__ __forceinline__ ProjDesc proj_at(const SgmmArgs& a, int p) {
 
 __device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : zero4(); }
 
-// The slot j with idx[t, j] == e, or -1.
-__device__ __forceinline__ int match_slot(const int* idx, int t, int k, int e) {
-  int js = -1;
-  for (int j = 0; j < k; ++j)
-    if (idx[t * k + j] == e) js = j;
-  return js;
+// True when some slot of token t chose adapter e.
+__device__ __forceinline__ bool chose(const int* idx, int t, int k, int e) {
+  bool any = false;
+  for (int j = 0; j < k; ++j) any |= idx[t * k + j] == e;
+  return any;
 }
 
-// Gated u row chunk [c, c+8) of pair p as hi/lo bf16 operands (zero if !ok).
-__device__ __forceinline__ void u_operand(const float* u, int r, int p, int c, bool ok, uint4& hi, uint4& lo) {
+// Gated u rows [c, c+8) summed over every slot of token t that chose adapter e
+// (a token may name one adapter in several slots), as hi/lo bf16 operands;
+// zero when !ok or no slot matches.
+__device__ __forceinline__ void u_operand(const float* u, const int* idx, int r, int t, int k, int e, int c, bool ok,
+                                          uint4& hi, uint4& lo) {
   float v[8];
-  if (ok) {
-    const float4 a = *reinterpret_cast<const float4*>(u + (size_t)p * r + c);
-    const float4 b = *reinterpret_cast<const float4*>(u + (size_t)p * r + c + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  if (ok) {
+    for (int j = 0; j < k; ++j) {
+      if (idx[t * k + j] != e) continue;
+      const float* p = u + (size_t)(t * k + j) * r + c;
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    }
   }
   split_hi_lo(v, hi, lo);
 }

@@ -519,37 +519,48 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
               }
             }
         }
+        // the two slots' adapters (dynamic index into sel, once per pass); a
+        // token that chose one adapter in both slots gets both gated terms in slot 0
+        int sa[MT][2];
+        bool dup[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) sa[m][q] = jp + q < a.k ? sel[m][min(jp + q, kMaxK - 1)] : -1;
+          dup[m] = sa[m][0] >= 0 && sa[m][0] == sa[m][1];
+        }
         // gated operands of the two slots, split once into (hi, lo) bf16 parts
         uint4 uhi[MT][2], ulo[MT][2];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m) {
+          const float g0 = gate[m][min(jp, kMaxK - 1)], g1 = gate[m][min(jp + 1, kMaxK - 1)];
+          float v0[8], v1[8];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const float g = gate[m][min(jp + q, kMaxK - 1)];
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v[i] = g * uu[m][q][0][i];
-              v[4 + i] = g * uu[m][q][1][i];
-            }
-            split_hi_lo(v, uhi[m][q], ulo[m][q]);
+          for (int i = 0; i < 4; ++i) {
+            v0[i] = g0 * uu[m][0][0][i];
+            v0[4 + i] = g0 * uu[m][0][1][i];
+            v1[i] = g1 * uu[m][1][0][i];
+            v1[4 + i] = g1 * uu[m][1][1][i];
           }
+          if (dup[m]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v0[i] += v1[i], v1[i] = 0.f;
+            sa[m][1] = -1;
+          }
+          split_hi_lo(v0, uhi[m][0], ulo[m][0]);
+          split_hi_lo(v1, uhi[m][1], ulo[m][1]);
+        }
         for (int e0 = 0; e0 < a.E; e0 += G) {
-          int js[G][MT];  // slot (jp or jp+1) of the lane's token that chose adapter e, else -1
+          // skip a batch no token of the tile chose; with many adapters, skip
+          // single adapters too (with few, all of them are applied branch-free)
           bool any[G];
           bool group = false;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const int e = e0 + g;
-            any[g] = false;
+            bool mine = false;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              js[g][m] = -1;
-#pragma unroll
-              for (int q = 0; q < 2; ++q)
-                if (jp + q < kMaxK && sel[m][min(jp + q, kMaxK - 1)] == e) js[g][m] = q;
-              any[g] |= __ballot(js[g][m] >= 0) != 0;
-            }
+            for (int m = 0; m < MT; ++m) mine |= sa[m][0] == e0 + g || sa[m][1] == e0 + g;
+            any[g] = __ballot(mine) != 0;
             group |= any[g];
           }
           if (!group) continue;
@@ -564,13 +575,16 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            if (!any[g]) continue;
-            const uint4 b = sel4(c < a.r, bo[g]);
+            if (!d.dense && !any[g]) continue;
+            const uint4 b = sel4(c < a.r && e0 + g < a.E, bo[g]);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-              const int q = js[g][m];
-              const uint4 hi = q == 0 ? uhi[m][0] : (q == 1 ? uhi[m][1] : zero4());
-              const uint4 lo = q == 0 ? ulo[m][0] : (q == 1 ? ulo[m][1] : zero4());
+              // operand of the slot that chose e0 + g (zero if none), by masks
+              const uint32_t k0 = sa[m][0] == e0 + g ? ~0u : 0u, k1 = sa[m][1] == e0 + g ? ~0u : 0u;
+              const uint4 hi = make_uint4((uhi[m][0].x & k0) | (uhi[m][1].x & k1), (uhi[m][0].y & k0) | (uhi[m][1].y & k1),
+                                          (uhi[m][0].z & k0) | (uhi[m][1].z & k1), (uhi[m][0].w & k0) | (uhi[m][1].w & k1));
+              const uint4 lo = make_uint4((ulo[m][0].x & k0) | (ulo[m][1].x & k1), (ulo[m][0].y & k0) | (ulo[m][1].y & k1),
+                                          (ulo[m][0].z & k0) | (ulo[m][1].z & k1), (ulo[m][0].w & k0) | (ulo[m][1].w & k1));
               acc[m] = mfma16(hi, b, acc[m]);
               acc[m] = mfma16(lo, b, acc[m]);
             }

@@ -165,13 +165,13 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
         bits &= bits - 1;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int js = tok_ok[f] ? match_slot(a.topk_idx, tok[f], a.k, e) : -1;
-          if (__ballot(js >= 0) == 0) continue;
+          const bool mine = tok_ok[f] && chose(a.topk_idx, tok[f], a.k, e);
+          if (__ballot(mine) == 0) continue;
           for (int c0 = 0; c0 < a.r; c0 += 16) {
             const int c = c0 + kg * 8;
             const bool cok = c < a.r;
             uint4 hi, lo;
-            u_operand(ub, a.r, tok[f] * a.k + max(js, 0), min(c, a.r - 8), cok && js >= 0, hi, lo);
+            u_operand(ub, a.topk_idx, a.r, tok[f], a.k, e, min(c, a.r - 8), cok && mine, hi, lo);
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
               const int row = min(row0 + wn * 64 + g * 32 + lr, pd.d_out - 1);

@@ -276,6 +276,21 @@ def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed=T + d_in + E)
 
 
+@pytest.mark.parametrize("T,d_in,d_out,E,r,k,dt", [
+    (32, 256, 128, 8, 16, 2, "bf16"),   # decode, adapters applied by row tiles of the stacked A
+    (48, 256, 96, 40, 16, 3, "bf16"),   # decode, E > 32: segment-chunk shrink
+    (100, 128, 64, 8, 16, 2, "bf16"),   # prefill
+    (16, 64, 64, 4, 8, 2, "f32"),
+])
+def test_projection_duplicate_adapters(T, d_in, d_out, E, r, k, dt):
+    """A token may name one adapter in two slots (the C ABI allows it): both gated terms count."""
+    say("duplicate adapters", T, d_in, d_out, E, r, k, dt)
+    idx = datagen.uniform_indices(5 + T, T, E, k)
+    idx[::3, 1] = idx[::3, 0]
+    gate = datagen.random_gates(5 + T, T, k)
+    _run_projection_case(T, d_in, [d_out], E, r, k, dt, seed=T + 3, b_scale=1.0, idx=idx, gate=gate)
+
+
 @pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
     (1, 64, [64], 4, 8, 1),
     (33, 96, [208], 5, 16, 2),          # 208 rows: last 32-row tile half full
