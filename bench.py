@@ -2,9 +2,9 @@
 """Benchmark of the pre-gated fused multi-adapter projection step on one MI355X.
 
 A step is the whole hot path once over one batch (AdaFuse technical summary
-§2.A-§2.B): router pre-gating (rp_pregate), segmentation (rp_segment) and
-every projection group in dependency order (rp_sgmm_fused for q|k|v, then o,
-and for the MLP workloads gate|up, then down).  Weights and inputs are seeded
+§2.A-§2.B): router pre-gating, segmentation and every projection group in
+dependency order (q|k|v, then o, and for the MLP workloads gate|up, then down)
+through rp_sgmm_step, which computes the routing inside its first launch.  Weights and inputs are seeded
 synthetic data already resident in HBM; weight copies are rotated so repeated
 steps stream from HBM rather than the on-chip caches.  The step is captured
 in one HIP graph per weight copy and replayed.
@@ -205,22 +205,14 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-        # the dominant call (first projection group, the widest): one graph of
-        # that call alone on each weight copy in turn, replayed; events on the
+        # the dominant launch: the step's first multi-group launch (routing
+        # inside when fused, then up to eight projection groups), alone, one
+        # graph of it on each weight copy in turn, replayed; events on the
         # stream it is launched on bracket the replays
-        g0 = wl.groups[0]
-        layer = dw.layers[0]
-        xg = dw.inputs[(layer, g0.x_name)]
+        n_dom = min(8, len(dw.step_groups(0)))
 
         def dominant(c):
-            W = dw.weights[c]
-            projs = [(W[(layer, p)].W0, W[(layer, p)].A, W[(layer, p)].B, dw.outputs[(layer, p)]) for p in g0.projs]
-            if fused:
-                rp.route_sgmm_fused(projs, xg, dw.Wg, wl.E, wl.r, wl.k, dw.topk_idx, dw.topk_gate, dw.seg_offsets,
-                                    dw.pair_perm, ws=dw.ws)
-            else:
-                rp.sgmm_fused(projs, xg, wl.E, wl.r, wl.k, dw.sel_idx, dw.sel_gate, dw.seg_offsets, dw.pair_perm,
-                              ws=dw.ws)
+            dw.run(c, fused=fused, n_groups=n_dom)
 
         reps = max(2, args.steps // copies)
         if args.no_graph:
@@ -264,12 +256,12 @@ def main():
     step_flops = dw.algorithmic_flops()
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_per_step * 1e-3)
-    bpe = 2 if wl.dtype == "bf16" else 4
-    dom_bytes = sum(g0.d_out * g0.d_in * bpe + n_touched * wl.r * (g0.d_in + g0.d_out) * bpe + wl.T * g0.d_out * bpe
-                    for _ in g0.projs) + wl.T * g0.d_in * bpe
+    dom_bytes = sum(dw.group_bytes(i, n_touched) for i in range(n_dom))
     if fused:  # the launch also reads the router weight and writes the routing arrays
-        dom_bytes += wl.d * wl.E * bpe + wl.T * wl.k * 8 + (wl.E + 1) * 4 + wl.T * wl.k * 4
-    dom_name = f"rp_{'route_' if fused else ''}sgmm_fused({'|'.join(g0.projs)})"
+        dom_bytes += dw.routing_bytes() - wl.T * wl.d * (2 if wl.dtype == "bf16" else 4)
+    names = [f"{g.name}" for g in wl.groups]
+    dom_groups = [names[i % len(names)] for i in range(n_dom)]
+    dom_name = f"rp_sgmm_step({'route, ' if fused else ''}{', '.join(dom_groups)})"
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, {tokens_per_s:,.0f} tokens/s, algorithmic {step_bytes / 1e6:.1f} MB "
         f"-> {gbs:,.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); {step_flops / (ms_per_step * 1e-3) / 1e12:.1f} "
@@ -298,7 +290,7 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes, "touched_adapters": n_touched},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(("route_sgmm_" if fused else "sgmm_") + g0.name, wl.name),
+                     "traffic": measured_traffic("step", wl.name),
                      "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
                      "bytes_per_launch": dom_bytes},
     }

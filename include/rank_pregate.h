@@ -17,6 +17,11 @@
  *   rp_route_sgmm_fused -- the three steps above for the first adapted layer
  *                    of a step, whose input is also the router input: one
  *                    launch for decode shapes, so routing overlaps the weights.
+ *   rp_sgmm_step  -- a decode step: many projection groups in dependency
+ *                    order (q|k|v, o, gate|up, down, layer after layer), the
+ *                    routing optionally computed first, as few launches as
+ *                    possible (page 2 of the sources: the whole decode step
+ *                    replayed as one unit).
  *
  * Conventions shared by every entry point
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -42,10 +47,11 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 3
+#define RP_ABI_VERSION 4
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
-#define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call */
+#define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call (per group) */
+#define RP_MAX_GROUPS 4096  /* projection groups per rp_sgmm_step call */
 
 typedef enum {
   RP_OK = 0,
@@ -177,6 +183,39 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
                               int64_t ld_x, const void* Wg, int64_t E, int64_t r, int32_t k, rp_dtype dt,
                               int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets, int32_t* pair_perm,
                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One group of projections that share their input x (see rp_sgmm_fused). */
+typedef struct {
+  const rp_proj* projs;  /* host array of n_proj (1..RP_MAX_PROJ) descriptors */
+  int32_t n_proj;
+  int32_t x_from_call;   /* 1 if x is written by an earlier group of the same call */
+  const void* x;         /* [T, d_in], leading dimension ld_x */
+  int64_t d_in;
+  int64_t ld_x;
+} rp_group;
+
+/* A decode step (AdaFuse §2.B decoding steps 1-3 over every adapted layer):
+ * the groups run in order, group g+1 reading its x only after every output
+ * of groups 0..g is written, so a group's x may be an earlier group's y
+ * (mark it with x_from_call).  All groups use one routing:
+ *
+ *   Wg_or_null non-null: the routing is computed first from groups[0].x, as
+ *                        rp_route_sgmm_fused does; topk_idx, topk_gate,
+ *                        seg_offsets, pair_perm are outputs
+ *   Wg_or_null NULL:     they are inputs (as for rp_sgmm_fused)
+ *
+ * For decode shapes (bf16, T <= 64) the groups run inside multi-group
+ * launches (up to eight groups each): a group's first weight chunk is already
+ * streaming while it waits for the previous group, and no launch boundary
+ * separates them.  Other shapes run group by group.
+ *   ws   rp_sgmm_step_workspace_size() bytes, same rules as rp_sgmm_fused
+ * Limits: 1 <= n_groups <= RP_MAX_GROUPS, each group as for rp_sgmm_fused; E, r,
+ * k shared by all groups; k >= 1 when the routing is computed. */
+rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                       const void* Wg_or_null, int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets,
+                       int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r,
+                                   int32_t k, rp_dtype dt);
 
 /* Repack a dense row-major bf16 W0 [d_out, d_in] into RP_W0_TILED order (a
  * one-time weight preparation; the result serves every later call).

@@ -28,7 +28,7 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
                  4: "RP_ERR_HIP"}
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
-            "rp_route_sgmm_fused", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+            "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
@@ -42,6 +42,11 @@ class RpProj(ctypes.Structure):
     _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("d_out", ctypes.c_int64), ("ld_y", ctypes.c_int64), ("w0_layout", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class RpGroup(ctypes.Structure):
+    _fields_ = [("projs", ctypes.POINTER(RpProj)), ("n_proj", ctypes.c_int32), ("x_from_call", ctypes.c_int32),
+                ("x", ctypes.c_void_p), ("d_in", ctypes.c_int64), ("ld_x", ctypes.c_int64)]
 
 
 _lib = None
@@ -65,6 +70,10 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_int, vp, sz, vp]
     L.rp_route_sgmm_fused.argtypes = [ctypes.POINTER(RpProj), i32, vp, i64, i64, i64, vp, i64, i64, i32,
                                       ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+    L.rp_sgmm_step.argtypes = [ctypes.POINTER(RpGroup), i32, i64, i64, i64, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                               sz, vp]
+    L.rp_sgmm_step_workspace_size.argtypes = [ctypes.POINTER(RpGroup), i32, i64, i64, i64, i32, ctypes.c_int]
+    L.rp_sgmm_step_workspace_size.restype = sz
     L.rp_sgmm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32, ctypes.c_int]
     L.rp_sgmm_workspace_size.restype = sz
     L.rp_last_error.argtypes = []
@@ -271,6 +280,63 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
     return ys
 
 
+def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx=None, topk_gate=None,
+              seg_offsets=None, pair_perm=None, ws=None, stream=None):
+    """rp_sgmm_step on torch tensors.
+
+    groups: sequence of (projs, x) or (projs, x, x_from_call); projs as for sgmm_fused.  With Wg the routing
+    is computed from the first group's x into the four routing tensors (allocated when None); without it
+    they are inputs.  Returns (list of y lists per group, topk_idx, topk_gate, seg_offsets, pair_perm).
+    """
+    torch = _torch()
+    x0 = groups[0][1]
+    T = x0.shape[0]
+    dt = _dtype_code(x0)
+    dev = x0.device
+    if Wg is not None:
+        if Wg.dtype != x0.dtype or not Wg.is_contiguous() or tuple(Wg.shape) != (x0.shape[1], E):
+            raise ValueError("Wg must be a dense [d_in, E] tensor with x's dtype")
+        if topk_idx is None:
+            topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if topk_gate is None:
+            topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+        if seg_offsets is None:
+            seg_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        if pair_perm is None:
+            pair_perm = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
+    garr = (RpGroup * len(groups))()
+    keep, ys = [], []
+    for i, g in enumerate(groups):
+        projs, x = g[0], g[1]
+        from_call = int(g[2]) if len(g) > 2 else 0
+        if x.shape[0] != T or x.dtype != x0.dtype:
+            raise ValueError(f"group {i}: x must have T rows and the first group's dtype")
+        arr, gys, _ = _proj_array(projs, x)
+        keep.append(arr)
+        ys.append(gys)
+        garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(projs), from_call, _ptr(x), x.shape[1],
+                          _rows(x, "x"))
+    if ws is None:
+        ws = _default_ws.get(lib().rp_sgmm_step_workspace_size(garr, len(groups), T, E, r, k, dt), dev)
+    st = lib().rp_sgmm_step(garr, len(groups), T, E, r, k, _ptr(Wg), _ptr(topk_idx), _ptr(topk_gate),
+                            _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(st, "rp_sgmm_step")
+    return ys, topk_idx, topk_gate, seg_offsets, pair_perm
+
+
+def step_workspace_size(groups: Sequence[Tuple], E: int, r: int, k: int) -> int:
+    """rp_sgmm_step_workspace_size for groups given as sgmm_step takes them."""
+    x0 = groups[0][1]
+    garr = (RpGroup * len(groups))()
+    keep = []
+    for i, g in enumerate(groups):
+        arr, _, _ = _proj_array(g[0], g[1])
+        keep.append(arr)
+        garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(g[0]), 0, _ptr(g[1]), g[1].shape[1],
+                          _rows(g[1], "x"))
+    return lib().rp_sgmm_step_workspace_size(garr, len(groups), x0.shape[0], E, r, k, _dtype_code(x0))
+
+
 def pack_w0(W0, out=None, stream=None):
     """rp_pack_w0: repack a dense bf16 W0 [d_out, d_in] into the tiled order.
 
@@ -299,3 +365,4 @@ def copy(dst, src, stream=None) -> None:
 
 # the C names, for callers that mirror the header
 rp_pregate, rp_segment, rp_sgmm_fused, rp_route_sgmm_fused = pregate, segment, sgmm_fused, route_sgmm_fused
+rp_sgmm_step = sgmm_step

@@ -197,58 +197,211 @@ rp_status check_sgmm(const char* fn, const rp_proj* projs, int32_t n_proj, const
   return RP_OK;
 }
 
-// Launch plan, workspace size check and kernel arguments (routing pointers
-// excepted) of a checked call.
-rp_status plan_sgmm_call(const char* fn, const rp_proj* projs, int32_t n_proj, const void* x, int64_t T,
-                         int64_t d_in, int64_t ld_x, int64_t E, int64_t r, int32_t k, rp_dtype dt, void* ws,
-                         size_t ws_bytes, bool fused_route, rp::SgmmArgs* out, rp::SgmmPlan* plan_out) {
-  int d_out[RP_MAX_PROJ];
-  for (int p = 0; p < n_proj; ++p) d_out[p] = (int)projs[p].d_out;
-  int n_cu = 0;
-  if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "%s: cannot query the current device", fn);
-  const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
-  const rp::SgmmPlan plan =
-      rp::plan_sgmm(rdt, n_proj, d_out, (int)T, (int)d_in, (int)E, (int)r, k, n_cu, fused_route);
-  if (ws_bytes < plan.bytes)
-    return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu (rp_sgmm_workspace_size)", fn, ws_bytes,
-                plan.bytes);
-
-  rp::SgmmArgs a{};
+// Kernel view of one projection group (routing pointers and workspace views
+// are filled by the caller).
+void fill_group(rp::SgmmArgs* a, const rp_proj* projs, int n_proj, const void* x, int64_t T, int64_t d_in,
+                int64_t ld_x, int64_t E, int64_t r, int32_t k, int tile_rows) {
   int tile = 0;
   for (int p = 0; p < RP_MAX_PROJ; ++p) {
     const int q = p < n_proj ? p : n_proj - 1;  // unused slots repeat the last projection
-    a.proj[p].W0 = projs[q].W0;
-    a.proj[p].A = projs[q].A;
-    a.proj[p].B = projs[q].B;
-    a.proj[p].y = projs[q].y;
-    a.proj[p].d_out = (int)projs[q].d_out;
-    a.proj[p].ld_y = (int)projs[q].ld_y;
-    a.proj[p].tile_begin = tile;
-    a.proj[p].tiled = projs[q].w0_layout == RP_W0_TILED;
-    if (p < n_proj) tile += (d_out[p] + plan.tile_rows - 1) / plan.tile_rows;
+    a->proj[p].W0 = projs[q].W0;
+    a->proj[p].A = projs[q].A;
+    a->proj[p].B = projs[q].B;
+    a->proj[p].y = projs[q].y;
+    a->proj[p].d_out = (int)projs[q].d_out;
+    a->proj[p].ld_y = (int)projs[q].ld_y;
+    a->proj[p].tile_begin = tile;
+    a->proj[p].tiled = projs[q].w0_layout == RP_W0_TILED;
+    if (p < n_proj) tile += ((int)projs[p].d_out + tile_rows - 1) / tile_rows;
   }
-  a.n_proj = n_proj;
-  a.x = x;
-  a.T = (int)T;
-  a.d_in = (int)d_in;
-  a.ld_x = (int)ld_x;
-  a.E = (int)E;
-  a.r = (int)r;
-  a.k = k;
-  char* w = static_cast<char*>(ws);
-  a.counters = reinterpret_cast<int*>(w + plan.off_counters);
-  a.u = reinterpret_cast<float*>(w + plan.off_u);
-  a.partial = reinterpret_cast<float*>(w + plan.off_partial);
-  a.n_tiles = plan.n_tiles;
-  a.S = plan.S;
-  *out = a;
-  *plan_out = plan;
-  return RP_OK;
+  a->n_proj = n_proj;
+  a->x = x;
+  a->T = (int)T;
+  a->d_in = (int)d_in;
+  a->ld_x = (int)ld_x;
+  a->E = (int)E;
+  a->r = (int)r;
+  a->k = k;
 }
 
 // Word of the workspace's control region that receives the count of
-// out-of-range router indices in a route-and-project call.
+// out-of-range router indices when a call computes the routing.
 constexpr size_t kSegErrWord = 64;
+
+struct Routing {
+  const void* Wg;  // non-null: compute the routing from the first group's x
+  int32_t* idx;
+  float* gate;
+  int32_t* off;
+  int32_t* perm;
+};
+
+bool decode_shape(rp_dtype dt, int64_t T) { return dt == RP_BF16 && T <= 64; }
+
+// Workspace bytes a validated call needs.
+size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                              rp_dtype dt) {
+  size_t need = 0;
+  if (decode_shape(dt, T)) {
+    for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
+      const int ng = std::min(rp::kMaxGroups, n_groups - g0);
+      rp::StepGroupDesc desc[rp::kMaxGroups];
+      int d_out[rp::kMaxGroups][RP_MAX_PROJ];
+      for (int i = 0; i < ng; ++i) {
+        for (int p = 0; p < gs[g0 + i].n_proj; ++p) d_out[i][p] = (int)gs[g0 + i].projs[p].d_out;
+        desc[i] = rp::StepGroupDesc{gs[g0 + i].n_proj, d_out[i], (int)gs[g0 + i].d_in, 0};
+      }
+      need = std::max(need, rp::step_workspace_upper_bound(desc, ng, (int)T, (int)E, (int)r, k));
+    }
+  } else {
+    for (int g = 0; g < n_groups; ++g) {
+      int64_t sum = 0;
+      for (int p = 0; p < gs[g].n_proj; ++p) sum += gs[g].projs[p].d_out;
+      need = std::max(need, rp::sgmm_workspace_upper_bound(dt == RP_BF16 ? rp::kBF16 : rp::kF32, gs[g].n_proj,
+                                                           (int)T, (int)gs[g].d_in, sum, (int)E, (int)r, k));
+    }
+  }
+  return need;
+}
+
+// Runs the groups of a validated call in order on `stream`.  Decode shapes go
+// through the multi-group decode kernel, up to kMaxGroups groups per launch;
+// routing to compute runs inside the first launch when T <= 32, otherwise as
+// router and segmentation launches of its own first.
+rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                     rp_dtype dt, const Routing& rt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int n_cu = 0;
+  if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "%s: cannot query the current device", fn);
+  const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
+  const bool decode = decode_shape(dt, T);
+  char* w = static_cast<char*>(ws);
+  rp::PregateArgs pg{};
+  rp::SegmentArgs sg{};
+  const bool route = rt.Wg != nullptr;
+  if (route) {
+    pg.x = gs[0].x;
+    pg.T = (int)T;
+    pg.d_in = (int)gs[0].d_in;
+    pg.ld_x = (int)gs[0].ld_x;
+    pg.Wg = rt.Wg;
+    pg.E = (int)E;
+    pg.k = k;
+    pg.dt = rdt;
+    pg.topk_idx = rt.idx;
+    pg.topk_gate = rt.gate;
+    pg.logits = nullptr;
+    sg.topk_idx = rt.idx;
+    sg.n_pairs = (int)(T * k);
+    sg.k = k;
+    sg.E = (int)E;
+    sg.seg_offsets = rt.off;
+    sg.pair_perm = rt.perm;
+    sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
+  }
+  const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T);
+  if (route && !fuse_route) {
+    hipError_t e = rp::launch_pregate(pg, stream);
+    if (e == hipSuccess) e = rp::launch_segment(sg, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  if (!decode) {
+    for (int g = 0; g < n_groups; ++g) {
+      int d_out[RP_MAX_PROJ];
+      for (int p = 0; p < gs[g].n_proj; ++p) d_out[p] = (int)gs[g].projs[p].d_out;
+      const rp::SgmmPlan plan =
+          rp::plan_sgmm(rdt, gs[g].n_proj, d_out, (int)T, (int)gs[g].d_in, (int)E, (int)r, k, n_cu, false);
+      if (ws_bytes < plan.bytes)
+        return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.bytes);
+      rp::SgmmArgs a{};
+      fill_group(&a, gs[g].projs, gs[g].n_proj, gs[g].x, T, gs[g].d_in, gs[g].ld_x, E, r, k, plan.tile_rows);
+      a.topk_idx = rt.idx;
+      a.topk_gate = rt.gate;
+      a.seg_offsets = rt.off;
+      a.pair_perm = rt.perm;
+      a.counters = reinterpret_cast<int*>(w);
+      a.u = reinterpret_cast<float*>(w + plan.off_u);
+      a.partial = reinterpret_cast<float*>(w + plan.off_partial);
+      a.n_tiles = plan.n_tiles;
+      a.S = plan.S;
+      hipError_t e = rp::launch_sgmm(a, plan, rdt, stream);
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+    return RP_OK;
+  }
+  for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
+    const int ng = std::min(rp::kMaxGroups, n_groups - g0);
+    rp::StepGroupDesc desc[rp::kMaxGroups];
+    int d_out[rp::kMaxGroups][RP_MAX_PROJ];
+    for (int i = 0; i < ng; ++i) {
+      const rp_group& g = gs[g0 + i];
+      for (int p = 0; p < g.n_proj; ++p) d_out[i][p] = (int)g.projs[p].d_out;
+      // across launches the kernel boundary orders the data already
+      desc[i] = rp::StepGroupDesc{g.n_proj, d_out[i], (int)g.d_in, i > 0 && g.x_from_call ? 1 : 0};
+    }
+    const bool fused_here = fuse_route && g0 == 0;
+    const rp::StepPlan sp = rp::plan_step(desc, ng, (int)T, (int)E, (int)r, k, n_cu, fused_here);
+    if (ws_bytes < sp.bytes)
+      return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, sp.bytes);
+    rp::StepArgs st{};
+    for (int i = 0; i < ng; ++i) {
+      const rp_group& g = gs[g0 + i];
+      const rp::SgmmPlan& gp = sp.gp[i];
+      rp::SgmmArgs& a = st.g[i];
+      fill_group(&a, g.projs, g.n_proj, g.x, T, g.d_in, g.ld_x, E, r, k, gp.tile_rows);
+      a.topk_idx = rt.idx;
+      a.topk_gate = rt.gate;
+      a.seg_offsets = rt.off;
+      a.pair_perm = rt.perm;
+      a.counters = reinterpret_cast<int*>(w);
+      a.u = reinterpret_cast<float*>(w + gp.off_u);
+      a.partial = reinterpret_cast<float*>(w + gp.off_partial);
+      a.n_tiles = gp.n_tiles;
+      a.S = gp.S;
+      rp::GroupPlan& q = st.gp[i];
+      q.item_begin = sp.item_begin[i];
+      q.n_shrink = gp.dense ? gp.n_atiles * gp.SA : gp.units_per_proj * g.n_proj;
+      q.n_items = gp.n_items;
+      q.shrink_target = gp.dense ? 0 : q.n_shrink;
+      q.units_per_proj = gp.units_per_proj;
+      q.KP = gp.KP;
+      q.atiles_per_proj = gp.atiles_per_proj;
+      q.n_atiles = gp.n_atiles;
+      q.SA = gp.SA;
+      q.x_acquire = desc[i].x_acquire;
+      q.count_done = i + 1 < ng;
+      q.release = i + 1 < ng && desc[i + 1].x_acquire;
+      q.partial_a = reinterpret_cast<float*>(w + gp.off_partial_a);
+    }
+    st.n_groups = ng;
+    st.n_items = sp.n_items;
+    st.n_route = sp.n_route;
+    st.n_pre = sp.n_pre;
+    st.fused = fused_here;
+    st.dense = sp.gp[0].dense;
+    st.t_pad = sp.gp[0].t_pad;
+    st.route_tagged = reinterpret_cast<unsigned int*>(w + sp.off_route);
+    st.pg = pg;
+    st.sg = sg;
+    hipError_t e = rp::launch_step(st, sp, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return RP_OK;
+}
+
+// Checks of a call's routing pointers; `compute` when the call writes them.
+rp_status check_routing(const char* fn, const Routing& rt, int64_t T, int64_t E, int32_t k, bool compute) {
+  if (compute) {
+    if (k < 1) return fail(RP_ERR_INVALID_ARG, "%s: k=%d, routing needs k >= 1", fn, k);
+    if (!rt.Wg || !aligned(rt.Wg, 16)) return fail(RP_ERR_INVALID_ARG, "%s: Wg must be non-null and 16-byte aligned", fn);
+    if (T * E > (int64_t)1 << 40) return fail(RP_ERR_INVALID_ARG, "%s: T*E too large", fn);
+  }
+  if (k > 0 && (!rt.idx || !rt.gate || !rt.off || !rt.perm))
+    return fail(RP_ERR_INVALID_ARG, "%s: k>0 needs topk_idx, topk_gate, seg_offsets and pair_perm", fn);
+  if ((rt.idx && !aligned(rt.idx, 4)) || (rt.gate && !aligned(rt.gate, 4)) || (rt.off && !aligned(rt.off, 4)) ||
+      (rt.perm && !aligned(rt.perm, 4)))
+    return fail(RP_ERR_INVALID_ARG, "%s: routing arrays must be 4-byte aligned", fn);
+  return RP_OK;
+}
 
 }  // namespace
 
@@ -262,18 +415,12 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
   const char* fn = "rp_sgmm_fused";
   rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws);
   if (st != RP_OK || T == 0) return st;
-  if (k > 0 && (!topk_idx || !topk_gate || !seg_offsets || !pair_perm))
-    return fail(RP_ERR_INVALID_ARG, "rp_sgmm_fused: k>0 needs topk_idx, topk_gate, seg_offsets and pair_perm");
-  rp::SgmmArgs a{};
-  rp::SgmmPlan plan{};
-  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, false, &a, &plan);
+  const Routing rt{nullptr, const_cast<int32_t*>(topk_idx), const_cast<float*>(topk_gate),
+                   const_cast<int32_t*>(seg_offsets), const_cast<int32_t*>(pair_perm)};
+  st = check_routing(fn, rt, T, E, k, false);
   if (st != RP_OK) return st;
-  a.topk_idx = topk_idx;
-  a.topk_gate = topk_gate;
-  a.seg_offsets = seg_offsets;
-  a.pair_perm = pair_perm;
-  hipError_t e = rp::launch_sgmm(a, plan, dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
-  return e == hipSuccess ? RP_OK : hip_fail("rp_sgmm_fused launch", e);
+  const rp_group g{projs, n_proj, 0, x, d_in, ld_x};
+  return run_groups(fn, &g, 1, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
 rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
@@ -282,54 +429,52 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   const char* fn = "rp_route_sgmm_fused";
-  if (k < 1) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: k=%d, routing needs k >= 1", k);
+  if (k < 1) return fail(RP_ERR_INVALID_ARG, "%s: k=%d, routing needs k >= 1", fn, k);
   rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws);
   if (st != RP_OK || T == 0) return st;
-  if (!Wg || !aligned(Wg, 16)) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: Wg must be non-null and 16-byte aligned");
-  if (!topk_idx || !topk_gate || !seg_offsets || !pair_perm)
-    return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: null routing output");
-  if (!aligned(topk_idx, 4) || !aligned(topk_gate, 4) || !aligned(seg_offsets, 4) || !aligned(pair_perm, 4))
-    return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: routing outputs must be 4-byte aligned");
-  if (T * E > (int64_t)1 << 40) return fail(RP_ERR_INVALID_ARG, "rp_route_sgmm_fused: T*E too large");
-  rp::SgmmArgs a{};
-  rp::SgmmPlan plan{};
-  const bool one_launch = dt == RP_BF16 && T <= 64 && rp::decode_fused_route_supported((int)T);
-  st = plan_sgmm_call(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, ws, ws_bytes, one_launch, &a, &plan);
+  const Routing rt{Wg, topk_idx, topk_gate, seg_offsets, pair_perm};
+  st = check_routing(fn, rt, T, E, k, true);
   if (st != RP_OK) return st;
-  a.topk_idx = topk_idx;
-  a.topk_gate = topk_gate;
-  a.seg_offsets = seg_offsets;
-  a.pair_perm = pair_perm;
-  rp::PregateArgs pg;
-  pg.x = x;
-  pg.T = (int)T;
-  pg.d_in = (int)d_in;
-  pg.ld_x = (int)ld_x;
-  pg.Wg = Wg;
-  pg.E = (int)E;
-  pg.k = k;
-  pg.dt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
-  pg.topk_idx = topk_idx;
-  pg.topk_gate = topk_gate;
-  pg.logits = nullptr;
-  rp::SegmentArgs sg;
-  sg.topk_idx = topk_idx;
-  sg.n_pairs = (int)(T * k);
-  sg.k = k;
-  sg.E = (int)E;
-  sg.seg_offsets = seg_offsets;
-  sg.pair_perm = pair_perm;
-  sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
-  hipError_t e;
-  if (one_launch && plan.path == 1) {
-    e = rp::launch_route_sgmm(a, pg, sg, plan, stream);
-  } else {
-    // other shapes: the same three steps as separate launches on the stream
-    e = rp::launch_pregate(pg, stream);
-    if (e == hipSuccess) e = rp::launch_segment(sg, stream);
-    if (e == hipSuccess) e = rp::launch_sgmm(a, plan, pg.dt, stream);
+  const rp_group g{projs, n_proj, 0, x, d_in, ld_x};
+  return run_groups(fn, &g, 1, T, E, r, k, dt, rt, ws, ws_bytes, stream);
+}
+
+size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r,
+                                   int32_t k, rp_dtype dt) {
+  if (!groups || n_groups < 1 || n_groups > RP_MAX_GROUPS || !valid_dtype(dt) || T < 0 || T > kIntMax || E < 1 ||
+      E > RP_MAX_E || k < 0 || k > RP_MAX_K || k > E || !(r == 8 || r == 16 || r == 32 || r == 64 || r == 128))
+    return 0;
+  for (int g = 0; g < n_groups; ++g) {
+    if (!groups[g].projs || groups[g].n_proj < 1 || groups[g].n_proj > RP_MAX_PROJ || groups[g].d_in < 1) return 0;
+    for (int p = 0; p < groups[g].n_proj; ++p)
+      if (groups[g].projs[p].d_out < 8 || groups[g].projs[p].d_out > kIntMax) return 0;
   }
-  return e == hipSuccess ? RP_OK : hip_fail("rp_route_sgmm_fused launch", e);
+  return groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
+}
+
+rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                       const void* Wg_or_null, int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets,
+                       int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_sgmm_step";
+  if (!groups || n_groups < 1 || n_groups > RP_MAX_GROUPS)
+    return fail(RP_ERR_INVALID_ARG, "%s: n_groups=%d not in [1, %d]", fn, n_groups, RP_MAX_GROUPS);
+  for (int g = 0; g < n_groups; ++g) {
+    char name[64];
+    snprintf(name, sizeof name, "%s: group %d", fn, g);
+    rp_status st = check_sgmm(name, groups[g].projs, groups[g].n_proj, groups[g].x, T, groups[g].d_in,
+                              groups[g].ld_x, E, r, k, dt, ws);
+    if (st != RP_OK) return st;
+    if (groups[g].x_from_call != 0 && groups[g].x_from_call != 1)
+      return fail(RP_ERR_INVALID_ARG, "%s: x_from_call must be 0 or 1", name);
+  }
+  if (T == 0) return RP_OK;
+  const Routing rt{Wg_or_null, topk_idx, topk_gate, seg_offsets, pair_perm};
+  rp_status st = check_routing(fn, rt, T, E, k, Wg_or_null != nullptr);
+  if (st != RP_OK) return st;
+  const size_t need = groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
+  if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  return run_groups(fn, groups, n_groups, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
 rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream) {

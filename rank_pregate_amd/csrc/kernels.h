@@ -64,26 +64,50 @@ struct SgmmArgs {
   int S;             // K splits per output tile (decode path)
 };
 
-// Extra launch constants of the decode kernel.  Items are numbered
-//   [0, n_route)                 router tiles (fused route-and-project launches)
-//   [n_route, n_pre)             the segmentation item (fused launches)
-//   [n_pre, n_pre + n_shrink)    shrink units, units_per_proj per projection
-//   [n_pre + n_shrink, n_items)  base items, n_tiles * S
+// Per-group launch constants of the decode kernel (the view its item
+// functions take).  Items of a group are numbered
+//   [0, n_shrink)          shrink: A-row tiles x SA splits (dense) or pair-chunk units
+//   [n_shrink, n_items)    backbone tiles x S splits
 struct DecodeArgs {
-  int n_route, n_pre, n_shrink, n_items;
+  int n_route, n_pre;  // routing items at the start of a fused launch
+  int n_shrink, n_items;
   int units_per_proj;  // pair-chunk shrink units per projection (E > 32)
-  int KP;         // K parts of a pair-chunk shrink unit (partial sums added in the expand)
-  int dense;      // 1: the shrink runs as row tiles of the stacked A_e over every token (E <= 32);
-                  // 0: pair-chunk shrink units of <= 16 pairs of one segment
+  int KP;              // K parts of a pair-chunk shrink unit (partial sums added in the expand)
+  int dense;           // 1: the shrink runs as row tiles of the stacked A_e over every token (E <= 32);
+                       // 0: pair-chunk shrink units of <= 16 pairs of one segment
   int atiles_per_proj, n_atiles, SA;  // dense: 32-row tiles of [A_0; ..; A_{E-1}] and their K splits
-  int shrink_target;                  // shrink_done count that means every u is written
+  int shrink_target;                  // shrink_done count that means every u is written (pair chunks)
+  int t_pad;                          // tokens padded to whole 16-token tiles
+  int fused;                          // routing runs inside the launch
+  int group;                          // position of the group in its launch
+  int prev_target;                    // > 0: wait until the previous group has written this many tiles
+  int x_acquire;                      // x was written earlier in this launch: acquire before reading it
+  int count_done;                     // a later group waits for this one: count finished tiles
+  int release;                        // ... and reads what this one wrote: release before counting
   float* partial_a;                   // dense: split-K partial tiles of the A tiles
   unsigned int* route_tagged;         // fused: (index, tag, gate, tag) per (token, slot)
-  int t_pad;      // tokens padded to whole 16-token tiles
-  int fused;      // routing runs inside the launch (router tiles + segmentation item)
-  PregateArgs pg; // fused: router arguments (outputs topk_idx, topk_gate)
-  SegmentArgs sg; // fused: segmentation arguments
-  int route_np, route_slice, route_vec, route_tt;  // fused: router tiling
+  PregateArgs pg;                     // fused: router arguments (outputs topk_idx, topk_gate)
+  SegmentArgs sg;                     // fused: segmentation arguments
+};
+
+// Projection groups run in order inside one decode launch (a decode step or
+// part of one); group g's items start reading their input only after every
+// output tile of group g-1 is written.
+constexpr int kMaxGroups = 8;
+struct GroupPlan {
+  int item_begin;  // first item of the group in the launch
+  int n_shrink, n_items, shrink_target, units_per_proj, KP, atiles_per_proj, n_atiles, SA;
+  int x_acquire, count_done, release;
+  float* partial_a;
+};
+struct StepArgs {
+  SgmmArgs g[kMaxGroups];
+  GroupPlan gp[kMaxGroups];
+  int n_groups, n_items;  // groups and items of the launch (routing items included)
+  int n_route, n_pre, fused, dense, t_pad;
+  unsigned int* route_tagged;
+  PregateArgs pg;
+  SegmentArgs sg;
 };
 
 // Which kernel family serves a call, and the workspace it needs.
@@ -105,20 +129,36 @@ struct SgmmPlan {
 // fused_route: the launch also runs the router and segmentation (decode path only)
 SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
                    bool fused_route);
+
+// A decode launch over several projection groups (bf16, T <= 64).
+struct StepGroupDesc {
+  int n_proj;
+  const int* d_out;  // n_proj widths
+  int d_in;
+  int x_acquire;     // x is written by an earlier group of the same launch
+};
+struct StepPlan {
+  int n_groups;
+  SgmmPlan gp[kMaxGroups];  // per group: tiling, splits and its workspace offsets (absolute)
+  int item_begin[kMaxGroups];
+  int n_route, n_pre, n_items, grid;
+  size_t off_route, bytes;
+};
+StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int r, int k, int n_cu, bool fused_route);
+size_t step_workspace_upper_bound(const StepGroupDesc* groups, int n_groups, int T, int E, int r, int k);
+hipError_t launch_step(const StepArgs& st, const StepPlan& plan, hipStream_t s);
 int decode_mt(int T);       // 16-token tiles of the decode kernel
 int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
 int decode_resident_per_cu(int T, bool fused);  // workgroups of the decode kernel one CU holds at once
 int fused_route_tile_tokens();                  // tokens per router tile of a fused decode launch
 bool decode_fused_route_supported(int T);       // routing can run inside a decode launch of T tokens
-hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
+
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
                                   int k);
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);
-// Router, segmentation and projections in one decode launch (plan.path == 1, built with fused_route).
-hipError_t launch_route_sgmm(const SgmmArgs& a, const PregateArgs& pg, const SegmentArgs& sg, const SgmmPlan& plan,
-                             hipStream_t s);
+
 
 hipError_t launch_pack_w0(const void* src, void* dst, int d_out, int d_in, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);

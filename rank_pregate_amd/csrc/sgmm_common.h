@@ -15,17 +15,23 @@ namespace rp {
 //   kCtlWaitOverflow  sticky flag: a wait gave up after its spin limit.
 //   kCtlSegErr     out-of-range router indices seen by a fused launch's
 //                  segmentation (always 0 for indices the router wrote).
+// In a control set, per group g of the launch (g < kMaxGroups):
+//   kSetShrinkDone + 32 g          pair-chunk shrink units finished
+//   kSetGroupDone + 256 g + 32 c   output tiles finished, counted per tile % 8
 constexpr int kCtlEpoch = 0;
 constexpr int kCtlWaitOverflow = 32;
 constexpr int kCtlSegErr = 64;
 constexpr int kCtlSet0 = 1024;
-constexpr int kCtlSetStride = 1024;
-constexpr int kSetShrinkDone = 0;   // shrink units finished
-constexpr int kSetRouteDone = 32;   // router tiles finished
-constexpr int kSetSegDone = 64;     // segmentation finished
-constexpr int kSetArrive = 96;      // + 32 * (blockIdx % 8): workgroups that read the epoch
-constexpr int kSetArriveAll = 96 + 8 * 32;
-constexpr int kSetWords = kSetArriveAll + 32;
+constexpr int kCtlSetStride = 4096;
+constexpr int kSetShrinkDone = 0;
+constexpr int kSetRouteDone = 32 * kMaxGroups;  // router tiles finished
+constexpr int kSetSegDone = kSetRouteDone + 32;  // segmentation finished
+constexpr int kSetArrive = kSetSegDone + 32;     // + 32 * (blockIdx % 8): workgroups that read the epoch
+constexpr int kSetArriveAll = kSetArrive + 8 * 32;
+constexpr int kSetGroupDone = kSetArriveAll + 64;
+constexpr int kSetWords = kSetGroupDone + 256 * kMaxGroups;
+static_assert(kCtlSet0 + 2 * kCtlSetStride <= 65536 / 4, "control sets exceed the reserved region");
+static_assert(kSetWords <= kCtlSetStride, "control set overflow");
 
 // Device-scope (sc1) loads of routing data another workgroup of the same
 // launch may have written; plain loads when it was written by an earlier launch.

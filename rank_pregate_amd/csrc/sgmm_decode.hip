@@ -47,6 +47,7 @@ constexpr int kKC = 256;             // K per LDS chunk
 constexpr int kSteps = kKC / 32;     // MFMA k-steps per chunk
 constexpr int kLD = kKC + 8;         // padded LDS row (elements)
 static_assert(kThreads == kRouteThreads, "router tiles run on the decode workgroup shape");
+static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
 constexpr int kMaxSplits = 8;         // K splits of a tile (the launch plan keeps S <= this)
 
@@ -126,6 +127,28 @@ __device__ __forceinline__ void wait_geq(int* ctl, const int* p, int target) {
 
 __device__ __forceinline__ int* ctl_set(int* ctl, int ep) { return ctl + kCtlSet0 + (ep & 1) * kCtlSetStride; }
 
+// Before reading its input, an item of group g > 0 waits until every output
+// tile of group g-1 is written (tiles are counted per tile % 8 so no single
+// counter takes every workgroup); wave 0 polls, the workgroup then proceeds.
+__device__ __forceinline__ void wait_prev_group(int* ctl, int ep, const DecodeArgs& d) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    const int* base = ctl + kCtlSet0 + (ep & 1) * kCtlSetStride + kSetGroupDone + 256 * (d.group - 1);
+    int spins = 0;
+    while (true) {
+      const int v = lane < 8 ? __hip_atomic_load(base + 32 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      if (wave_sum_int(v) >= d.prev_target) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        if (lane == 0) atomicOr(&ctl[kCtlWaitOverflow], 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (d.x_acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // Thread 0, once per workgroup: record that this workgroup has read the epoch.
 __device__ __forceinline__ int arrive(int* ctl, int ep) {
   return atomicAdd(&ctl_set(ctl, ep)[kSetArrive + 32 * (blockIdx.x & 7)], 1);
@@ -146,11 +169,12 @@ __device__ __forceinline__ size_t upart_slots(const SgmmArgs& a, const DecodeArg
 // were written by this launch.
 template <int MTR, bool COH>
 __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs& d, int proj, int unit, int kp,
-                                            float* red, int* s_loc) {
+                                            float* red, int* s_loc, int* ctl, int ep) {
   // k-steps per batch: all loads of a batch are issued before its MFMAs, so a
   // unit costs about one memory round trip per batch
   constexpr int U = MTR <= 2 ? 8 : (MTR <= 8 ? 2 : 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (d.prev_target > 0) wait_prev_group(ctl, ep, d);
   if (tid < 64) {
     int ee, c;
     locate_chunk<COH>(a, unit, 16, tid, &ee, &c);
@@ -372,6 +396,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   {
     uint4 wA[kSteps], wB[kSteps], XA[XCH], XB[XCH];
     load_w(wA, cb);
+    // weights do not depend on the previous group: the first chunk is in flight during the wait
+    if (d.prev_target > 0) wait_prev_group(ctl, first ? __builtin_amdgcn_readfirstlane(ep_in) : *s_ep, d);
     load_x(XA, cb);
     load_x(XB, cb + 1);
     if (first && tid == 0) {
@@ -451,7 +477,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         for (int j = 0; j < kMaxK; ++j)
           if (j >= a.k) sel[m][j] = -1, gate[m][j] = 0.f;
     }
-    if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone], d.shrink_target);
+    if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
     const size_t slots = upart_slots(a, d);
     const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
     const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
@@ -664,83 +690,127 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         if (t < a.T) y[(size_t)t * pd.ld_y + row0 + lr] = f32_to_bf16(acc[m][v]);
       }
   }
+  if (d.count_done) {
+    // a later group of this launch waits for this tile (and, with release, reads it)
+    if (d.release) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) atomicAdd(&set[kSetGroupDone + 256 * d.group + 32 * (tile & 7)], 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // kernel
 // ---------------------------------------------------------------------------
+// The view of group gi that the item functions take.
+__device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
+  const GroupPlan& gp = st.gp[gi];
+  DecodeArgs d;
+  d.n_route = st.n_route;
+  d.n_pre = st.n_pre;
+  d.n_shrink = gp.n_shrink;
+  d.n_items = gp.n_items;
+  d.units_per_proj = gp.units_per_proj;
+  d.KP = gp.KP;
+  d.dense = st.dense;
+  d.atiles_per_proj = gp.atiles_per_proj;
+  d.n_atiles = gp.n_atiles;
+  d.SA = gp.SA;
+  d.shrink_target = gp.shrink_target;
+  d.t_pad = st.t_pad;
+  d.fused = st.fused;
+  d.group = gi;
+  d.prev_target = gi > 0 ? st.g[gi - 1].n_tiles : 0;
+  d.x_acquire = gp.x_acquire;
+  d.count_done = gp.count_done;
+  d.release = gp.release;
+  d.partial_a = gp.partial_a;
+  d.route_tagged = st.route_tagged;
+  return d;
+}
+
 template <int MT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_kernel(SgmmArgs a, DecodeArgs d) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(StepArgs st) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<MT, FUSED>()];
   __shared__ int s_ep, s_loc[2], s_wave_tot[2], s_bad;
-  int* ctl = a.counters;
+  int* ctl = st.g[0].counters;
   const int tid = threadIdx.x;
-  // the epoch is read once per workgroup; base items publish it after their
-  // first loads are in flight, other items right away
+  // the epoch is read once per workgroup; backbone items publish it after
+  // their first loads are in flight, other items right away
   int ep_in = 0, arrive_old = 0;
   if (tid == 0) ep_in = __hip_atomic_load(&ctl[kCtlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int n_base0 = d.n_pre + d.n_shrink;
   bool first = true;
-  for (int item = blockIdx.x; item < d.n_items; item += gridDim.x) {
-    if (item < n_base0 && first) {
-      if (tid == 0) {
-        s_ep = ep_in;
-        arrive_old = arrive(ctl, ep_in);
+  for (int item = blockIdx.x; item < st.n_items; item += gridDim.x) {
+    if (FUSED && item < st.n_pre) {
+      if (first) {
+        if (tid == 0) {
+          s_ep = ep_in;
+          arrive_old = arrive(ctl, ep_in);
+        }
+        __syncthreads();
+        first = false;
       }
-      __syncthreads();
-      first = false;
-    }
-    if (FUSED && item < d.n_route) {
-      // router tile: top-k and gates of TT tokens
       int* set = ctl_set(ctl, s_ep);
-      const RoutePlan rpl = route_plan(d.pg.E, d.pg.d_in, (int)sizeof(bf16_t));
-      float* f = reinterpret_cast<float*>(smem);
-      // two tokens per tile whatever E (the sums do not depend on the tile size)
-      route_tile<bf16_t, kFusedRouteTokens>(d.pg, item * kFusedRouteTokens, rpl, f,
-                                            reinterpret_cast<unsigned long long*>(d.route_tagged), launch_tag(s_ep));
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) atomicAdd(&set[kSetRouteDone], 1);
-    } else if (FUSED && item < d.n_pre) {
-      int* set = ctl_set(ctl, s_ep);
-      wait_geq(ctl, &set[kSetRouteDone], d.n_route);
-      segment_block<kWV>(d.sg, reinterpret_cast<int*>(smem), s_wave_tot, &s_bad);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) atomicAdd(&set[kSetSegDone], 1);
-    } else if (item < n_base0 && d.dense) {
-      base_item<MT, false, FUSED, true>(a, d, item - d.n_pre, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first,
-                                        ep_in, &arrive_old);
-      first = false;
-    } else if (item < n_base0) {
-      int* set = ctl_set(ctl, s_ep);
-      const int si = item - d.n_pre;
-      const int proj = si / d.units_per_proj, w = si % d.units_per_proj;
-      const int unit = w / d.KP, kp = w % d.KP;
-      float* red = reinterpret_cast<float*>(smem);
-      {
+      if (item < st.n_route) {
+        // router tile: top-k and gates of two tokens (the sums do not depend on the tile size)
+        const RoutePlan rpl = route_plan(st.pg.E, st.pg.d_in, (int)sizeof(bf16_t));
+        route_tile<bf16_t, kFusedRouteTokens>(st.pg, item * kFusedRouteTokens, rpl, reinterpret_cast<float*>(smem),
+                                              reinterpret_cast<unsigned long long*>(st.route_tagged), launch_tag(s_ep));
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) atomicAdd(&set[kSetRouteDone], 1);
+      } else {
+        wait_geq(ctl, &set[kSetRouteDone], st.n_route);
+        segment_block<kWV>(st.sg, reinterpret_cast<int*>(smem), s_wave_tot, &s_bad);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) atomicAdd(&set[kSetSegDone], 1);
+      }
+    } else {
+      int gi = 0;
+      while (gi + 1 < st.n_groups && item >= st.gp[gi + 1].item_begin) ++gi;
+      const SgmmArgs& a = st.g[gi];
+      const DecodeArgs d = group_view(st, gi);
+      const int li = item - st.gp[gi].item_begin;
+      if (li < d.n_shrink && d.dense) {
+        base_item<MT, false, FUSED, true>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
+                                          &arrive_old);
+        first = false;
+      } else if (li < d.n_shrink) {
+        if (first) {
+          if (tid == 0) {
+            s_ep = ep_in;
+            arrive_old = arrive(ctl, ep_in);
+          }
+          __syncthreads();
+          first = false;
+        }
+        int* set = ctl_set(ctl, s_ep);
+        const int proj = li / d.units_per_proj, w = li % d.units_per_proj;
+        const int unit = w / d.KP, kp = w % d.KP;
+        float* red = reinterpret_cast<float*>(smem);
         if (FUSED) wait_geq(ctl, &set[kSetSegDone], 1);
         switch ((a.r + 15) >> 4) {
-          case 1: shrink_item<1, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 2: shrink_item<2, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          case 4: shrink_item<4, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
-          default: shrink_item<8, FUSED>(a, d, proj, unit, kp, red, s_loc); break;
+          case 1: shrink_item<1, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          case 2: shrink_item<2, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          case 4: shrink_item<4, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          default: shrink_item<8, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
         }
+        // the u stores are device-coherent; wait for them before counting this unit done
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) atomicAdd(&set[kSetShrinkDone + 32 * gi], 1);
+      } else {
+        const int bi = li - d.n_shrink;
+        const int bp = proj_of_tile(a, bi / a.S);
+        if (RP_PICK(a, bp, tiled))
+          base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
+                                            &arrive_old);
+        else
+          base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
+                                             &arrive_old);
+        first = false;
       }
-      // the u stores are device-coherent; wait for them before counting this unit done
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) atomicAdd(&set[kSetShrinkDone], 1);
-    } else {
-      const int bi = item - n_base0;
-      const int bp = proj_of_tile(a, bi / a.S);
-      if (RP_PICK(a, bp, tiled))
-        base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
-                                          &arrive_old);
-      else
-        base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
-                                           &arrive_old);
-      first = false;
     }
     __syncthreads();  // LDS is reused by the next item
   }
@@ -775,24 +845,22 @@ int resident_per_cu() {
   return n;
 }
 
-hipError_t launch_plain(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan, hipStream_t s) {
+hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
   const dim3 grid(plan.grid);
-  switch (decode_mt(a.T)) {
-    case 1: decode_kernel<1, false><<<grid, kThreads, 0, s>>>(a, d); break;
-    case 2: decode_kernel<2, false><<<grid, kThreads, 0, s>>>(a, d); break;
-    default: decode_kernel<4, false><<<grid, kThreads, 0, s>>>(a, d); break;
-  }
-  return hipGetLastError();
-}
-
-// Routing inside the launch is built for up to two token tiles (T <= 32);
-// larger decode batches route in launches of their own.
-hipError_t launch_fused(const SgmmArgs& a, const DecodeArgs& d, const SgmmPlan& plan, hipStream_t s) {
-  const dim3 grid(plan.grid);
-  switch (decode_mt(a.T)) {
-    case 1: decode_kernel<1, true><<<grid, kThreads, 0, s>>>(a, d); break;
-    case 2: decode_kernel<2, true><<<grid, kThreads, 0, s>>>(a, d); break;
-    default: return hipErrorInvalidValue;
+  const int T = st.g[0].T;
+  if (st.fused) {
+    // routing inside the launch is built for up to two token tiles (T <= 32)
+    switch (decode_mt(T)) {
+      case 1: decode_kernel<1, true><<<grid, kThreads, 0, s>>>(st); break;
+      case 2: decode_kernel<2, true><<<grid, kThreads, 0, s>>>(st); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (decode_mt(T)) {
+      case 1: decode_kernel<1, false><<<grid, kThreads, 0, s>>>(st); break;
+      case 2: decode_kernel<2, false><<<grid, kThreads, 0, s>>>(st); break;
+      default: decode_kernel<4, false><<<grid, kThreads, 0, s>>>(st); break;
+    }
   }
   return hipGetLastError();
 }
@@ -814,38 +882,6 @@ int decode_resident_per_cu(int T, bool fused) {
 
 bool decode_fused_route_supported(int T) { return decode_mt(T) <= 2; }
 
-static DecodeArgs decode_args(const SgmmArgs& a, const SgmmPlan& plan) {
-  DecodeArgs d{};
-  d.n_route = plan.n_route;
-  d.n_pre = plan.n_pre;
-  d.units_per_proj = plan.units_per_proj;
-  d.atiles_per_proj = plan.atiles_per_proj;
-  d.n_atiles = plan.n_atiles;
-  d.SA = plan.SA;
-  d.n_shrink = plan.dense ? plan.n_atiles * plan.SA : plan.units_per_proj * a.n_proj;
-  d.shrink_target = d.n_shrink;  // pair-chunk units (dense u is tagged instead)
-  d.partial_a = a.partial + (plan.off_partial_a - plan.off_partial) / sizeof(float);
-  d.route_tagged = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(a.counters) + plan.off_route);
-  d.n_items = plan.n_items;
-  d.KP = plan.KP;
-  d.dense = plan.dense;
-  d.t_pad = plan.t_pad;
-  return d;
-}
-
-hipError_t launch_decode(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s) {
-  DecodeArgs d = decode_args(a, plan);
-  d.fused = 0;
-  return launch_plain(a, d, plan, s);
-}
-
-hipError_t launch_route_sgmm(const SgmmArgs& a, const PregateArgs& pg, const SegmentArgs& sg, const SgmmPlan& plan,
-                             hipStream_t s) {
-  DecodeArgs d = decode_args(a, plan);
-  d.fused = 1;
-  d.pg = pg;
-  d.sg = sg;
-  return launch_fused(a, d, plan, s);
-}
+hipError_t launch_step(const StepArgs& st, const StepPlan& plan, hipStream_t s) { return launch_t(st, plan, s); }
 
 }  // namespace rp

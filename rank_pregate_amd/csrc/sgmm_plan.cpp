@@ -1,5 +1,5 @@
-// Launch planning for rp_sgmm_fused / rp_route_sgmm_fused: which kernel family
-// serves a call, its output-row tiling, K splits, grid and workspace layout.
+// Launch planning for the SGMM entry points: which kernel family serves a
+// call, output-row tiling, K splits, grid and workspace layout.
 #include <algorithm>
 #include <cstdlib>
 
@@ -13,11 +13,11 @@ constexpr int kDecodeTileRows = 32;
 constexpr int kDecodeMaxT = 64;
 constexpr int kPrefillTileRows = 128;
 constexpr int kF32TileRows = 64;
-constexpr int kDenseMaxE = 32;      // decode shrink covers every token per adapter up to this many adapters
-constexpr int kMaxSplits = 8;       // decode split-K
-constexpr int kMaxKParts = 8;       // decode shrink K parts
-constexpr int kShrinkPartBytes = 16384;  // target A bytes per decode shrink unit
-constexpr int kItemsPerCu2 = 3;          // twice the backbone items per CU a decode launch aims for
+constexpr int kDenseMaxE = 32;           // decode shrink covers every token per adapter up to this many adapters
+constexpr int kMaxSplits = 8;            // decode split-K
+constexpr int kMaxKParts = 8;            // decode pair-chunk shrink K parts
+constexpr int kShrinkPartBytes = 16384;  // target A bytes per decode pair-chunk shrink unit
+constexpr int kItemsPerCu2 = 3;          // twice the backbone items per CU a decode group aims for
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -42,35 +42,19 @@ size_t decode_partial_bytes(int n_tiles, int S, int T) {
 }
 
 int a_tiles_per_proj(int E, int r) { return (E * r + kDecodeTileRows - 1) / kDecodeTileRows; }
-}  // namespace
 
-SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
-                   bool fused_route) {
+// One decode group: tiling, splits, items, and its workspace starting at `off`.
+SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu, size_t off) {
   SgmmPlan p{};
-  p.path = (dt == kF32) ? 0 : (T <= kDecodeMaxT ? 1 : 2);
-  p.tile_rows = p.path == 0 ? kF32TileRows : p.path == 1 ? kDecodeTileRows : kPrefillTileRows;
+  p.path = 1;
+  p.tile_rows = kDecodeTileRows;
   p.n_tiles = 0;
-  for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + p.tile_rows - 1) / p.tile_rows;
-  p.S = 1;
-  p.off_counters = 0;
-  size_t off = kCounterBytes;
-  p.off_u = off;
-  if (p.path != 1) {
-    off = align256(off + (size_t)n_proj * T * k * r * sizeof(float));
-    p.off_partial = off;
-    p.bytes = off;
-    return p;
-  }
-  // decode: every item of the launch is resident at once when it fits; the
-  // row tiles are split along K until the chip holds about as many items as
-  // it can run together
+  for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + kDecodeTileRows - 1) / kDecodeTileRows;
   p.t_pad = 16 * decode_mt(T);
   p.dense = E <= kDenseMaxE;
   const int nchunks = (d_in + decode_chunk_k(T) - 1) / decode_chunk_k(T);
-  int s_max = std::max(1, std::min(kMaxSplits, nchunks / 2));
+  const int s_max = std::max(1, std::min(kMaxSplits, nchunks / 2));
   p.KP = 1;
-  p.units_per_proj = 0;
-  p.atiles_per_proj = p.n_atiles = 0;
   p.SA = 1;
   int n_shrink = 0;
   if (k > 0 && p.dense) {
@@ -85,47 +69,90 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
     p.units_per_proj = (E + (T * k + 15) / 16) * p.KP;
     n_shrink = p.units_per_proj * n_proj;
   }
-  p.n_route = fused_route ? (T + fused_route_tile_tokens() - 1) / fused_route_tile_tokens() : 0;
-  p.n_pre = fused_route ? p.n_route + 1 : 0;
-  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
-
   // about 1.5 backbone items per CU: enough loads in flight to saturate HBM,
   // and no more (extra bytes in flight only queue, and every dependent round
   // trip of the launch then waits behind them)
   int S = (kItemsPerCu2 * n_cu / 2 + p.n_tiles / 2) / p.n_tiles;
-  S = std::min(S, (cap - p.n_pre - n_shrink) / p.n_tiles);
   if (const char* env = std::getenv("RP_DECODE_SPLITS")) {  // tuning override
     const int v = std::atoi(env);
     if (v > 0) S = v;
   }
   p.S = std::max(1, std::min(S, s_max));
-  p.n_items = p.n_pre + n_shrink + p.n_tiles * p.S;
-  p.grid = std::min(p.n_items, cap);
+  p.n_items = n_shrink + p.n_tiles * p.S;
+  p.off_u = off;
   off = align256(off + decode_u_bytes(n_proj, T, E, r, k, p.KP, p.dense));
   p.off_partial = off;
   off = align256(off + decode_partial_bytes(p.n_tiles, p.S, T));
   p.off_partial_a = off;
   off = align256(off + decode_partial_bytes(p.n_atiles, p.SA, T));
-  p.off_route = off;  // fused launches: tagged routing results
-  if (fused_route) off = align256(off + (size_t)T * k * 16);
   p.bytes = off;
   return p;
 }
+}  // namespace
+
+SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
+                   bool fused_route) {
+  (void)fused_route;
+  if (dt == kBF16 && T <= kDecodeMaxT) return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, kCounterBytes);
+  SgmmPlan p{};
+  p.path = (dt == kF32) ? 0 : 2;
+  p.tile_rows = p.path == 0 ? kF32TileRows : kPrefillTileRows;
+  p.n_tiles = 0;
+  for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + p.tile_rows - 1) / p.tile_rows;
+  p.S = 1;
+  p.off_counters = 0;
+  p.off_u = kCounterBytes;
+  p.off_partial = align256(p.off_u + (size_t)n_proj * T * k * r * sizeof(float));
+  p.bytes = p.off_partial;
+  return p;
+}
+
+StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int r, int k, int n_cu, bool fused_route) {
+  StepPlan sp{};
+  sp.n_groups = n_groups;
+  sp.n_route = fused_route ? (T + fused_route_tile_tokens() - 1) / fused_route_tile_tokens() : 0;
+  sp.n_pre = fused_route ? sp.n_route + 1 : 0;
+  size_t off = kCounterBytes;
+  int items = sp.n_pre;
+  for (int g = 0; g < n_groups; ++g) {
+    sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, off);
+    off = sp.gp[g].bytes;
+    sp.item_begin[g] = items;
+    items += sp.gp[g].n_items;
+  }
+  sp.off_route = off;
+  if (fused_route) off = align256(off + (size_t)T * k * 16);
+  sp.bytes = off;
+  sp.n_items = items;
+  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
+  sp.grid = std::min(sp.n_items, cap);
+  return sp;
+}
+
+size_t step_workspace_upper_bound(const StepGroupDesc* groups, int n_groups, int T, int E, int r, int k) {
+  size_t b = kCounterBytes;
+  for (int g = 0; g < n_groups; ++g) {
+    long long sum_d_out = 0;
+    for (int i = 0; i < groups[g].n_proj; ++i) sum_d_out += groups[g].d_out[i];
+    const bool dense = E <= kDenseMaxE;
+    const int KP = (k > 0 && !dense) ? shrink_kparts(groups[g].d_in, r) : 1;
+    b = align256(b + decode_u_bytes(groups[g].n_proj, T, E, r, k, KP, dense));
+    const int tiles = (int)(sum_d_out / kDecodeTileRows + groups[g].n_proj);
+    b = align256(b + decode_partial_bytes(tiles, kMaxSplits, T));
+    if (k > 0 && dense) b = align256(b + decode_partial_bytes(a_tiles_per_proj(E, r) * groups[g].n_proj, kMaxSplits, T));
+  }
+  return align256(b + (size_t)T * k * 16);
+}
 
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r, int k) {
-  size_t b = kCounterBytes;
   if (dt == kBF16 && T <= kDecodeMaxT) {
-    const bool dense = E <= kDenseMaxE;
-    const int KP = (k > 0 && !dense) ? shrink_kparts(d_in, r) : 1;
-    b = align256(b + decode_u_bytes(n_proj, T, E, r, k, KP, dense));
-    const int tiles = (int)(sum_d_out / kDecodeTileRows + n_proj);
-    b = align256(b + decode_partial_bytes(tiles, kMaxSplits, T));
-    if (k > 0 && dense) b = align256(b + decode_partial_bytes(a_tiles_per_proj(E, r) * n_proj, kMaxSplits, T));
-    b = align256(b + (size_t)T * k * 16);
-  } else {
-    b = align256(b + (size_t)n_proj * T * k * r * sizeof(float));
+    // one group whose widths sum to sum_d_out (the bound only depends on the sum)
+    int d_out[kMaxProj];
+    for (int i = 0; i < n_proj; ++i) d_out[i] = (int)(sum_d_out / n_proj) + (i < sum_d_out % n_proj ? 1 : 0);
+    StepGroupDesc g{n_proj, d_out, d_in, 0};
+    return step_workspace_upper_bound(&g, 1, T, E, r, k);
   }
-  return b;
+  return align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
 }
 
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s) {
@@ -133,8 +160,8 @@ hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStr
   if (a.T == 0) return hipSuccess;
   switch (plan.path) {
     case 0: return launch_f32(a, plan, s);
-    case 1: return launch_decode(a, plan, s);
-    default: return launch_prefill(a, plan, s);
+    case 2: return launch_prefill(a, plan, s);
+    default: return hipErrorInvalidValue;  // decode groups launch through launch_step
   }
 }
 

@@ -3,10 +3,10 @@
 A step is the whole hot path once (AdaFuse technical summary §2.A-§2.B):
 route the router input once (rp_pregate), group pairs by adapter
 (rp_segment), then every projection group of every layer in dependency order
-(q|k|v -> o -> gate|up -> down), each one rp_sgmm_fused call.  The same
-gate and segments serve every layer.  By default the routing runs inside the
-first group's launch (rp_route_sgmm_fused), since the router's input is that
-group's input.
+(q|k|v -> o -> gate|up -> down) through rp_sgmm_step, which runs them in
+order inside multi-group launches.  The same gate and segments serve every
+layer.  By default the routing runs inside the step's first launch, since the
+router's input is the first group's input.
 
 Inputs come from rank_pregate_amd.datagen (seeded); weights are uploaded
 once and stay resident in HBM.  `copies` > 1 keeps several copies of the
@@ -22,7 +22,7 @@ import numpy as np
 
 from . import datagen
 from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
-from . import route_sgmm_fused as rp_route_sgmm_fused
+from . import route_sgmm_fused as rp_route_sgmm_fused, sgmm_step as rp_sgmm_step, step_workspace_size
 from . import sgmm_workspace_size, segment_workspace_size, pack_w0, RP_BF16, RP_F32
 
 
@@ -94,13 +94,11 @@ class DeviceWorkload:
             self.sel_idx = torch.from_numpy(fi).to(self.device)
             self.sel_gate = torch.from_numpy(fg).to(self.device)
         self.outputs: Dict[Tuple[int, str], object] = {}
-        ws_bytes = 0
         for g in wl.groups:
-            ws_bytes = max(ws_bytes, sgmm_workspace_size(len(g.projs), T, g.d_in, g.d_out * len(g.projs), E,
-                                                         wl.r, k, self.code))
             for l in self.layers:
                 for p in g.projs:
                     self.outputs[(l, p)] = torch.empty((T, g.d_out), dtype=tdt, device=self.device)
+        ws_bytes = step_workspace_size(self.step_groups(0), E, wl.r, k)
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device)
         self.step_count = 0
 
@@ -112,44 +110,70 @@ class DeviceWorkload:
         rp_pregate(self.x_router, self.Wg, wl.k, self.topk_idx, self.topk_gate, stream=stream)
         rp_segment(self.sel_idx, wl.E, self.seg_offsets, self.pair_perm, ws=self.seg_ws, stream=stream)
 
-    def project(self, copy: int = 0, k: Optional[int] = None, stream=None, skip_first: bool = False):
-        wl = self.wl
-        kk = wl.k if k is None else k
+    def step_groups(self, copy: int = 0):
+        """The step's projection groups in dependency order: (projs, x) per (layer, group)."""
         W = self.weights[copy]
-        first = True
+        groups = []
         for l in self.layers:
-            for g in wl.groups:
-                if first and skip_first:
-                    first = False
-                    continue
-                first = False
-                x = self.inputs[(l, g.x_name)]
+            for g in self.wl.groups:
                 projs = [(W[(l, p)].W0, W[(l, p)].A, W[(l, p)].B, self.outputs[(l, p)]) for p in g.projs]
-                rp_sgmm_fused(projs, x, wl.E, wl.r, kk, self.sel_idx, self.sel_gate, self.seg_offsets,
-                              self.pair_perm, ws=self.ws, stream=stream)
+                groups.append((projs, self.inputs[(l, g.x_name)]))
+        return groups
 
     def can_fuse_route(self) -> bool:
         """The router's input is layer 0's first group input and its choice is the one used."""
         return self.layers[0] == 0 and self.sel_idx is self.topk_idx
 
-    def run(self, copy: int = 0, fused: bool = True, stream=None):
-        """One step: routing, then every projection group in order.  With `fused`, the router and the
-        segmentation run inside the first group's launch (rp_route_sgmm_fused)."""
+    def run(self, copy: int = 0, fused: bool = True, k: Optional[int] = None, n_groups: Optional[int] = None,
+            stream=None):
+        """One step: routing, then every projection group in order (rp_sgmm_step).  With `fused` the
+        router and the segmentation run inside the step's first launch; k = 0 gives the base projections
+        only.  n_groups limits the step to its first groups (for timing one launch)."""
         wl = self.wl
-        if fused and self.can_fuse_route():
-            g = wl.groups[0]
-            W = self.weights[copy]
-            projs = [(W[(0, p)].W0, W[(0, p)].A, W[(0, p)].B, self.outputs[(0, p)]) for p in g.projs]
-            rp_route_sgmm_fused(projs, self.inputs[(0, g.x_name)], self.Wg, wl.E, wl.r, wl.k, self.topk_idx,
-                                self.topk_gate, self.seg_offsets, self.pair_perm, ws=self.ws, stream=stream)
-            self.project(copy, stream=stream, skip_first=True)
-        else:
+        kk = wl.k if k is None else k
+        groups = self.step_groups(copy)
+        if n_groups is not None:
+            groups = groups[:n_groups]
+        if kk > 0 and fused and self.can_fuse_route():
+            rp_sgmm_step(groups, wl.E, wl.r, kk, Wg=self.Wg, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
+                         seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+            return
+        if kk > 0:
             self.route(stream)
-            self.project(copy, stream=stream)
+        rp_sgmm_step(groups, wl.E, wl.r, kk, topk_idx=self.sel_idx if kk else None,
+                     topk_gate=self.sel_gate if kk else None, seg_offsets=self.seg_offsets if kk else None,
+                     pair_perm=self.pair_perm if kk else None, ws=self.ws, stream=stream)
+
+    def project(self, copy: int = 0, k: Optional[int] = None, stream=None):
+        """Every projection group with the routing already in place (no routing work)."""
+        wl = self.wl
+        kk = wl.k if k is None else k
+        rp_sgmm_step(self.step_groups(copy), wl.E, wl.r, kk, topk_idx=self.sel_idx if kk else None,
+                     topk_gate=self.sel_gate if kk else None, seg_offsets=self.seg_offsets if kk else None,
+                     pair_perm=self.pair_perm if kk else None, ws=self.ws, stream=stream)
 
     def step(self, stream=None, fused: bool = True):
         self.run(self.step_count % self.copies, fused=fused, stream=stream)
         self.step_count += 1
+
+    def group_bytes(self, gi: int, n_touched: int, k: Optional[int] = None) -> int:
+        """Algorithmic bytes of projection group number gi of the step (weights, touched adapters, input, outputs)."""
+        wl = self.wl
+        kk = wl.k if k is None else k
+        g = wl.groups[gi % len(wl.groups)]
+        bpe = 2 if wl.dtype == "bf16" else 4
+        b = wl.T * g.d_in * bpe
+        for _ in g.projs:
+            b += g.d_out * g.d_in * bpe + wl.T * g.d_out * bpe
+            if kk > 0:
+                b += n_touched * wl.r * (g.d_in + g.d_out) * bpe
+        return b
+
+    def routing_bytes(self) -> int:
+        """Router weight and input, and the routing arrays."""
+        wl = self.wl
+        bpe = 2 if wl.dtype == "bf16" else 4
+        return wl.d * wl.E * bpe + wl.T * wl.d * bpe + wl.T * wl.k * 8 + (wl.E + 1) * 4 + wl.T * wl.k * 4
 
     # -- accounting ------------------------------------------------------------
     def algorithmic_bytes(self, n_touched: int, k: Optional[int] = None) -> int:

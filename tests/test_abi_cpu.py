@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 3
+    assert rp.abi_version() == 4
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -209,3 +209,61 @@ def test_route_sgmm_rejects(kw, status):
 
 def test_route_sgmm_T0_is_noop():
     assert _route(T=0, x=None, Wg=None, idx=None, gate=None, off=None, perm=None, ws=None) == rp.RP_OK
+
+
+def _step(groups=None, n_groups=None, **kw):
+    a = dict(T=32, E=8, r=16, k=2, Wg=None, idx=FAKE, gate=FAKE, off=FAKE, perm=FAKE, dt=rp.RP_BF16, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    proj = (rp.RpProj * 1)(rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 0))
+    if groups is None:
+        groups = [rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), 1, 0, FAKE, 256, 256)] * 2
+    arr = (rp.RpGroup * max(1, len(groups)))(*groups)
+    n = len(groups) if n_groups is None else n_groups
+    return rp.lib().rp_sgmm_step(arr, n, a["T"], a["E"], a["r"], a["k"], a["Wg"], a["idx"], a["gate"], a["off"],
+                                 a["perm"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_groups=0), rp.RP_ERR_INVALID_ARG),
+    (dict(n_groups=4097), rp.RP_ERR_INVALID_ARG),
+    (dict(r=12), rp.RP_ERR_UNSUPPORTED),
+    (dict(k=9), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),      # routing given: inputs needed
+    (dict(Wg=FAKE, k=0), rp.RP_ERR_INVALID_ARG),  # routing computed: k >= 1
+    (dict(Wg=FAKE + 8), rp.RP_ERR_INVALID_ARG),
+    (dict(ws=None), rp.RP_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), rp.RP_ERR_WORKSPACE),
+])
+def test_step_rejects(kw, status):
+    assert _step(**kw) == status
+    assert rp.last_error()
+
+
+def test_step_rejects_bad_group():
+    proj = (rp.RpProj * 1)(rp.RpProj(FAKE, FAKE, FAKE, FAKE, 100, 104, 0, 0))  # d_out % 8
+    good = (rp.RpProj * 1)(rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 0))
+    g_bad = rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), 1, 0, FAKE, 256, 256)
+    g_ok = rp.RpGroup(ctypes.cast(good, ctypes.POINTER(rp.RpProj)), 1, 0, FAKE, 256, 256)
+    assert _step(groups=[g_ok, g_bad]) == rp.RP_ERR_INVALID_ARG
+    assert "group 1" in rp.last_error()
+    g_flag = rp.RpGroup(ctypes.cast(good, ctypes.POINTER(rp.RpProj)), 1, 2, FAKE, 256, 256)
+    assert _step(groups=[g_ok, g_flag]) == rp.RP_ERR_INVALID_ARG
+
+
+def test_step_T0_is_noop():
+    assert _step(T=0, idx=None, gate=None, off=None, perm=None, ws=None) == rp.RP_OK
+
+
+def test_step_workspace_size():
+    L = rp.lib()
+    proj = (rp.RpProj * 3)(*[rp.RpProj(FAKE, FAKE, FAKE, FAKE, 4096, 4096, 0, 0)] * 3)
+    g = rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), 3, 0, FAKE, 4096, 4096)
+    arr = (rp.RpGroup * 10)(*[g] * 10)
+    one = L.rp_sgmm_step_workspace_size(arr, 1, 32, 8, 16, 2, rp.RP_BF16)
+    ten = L.rp_sgmm_step_workspace_size(arr, 10, 32, 8, 16, 2, rp.RP_BF16)
+    assert one > 0 and one % 256 == 0
+    # eight groups share one launch's workspace; later launches reuse it
+    assert ten >= one and ten <= 8 * one
+    assert L.rp_sgmm_step_workspace_size(arr, 0, 32, 8, 16, 2, rp.RP_BF16) == 0
+    assert L.rp_sgmm_step_workspace_size(arr, 1, 32, 8, 12, 2, rp.RP_BF16) == 0

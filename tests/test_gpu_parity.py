@@ -434,6 +434,100 @@ def test_workspace_shared_across_call_kinds():
             _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=200 + i, ws=ws)
 
 
+# --------------------------------------------------------------------------- multi-group steps
+
+def _group_weights(rng, d_in, d_outs, E, r, dt, b_scale=1.0):
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    hw, dev = [], []
+    for d_out in d_outs:
+        W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) * np.float32(b_scale / np.sqrt(r)))
+        hw.append((W0, A, B))
+        dev.append((to_device(W0, dt, DEV), to_device(A, dt, DEV), to_device(B, dt, DEV)))
+    return hw, dev
+
+
+@pytest.mark.parametrize("T,specs,E,r,k,route", [
+    (32, [(512, [256, 128, 128]), (256, [512]), (512, [384])], 8, 16, 2, True),   # routing inside, three groups
+    (17, [(256, [96]), (96, [256])], 40, 16, 2, False),                            # E > 32, routing given
+    (64, [(256, [128, 64]), (128, [256])], 16, 8, 2, True),                         # T = 64: routing launched first
+    (100, [(128, [64]), (64, [128])], 8, 16, 2, True),                              # prefill shapes, group by group
+    (9, [(128, [64])] * 11, 6, 8, 1, True),                                        # more groups than one launch holds
+])
+def test_step_groups(T, specs, E, r, k, route):
+    """rp_sgmm_step: every group against the oracle with the step's routing."""
+    say("step", T, len(specs), E, r, k, route)
+    rng = np.random.default_rng(T * 7 + len(specs))
+    dt = "bf16"
+    conv = datagen.f32_to_bf16_bits
+    groups, hws, xs = [], [], []
+    for d_in, d_outs in specs:
+        hw, dev = _group_weights(rng, d_in, d_outs, E, r, dt)
+        x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+        xs.append(x)
+        hws.append(hw)
+        groups.append(([dv for dv in dev], to_device(x, dt, DEV)))
+    Wg = conv(rng.standard_normal((specs[0][0], E), dtype=np.float32) / np.float32(np.sqrt(specs[0][0])))
+    if route:
+        ys, idx, gate, off, perm = rp.sgmm_step(groups, E, r, k, Wg=to_device(Wg, dt, DEV))
+        torch.cuda.synchronize()
+        same, idx_ref, gate_ref = compare_routing(idx, gate, None, widen(xs[0], dt), widen(Wg, dt), k)
+        assert same.all()
+        off_ref, perm_ref = oracle.segment(idx_ref, E)
+        np.testing.assert_array_equal(off.cpu().numpy(), off_ref)
+        np.testing.assert_array_equal(perm.cpu().numpy()[: T * k], perm_ref)
+    else:
+        idx_ref = datagen.uniform_indices(T, T, E, k)
+        gate_ref = datagen.random_gates(T, T, k).astype(np.float64)
+        idx_d = torch.from_numpy(idx_ref).to(DEV)
+        gate_d = torch.from_numpy(gate_ref.astype(np.float32)).to(DEV)
+        off, perm = rp.segment(idx_d, E)
+        ys, *_ = rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+        torch.cuda.synchronize()
+    for gi, (hw, gys) in enumerate(zip(hws, ys)):
+        x64 = widen(xs[gi], dt)
+        for (W0, A, B), y in zip(hw, gys):
+            ref = oracle.sgmm(x64, widen(W0, dt), widen(A, dt), widen(B, dt), idx_ref, gate_ref)
+            check_y(y, ref, dt, f"step group {gi} d_out={W0.shape[0]}")
+
+
+@pytest.mark.parametrize("T", [32, 64])
+def test_step_chained(T):
+    """A group whose input is an earlier group's output in the same call (x_from_call): the later
+    group must read what the earlier one wrote."""
+    say("step chained", T)
+    rng = np.random.default_rng(400 + T)
+    dt, E, r, k = "bf16", 8, 16, 2
+    conv = datagen.f32_to_bf16_bits
+    d = 256
+    hw0, dev0 = _group_weights(rng, d, [d, 128], E, r, dt)
+    hw1, dev1 = _group_weights(rng, d, [192], E, r, dt)
+    hw2, dev2 = _group_weights(rng, 192, [256], E, r, dt)
+    x0 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    y0 = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    y1 = torch.empty((T, 192), dtype=torch.bfloat16, device=DEV)
+    idx = datagen.uniform_indices(T + 1, T, E, k)
+    gate = datagen.random_gates(T + 1, T, k)
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    groups = [([dev0[0] + (y0,), dev0[1]], to_device(x0, dt, DEV)),
+              ([dev1[0] + (y1,)], y0, 1),
+              ([dev2[0]], y1, 1)]
+    for rep in range(3):  # fresh outputs each time: a stale read would show
+        y0.zero_()
+        y1.zero_()
+        ys, *_ = rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+        torch.cuda.synchronize()
+        g64 = gate.astype(np.float64)
+        ref0 = oracle.sgmm(widen(x0, dt), *(widen(a, dt) for a in hw0[0]), idx, g64)
+        check_y(y0, ref0, dt, "chained group 0")
+        ref1 = oracle.sgmm(dl_widen(y0, dt), *(widen(a, dt) for a in hw1[0]), idx, g64)
+        check_y(y1, ref1, dt, "chained group 1")
+        ref2 = oracle.sgmm(dl_widen(y1, dt), *(widen(a, dt) for a in hw2[0]), idx, g64)
+        check_y(ys[2][0], ref2, dt, "chained group 2")
+
+
 def test_adapter_sensitivity():
     """B without the 0.1 factor: a wrong adapter or gate could not hide under the bf16 tolerance."""
     say("adapter sensitivity")
