@@ -194,10 +194,12 @@ typedef struct {
   int64_t ld_x;
 } rp_group;
 
-/* A decode step (AdaFuse §2.B decoding steps 1-3 over every adapted layer):
- * the groups run in order, group g+1 reading its x only after every output
- * of groups 0..g is written, so a group's x may be an earlier group's y
- * (mark it with x_from_call).  All groups use one routing:
+/* A decode step (AdaFuse §2.B decoding steps 1-3 over every adapted layer).
+ * A group marked x_from_call reads its x only after every output of the
+ * groups before it is written, so its x may be any earlier group's y.  A
+ * group without the mark does not wait and may run concurrently with earlier
+ * groups: its x must not be written by this call.  No y may overlap another
+ * y or any group's x.  All groups use one routing:
  *
  *   Wg_or_null non-null: the routing is computed first from groups[0].x, as
  *                        rp_route_sgmm_fused does; topk_idx, topk_gate,

@@ -367,9 +367,16 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       q.atiles_per_proj = gp.atiles_per_proj;
       q.n_atiles = gp.n_atiles;
       q.SA = gp.SA;
+      // only a group whose x an earlier group writes waits, and it waits for
+      // all of them; the others stream as soon as they are scheduled
+      bool later_reads = false;
+      for (int j = i + 1; j < ng; ++j) later_reads = later_reads || desc[j].x_acquire;
       q.x_acquire = desc[i].x_acquire;
-      q.count_done = i + 1 < ng;
-      q.release = i + 1 < ng && desc[i + 1].x_acquire;
+      q.count_done = later_reads;
+      q.release = later_reads;
+      q.wait_target = 0;
+      if (desc[i].x_acquire)
+        for (int j = 0; j < i; ++j) q.wait_target += sp.gp[j].n_tiles;
       q.partial_a = reinterpret_cast<float*>(w + gp.off_partial_a);
     }
     st.n_groups = ng;

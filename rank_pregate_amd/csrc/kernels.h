@@ -80,7 +80,7 @@ struct DecodeArgs {
   int t_pad;                          // tokens padded to whole 16-token tiles
   int fused;                          // routing runs inside the launch
   int group;                          // position of the group in its launch
-  int prev_target;                    // > 0: wait until the previous group has written this many tiles
+  int prev_target;                    // > 0: wait until groups 0..group-1 have written this many tiles
   int x_acquire;                      // x was written earlier in this launch: acquire before reading it
   int count_done;                     // a later group waits for this one: count finished tiles
   int release;                        // ... and reads what this one wrote: release before counting
@@ -98,6 +98,7 @@ struct GroupPlan {
   int item_begin;  // first item of the group in the launch
   int n_shrink, n_items, shrink_target, units_per_proj, KP, atiles_per_proj, n_atiles, SA;
   int x_acquire, count_done, release;
+  int wait_target;  // x_acquire: output tiles of every earlier group of the launch, else 0
   float* partial_a;
 };
 struct StepArgs {

@@ -127,16 +127,20 @@ __device__ __forceinline__ void wait_geq(int* ctl, const int* p, int target) {
 
 __device__ __forceinline__ int* ctl_set(int* ctl, int ep) { return ctl + kCtlSet0 + (ep & 1) * kCtlSetStride; }
 
-// Before reading its input, an item of group g > 0 waits until every output
-// tile of group g-1 is written (tiles are counted per tile % 8 so no single
-// counter takes every workgroup); wave 0 polls, the workgroup then proceeds.
+// Before reading an input that earlier groups of the launch write, an item of
+// group g waits until every output tile of groups 0..g-1 is written (tiles are
+// counted per group and tile % 8, so no single counter takes every workgroup;
+// lane 8*h + c reads group h's class c); wave 0 polls, the workgroup then
+// proceeds.
 __device__ __forceinline__ void wait_prev_group(int* ctl, int ep, const DecodeArgs& d) {
+  static_assert(8 * kMaxGroups <= 64, "one counter per lane");
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
-    const int* base = ctl + kCtlSet0 + (ep & 1) * kCtlSetStride + kSetGroupDone + 256 * (d.group - 1);
+    const int* p = ctl + kCtlSet0 + (ep & 1) * kCtlSetStride + kSetGroupDone + 256 * (lane >> 3) + 32 * (lane & 7);
+    const bool mine = lane < 8 * d.group;
     int spins = 0;
     while (true) {
-      const int v = lane < 8 ? __hip_atomic_load(base + 32 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      const int v = mine ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       if (wave_sum_int(v) >= d.prev_target) break;
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kSpinLimit) {
@@ -720,7 +724,7 @@ __device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
   d.t_pad = st.t_pad;
   d.fused = st.fused;
   d.group = gi;
-  d.prev_target = gi > 0 ? st.g[gi - 1].n_tiles : 0;
+  d.prev_target = gp.wait_target;
   d.x_acquire = gp.x_acquire;
   d.count_done = gp.count_done;
   d.release = gp.release;

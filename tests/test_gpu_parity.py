@@ -528,6 +528,41 @@ def test_step_chained(T):
         check_y(ys[2][0], ref2, dt, "chained group 2")
 
 
+@pytest.mark.parametrize("T", [32, 64])
+def test_step_skip_dependency(T):
+    """Independent groups do not wait, a dependent one waits for every earlier group: group 2 reads
+    group 0's output across an independent group 1."""
+    say("step skip dependency", T)
+    rng = np.random.default_rng(500 + T)
+    dt, E, r, k = "bf16", 8, 16, 2
+    conv = datagen.f32_to_bf16_bits
+    d = 256
+    hw0, dev0 = _group_weights(rng, d, [d], E, r, dt)
+    hw1, dev1 = _group_weights(rng, d, [4096], E, r, dt)
+    hw2, dev2 = _group_weights(rng, d, [128], E, r, dt)
+    hw3, dev3 = _group_weights(rng, d, [512], E, r, dt)
+    x0 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    x1 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    y0 = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    idx = datagen.uniform_indices(T + 2, T, E, k)
+    gate = datagen.random_gates(T + 2, T, k)
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    x0_d, x1_d = to_device(x0, dt, DEV), to_device(x1, dt, DEV)
+    groups = [([dev0[0] + (y0,)], x0_d), ([dev1[0]], x1_d), ([dev2[0]], y0, 1), ([dev3[0]], x1_d)]
+    g64 = gate.astype(np.float64)
+    for rep in range(3):
+        y0.zero_()
+        ys, *_ = rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+        torch.cuda.synchronize()
+        ref0 = oracle.sgmm(widen(x0, dt), *(widen(a, dt) for a in hw0[0]), idx, g64)
+        check_y(y0, ref0, dt, "group 0")
+        check_y(ys[1][0], oracle.sgmm(widen(x1, dt), *(widen(a, dt) for a in hw1[0]), idx, g64), dt, "group 1")
+        ref2 = oracle.sgmm(dl_widen(y0, dt), *(widen(a, dt) for a in hw2[0]), idx, g64)
+        check_y(ys[2][0], ref2, dt, "group 2")
+        check_y(ys[3][0], oracle.sgmm(widen(x1, dt), *(widen(a, dt) for a in hw3[0]), idx, g64), dt, "group 3")
+
+
 def test_adapter_sensitivity():
     """B without the 0.1 factor: a wrong adapter or gate could not hide under the bf16 tolerance."""
     say("adapter sensitivity")
