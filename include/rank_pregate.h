@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 4
+#define RP_ABI_VERSION 5
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
 #define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call (per group) */
@@ -66,10 +66,16 @@ typedef enum { RP_F32 = 0, RP_BF16 = 1 } rp_dtype;
 /* Storage order of a backbone weight W0.
  *   RP_W0_ROWS   dense row-major [d_out, d_in]
  *   RP_W0_TILED  the order rp_pack_w0 writes (bf16 only): blocks of 16 rows x 32
- *                columns, block (rb, cb) at element offset (rb * d_in/32 + cb) * 512;
- *                inside a block, 64 groups of 8 consecutive columns, group g
- *                holding row 16*rb + g%16, columns 32*cb + 8*(g/16) .. +7.
- *                Each decode wave then streams one contiguous run of memory. */
+ *                columns (nb = d_in/32 block columns, n_rb = d_out/16 row
+ *                blocks), grouped in chunks of four block columns.  Chunk g
+ *                (block columns 4g .. 4g+nbg-1, nbg = min(4, nb - 4g)) starts at
+ *                element 4g * n_rb * 512 and holds its blocks row block by row
+ *                block: block (rb, cb) at element offset
+ *                (4g * n_rb + rb * nbg + cb - 4g) * 512, g = cb / 4.  Inside a
+ *                block, 64 groups of 8 consecutive columns, group q holding row
+ *                16*rb + q%16, columns 32*cb + 8*(q/16) .. +7.  A decode launch
+ *                reads the same chunk of every row block at about the same
+ *                time, and those blocks are contiguous. */
 typedef enum { RP_W0_ROWS = 0, RP_W0_TILED = 1 } rp_w0_layout;
 
 /* One adapted projection (one linear layer with its adapter bank).

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -17,6 +19,28 @@ constexpr int kMaxEWords = kMaxE / 32;
 
 // bfloat16 values travel as raw 16-bit patterns.
 typedef uint16_t bf16_t;
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time (for
+// register arrays indexed by a loop position).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Packed backbone weights (RP_W0_TILED): 16-row x 32-column blocks of 1 KB,
+// grouped in chunks of four block columns (128 columns).  Chunk g stores its
+// blocks row block by row block, nbg = min(4, nb - 4g) blocks each, so the
+// blocks a decode launch reads at one moment (the same chunk of every row
+// block) sit together in memory.  Element offset of block (rb, cb), for n_rb
+// row blocks and nb block columns:
+__host__ __device__ inline size_t w0_block_offset(int rb, int cb, int n_rb, int nb) {
+  const int g = cb >> 2;
+  const int nbg = nb - 4 * g < 4 ? nb - 4 * g : 4;
+  return ((size_t)g * 4 * n_rb + (size_t)rb * nbg + (cb & 3)) * 512;
+}
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -120,14 +120,16 @@ __host__ __device__ inline int route_lds_floats(int E, int TT) { return 3 * TT *
 // walks its k-slice in ascending k with one fp32 sum per (token, column); the
 // slices are combined with a fixed butterfly inside each wave and then in wave
 // order, so equal router columns give bit-equal logits.
-// NCBp <= 128 (E <= 1024).  Must be called by all kRouteThreads threads.
+// NCBp <= 128 (E <= 1024).  Must be called by all kRouteThreads threads of a
+// group (every group of a wider workgroup calls it, with its own smem and t0).
 // With `tagged` set, each (token, slot) result is also written as two tagged
 // 8-byte pairs (index, tag) and (gate bits, tag) for readers in the same launch.
 template <typename Tin, int TT>
 __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem,
                                            unsigned long long* tagged = nullptr, uint32_t tag = 0) {
   const int NCBp = rp_.NCBp;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // a wider workgroup runs one tile per group of kRouteThreads threads
+  const int tid = threadIdx.x & (kRouteThreads - 1), lane = tid & 63, wave = tid >> 6;
   const int nt = min(TT, a.T - t0);
   const int E = a.E;
   const Tin* x = static_cast<const Tin*>(a.x);

@@ -40,13 +40,14 @@ namespace rp {
 namespace {
 
 constexpr int kSpinLimit = 1 << 22;  // ~seconds; a wait this long flags kCtlWaitOverflow and gives up
-constexpr int kWV = 2;               // waves per item
+constexpr int kWV = 4;               // waves per item
 constexpr int kThreads = 64 * kWV;
-constexpr int kTileRows = 16 * kWV;
-constexpr int kKC = 256;             // K per LDS chunk
-constexpr int kSteps = kKC / 32;     // MFMA k-steps per chunk
-constexpr int kLD = kKC + 8;         // padded LDS row (elements)
-static_assert(kThreads == kRouteThreads, "router tiles run on the decode workgroup shape");
+constexpr int kTileRows = 16 * kWV;  // output rows per item, 16 per wave
+constexpr int kKC = 128;             // K per chunk
+constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
+constexpr int kRing = 3;             // chunks whose loads are in flight ahead of the math
+static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
+static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
 constexpr int kMaxSplits = 8;         // K splits of a tile (the launch plan keeps S <= this)
@@ -102,10 +103,10 @@ __device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins)
 
 template <int MT, bool FUSED>
 constexpr size_t smem_bytes() {
-  constexpr size_t xs = 2ull * 16 * MT * kLD * sizeof(bf16_t);
-  constexpr size_t red = 8ull * MT * 64 * 4 * sizeof(float);             // shrink: up to 8 rank tiles x MT token tiles
-  constexpr size_t route = FUSED ? 3ull * 2 * kMaxE * sizeof(float) : 0;  // router tile, E = 1024
-  constexpr size_t seg = FUSED ? 2ull * kMaxE * sizeof(int) : 0;          // two-wave segmentation histograms
+  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t);             // activation chunks, double-buffered
+  constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
+  constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxE * sizeof(float) : 0;  // two router tiles
+  constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
   size_t m = xs;
   if (red > m) m = red;
   if (route > m) m = route;
@@ -225,14 +226,19 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) acc[mt] = mfma16(av[u][mt], bv[u], acc[mt]);
   }
-  // wave 0 + wave 1, in that order; D layout: lane -> pair slot0 + lane%16,
-  // rank rows mt*16 + 4*(lane/16) + 0..3
-  if (wave == 1) {
+  // waves 0, 1, .. added in that order; D layout: lane -> pair slot0 +
+  // lane%16, rank rows mt*16 + 4*(lane/16) + 0..3
+  if (wave > 0) {
 #pragma unroll
-    for (int mt = 0; mt < MTR; ++mt) *reinterpret_cast<f32x4_t*>(&red[(mt * 64 + lane) * 4]) = acc[mt];
+    for (int mt = 0; mt < MTR; ++mt)
+      *reinterpret_cast<f32x4_t*>(&red[(((wave - 1) * 8 + mt) * 64 + lane) * 4]) = acc[mt];
   }
   __syncthreads();
   if (wave == 0) {
+#pragma unroll
+    for (int w = 1; w < kWV; ++w)
+#pragma unroll
+      for (int mt = 0; mt < MTR; ++mt) acc[mt] += *reinterpret_cast<const f32x4_t*>(&red[(((w - 1) * 8 + mt) * 64 + lane) * 4]);
     const size_t slots = upart_slots(a, d);
     const float* ub = a.u + ((size_t)proj * d.KP + kp) * slots * a.r;
     const __amdgpu_buffer_rsrc_t r = rsrc(ub, (uint32_t)(slots * a.r * sizeof(float)));
@@ -242,10 +248,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) {
         const int c = mt * 16 + 4 * kg;
-        if (c < a.r) {
-          const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[(mt * 64 + lane) * 4]);
-          st_coh16(r, (uint32_t)(((size_t)p * a.r + c) * sizeof(float)), acc[mt] + o);
-        }
+        if (c < a.r) st_coh16(r, (uint32_t)(((size_t)p * a.r + c) * sizeof(float)), acc[mt]);
       }
     }
   }
@@ -254,20 +257,27 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 // ---------------------------------------------------------------------------
 // base item
 // ---------------------------------------------------------------------------
-// One output tile of 32 rows over one K split.  With ATILE the rows are
-// those of the stacked adapter down-projections [A_0; ..; A_{E-1}] of one
-// projection and the result is the rank-r intermediate u[e][t] (fp32, every
-// token) instead of y.  The last of a tile's S splits applies the adapter
-// deltas and sums the other splits' partial tiles; the operands of its first
-// expand pass are requested during its final chunk pair, so they arrive while
-// the last chunks compute.
+// One output tile of 64 rows (16 per wave) over one K split.  With ATILE the
+// rows are those of the stacked adapter down-projections [A_0; ..; A_{E-1}]
+// of one projection and the result is the rank-r intermediate u[e][t] (fp32,
+// every token) instead of y.  The last of a tile's S splits applies the
+// adapter deltas and sums the other splits' partial tiles; the operands of its
+// first expand pass are requested before its final chunks, so they arrive
+// while those compute.
+//
+// The stream: K goes in chunks of 128 columns.  For every chunk each thread
+// issues its activation pieces first, then its wave's four 1 KB weight blocks,
+// kRing chunks ahead of the math, into register rings; the activations of the
+// next chunk move to an LDS double buffer (in MFMA fragment order) one chunk
+// before use.  Loads retire in issue order, so waiting for a chunk's
+// activations leaves the weight loads of the kRing chunks issued after them in
+// flight.
 template <int MT, bool TILED, bool FUSED, bool ATILE>
 __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d, int bi, bf16_t* xs, int* ctl, int* s_ep,
                           bool first, int ep_in, int* arrive_old) {
-  constexpr int TP = 16 * MT;
-  constexpr int XCH = TP * kKC / 8 / kThreads;  // 16-byte x pieces per thread per chunk
   constexpr int G = 8;                          // adapters per batch of B loads
   constexpr uint32_t kOob = 0x80000000u;        // past any buffer: a buffer load returns zero
+  constexpr int XB = MT * kKS;                  // 1 KB activation fragment blocks per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = ATILE ? d.SA : a.S;
   const int tile = bi / S, split = bi % S;
@@ -281,206 +291,169 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int row = min(row0 + lr, n_rows - 1);
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
-  // row-major: this lane's row at column 8*kg; tiled: this wave's run of 1 KB blocks
-  const bf16_t* wrow = TILED
-      ? static_cast<const bf16_t*>(pd.W0) + (size_t)(row0 / 16) * (a.d_in / 32) * 512 + lane * 8
-      : static_cast<const bf16_t*>(ATILE ? pd.A : pd.W0) + (size_t)row * a.d_in + kg * 8;
+  const bf16_t* w0 = static_cast<const bf16_t*>(ATILE ? pd.A : pd.W0);
+  // tiled: this wave's row block; row-major: this lane's row at column 8*kg of each k-step
+  const int nb = a.d_in / 32, n_rb = pd.d_out / 16;
+  const int rblk = min(row0 / 16, n_rb - 1);
+  const bf16_t* wrow = w0 + (size_t)row * a.d_in + kg * 8;
   const int nch = (a.d_in + kKC - 1) / kKC;
-  const int cb = (int)((long long)nch * split / S), ce = (int)((long long)nch * (split + 1) / S);
+  const int cbeg = (int)((long long)nch * split / S);
+  const int nc = (int)((long long)nch * (split + 1) / S) - cbeg;  // >= 1: the plan keeps S <= nch
+  // activation piece m of this thread: token m*16 + lane%16, columns
+  // 32*wave + 8*kg .. +7 of the chunk (k-step `wave` of token tile m)
+  const int xcol = wave * 32 + kg * 8;
+  const bf16_t* xq[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xq[m] = x + (size_t)min(m * 16 + lr, a.T - 1) * a.ld_x;
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 wr[kRing][kKS];
+  uint4 xr[kRing][MT];
 
-  // Loads in the loop are never masked (a select would force a wait right
-  // after the load): W0 addresses are clamped into the row, and whatever they
-  // read past d_in meets activations that store_x wrote as zero.
-  auto load_w = [&](uint4 (&w)[kSteps], int c) {
-    const int cc = min(c, ce - 1);
-    if (TILED) {
+  // Loads are never masked (a select would force a wait right after them).
+  // Chunks past this split's last re-read activations (cache-resident) and
+  // put an activation address in the weight loads; weight blocks past d_in are
+  // clamped to a real block and meet activations that store_x wrote as zero.
+  auto issue = [&](int slot, int c) {
+    const bool real = c < nc;
+    const int cc = cbeg + min(c, nc - 1);
+    const int col = min(cc * kKC + xcol, a.d_in - 8);
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) w[st] = ld16(wrow + (size_t)min(cc * kSteps + st, a.d_in / 32 - 1) * 512);
+    for (int m = 0; m < MT; ++m) xr[slot][m] = ld16(xq[m] + col);
+    if (TILED) {
+      const int nbg = min(4, nb - 4 * cc);
+      const bf16_t* blk = w0 + ((size_t)cc * 4 * n_rb + (size_t)rblk * nbg) * 512 + lane * 8;
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(real ? blk + (size_t)min(s, nbg - 1) * 512 : xq[0] + col);
     } else {
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) w[st] = ld16(wrow + min(cc * kKC + st * 32, a.d_in - 8 - kg * 8));
+      for (int s = 0; s < kKS; ++s)
+        wr[slot][s] = ld16_stream(real ? wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8) : xq[0] + col);
     }
   };
-  auto load_x = [&](uint4 (&xr)[XCH], int c) {
-    const int cc = min(c, ce - 1);
+  auto issue_w = [&](int slot, int c) {  // weights alone (first chunks, before a group wait)
+    const int cc = cbeg + min(c, nc - 1);
+    if (TILED) {
+      const int nbg = min(4, nb - 4 * cc);
+      const bf16_t* blk = w0 + ((size_t)cc * 4 * n_rb + (size_t)rblk * nbg) * 512 + lane * 8;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int q = tid + i * kThreads;
-      const int tok = q / (kKC / 8), kc = (q % (kKC / 8)) * 8;
-      xr[i] = ld16(x + (size_t)min(tok, a.T - 1) * a.ld_x + min(cc * kKC + kc, a.d_in - 8));
+      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(blk + (size_t)min(s, nbg - 1) * 512);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8));
     }
   };
-  auto store_x = [&](const uint4 (&xr)[XCH], int buf, int c) {
+  auto issue_x = [&](int slot, int c) {
+    const int col = min((cbeg + min(c, nc - 1)) * kKC + xcol, a.d_in - 8);
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int q = tid + i * kThreads;
-      const int tok = q / (kKC / 8), kc = (q % (kKC / 8)) * 8;
-      *reinterpret_cast<uint4*>(&xs[((size_t)buf * TP + tok) * kLD + kc]) =
-          sel4(tok < a.T && c < ce && c * kKC + kc < a.d_in, xr[i]);
-    }
+    for (int m = 0; m < MT; ++m) xr[slot][m] = ld16(xq[m] + col);
   };
-  auto compute = [&](const uint4 (&w)[kSteps], int buf) {
+  // piece m of thread tid goes to fragment block m*kKS + wave, lane `lane`
+  auto store_x = [&](int slot, int buf, int c) {
+    const bool ok = (cbeg + c) * kKC + xcol < a.d_in;
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st)
+    for (int m = 0; m < MT; ++m) *reinterpret_cast<uint4*>(&xs[(buf * XB + m * kKS) * 512 + tid * 8]) = sel4(ok, xr[slot][m]);
+  };
+  auto compute = [&](int slot, int buf) {
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const uint4 xf = *reinterpret_cast<const uint4*>(&xs[((size_t)buf * TP + m * 16 + lr) * kLD + st * 32 + kg * 8]);
-        acc[m] = mfma16(xf, w[st], acc[m]);
+        const uint4 xf = *reinterpret_cast<const uint4*>(&xs[((buf * XB + m * kKS + s) * 64 + lane) * 8]);
+        acc[m] = mfma16(xf, wr[slot][s], acc[m]);
       }
   };
 
-  // routing of the lane's tokens, slots 0..k-1: read before the stream when
-  // the registers allow (and this launch does not compute it), else after
-  constexpr bool kEarlyRoute = MT <= 2;
-  int sel[MT][kMaxK];
-  float gate[MT][kMaxK];
-  auto read_route = [&]() {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = m * 16 + lr;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        const bool v = j < a.k && t < a.T;
-        sel[m][j] = v ? a.topk_idx[t * a.k + j] : -1;
-        gate[m][j] = v ? a.topk_gate[t * a.k + j] : 0.f;
-      }
-    }
-  };
-  if (!FUSED && expand && kEarlyRoute) read_route();
-
-  // operands of the first expand pass (rank columns 8*kg..+7, slots 0 and 1),
-  // requested in the final chunk pair
-  const int c_first = min(kg * 8, a.r - 8);
+  // dense u as tagged pairs [proj][e][t_pad][r]
   const __amdgpu_buffer_rsrc_t ru =
       rsrc(reinterpret_cast<const char*>(a.u) + (size_t)proj * a.E * d.t_pad * a.r * 8,
            (uint32_t)((size_t)a.E * d.t_pad * a.r * 8));
-  const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)a.T * a.k * 16));
-  constexpr bool kPrefetchU = MT <= 2;  // registers allow the u pairs to ride along too
-  uint4 bpf[G];                         // B rows of adapters 0..G-1, this lane's output row
-  u32x4_v upf[kPrefetchU ? MT : 1][2][4];  // dense u as tagged pairs (non-fused: the choices are known)
-  u32x4_v rpf[MT][2];                   // fused: tagged (index, gate) of the lane's tokens, slots 0 and 1
-  auto u_offset = [&](int m, int q, int c) -> uint32_t {
-    const int t = m * 16 + lr;
-    const bool ok = q < a.k && c < a.r && sel[m][min(q, kMaxK - 1)] >= 0;
-    return ok ? (uint32_t)((((size_t)sel[m][min(q, kMaxK - 1)] * d.t_pad + t) * a.r + c) * 8) : kOob;
-  };
   auto load_u4 = [&](u32x4_v (&w)[4], uint32_t off) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off == kOob ? kOob : off + 16 * i, 0, kSc1);
   };
-  auto load_route = [&](u32x4_v (&r)[MT][2], int j0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = min(m * 16 + lr, a.T - 1);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        r[m][q] = __builtin_amdgcn_raw_buffer_load_b128(rt, j0 + q < a.k ? (uint32_t)((t * a.k + j0 + q) * 16) : kOob, 0,
-                                                         kSc1);
-    }
-  };
-  auto prefetch = [&]() {
-    if (!expand || !kEarlyRoute) return;
-#pragma unroll
-    for (int g = 0; g < G; ++g) bpf[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + c_first);
-    if (FUSED) {
-      load_route(rpf, 0);
-    } else if (kPrefetchU && d.dense) {
-#pragma unroll
-      for (int m = 0; m < (kPrefetchU ? MT : 1); ++m)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) load_u4(upf[m][q], u_offset(m, q, kg * 8));
-    }
-  };
 
   {
-    uint4 wA[kSteps], wB[kSteps], XA[XCH], XB[XCH];
-    load_w(wA, cb);
-    // weights do not depend on the previous group: the first chunk is in flight during the wait
-    if (d.prev_target > 0) wait_prev_group(ctl, first ? __builtin_amdgcn_readfirstlane(ep_in) : *s_ep, d);
-    load_x(XA, cb);
-    load_x(XB, cb + 1);
+    if (d.prev_target > 0) {
+      // weights do not depend on the earlier groups: they are in flight during the wait
+      static_for<0, kRing>([&](auto I) { issue_w(decltype(I)::value, decltype(I)::value); });
+      wait_prev_group(ctl, first ? __builtin_amdgcn_readfirstlane(ep_in) : *s_ep, d);
+      static_for<0, kRing>([&](auto I) { issue_x(decltype(I)::value, decltype(I)::value); });
+    } else {
+      static_for<0, kRing>([&](auto I) { issue(decltype(I)::value, decltype(I)::value); });
+    }
     if (first && tid == 0) {
       *s_ep = ep_in;
       *arrive_old = arrive(ctl, ep_in);
     }
-    if (ce - cb < 2) prefetch();
-    store_x(XA, 0, cb);
+    store_x(0, 0, 0);
     __syncthreads();
-    // chunk pairs, no exit between the two halves; an odd last chunk follows
-    int c = cb;
-    for (; c + 2 <= ce; c += 2) {
-      // chunk c: x in LDS buffer 0, W0 in wA; XB holds chunk c+1
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(wB, c + 1);
-      load_x(XA, c + 2);
-      if (c + 4 > ce) prefetch();
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wA, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      store_x(XB, 1, c + 1);
-      __syncthreads();
-      // chunk c+1: x in buffer 1, W0 in wB; XA holds chunk c+2
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(wA, c + 2);
-      load_x(XB, c + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wB, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      store_x(XA, 0, c + 2);
-      __syncthreads();
+    // full rings while every chunk has a successor in this split
+    int c0 = 0;
+    for (; c0 + kRing < nc; c0 += kRing) {
+      static_for<0, kRing>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int c = c0 + i;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, c & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i, c + kRing);
+        __builtin_amdgcn_sched_barrier(0);
+        store_x((i + 1) % kRing, (c + 1) & 1, c + 1);
+        __syncthreads();
+      });
     }
-    if (c < ce) compute(wA, 0);
+    // the last 1..kRing chunks, already issued
+    static_for<0, kRing>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int c = c0 + i;
+      if (c < nc) {
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, c & 1);
+        if (c + 1 < nc) store_x((i + 1) % kRing, (c + 1) & 1, c + 1);
+        __syncthreads();
+      }
+    });
   }
   const int ep = *s_ep;
   int* set = ctl_set(ctl, ep);
   const uint32_t tag = launch_tag(ep);
 
-  // adapter deltas for this wave's 16 rows.  A lane's tokens chose at most k
-  // adapters, so it needs u only for its own (token, slot) pairs, two slots
-  // per pass, scaled by the gate; the operand for adapter e is then picked in
-  // registers.  B rows are loaded eight adapters at a time.
+  // adapter deltas for this wave's 16 rows.  The workgroup first stages the
+  // routing of the tile's tokens (adapter and gate of every (token, slot)
+  // pair) in LDS, where the activation chunks were.  A lane's tokens chose at
+  // most k adapters, so it needs u only for its own (token, slot) pairs, two
+  // slots per pass, scaled by the gate; the operand for adapter e is then
+  // picked in registers.  B rows are loaded eight adapters at a time.
   if (expand) {
-    if (!FUSED && !kEarlyRoute) read_route();
+    const int n_pairs = a.T * a.k;  // <= 16 * MT * kMaxK: fits the activation buffers
+    int* s_sel = reinterpret_cast<int*>(xs);
+    float* s_gate = reinterpret_cast<float*>(xs) + n_pairs;
     if (FUSED) {
-      // the routing this launch's router tiles wrote, validated by tag; slots
-      // 0 and 1 were requested in the final chunk pair, the rest go now
-#pragma unroll
-      for (int j0 = 0; j0 < kMaxK; j0 += 2) {
-        if (j0 >= a.k) break;
-        u32x4_v r[MT][2];
-        if (j0 == 0 && kEarlyRoute) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) r[m][0] = rpf[m][0], r[m][1] = rpf[m][1];
-        } else {
-          load_route(r, j0);
-        }
+      // written by this launch's router tiles as (index, tag, gate, tag), validated by tag
+      const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)n_pairs * 16));
+      for (int p0 = 0; p0 < n_pairs; p0 += kThreads) {
+        const int p = p0 + tid;
+        const uint32_t off = p < n_pairs ? (uint32_t)(p * 16) : kOob;
+        u32x4_v rr = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, kSc1);
         int spins = 0;
-        while (true) {
-          bool good = true;
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const bool v = j0 + q < a.k && m * 16 + lr < a.T;
-              sel[m][j0 + q] = v ? (int)r[m][q].x : -1;
-              gate[m][j0 + q] = v ? __uint_as_float(r[m][q].z) : 0.f;
-              if (v) good &= r[m][q].y == tag && r[m][q].w == tag;
-            }
-          if (!retry_tagged(ctl, good, &spins)) break;
-          load_route(r, j0);
+        while (retry_tagged(ctl, p >= n_pairs || (rr.y == tag && rr.w == tag), &spins))
+          rr = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, kSc1);
+        if (p < n_pairs) {
+          s_sel[p] = (int)rr.x;
+          s_gate[p] = __uint_as_float(rr.z);
         }
       }
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-          if (j >= a.k) sel[m][j] = -1, gate[m][j] = 0.f;
+    } else {
+      for (int p = tid; p < n_pairs; p += kThreads) {
+        s_sel[p] = a.topk_idx[p];
+        s_gate[p] = a.topk_gate[p];
+      }
     }
+    __syncthreads();
     if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
     const size_t slots = upart_slots(a, d);
     const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
@@ -489,11 +462,23 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       const int c = c0 + kg * 8;
       const int cc = min(c, a.r - 8);
       for (int jp = 0; jp < a.k; jp += 2) {
+        // the lane's adapters and gates of slots jp, jp + 1 (-1: none)
+        int sa[MT][2];
+        float ga[MT][2];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int t = m * 16 + lr, j = jp + q;
+            const bool v = j < a.k && t < a.T;
+            sa[m][q] = v ? s_sel[t * a.k + j] : -1;
+            ga[m][q] = v ? s_gate[t * a.k + j] : 0.f;
+          }
         f32x4_t uu[MT][2][2];
         if (d.dense) {
           // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
           // at a time (all their loads out before any is checked)
-          constexpr int MU = MT <= 2 ? MT : 2;
+          constexpr int MU = 1;
 #pragma unroll
           for (int m0 = 0; m0 < MT; m0 += MU) {
             u32x4_v w[MU][2][4];
@@ -502,13 +487,10 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
             for (int mm = 0; mm < MU; ++mm)
 #pragma unroll
               for (int q = 0; q < 2; ++q) {
-                offv[mm][q] = u_offset(m0 + mm, jp + q, c);
-                if (kPrefetchU && !FUSED && c0 == 0 && jp == 0) {
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) w[mm][q][i] = upf[kPrefetchU ? m0 + mm : 0][q][i];
-                } else {
-                  load_u4(w[mm][q], offv[mm][q]);
-                }
+                const int e = sa[m0 + mm][q];
+                offv[mm][q] = e >= 0 && c < a.r
+                    ? (uint32_t)((((size_t)e * d.t_pad + (m0 + mm) * 16 + lr) * a.r + c) * 8) : kOob;
+                load_u4(w[mm][q], offv[mm][q]);
               }
             int spins = 0;
             while (true) {
@@ -538,8 +520,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-              const int t = m * 16 + lr, j = min(jp + q, kMaxK - 1);
-              const bool ok = jp + q < a.k && c < a.r && sel[m][j] >= 0;
+              const int t = m * 16 + lr, j = jp + q;
+              const bool ok = c < a.r && sa[m][q] >= 0;
               const uint32_t off = ok ? (uint32_t)((((size_t)t * a.k + j) * a.r + cc) * sizeof(float)) : kOob;
               uu[m][q][0] = ld_coh16(rp, off);
               uu[m][q][1] = ld_coh16(rp, ok ? off + 16 : kOob);
@@ -549,21 +531,15 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
               }
             }
         }
-        // the two slots' adapters (dynamic index into sel, once per pass); a
-        // token that chose one adapter in both slots gets both gated terms in slot 0
-        int sa[MT][2];
+        // a token that chose one adapter in both slots gets both gated terms in slot 0
         bool dup[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) sa[m][q] = jp + q < a.k ? sel[m][min(jp + q, kMaxK - 1)] : -1;
-          dup[m] = sa[m][0] >= 0 && sa[m][0] == sa[m][1];
-        }
+        for (int m = 0; m < MT; ++m) dup[m] = sa[m][0] >= 0 && sa[m][0] == sa[m][1];
         // gated operands of the two slots, split once into (hi, lo) bf16 parts
         uint4 uhi[MT][2], ulo[MT][2];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const float g0 = gate[m][min(jp, kMaxK - 1)], g1 = gate[m][min(jp + 1, kMaxK - 1)];
+          const float g0 = ga[m][0], g1 = ga[m][1];
           float v0[8], v1[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -595,14 +571,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           }
           if (!group) continue;
           uint4 bo[G];
-          if (kEarlyRoute && c0 == 0 && e0 == 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) bo[g] = bpf[g];
-          } else {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-              bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
-          }
+          for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             if (!d.dense && !any[g]) continue;
@@ -734,9 +704,9 @@ __device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
 }
 
 template <int MT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_kernel(StepArgs st) {
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<MT, FUSED>()];
-  __shared__ int s_ep, s_loc[2], s_wave_tot[2], s_bad;
+  __shared__ int s_ep, s_loc[2], s_wave_tot[kWV], s_bad;
   int* ctl = st.g[0].counters;
   const int tid = threadIdx.x;
   // the epoch is read once per workgroup; backbone items publish it after
@@ -756,9 +726,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(StepArgs st) {
       }
       int* set = ctl_set(ctl, s_ep);
       if (item < st.n_route) {
-        // router tile: top-k and gates of two tokens (the sums do not depend on the tile size)
+        // two router tiles, one per half of the workgroup: top-k and gates of
+        // kFusedRouteTokens tokens each (the sums do not depend on the tile size)
+        const int half = tid / kRouteThreads;
         const RoutePlan rpl = route_plan(st.pg.E, st.pg.d_in, (int)sizeof(bf16_t));
-        route_tile<bf16_t, kFusedRouteTokens>(st.pg, item * kFusedRouteTokens, rpl, reinterpret_cast<float*>(smem),
+        route_tile<bf16_t, kFusedRouteTokens>(st.pg, (item * 2 + half) * kFusedRouteTokens, rpl,
+                                              reinterpret_cast<float*>(smem) + half * route_lds_floats(st.pg.E, kFusedRouteTokens),
                                               reinterpret_cast<unsigned long long*>(st.route_tagged), launch_tag(s_ep));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -874,7 +847,7 @@ hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
 int decode_mt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 int decode_chunk_k(int T) { (void)T; return kKC; }
 int decode_tile_rows() { return kTileRows; }
-int fused_route_tile_tokens() { return kFusedRouteTokens; }
+int fused_route_tile_tokens() { return 2 * kFusedRouteTokens; }  // tokens per router item
 
 int decode_resident_per_cu(int T, bool fused) {
   switch (decode_mt(T)) {

@@ -9,7 +9,7 @@ namespace rp {
 
 namespace {
 constexpr size_t kCounterBytes = 65536;  // reserved control region at the start of the workspace
-constexpr int kDecodeTileRows = 32;
+constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeMaxT = 64;
 constexpr int kPrefillTileRows = 128;
 constexpr int kF32TileRows = 64;
@@ -17,7 +17,7 @@ constexpr int kDenseMaxE = 32;           // decode shrink covers every token per
 constexpr int kMaxSplits = 8;            // decode split-K
 constexpr int kMaxKParts = 8;            // decode pair-chunk shrink K parts
 constexpr int kShrinkPartBytes = 16384;  // target A bytes per decode pair-chunk shrink unit
-constexpr int kItemsPerCu2 = 3;          // twice the backbone items per CU a decode group aims for
+constexpr int kSplitCols = 4096;         // decode backbone: about this many K columns per item
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -43,8 +43,16 @@ size_t decode_partial_bytes(int n_tiles, int S, int T) {
 
 int a_tiles_per_proj(int E, int r) { return (E * r + kDecodeTileRows - 1) / kDecodeTileRows; }
 
+int decode_tiles(int n_proj, const int* d_out) {
+  int n = 0;
+  for (int i = 0; i < n_proj; ++i) n += (d_out[i] + kDecodeTileRows - 1) / kDecodeTileRows;
+  return n;
+}
+
 // One decode group: tiling, splits, items, and its workspace starting at `off`.
-SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu, size_t off) {
+// `launch_tiles` counts the backbone tiles of every group sharing the launch.
+SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
+                           int launch_tiles, size_t off) {
   SgmmPlan p{};
   p.path = 1;
   p.tile_rows = kDecodeTileRows;
@@ -69,10 +77,11 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
     p.units_per_proj = (E + (T * k + 15) / 16) * p.KP;
     n_shrink = p.units_per_proj * n_proj;
   }
-  // about 1.5 backbone items per CU: enough loads in flight to saturate HBM,
-  // and no more (extra bytes in flight only queue, and every dependent round
-  // trip of the launch then waits behind them)
-  int S = (kItemsPerCu2 * n_cu / 2 + p.n_tiles / 2) / p.n_tiles;
+  // one whole-K item per tile streams best (no partial tiles to hand over);
+  // long K is split to about kSplitCols columns per item so items stay alike,
+  // and a launch with fewer tiles than CUs splits until every CU has an item
+  int S = (d_in + kSplitCols / 2) / kSplitCols;
+  S = std::max(S, (n_cu + launch_tiles - 1) / std::max(1, launch_tiles));
   if (const char* env = std::getenv("RP_DECODE_SPLITS")) {  // tuning override
     const int v = std::atoi(env);
     if (v > 0) S = v;
@@ -93,7 +102,8 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
 SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
                    bool fused_route) {
   (void)fused_route;
-  if (dt == kBF16 && T <= kDecodeMaxT) return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, kCounterBytes);
+  if (dt == kBF16 && T <= kDecodeMaxT)
+    return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, decode_tiles(n_proj, d_out), kCounterBytes);
   SgmmPlan p{};
   p.path = (dt == kF32) ? 0 : 2;
   p.tile_rows = p.path == 0 ? kF32TileRows : kPrefillTileRows;
@@ -114,8 +124,11 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
   sp.n_pre = fused_route ? sp.n_route + 1 : 0;
   size_t off = kCounterBytes;
   int items = sp.n_pre;
+  int launch_tiles = 0;
+  for (int g = 0; g < n_groups; ++g) launch_tiles += decode_tiles(groups[g].n_proj, groups[g].d_out);
   for (int g = 0; g < n_groups; ++g) {
-    sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, off);
+    sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
+                                 off);
     off = sp.gp[g].bytes;
     sp.item_begin[g] = items;
     items += sp.gp[g].n_items;

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
   // holds row 16*(q/64) + (q%64)%16, columns 8*((q%64)/16).
   const bf16_t* gA[2];
   const bf16_t* gB[2];
-  int lrow[2], lk[2], brow[2], bk[2];
-  const int nkb = a.d_in / 32;
+  int lrow[2], lk[2], brow[2], bk[2], tblk[2];
+  const int nkb = a.d_in / 32, n_rb = pd.d_out / 16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = tid + i * 256;
@@ -68,13 +68,14 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
     const int pos = min(i0 + lrow[i], a.T - 1);
     gA[i] = x + (size_t)token_at(a, pos) * a.ld_x;
     if (pd.tiled) {
-      const int blk = min(row0 / 16 + q / 64, pd.d_out / 16 - 1);
+      tblk[i] = min(row0 / 16 + q / 64, n_rb - 1);
       brow[i] = (q / 64) * 16 + (q % 64) % 16;
       bk[i] = ((q % 64) / 16) * 8;
-      gB[i] = W0 + (size_t)blk * nkb * 512 + (q % 64) * 8;
+      gB[i] = W0 + (q % 64) * 8;
     } else {
       brow[i] = lrow[i];
       bk[i] = lk[i];
+      tblk[i] = 0;
       gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in;
     }
   }
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
       const int kc = min(k, a.d_in - 8);
       ra[i] = sel4(ok, ld16(gA[i] + kc));
       if (pd.tiled)
-        rb[i] = ld16(gB[i] + (size_t)min(kt, nkb - 1) * 512);  // d_in % 32 == 0: whole blocks
+        rb[i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt, nkb - 1), n_rb, nkb));  // d_in % 32 == 0: whole blocks
       else
         rb[i] = sel4(k < a.d_in, ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8)));
     }

@@ -34,18 +34,19 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(uint4* dst, const uint4*
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = ld16_stream(src + i);
 }
 
-// One 16-byte output piece per thread: piece o is group o%64 of block o/64,
-// block (rb, cb) = (o/64 / ncb, o/64 % ncb); group g holds row 16*rb + g%16,
-// columns 32*cb + 8*(g/16) .. +7 of the row-major source.
+// One 16-byte piece per thread: piece o is lane o%64 of block o/64, block
+// (rb, cb) = (o/64 / nb, o/64 % nb); lane g holds row 16*rb + g%16, columns
+// 32*cb + 8*(g/16) .. +7 of the row-major source, and the block lands where
+// w0_block_offset puts it.
 __global__ __launch_bounds__(kThreads) void pack_w0_kernel(const uint4* src, uint4* dst, int d_out, int d_in) {
   const size_t n = (size_t)d_out * d_in / 8;
-  const int ncb = d_in / 32;
+  const int nb = d_in / 32, n_rb = d_out / 16;
   for (size_t o = (size_t)blockIdx.x * kThreads + threadIdx.x; o < n; o += (size_t)gridDim.x * kThreads) {
     const size_t blk = o / 64;
     const int g = (int)(o % 64);
-    const size_t rb = blk / ncb, cb = blk % ncb;
-    const size_t row = rb * 16 + (g % 16), col = cb * 32 + (g / 16) * 8;
-    dst[o] = src[(row * d_in + col) / 8];
+    const int rb = (int)(blk / nb), cb = (int)(blk % nb);
+    const size_t row = (size_t)rb * 16 + (g % 16), col = (size_t)cb * 32 + (g / 16) * 8;
+    dst[(w0_block_offset(rb, cb, n_rb, nb) + (size_t)g * 8) / 8] = src[(row * d_in + col) / 8];
   }
 }
 

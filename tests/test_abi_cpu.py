@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 4
+    assert rp.abi_version() == 5
 
 
 def test_missing_library_fails_loudly(monkeypatch):

@@ -206,21 +206,24 @@ def test_golden_end_to_end(name):
         check_y(y, ref, dt, name)
 
 
-def test_pack_w0_layout():
-    """rp_pack_w0 writes the documented block order (checked against a NumPy permutation)."""
-    say("pack_w0")
+@pytest.mark.parametrize("d_out,d_in", [(48, 96), (32, 160), (64, 256)])
+def test_pack_w0_layout(d_out, d_in):
+    """rp_pack_w0 writes the documented block order: chunks of four block columns, each chunk's blocks
+    row block by row block (ragged last chunks included), checked against a NumPy placement."""
+    say("pack_w0", d_out, d_in)
     rng = np.random.default_rng(4)
-    d_out, d_in = 48, 96
     W = datagen.f32_to_bf16_bits(rng.standard_normal((d_out, d_in), dtype=np.float32))
     packed = to_host(rp.pack_w0(to_device(W, "bf16", DEV))).reshape(-1)
     want = np.empty(d_out * d_in, np.uint16)
-    o = 0
-    for rb in range(d_out // 16):
-        for cb in range(d_in // 32):
-            for g in range(64):
-                row, col = rb * 16 + g % 16, cb * 32 + (g // 16) * 8
-                want[o:o + 8] = W[row, col:col + 8]
-                o += 8
+    nb, n_rb = d_in // 32, d_out // 16
+    for rb in range(n_rb):
+        for cb in range(nb):
+            g = cb // 4
+            nbg = min(4, nb - 4 * g)
+            o = (4 * g * n_rb + rb * nbg + cb - 4 * g) * 512
+            for q in range(64):
+                row, col = rb * 16 + q % 16, cb * 32 + (q // 16) * 8
+                want[o + 8 * q:o + 8 * q + 8] = W[row, col:col + 8]
     np.testing.assert_array_equal(packed, want)
 
 
@@ -293,7 +296,9 @@ def test_projection_duplicate_adapters(T, d_in, d_out, E, r, k, dt):
 
 @pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
     (1, 64, [64], 4, 8, 1),
-    (33, 96, [208], 5, 16, 2),          # 208 rows: last 32-row tile half full
+    (33, 96, [208], 5, 16, 2),          # 208 rows: last 64-row tile a quarter full
+    (16, 160, [80], 4, 8, 2),           # a full 128-column chunk and a one-block chunk
+    (32, 1120, [320], 8, 16, 2),        # K split four ways, last chunk of three blocks
     (64, 256, [128, 96], 16, 8, 2),
     (48, 4096, [4096], 8, 16, 2),
     (100, 128, [64, 64, 64], 9, 32, 3),  # tiled order through the prefill path
