@@ -358,8 +358,9 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       a.n_tiles = gp.n_tiles;
       a.S = gp.S;
       rp::GroupPlan& q = st.gp[i];
-      q.item_begin = sp.item_begin[i];
-      q.n_shrink = gp.dense ? gp.n_atiles * gp.SA : gp.units_per_proj * g.n_proj;
+      q.shrink_begin = sp.shrink_begin[i];
+      q.base_begin = sp.base_begin[i];
+      q.n_shrink = gp.n_shrink;
       q.n_items = gp.n_items;
       q.shrink_target = gp.dense ? 0 : q.n_shrink;
       q.units_per_proj = gp.units_per_proj;

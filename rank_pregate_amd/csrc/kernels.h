@@ -95,7 +95,7 @@ struct DecodeArgs {
 // output tile of group g-1 is written.
 constexpr int kMaxGroups = 8;
 struct GroupPlan {
-  int item_begin;  // first item of the group in the launch
+  int shrink_begin, base_begin;  // first shrink item and first backbone item of the group in the launch
   int n_shrink, n_items, shrink_target, units_per_proj, KP, atiles_per_proj, n_atiles, SA;
   int x_acquire, count_done, release;
   int wait_target;  // x_acquire: output tiles of every earlier group of the launch, else 0
@@ -125,6 +125,7 @@ struct SgmmPlan {
   size_t off_partial_a, off_route;
   int n_pre, n_route;  // decode: routing items of a fused launch
   int n_items, grid;   // decode: work items and workgroups (grid <= resident capacity)
+  int n_shrink;        // decode: shrink items among n_items
   size_t off_u, off_partial, off_counters, bytes;
 };
 // fused_route: the launch also runs the router and segmentation (decode path only)
@@ -141,7 +142,7 @@ struct StepGroupDesc {
 struct StepPlan {
   int n_groups;
   SgmmPlan gp[kMaxGroups];  // per group: tiling, splits and its workspace offsets (absolute)
-  int item_begin[kMaxGroups];
+  int shrink_begin[kMaxGroups], base_begin[kMaxGroups];
   int n_route, n_pre, n_items, grid;
   size_t off_route, bytes;
 };

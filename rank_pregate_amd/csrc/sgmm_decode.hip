@@ -607,31 +607,48 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         st_tagged4(pr, (uint32_t)((split * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32), acc[m], tag);
       return;
     }
-    // all S-1 partials are requested in one pass (retried whole while any tag
-    // is stale), then summed in split order
+    // SU splits at a time: all their loads go out before any is checked (a
+    // split past S, and this split itself, read zero from past the buffer);
+    // a batch with a stale tag is read again; the sums run in split order
+    constexpr int SU = MT <= 2 ? 4 : 2;
     f32x4_t tot[MT];
-    int spins = 0;
-    bool good;
-    do {
-      good = true;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) tot[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      constexpr int SU = MT <= 2 ? kMaxSplits : 2;  // splits whose loads go out together
-      for (int s0 = 0; s0 < S; s0 += SU) {
+    for (int m = 0; m < MT; ++m) tot[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += SU) {
+      f32x4_t part[SU][MT];
+      int spins = 0;
+      while (true) {
+        u32x4_v raw[SU][MT][2];
 #pragma unroll
-        for (int i = 0; i < SU; ++i) {
-          const int s = s0 + i;
-          if (s >= S) break;
+        for (int i = 0; i < SU; ++i)
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            f32x4_t part = acc[m];
-            if (s != split)
-              good &= ld_tagged4(pr, (uint32_t)((s * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32), tag, part);
-            tot[m] += part;
+            const int s = s0 + i;
+            const uint32_t off = s < S && s != split ? (uint32_t)((s * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32) : kOob;
+            raw[i][m][0] = __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kSc1);
+            raw[i][m][1] = __builtin_amdgcn_raw_buffer_load_b128(pr, off == kOob ? kOob : off + 16, 0, kSc1);
           }
-        }
+        bool good = true;
+#pragma unroll
+        for (int i = 0; i < SU; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4_v& lo4 = raw[i][m][0];
+            const u32x4_v& hi4 = raw[i][m][1];
+            part[i][m] = f32x4_t{__uint_as_float(lo4.x), __uint_as_float(lo4.z), __uint_as_float(hi4.x), __uint_as_float(hi4.z)};
+            const int s = s0 + i;
+            if (s < S && s != split) good &= lo4.y == tag && lo4.w == tag && hi4.y == tag && hi4.w == tag;
+          }
+        if (!retry_tagged(ctl, good, &spins)) break;
       }
-    } while (retry_tagged(ctl, good, &spins));
+#pragma unroll
+      for (int i = 0; i < SU; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int s = s0 + i;
+          if (s < S) tot[m] += s == split ? acc[m] : part[i][m];
+        }
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = tot[m];
   }
@@ -744,11 +761,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         if (tid == 0) atomicAdd(&set[kSetSegDone], 1);
       }
     } else {
-      int gi = 0;
-      while (gi + 1 < st.n_groups && item >= st.gp[gi + 1].item_begin) ++gi;
+      // the group owning this item: li < n_shrink is shrink item li, else
+      // backbone item li - n_shrink
+      int gi = 0, li = 0;
+      for (int g = 0; g < st.n_groups; ++g) {
+        const GroupPlan& q = st.gp[g];
+        if (item >= q.shrink_begin && item < q.shrink_begin + q.n_shrink) gi = g, li = item - q.shrink_begin;
+        if (item >= q.base_begin && item < q.base_begin + q.n_items - q.n_shrink) gi = g, li = q.n_shrink + item - q.base_begin;
+      }
       const SgmmArgs& a = st.g[gi];
       const DecodeArgs d = group_view(st, gi);
-      const int li = item - st.gp[gi].item_begin;
       if (li < d.n_shrink && d.dense) {
         base_item<MT, false, FUSED, true>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
                                           &arrive_old);

@@ -87,6 +87,7 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
     if (v > 0) S = v;
   }
   p.S = std::max(1, std::min(S, s_max));
+  p.n_shrink = n_shrink;
   p.n_items = n_shrink + p.n_tiles * p.S;
   p.off_u = off;
   off = align256(off + decode_u_bytes(n_proj, T, E, r, k, p.KP, p.dense));
@@ -130,8 +131,24 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
     sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
                                  off);
     off = sp.gp[g].bytes;
-    sp.item_begin[g] = items;
-    items += sp.gp[g].n_items;
+  }
+  // Item order: routing; the shrink items of every group whose input comes
+  // from the call (short, so a CU holding two workgroups pairs a backbone tile
+  // with one of them); then group by group, a dependent group's shrink items
+  // and every group's backbone items.  An item still only waits for items
+  // numbered below it.
+  for (int g = 0; g < n_groups; ++g)
+    if (!groups[g].x_acquire) {
+      sp.shrink_begin[g] = items;
+      items += sp.gp[g].n_shrink;
+    }
+  for (int g = 0; g < n_groups; ++g) {
+    if (groups[g].x_acquire) {
+      sp.shrink_begin[g] = items;
+      items += sp.gp[g].n_shrink;
+    }
+    sp.base_begin[g] = items;
+    items += sp.gp[g].n_items - sp.gp[g].n_shrink;
   }
   sp.off_route = off;
   if (fused_route) off = align256(off + (size_t)T * k * 16);
