@@ -6,8 +6,9 @@ A step is the whole hot path once over one batch (AdaFuse technical summary
 dependency order (q|k|v, then o, and for the MLP workloads gate|up, then down)
 through rp_sgmm_step, which computes the routing inside its first launch.  Weights and inputs are seeded
 synthetic data already resident in HBM; weight copies are rotated so repeated
-steps stream from HBM rather than the on-chip caches.  The step is captured
-in one HIP graph per weight copy and replayed.
+steps stream from HBM rather than the on-chip caches.  A round of steps, one
+on each weight copy in turn, is captured in one HIP graph and replayed (as a
+decode loop captures its steps); single-step graphs make up the rest of K.
 
 Prints one JSON line on stdout; details go to stderr.
 """
@@ -184,23 +185,38 @@ def main():
             def run(i):
                 dw.run(i % copies, fused=fused)
         else:
+            # one graph per weight copy (single steps) and one graph of a round
+            # of steps, one on each copy in turn, as a decode loop captures its
+            # steps; K steps = K // copies rounds + K % copies single steps
             graphs = []
             for c in range(copies):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
                     dw.run(c, fused=fused)
                 graphs.append(g)
+            round_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(round_graph, stream=stream):
+                for c in range(copies):
+                    dw.run(c, fused=fused)
 
             def run(i):
                 graphs[i % copies].replay()
 
-        for i in range(args.warmup):
-            run(i)
+        def run_steps(n):
+            if args.no_graph:
+                for i in range(n):
+                    run(i)
+                return
+            for _ in range(n // copies):
+                round_graph.replay()
+            for i in range(n % copies):
+                run(i)
+
+        run_steps(args.warmup)
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for i in range(args.steps):
-            run(i)
+        run_steps(args.steps)
         ev1.record(stream)
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps

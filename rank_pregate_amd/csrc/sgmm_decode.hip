@@ -375,6 +375,26 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     for (int i = 0; i < 4; ++i)
       w[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off == kOob ? kOob : off + 16 * i, 0, kSc1);
   };
+  // routing of the tile's tokens for the expand: pair p = tid + j * kThreads
+  // as (index, tag, gate bits, tag) when this launch's router tiles wrote it,
+  // else (index, -, gate bits, -) from the inputs
+  constexpr int kRP = (16 * MT * kMaxK + kThreads - 1) / kThreads;
+  const int n_pairs = a.T * a.k;
+  const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)n_pairs * 16));
+  u32x4_v rraw[kRP];
+  auto route_load = [&](int j) {
+    const int p = tid + j * kThreads;
+    if (FUSED) {
+      rraw[j] = __builtin_amdgcn_raw_buffer_load_b128(rt, p < n_pairs ? (uint32_t)(p * 16) : kOob, 0, kSc1);
+    } else {
+      const int q = min(p, n_pairs - 1);
+      rraw[j] = u32x4_v{(uint32_t)a.topk_idx[q], 0u, __float_as_uint(a.topk_gate[q]), 0u};
+    }
+  };
+  auto route_issue = [&]() {
+#pragma unroll
+    for (int j = 0; j < kRP; ++j) route_load(j);
+  };
 
   {
     if (d.prev_target > 0) {
@@ -406,6 +426,9 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         __syncthreads();
       });
     }
+    // the expand's routing is requested now, so it lands while the last
+    // chunks compute
+    if (expand) route_issue();
     // the last 1..kRing chunks, already issued
     static_for<0, kRing>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -429,28 +452,20 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   // slots per pass, scaled by the gate; the operand for adapter e is then
   // picked in registers.  B rows are loaded eight adapters at a time.
   if (expand) {
-    const int n_pairs = a.T * a.k;  // <= 16 * MT * kMaxK: fits the activation buffers
+    // n_pairs <= 16 * MT * kMaxK: the routing fits the activation buffers
     int* s_sel = reinterpret_cast<int*>(xs);
     float* s_gate = reinterpret_cast<float*>(xs) + n_pairs;
-    if (FUSED) {
-      // written by this launch's router tiles as (index, tag, gate, tag), validated by tag
-      const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)n_pairs * 16));
-      for (int p0 = 0; p0 < n_pairs; p0 += kThreads) {
-        const int p = p0 + tid;
-        const uint32_t off = p < n_pairs ? (uint32_t)(p * 16) : kOob;
-        u32x4_v rr = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, kSc1);
+#pragma unroll
+    for (int j = 0; j < kRP; ++j) {
+      const int p = tid + j * kThreads;
+      if (FUSED) {
+        // written by this launch's router tiles, validated by tag
         int spins = 0;
-        while (retry_tagged(ctl, p >= n_pairs || (rr.y == tag && rr.w == tag), &spins))
-          rr = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, kSc1);
-        if (p < n_pairs) {
-          s_sel[p] = (int)rr.x;
-          s_gate[p] = __uint_as_float(rr.z);
-        }
+        while (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tag && rraw[j].w == tag), &spins)) route_load(j);
       }
-    } else {
-      for (int p = tid; p < n_pairs; p += kThreads) {
-        s_sel[p] = a.topk_idx[p];
-        s_gate[p] = a.topk_gate[p];
+      if (p < n_pairs) {
+        s_sel[p] = (int)rraw[j].x;
+        s_gate[p] = __uint_as_float(rraw[j].z);
       }
     }
     __syncthreads();
@@ -458,6 +473,14 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     const size_t slots = upart_slots(a, d);
     const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
     const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
+    // B rows of the first eight adapters for the first pass, requested with
+    // its u (with up to 32 tokens: more token tiles leave no registers for them)
+    constexpr bool kBFirst = MT <= 2;
+    uint4 bfirst[kBFirst ? G : 1];
+    if (kBFirst) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) bfirst[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + min(kg * 8, a.r - 8));
+    }
     for (int c0 = 0; c0 < a.r; c0 += 32) {
       const int c = c0 + kg * 8;
       const int cc = min(c, a.r - 8);
@@ -571,8 +594,13 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           }
           if (!group) continue;
           uint4 bo[G];
+          if (kBFirst && c0 == 0 && e0 == 0) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
+            for (int g = 0; g < G; ++g) bo[g] = bfirst[kBFirst ? g : 0];
+          } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
+          }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             if (!d.dense && !any[g]) continue;
