@@ -46,11 +46,11 @@ constexpr int kTileRows = 16 * kWV;  // output rows per item, 16 per wave
 constexpr int kKC = 128;             // K per chunk
 constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
 constexpr int kRing = 3;             // chunks whose loads are in flight ahead of the math
+constexpr int kUStageBytes = 16384;  // LDS for the u rows of a tile's (token, slot) pairs
 static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
 static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
-constexpr int kMaxSplits = 8;         // K splits of a tile (the launch plan keeps S <= this)
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, CDNA
@@ -103,7 +103,8 @@ __device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins)
 
 template <int MT, bool FUSED>
 constexpr size_t smem_bytes() {
-  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t);             // activation chunks, double-buffered
+  // activation chunks (double-buffered), then the expand's routing and u rows
+  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + kUStageBytes;
   constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
   constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxE * sizeof(float) : 0;  // two router tiles
   constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
@@ -154,9 +155,21 @@ __device__ __forceinline__ void wait_prev_group(int* ctl, int ep, const DecodeAr
   if (d.x_acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Thread 0, once per workgroup: record that this workgroup has read the epoch.
-__device__ __forceinline__ int arrive(int* ctl, int ep) {
-  return atomicAdd(&ctl_set(ctl, ep)[kSetArrive + 32 * (blockIdx.x & 7)], 1);
+// Thread 0, once per workgroup, after reading the epoch: count in per
+// blockIdx % 8 class (no single counter takes every workgroup); the last of a
+// class counts into the launch total, and the last of those (every workgroup
+// has now read the epoch) clears the other control set for the next launch and
+// advances the epoch, early in the launch rather than after its last item.
+__device__ __forceinline__ void arrive(int* ctl, int ep) {
+  int* set = ctl_set(ctl, ep);
+  const int G = gridDim.x, cls = blockIdx.x & 7;
+  const int count_c = (G - 1 - cls) / 8 + 1;
+  if (atomicAdd(&set[kSetArrive + 32 * cls], 1) != count_c - 1) return;
+  const int n_classes = G < 8 ? G : 8;
+  if (atomicAdd(&set[kSetArriveAll], 1) != n_classes - 1) return;
+  int* other = ctl_set(ctl, ep + 1);
+  for (int w = 0; w < kSetWords; w += 32) __hip_atomic_store(&other[w], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&ctl[kCtlEpoch], ep + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // u partials of projection `proj`, part kp: [slots][r] fp32 with
@@ -274,7 +287,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 // flight.
 template <int MT, bool TILED, bool FUSED, bool ATILE>
 __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d, int bi, bf16_t* xs, int* ctl, int* s_ep,
-                          bool first, int ep_in, int* arrive_old) {
+                          bool first, int ep_in) {
   constexpr int G = 8;                          // adapters per batch of B loads
   constexpr uint32_t kOob = 0x80000000u;        // past any buffer: a buffer load returns zero
   constexpr int XB = MT * kKS;                  // 1 KB activation fragment blocks per chunk
@@ -395,6 +408,67 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
     for (int j = 0; j < kRP; ++j) route_load(j);
   };
+  // expand staging, after the activation buffers: adapter and gate of every
+  // (token, slot) pair, then (dense u that fits) the pairs' u rows in fp32
+  int* s_sel = reinterpret_cast<int*>(xs + 2 * XB * 512);
+  float* s_gate = reinterpret_cast<float*>(s_sel + 16 * MT * kMaxK);
+  float* s_u = s_gate + 16 * MT * kMaxK;
+  auto stage_route = [&](uint32_t tg) {
+#pragma unroll
+    for (int j = 0; j < kRP; ++j) {
+      const int p = tid + j * kThreads;
+      if (FUSED) {
+        // written by this launch's router tiles, validated by tag
+        int spins = 0;
+        while (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tg && rraw[j].w == tg), &spins)) route_load(j);
+      }
+      if (p < n_pairs) {
+        s_sel[p] = (int)rraw[j].x;
+        s_gate[p] = __uint_as_float(rraw[j].z);
+      }
+    }
+  };
+  // u rows by pieces of two tagged values: piece q is pair q / (r/2), values
+  // 2 * (q % (r/2)) and the next
+  const int half_r = a.r >> 1;
+  constexpr int kUP = 4;  // pieces per thread: staged when the tile's pieces fit (and their fp32 fit the LDS)
+  static_assert(kUP * kThreads * 8 <= kUStageBytes, "staged u rows overflow their LDS");
+  const bool stage_u = d.dense && n_pairs * half_r <= kUP * kThreads;
+  u32x4_v uraw[kUP];
+  auto u_piece = [&](int q) -> uint32_t {
+    if (q >= n_pairs * half_r) return kOob;
+    const int p = q / half_r, c = 2 * (q % half_r);
+    return (uint32_t)((((size_t)s_sel[p] * d.t_pad + p / a.k) * a.r + c) * 8);
+  };
+  // B rows of the first eight adapters for the expand's first pass, requested
+  // with the u rows (with up to 32 tokens: more token tiles leave no registers)
+  constexpr bool kBFirst = MT <= 2;
+  uint4 bfirst[kBFirst ? G : 1];
+  auto b_issue = [&]() {
+    if (kBFirst) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) bfirst[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + min(kg * 8, a.r - 8));
+    }
+  };
+  auto u_issue = [&]() {
+#pragma unroll
+    for (int i = 0; i < kUP; ++i) uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, u_piece(tid + i * kThreads), 0, kSc1);
+  };
+  auto u_store = [&](uint32_t tg) {
+#pragma unroll
+    for (int i = 0; i < kUP; ++i) {
+      const int q = tid + i * kThreads;
+      const uint32_t off = u_piece(q);
+      int spins = 0;
+      while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins))
+        uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, kSc1);
+      if (off != kOob) {
+        const int p = q / half_r, c = 2 * (q % half_r);
+        s_u[p * a.r + c] = __uint_as_float(uraw[i].x);
+        s_u[p * a.r + c + 1] = __uint_as_float(uraw[i].z);
+      }
+    }
+  };
 
   {
     if (d.prev_target > 0) {
@@ -407,7 +481,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     }
     if (first && tid == 0) {
       *s_ep = ep_in;
-      *arrive_old = arrive(ctl, ep_in);
+      arrive(ctl, ep_in);
     }
     store_x(0, 0, 0);
     __syncthreads();
@@ -426,9 +500,11 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         __syncthreads();
       });
     }
-    // the expand's routing is requested now, so it lands while the last
-    // chunks compute
+    // the expand's routing is requested now and staged after the first of
+    // the last chunks; the u rows and B rows it selects are then requested,
+    // so they land while the last chunks compute
     if (expand) route_issue();
+    const uint32_t tag_r = launch_tag(*s_ep);
     // the last 1..kRing chunks, already issued
     static_for<0, kRing>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -437,7 +513,12 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         __builtin_amdgcn_sched_barrier(0);
         compute(i, c & 1);
         if (c + 1 < nc) store_x((i + 1) % kRing, (c + 1) & 1, c + 1);
+        if (i == 0 && expand) stage_route(tag_r);
         __syncthreads();
+        if (i == 0 && expand) {
+          if (stage_u) u_issue();
+          b_issue();
+        }
       }
     });
   }
@@ -445,42 +526,22 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   int* set = ctl_set(ctl, ep);
   const uint32_t tag = launch_tag(ep);
 
-  // adapter deltas for this wave's 16 rows.  The workgroup first stages the
-  // routing of the tile's tokens (adapter and gate of every (token, slot)
-  // pair) in LDS, where the activation chunks were.  A lane's tokens chose at
-  // most k adapters, so it needs u only for its own (token, slot) pairs, two
-  // slots per pass, scaled by the gate; the operand for adapter e is then
-  // picked in registers.  B rows are loaded eight adapters at a time.
+  // adapter deltas for this wave's 16 rows.  The routing of the tile's
+  // tokens (adapter and gate of every (token, slot) pair) is in LDS, and with
+  // dense u that fits, the pairs' u rows too (staged once per workgroup, not
+  // per wave).  A lane's tokens chose at most k adapters, so it needs u only
+  // for its own (token, slot) pairs, two slots per pass, scaled by the gate;
+  // the operand for adapter e is then picked in registers.  B rows are loaded
+  // eight adapters at a time.
   if (expand) {
-    // n_pairs <= 16 * MT * kMaxK: the routing fits the activation buffers
-    int* s_sel = reinterpret_cast<int*>(xs);
-    float* s_gate = reinterpret_cast<float*>(xs) + n_pairs;
-#pragma unroll
-    for (int j = 0; j < kRP; ++j) {
-      const int p = tid + j * kThreads;
-      if (FUSED) {
-        // written by this launch's router tiles, validated by tag
-        int spins = 0;
-        while (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tag && rraw[j].w == tag), &spins)) route_load(j);
-      }
-      if (p < n_pairs) {
-        s_sel[p] = (int)rraw[j].x;
-        s_gate[p] = __uint_as_float(rraw[j].z);
-      }
+    if (stage_u) {
+      u_store(tag);
+      __syncthreads();
     }
-    __syncthreads();
     if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
     const size_t slots = upart_slots(a, d);
     const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
     const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
-    // B rows of the first eight adapters for the first pass, requested with
-    // its u (with up to 32 tokens: more token tiles leave no registers for them)
-    constexpr bool kBFirst = MT <= 2;
-    uint4 bfirst[kBFirst ? G : 1];
-    if (kBFirst) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) bfirst[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + min(kg * 8, a.r - 8));
-    }
     for (int c0 = 0; c0 < a.r; c0 += 32) {
       const int c = c0 + kg * 8;
       const int cc = min(c, a.r - 8);
@@ -498,7 +559,18 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
             ga[m][q] = v ? s_gate[t * a.k + j] : 0.f;
           }
         f32x4_t uu[MT][2][2];
-        if (d.dense) {
+        if (stage_u) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int p = (m * 16 + lr) * a.k + jp + q;
+              const bool ok = sa[m][q] >= 0 && c < a.r;
+              const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              uu[m][q][0] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]) : z;
+              uu[m][q][1] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]) : z;
+            }
+        } else if (d.dense) {
           // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
           // at a time (all their loads out before any is checked)
           constexpr int MU = 1;
@@ -756,7 +828,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
   const int tid = threadIdx.x;
   // the epoch is read once per workgroup; backbone items publish it after
   // their first loads are in flight, other items right away
-  int ep_in = 0, arrive_old = 0;
+  int ep_in = 0;
   if (tid == 0) ep_in = __hip_atomic_load(&ctl[kCtlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool first = true;
   for (int item = blockIdx.x; item < st.n_items; item += gridDim.x) {
@@ -764,7 +836,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
       if (first) {
         if (tid == 0) {
           s_ep = ep_in;
-          arrive_old = arrive(ctl, ep_in);
+          arrive(ctl, ep_in);
         }
         __syncthreads();
         first = false;
@@ -800,14 +872,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
       const SgmmArgs& a = st.g[gi];
       const DecodeArgs d = group_view(st, gi);
       if (li < d.n_shrink && d.dense) {
-        base_item<MT, false, FUSED, true>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
-                                          &arrive_old);
+        base_item<MT, false, FUSED, true>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         first = false;
       } else if (li < d.n_shrink) {
         if (first) {
           if (tid == 0) {
             s_ep = ep_in;
-            arrive_old = arrive(ctl, ep_in);
+            arrive(ctl, ep_in);
           }
           __syncthreads();
           first = false;
@@ -831,31 +902,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         const int bi = li - d.n_shrink;
         const int bp = proj_of_tile(a, bi / a.S);
         if (RP_PICK(a, bp, tiled))
-          base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
-                                            &arrive_old);
+          base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         else
-          base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in,
-                                             &arrive_old);
+          base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         first = false;
       }
     }
     __syncthreads();  // LDS is reused by the next item
-  }
-  // The last workgroup to have read the epoch clears the other control set
-  // for the next launch and advances the epoch.  Arrivals are counted per
-  // blockIdx % 8 class first, so no single counter takes every workgroup.
-  if (tid == 0) {
-    const int G = gridDim.x, cls = blockIdx.x & 7;
-    const int count_c = (G - 1 - cls) / 8 + 1;
-    if (arrive_old == count_c - 1) {
-      const int n_classes = G < 8 ? G : 8;
-      int* set = ctl_set(ctl, s_ep);
-      if (atomicAdd(&set[kSetArriveAll], 1) == n_classes - 1) {
-        int* other = ctl_set(ctl, s_ep + 1);
-        for (int w = 0; w < kSetWords; w += 32) __hip_atomic_store(&other[w], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctl[kCtlEpoch], s_ep + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
   }
 }
 
