@@ -47,7 +47,11 @@ constexpr int kKC = 128;             // K per chunk
 constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
 constexpr int kRing = 3;             // chunks whose loads are in flight ahead of the math
 constexpr int kUStageBytes = 16384;  // LDS for the u rows of a tile's (token, slot) pairs
+constexpr int kBStageBytes = 16384;  // LDS for the tile's rows of every B_e
 static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
+// the staged expand's token fragments (MT tiles x 4 steps x 64 lanes, hi and
+// lo, 16 bytes each) reuse the activation double buffer (2 x MT x kKS KB)
+static_assert(2 * 4 * 64 * 16 <= 2 * kKS * 1024, "expand fragments must fit the activation buffers");
 static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
@@ -104,7 +108,7 @@ __device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins)
 template <int MT, bool FUSED>
 constexpr size_t smem_bytes() {
   // activation chunks (double-buffered), then the expand's routing and u rows
-  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + kUStageBytes;
+  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + kUStageBytes + kBStageBytes;
   constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
   constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxE * sizeof(float) : 0;  // two router tiles
   constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
@@ -429,7 +433,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     }
   };
   // u rows by pieces of two tagged values: piece q is pair q / (r/2), values
-  // 2 * (q % (r/2)) and the next
+  // 2 * (q % (r/2)) and the next; staged already scaled by the pair's gate
   const int half_r = a.r >> 1;
   constexpr int kUP = 4;  // pieces per thread: staged when the tile's pieces fit (and their fp32 fit the LDS)
   static_assert(kUP * kThreads * 8 <= kUStageBytes, "staged u rows overflow their LDS");
@@ -440,14 +444,29 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     const int p = q / half_r, c = 2 * (q % half_r);
     return (uint32_t)((((size_t)s_sel[p] * d.t_pad + p / a.k) * a.r + c) * 8);
   };
-  // B rows of the first eight adapters for the expand's first pass, requested
-  // with the u rows (with up to 32 tokens: more token tiles leave no registers)
-  constexpr bool kBFirst = MT <= 2;
-  uint4 bfirst[kBFirst ? G : 1];
+  // the tile's rows of every B_e (dense, when they fit): [e][64 rows][r] bf16,
+  // requested with the u rows by 16-byte pieces, piece q = e's run of 64*r
+  // elements at 8*(q % (8*r)), e = q / (8*r)
+  bf16_t* s_b = reinterpret_cast<bf16_t*>(s_u + kUStageBytes / 4);
+  const int tile_row0 = row0 - wave * 16;
+  const bool stage_b = d.dense && a.E * kTileRows * a.r * 2 <= kBStageBytes;
+  constexpr int kBP = kBStageBytes / 16 / kThreads;
+  uint4 braw[kBP];
+  auto b_src = [&](int q) -> const bf16_t* {
+    const int per_e = kTileRows * a.r / 8;
+    const int e = q / per_e, o = (q % per_e) * 8;
+    const int lrow = o / a.r, c = o % a.r;
+    return Bm + ((size_t)min(e, a.E - 1) * pd.d_out + min(tile_row0 + lrow, pd.d_out - 1)) * a.r + c;
+  };
   auto b_issue = [&]() {
-    if (kBFirst) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) bfirst[g] = ld16(Bm + ((size_t)min(g, a.E - 1) * pd.d_out + row) * a.r + min(kg * 8, a.r - 8));
+    for (int i = 0; i < kBP; ++i) braw[i] = ld16(b_src(min(tid + i * kThreads, a.E * kTileRows * a.r / 8 - 1)));
+  };
+  auto b_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < kBP; ++i) {
+      const int q = tid + i * kThreads;
+      if (q < a.E * kTileRows * a.r / 8) *reinterpret_cast<uint4*>(&s_b[q * 8]) = braw[i];
     }
   };
   auto u_issue = [&]() {
@@ -463,9 +482,11 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins))
         uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, kSc1);
       if (off != kOob) {
+        // scaled by the pair's gate here, once
         const int p = q / half_r, c = 2 * (q % half_r);
-        s_u[p * a.r + c] = __uint_as_float(uraw[i].x);
-        s_u[p * a.r + c + 1] = __uint_as_float(uraw[i].z);
+        const float g = s_gate[p];
+        s_u[p * a.r + c] = g * __uint_as_float(uraw[i].x);
+        s_u[p * a.r + c + 1] = g * __uint_as_float(uraw[i].z);
       }
     }
   };
@@ -517,7 +538,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         __syncthreads();
         if (i == 0 && expand) {
           if (stage_u) u_issue();
-          b_issue();
+          if (stage_b) b_issue();
         }
       }
     });
@@ -534,159 +555,214 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   // the operand for adapter e is then picked in registers.  B rows are loaded
   // eight adapters at a time.
   if (expand) {
-    if (stage_u) {
-      u_store(tag);
+    if (stage_u || stage_b) {
+      if (stage_u) u_store(tag);
+      if (stage_b) b_store();
       __syncthreads();
     }
-    if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
-    const size_t slots = upart_slots(a, d);
-    const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
-    const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
-    for (int c0 = 0; c0 < a.r; c0 += 32) {
-      const int c = c0 + kg * 8;
-      const int cc = min(c, a.r - 8);
-      for (int jp = 0; jp < a.k; jp += 2) {
-        // the lane's adapters and gates of slots jp, jp + 1 (-1: none)
-        int sa[MT][2];
-        float ga[MT][2];
+    if (stage_u && stage_b) {
+      // The E rank-r blocks side by side along K (E*r <= 128 here), 32
+      // columns per MFMA step.  The token operand does not depend on the
+      // wave, so the workgroup builds it once: for token tile m, step st and
+      // lane position (row lr, group kg) -- adapter e = (32 st + 8 kg) / r,
+      // rank columns c .. c+7 -- the gated u of the token's slots that chose
+      // e, summed in slot order and split into bf16 (hi, lo), stored in MFMA
+      // fragment order where the activation chunks were.  Each wave then adds
+      // two MFMAs per step against its rows of B_e.
+      const int kcat = a.E * a.r;
+      const int nst = (kcat + 31) >> 5;
+      const int lg_r = __builtin_ctz(a.r);  // r is a power of two
+      uint4* fhi = reinterpret_cast<uint4*>(xs);
+      uint4* flo = fhi + MT * 4 * 64;
+      for (int q = tid; q < MT * nst * 64; q += kThreads) {
+        const int ln = q & 63, ms = q >> 6, m = ms / nst, st = ms % nst;
+        const int t = m * 16 + (ln & 15), kcol = st * 32 + (ln >> 4) * 8;
+        float v[8];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        if (t < a.T && kcol < kcat) {
+          const int e = kcol >> lg_r, c = kcol & (a.r - 1);
+          for (int j = 0; j < a.k; ++j) {
+            const int p = t * a.k + j;
+            if (s_sel[p] == e) {
+              const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]);
+              const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]);
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int t = m * 16 + lr, j = jp + q;
-            const bool v = j < a.k && t < a.T;
-            sa[m][q] = v ? s_sel[t * a.k + j] : -1;
-            ga[m][q] = v ? s_gate[t * a.k + j] : 0.f;
-          }
-        f32x4_t uu[MT][2][2];
-        if (stage_u) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int p = (m * 16 + lr) * a.k + jp + q;
-              const bool ok = sa[m][q] >= 0 && c < a.r;
-              const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-              uu[m][q][0] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]) : z;
-              uu[m][q][1] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]) : z;
-            }
-        } else if (d.dense) {
-          // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
-          // at a time (all their loads out before any is checked)
-          constexpr int MU = 1;
-#pragma unroll
-          for (int m0 = 0; m0 < MT; m0 += MU) {
-            u32x4_v w[MU][2][4];
-            uint32_t offv[MU][2];
-#pragma unroll
-            for (int mm = 0; mm < MU; ++mm)
-#pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                const int e = sa[m0 + mm][q];
-                offv[mm][q] = e >= 0 && c < a.r
-                    ? (uint32_t)((((size_t)e * d.t_pad + (m0 + mm) * 16 + lr) * a.r + c) * 8) : kOob;
-                load_u4(w[mm][q], offv[mm][q]);
-              }
-            int spins = 0;
-            while (true) {
-              bool good = true;
-#pragma unroll
-              for (int mm = 0; mm < MU; ++mm)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                  for (int i = 0; i < 2; ++i) {
-                    const u32x4_v& lo4 = w[mm][q][2 * i];
-                    const u32x4_v& hi4 = w[mm][q][2 * i + 1];
-                    uu[m0 + mm][q][i] = f32x4_t{__uint_as_float(lo4.x), __uint_as_float(lo4.z), __uint_as_float(hi4.x),
-                                                __uint_as_float(hi4.z)};
-                    if (offv[mm][q] != kOob) good &= lo4.y == tag && lo4.w == tag && hi4.y == tag && hi4.w == tag;
-                  }
-              if (!retry_tagged(ctl, good, &spins)) break;
-#pragma unroll
-              for (int mm = 0; mm < MU; ++mm)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) load_u4(w[mm][q], offv[mm][q]);
+              for (int i = 0; i < 4; ++i) v[i] += u0[i], v[4 + i] += u1[i];
             }
           }
-        } else {
-          const uint32_t part = (uint32_t)(slots * a.r * sizeof(float));
+        }
+        uint4 hi, lo;
+        split_hi_lo(v, hi, lo);
+        fhi[(m * 4 + st) * 64 + ln] = hi;
+        flo[(m * 4 + st) * 64 + ln] = lo;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {  // at most four steps
+        if (st >= nst) break;
+        const int kcol = st * 32 + kg * 8;
+        const bool colok = kcol < kcat;
+        const int e = colok ? kcol >> lg_r : 0, c = colok ? kcol & (a.r - 1) : 0;
+        const uint4 b = sel4(colok, *reinterpret_cast<const uint4*>(&s_b[((e * kTileRows + wave * 16 + lr) << lg_r) + c]));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          acc[m] = mfma16(fhi[(m * 4 + st) * 64 + lane], b, acc[m]);
+          acc[m] = mfma16(flo[(m * 4 + st) * 64 + lane], b, acc[m]);
+        }
+      }
+    } else {
+      if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
+      const size_t slots = upart_slots(a, d);
+      const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
+      const __amdgpu_buffer_rsrc_t rp = rsrc(reinterpret_cast<const char*>(a.u) + proj * pbytes, (uint32_t)pbytes);
+      for (int c0 = 0; c0 < a.r; c0 += 32) {
+        const int c = c0 + kg * 8;
+        const int cc = min(c, a.r - 8);
+        for (int jp = 0; jp < a.k; jp += 2) {
+          // the lane's adapters and gates of slots jp, jp + 1 (-1: none)
+          int sa[MT][2];
+          float ga[MT][2];
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int t = m * 16 + lr, j = jp + q;
-              const bool ok = c < a.r && sa[m][q] >= 0;
-              const uint32_t off = ok ? (uint32_t)((((size_t)t * a.k + j) * a.r + cc) * sizeof(float)) : kOob;
-              uu[m][q][0] = ld_coh16(rp, off);
-              uu[m][q][1] = ld_coh16(rp, ok ? off + 16 : kOob);
-              for (int kp = 1; kp < d.KP; ++kp) {
-                uu[m][q][0] += ld_coh16(rp, ok ? off + kp * part : kOob);
-                uu[m][q][1] += ld_coh16(rp, ok ? off + kp * part + 16 : kOob);
+              const bool v = j < a.k && t < a.T;
+              sa[m][q] = v ? s_sel[t * a.k + j] : -1;
+              ga[m][q] = v ? s_gate[t * a.k + j] : 0.f;
+            }
+          f32x4_t uu[MT][2][2];
+          if (stage_u) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const int p = (m * 16 + lr) * a.k + jp + q;
+                const bool ok = sa[m][q] >= 0 && c < a.r;
+                const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                uu[m][q][0] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]) : z;
+                uu[m][q][1] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]) : z;
+              }
+          } else if (d.dense) {
+            // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
+            // at a time (all their loads out before any is checked)
+            constexpr int MU = 1;
+#pragma unroll
+            for (int m0 = 0; m0 < MT; m0 += MU) {
+              u32x4_v w[MU][2][4];
+              uint32_t offv[MU][2];
+#pragma unroll
+              for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  const int e = sa[m0 + mm][q];
+                  offv[mm][q] = e >= 0 && c < a.r
+                      ? (uint32_t)((((size_t)e * d.t_pad + (m0 + mm) * 16 + lr) * a.r + c) * 8) : kOob;
+                  load_u4(w[mm][q], offv[mm][q]);
+                }
+              int spins = 0;
+              while (true) {
+                bool good = true;
+#pragma unroll
+                for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+                  for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                      const u32x4_v& lo4 = w[mm][q][2 * i];
+                      const u32x4_v& hi4 = w[mm][q][2 * i + 1];
+                      uu[m0 + mm][q][i] = f32x4_t{__uint_as_float(lo4.x), __uint_as_float(lo4.z), __uint_as_float(hi4.x),
+                                                  __uint_as_float(hi4.z)};
+                      if (offv[mm][q] != kOob) good &= lo4.y == tag && lo4.w == tag && hi4.y == tag && hi4.w == tag;
+                    }
+                if (!retry_tagged(ctl, good, &spins)) break;
+#pragma unroll
+                for (int mm = 0; mm < MU; ++mm)
+#pragma unroll
+                  for (int q = 0; q < 2; ++q) load_u4(w[mm][q], offv[mm][q]);
               }
             }
-        }
-        // a token that chose one adapter in both slots gets both gated terms in slot 0
-        bool dup[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) dup[m] = sa[m][0] >= 0 && sa[m][0] == sa[m][1];
-        // gated operands of the two slots, split once into (hi, lo) bf16 parts
-        uint4 uhi[MT][2], ulo[MT][2];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const float g0 = ga[m][0], g1 = ga[m][1];
-          float v0[8], v1[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v0[i] = g0 * uu[m][0][0][i];
-            v0[4 + i] = g0 * uu[m][0][1][i];
-            v1[i] = g1 * uu[m][1][0][i];
-            v1[4 + i] = g1 * uu[m][1][1][i];
-          }
-          if (dup[m]) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v0[i] += v1[i], v1[i] = 0.f;
-            sa[m][1] = -1;
-          }
-          split_hi_lo(v0, uhi[m][0], ulo[m][0]);
-          split_hi_lo(v1, uhi[m][1], ulo[m][1]);
-        }
-        for (int e0 = 0; e0 < a.E; e0 += G) {
-          // skip a batch no token of the tile chose; with many adapters, skip
-          // single adapters too (with few, all of them are applied branch-free)
-          bool any[G];
-          bool group = false;
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            bool mine = false;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) mine |= sa[m][0] == e0 + g || sa[m][1] == e0 + g;
-            any[g] = __ballot(mine) != 0;
-            group |= any[g];
-          }
-          if (!group) continue;
-          uint4 bo[G];
-          if (kBFirst && c0 == 0 && e0 == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) bo[g] = bfirst[kBFirst ? g : 0];
           } else {
+            const uint32_t part = (uint32_t)(slots * a.r * sizeof(float));
 #pragma unroll
-            for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const int t = m * 16 + lr, j = jp + q;
+                const bool ok = c < a.r && sa[m][q] >= 0;
+                const uint32_t off = ok ? (uint32_t)((((size_t)t * a.k + j) * a.r + cc) * sizeof(float)) : kOob;
+                uu[m][q][0] = ld_coh16(rp, off);
+                uu[m][q][1] = ld_coh16(rp, ok ? off + 16 : kOob);
+                for (int kp = 1; kp < d.KP; ++kp) {
+                  uu[m][q][0] += ld_coh16(rp, ok ? off + kp * part : kOob);
+                  uu[m][q][1] += ld_coh16(rp, ok ? off + kp * part + 16 : kOob);
+                }
+              }
           }
+          // a token that chose one adapter in both slots gets both gated terms in slot 0
+          bool dup[MT];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            if (!d.dense && !any[g]) continue;
-            const uint4 b = sel4(c < a.r && e0 + g < a.E, bo[g]);
+          for (int m = 0; m < MT; ++m) dup[m] = sa[m][0] >= 0 && sa[m][0] == sa[m][1];
+          // gated operands of the two slots, split once into (hi, lo) bf16 parts
+          uint4 uhi[MT][2], ulo[MT][2];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              // operand of the slot that chose e0 + g (zero if none), by masks
-              const uint32_t k0 = sa[m][0] == e0 + g ? ~0u : 0u, k1 = sa[m][1] == e0 + g ? ~0u : 0u;
-              const uint4 hi = make_uint4((uhi[m][0].x & k0) | (uhi[m][1].x & k1), (uhi[m][0].y & k0) | (uhi[m][1].y & k1),
-                                          (uhi[m][0].z & k0) | (uhi[m][1].z & k1), (uhi[m][0].w & k0) | (uhi[m][1].w & k1));
-              const uint4 lo = make_uint4((ulo[m][0].x & k0) | (ulo[m][1].x & k1), (ulo[m][0].y & k0) | (ulo[m][1].y & k1),
-                                          (ulo[m][0].z & k0) | (ulo[m][1].z & k1), (ulo[m][0].w & k0) | (ulo[m][1].w & k1));
-              acc[m] = mfma16(hi, b, acc[m]);
-              acc[m] = mfma16(lo, b, acc[m]);
+          for (int m = 0; m < MT; ++m) {
+            const float g0 = stage_u ? 1.f : ga[m][0], g1 = stage_u ? 1.f : ga[m][1];  // staged u is gated
+            float v0[8], v1[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v0[i] = g0 * uu[m][0][0][i];
+              v0[4 + i] = g0 * uu[m][0][1][i];
+              v1[i] = g1 * uu[m][1][0][i];
+              v1[4 + i] = g1 * uu[m][1][1][i];
+            }
+            if (dup[m]) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) v0[i] += v1[i], v1[i] = 0.f;
+              sa[m][1] = -1;
+            }
+            split_hi_lo(v0, uhi[m][0], ulo[m][0]);
+            split_hi_lo(v1, uhi[m][1], ulo[m][1]);
+          }
+          for (int e0 = 0; e0 < a.E; e0 += G) {
+            // skip a batch no token of the tile chose; with many adapters, skip
+            // single adapters too (with few, all of them are applied branch-free)
+            bool any[G];
+            bool group = false;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              bool mine = false;
+#pragma unroll
+              for (int m = 0; m < MT; ++m) mine |= sa[m][0] == e0 + g || sa[m][1] == e0 + g;
+              any[g] = __ballot(mine) != 0;
+              group |= any[g];
+            }
+            if (!group) continue;
+            uint4 bo[G];
+            if (stage_b) {
+#pragma unroll
+              for (int g = 0; g < G; ++g)
+                bo[g] = *reinterpret_cast<const uint4*>(&s_b[((min(e0 + g, a.E - 1) * kTileRows + wave * 16 + lr) * a.r + cc)]);
+            } else {
+#pragma unroll
+              for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              if (!d.dense && !any[g]) continue;
+              const uint4 b = sel4(c < a.r && e0 + g < a.E, bo[g]);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                // operand of the slot that chose e0 + g (zero if none), by masks
+                const uint32_t k0 = sa[m][0] == e0 + g ? ~0u : 0u, k1 = sa[m][1] == e0 + g ? ~0u : 0u;
+                const uint4 hi = make_uint4((uhi[m][0].x & k0) | (uhi[m][1].x & k1), (uhi[m][0].y & k0) | (uhi[m][1].y & k1),
+                                            (uhi[m][0].z & k0) | (uhi[m][1].z & k1), (uhi[m][0].w & k0) | (uhi[m][1].w & k1));
+                const uint4 lo = make_uint4((ulo[m][0].x & k0) | (ulo[m][1].x & k1), (ulo[m][0].y & k0) | (ulo[m][1].y & k1),
+                                            (ulo[m][0].z & k0) | (ulo[m][1].z & k1), (ulo[m][0].w & k0) | (ulo[m][1].w & k1));
+                acc[m] = mfma16(hi, b, acc[m]);
+                acc[m] = mfma16(lo, b, acc[m]);
+              }
             }
           }
         }
