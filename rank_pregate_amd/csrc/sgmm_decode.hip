@@ -45,13 +45,13 @@ constexpr int kThreads = 64 * kWV;
 constexpr int kTileRows = 16 * kWV;  // output rows per item, 16 per wave
 constexpr int kKC = 128;             // K per chunk
 constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
-constexpr int kRing = 3;             // chunks whose loads are in flight ahead of the math
-constexpr int kUStageBytes = 16384;  // LDS for the u rows of a tile's (token, slot) pairs
-constexpr int kBStageBytes = 16384;  // LDS for the tile's rows of every B_e
+// Chunks whose loads are in flight ahead of the math.  A load returns about
+// that many chunk times after issue (returns are in order behind the stream),
+// so the ring is no deeper than the bandwidth needs: with 64 tokens the
+// activation bytes equal the weight bytes and two chunks suffice.
+template <int MT>
+constexpr int kRingOf = MT >= 4 ? 2 : 3;
 static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
-// the staged expand's token fragments (MT tiles x 4 steps x 64 lanes, hi and
-// lo, 16 bytes each) reuse the activation double buffer (2 x MT x kKS KB)
-static_assert(2 * 4 * 64 * 16 <= 2 * kKS * 1024, "expand fragments must fit the activation buffers");
 static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
@@ -107,8 +107,8 @@ __device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins)
 
 template <int MT, bool FUSED>
 constexpr size_t smem_bytes() {
-  // activation chunks (double-buffered), then the expand's routing and u rows
-  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + kUStageBytes + kBStageBytes;
+  // activation chunks (double-buffered), the expand's routing, its token operand (hi, lo)
+  constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + MT * 4 * 64 * 16 * 2;
   constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
   constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxE * sizeof(float) : 0;  // two router tiles
   constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
@@ -278,23 +278,24 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 // rows are those of the stacked adapter down-projections [A_0; ..; A_{E-1}]
 // of one projection and the result is the rank-r intermediate u[e][t] (fp32,
 // every token) instead of y.  The last of a tile's S splits applies the
-// adapter deltas and sums the other splits' partial tiles; the operands of its
-// first expand pass are requested before its final chunks, so they arrive
-// while those compute.
+// adapter deltas and sums the other splits' partial tiles.
 //
 // The stream: K goes in chunks of 128 columns.  For every chunk each thread
 // issues its activation pieces first, then its wave's four 1 KB weight blocks,
-// kRing chunks ahead of the math, into register rings; the activations of the
+// NR chunks ahead of the math, into register rings; the activations of the
 // next chunk move to an LDS double buffer (in MFMA fragment order) one chunk
 // before use.  Loads retire in issue order, so waiting for a chunk's
-// activations leaves the weight loads of the kRing chunks issued after them in
-// flight.
+// activations leaves the weight loads of the NR chunks issued after them in
+// flight.  The expand's operands (routing, u, B) are requested inside the last
+// two rings at fixed positions, each before the weights it must not wait for,
+// so only the expand's MFMAs and the stores follow the last chunk.
 template <int MT, bool TILED, bool FUSED, bool ATILE>
 __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d, int bi, bf16_t* xs, int* ctl, int* s_ep,
                           bool first, int ep_in) {
   constexpr int G = 8;                          // adapters per batch of B loads
   constexpr uint32_t kOob = 0x80000000u;        // past any buffer: a buffer load returns zero
   constexpr int XB = MT * kKS;                  // 1 KB activation fragment blocks per chunk
+  constexpr int NR = kRingOf<MT>;               // chunks in flight ahead of the math
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = ATILE ? d.SA : a.S;
   const int tile = bi / S, split = bi % S;
@@ -326,50 +327,46 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   f32x4_t acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 wr[kRing][kKS];
-  uint4 xr[kRing][MT];
+  uint4 wr[NR][kKS];
+  uint4 xr[NR][MT];
 
-  // Loads are never masked (a select would force a wait right after them).
-  // Chunks past this split's last re-read activations (cache-resident) and
-  // put an activation address in the weight loads; weight blocks past d_in are
-  // clamped to a real block and meet activations that store_x wrote as zero.
-  auto issue = [&](int slot, int c) {
-    const bool real = c < nc;
-    const int cc = cbeg + min(c, nc - 1);
-    const int col = min(cc * kKC + xcol, a.d_in - 8);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xr[slot][m] = ld16(xq[m] + col);
+  // The split's nc chunks are preceded by `pad` empty ones so that their count
+  // V is a multiple of NR: chunk v then always sits in ring slot v % NR
+  // and the last chunks at fixed positions of the code.  An empty chunk loads
+  // activation bytes (cache-resident) in place of weights and stages zero
+  // activations.  Loads are never masked (a select would force a wait right
+  // after them); weight blocks past d_in are clamped to a real block and meet
+  // activations that store_x wrote as zero.
+  const int pad = (NR - nc % NR) % NR;
+  const int V = nc + pad;
+  auto issue_w = [&](int slot, int v) {
+    const int c = v - pad;
+    const int cc = cbeg + max(c, 0);
+    const bf16_t* xa = xq[0] + min(cc * kKC + xcol, a.d_in - 8);
     if (TILED) {
       const int nbg = min(4, nb - 4 * cc);
       const bf16_t* blk = w0 + ((size_t)cc * 4 * n_rb + (size_t)rblk * nbg) * 512 + lane * 8;
 #pragma unroll
-      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(real ? blk + (size_t)min(s, nbg - 1) * 512 : xq[0] + col);
+      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(c >= 0 ? blk + (size_t)min(s, nbg - 1) * 512 : xa);
     } else {
 #pragma unroll
       for (int s = 0; s < kKS; ++s)
-        wr[slot][s] = ld16_stream(real ? wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8) : xq[0] + col);
+        wr[slot][s] = ld16_stream(c >= 0 ? wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8) : xa);
     }
   };
-  auto issue_w = [&](int slot, int c) {  // weights alone (first chunks, before a group wait)
-    const int cc = cbeg + min(c, nc - 1);
-    if (TILED) {
-      const int nbg = min(4, nb - 4 * cc);
-      const bf16_t* blk = w0 + ((size_t)cc * 4 * n_rb + (size_t)rblk * nbg) * 512 + lane * 8;
-#pragma unroll
-      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(blk + (size_t)min(s, nbg - 1) * 512);
-    } else {
-#pragma unroll
-      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8));
-    }
-  };
-  auto issue_x = [&](int slot, int c) {
-    const int col = min((cbeg + min(c, nc - 1)) * kKC + xcol, a.d_in - 8);
+  auto issue_x = [&](int slot, int v) {
+    const int col = min((cbeg + max(v - pad, 0)) * kKC + xcol, a.d_in - 8);
 #pragma unroll
     for (int m = 0; m < MT; ++m) xr[slot][m] = ld16(xq[m] + col);
   };
+  auto issue = [&](int slot, int v) {  // activations first, then weights
+    issue_x(slot, v);
+    issue_w(slot, v);
+  };
   // piece m of thread tid goes to fragment block m*kKS + wave, lane `lane`
-  auto store_x = [&](int slot, int buf, int c) {
-    const bool ok = (cbeg + c) * kKC + xcol < a.d_in;
+  auto store_x = [&](int slot, int buf, int v) {
+    const int c = v - pad;
+    const bool ok = c >= 0 && (cbeg + c) * kKC + xcol < a.d_in;
 #pragma unroll
     for (int m = 0; m < MT; ++m) *reinterpret_cast<uint4*>(&xs[(buf * XB + m * kKS) * 512 + tid * 8]) = sel4(ok, xr[slot][m]);
   };
@@ -412,11 +409,12 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
     for (int j = 0; j < kRP; ++j) route_load(j);
   };
-  // expand staging, after the activation buffers: adapter and gate of every
-  // (token, slot) pair, then (dense u that fits) the pairs' u rows in fp32
+  // LDS after the activation buffers: adapter and gate of every (token, slot)
+  // pair, then the expand's token operand in MFMA fragment order
   int* s_sel = reinterpret_cast<int*>(xs + 2 * XB * 512);
   float* s_gate = reinterpret_cast<float*>(s_sel + 16 * MT * kMaxK);
-  float* s_u = s_gate + 16 * MT * kMaxK;
+  uint4* fhi = reinterpret_cast<uint4*>(s_gate + 16 * MT * kMaxK);
+  uint4* flo = fhi + MT * 4 * 64;
   auto stage_route = [&](uint32_t tg) {
 #pragma unroll
     for (int j = 0; j < kRP; ++j) {
@@ -432,48 +430,45 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       }
     }
   };
-  // u rows by pieces of two tagged values: piece q is pair q / (r/2), values
-  // 2 * (q % (r/2)) and the next; staged already scaled by the pair's gate
+
+  // The expand with every adapter's rank columns side by side along K (dense
+  // u, E*r <= 128, the tile's u pieces fitting kUP per thread): column e*r + c
+  // of the token operand is sum_j [idx(t,j) = e] g(t,j) u_e[t][c], split into
+  // bf16 (hi, lo); each wave adds two MFMAs per 32 columns against its rows of
+  // the B_e placed side by side the same way.  u pieces are scattered straight
+  // into fragment order; B fragments go straight to registers.
+  const int kcat = a.E * a.r;
   const int half_r = a.r >> 1;
-  constexpr int kUP = 4;  // pieces per thread: staged when the tile's pieces fit (and their fp32 fit the LDS)
-  static_assert(kUP * kThreads * 8 <= kUStageBytes, "staged u rows overflow their LDS");
-  const bool stage_u = d.dense && n_pairs * half_r <= kUP * kThreads;
+  const int lg_r = __builtin_ctz(a.r);  // r is a power of two >= 8
+  constexpr int kUP = 4;                // u pieces (two tagged values) per thread
+  const bool px = expand && d.dense && kcat <= 128 && n_pairs * half_r <= kUP * kThreads;
+  // with two rings or more, the expand's operands are requested and placed
+  // while the last chunks stream, so only its MFMAs follow the last chunk
+  const bool early = MT <= 2 && px && V >= 2 * NR;
+  uint4 bfr[4];
+  auto b_issue = [&]() {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kcol = min(st * 32 + kg * 8, kcat - 8);
+      bfr[st] = ld16(Bm + ((size_t)(kcol >> lg_r) * pd.d_out + row) * a.r + (kcol & (a.r - 1)));
+    }
+  };
+  // piece q: pair q / (r/2), values 2 * (q % (r/2)) and the next
   u32x4_v uraw[kUP];
   auto u_piece = [&](int q) -> uint32_t {
     if (q >= n_pairs * half_r) return kOob;
     const int p = q / half_r, c = 2 * (q % half_r);
     return (uint32_t)((((size_t)s_sel[p] * d.t_pad + p / a.k) * a.r + c) * 8);
   };
-  // the tile's rows of every B_e (dense, when they fit): [e][64 rows][r] bf16,
-  // requested with the u rows by 16-byte pieces, piece q = e's run of 64*r
-  // elements at 8*(q % (8*r)), e = q / (8*r)
-  bf16_t* s_b = reinterpret_cast<bf16_t*>(s_u + kUStageBytes / 4);
-  const int tile_row0 = row0 - wave * 16;
-  const bool stage_b = d.dense && a.E * kTileRows * a.r * 2 <= kBStageBytes;
-  constexpr int kBP = kBStageBytes / 16 / kThreads;
-  uint4 braw[kBP];
-  auto b_src = [&](int q) -> const bf16_t* {
-    const int per_e = kTileRows * a.r / 8;
-    const int e = q / per_e, o = (q % per_e) * 8;
-    const int lrow = o / a.r, c = o % a.r;
-    return Bm + ((size_t)min(e, a.E - 1) * pd.d_out + min(tile_row0 + lrow, pd.d_out - 1)) * a.r + c;
-  };
-  auto b_issue = [&]() {
-#pragma unroll
-    for (int i = 0; i < kBP; ++i) braw[i] = ld16(b_src(min(tid + i * kThreads, a.E * kTileRows * a.r / 8 - 1)));
-  };
-  auto b_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < kBP; ++i) {
-      const int q = tid + i * kThreads;
-      if (q < a.E * kTileRows * a.r / 8) *reinterpret_cast<uint4*>(&s_b[q * 8]) = braw[i];
-    }
-  };
   auto u_issue = [&]() {
 #pragma unroll
     for (int i = 0; i < kUP; ++i) uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, u_piece(tid + i * kThreads), 0, kSc1);
   };
-  auto u_store = [&](uint32_t tg) {
+  auto frag_zero = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) fhi[tid + i * kThreads] = zero4();  // fhi and flo, MT * 512 entries
+  };
+  auto u_scatter = [&](uint32_t tg) {
 #pragma unroll
     for (int i = 0; i < kUP; ++i) {
       const int q = tid + i * kThreads;
@@ -482,11 +477,26 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins))
         uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, kSc1);
       if (off != kOob) {
-        // scaled by the pair's gate here, once
         const int p = q / half_r, c = 2 * (q % half_r);
-        const float g = s_gate[p];
-        s_u[p * a.r + c] = g * __uint_as_float(uraw[i].x);
-        s_u[p * a.r + c + 1] = g * __uint_as_float(uraw[i].z);
+        const int t = p / a.k, j = p - t * a.k, e = s_sel[p];
+        // a token naming e in several slots: the first of them carries the
+        // gates of all of them (summed in slot order), the others add nothing
+        float g = 0.f;
+        bool lead = true;
+        for (int jj = 0; jj < a.k; ++jj)
+          if (s_sel[t * a.k + jj] == e) {
+            g += s_gate[t * a.k + jj];
+            lead &= jj >= j;
+          }
+        if (lead && (unsigned)e < (unsigned)a.E) {
+          const float v0 = g * __uint_as_float(uraw[i].x), v1 = g * __uint_as_float(uraw[i].z);
+          const uint32_t h = f32x2_to_bf16x2(v0, v1);
+          const uint32_t l = f32x2_to_bf16x2(v0 - __uint_as_float(h << 16), v1 - __uint_as_float(h & 0xffff0000u));
+          const int kcol = e * a.r + c;
+          const int w = ((((t >> 4) * 4 + (kcol >> 5)) * 64 + (t & 15) + 16 * ((kcol & 31) >> 3)) << 2) + ((kcol & 7) >> 1);
+          reinterpret_cast<uint32_t*>(fhi)[w] = h;
+          reinterpret_cast<uint32_t*>(flo)[w] = l;
+        }
       }
     }
   };
@@ -494,11 +504,11 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   {
     if (d.prev_target > 0) {
       // weights do not depend on the earlier groups: they are in flight during the wait
-      static_for<0, kRing>([&](auto I) { issue_w(decltype(I)::value, decltype(I)::value); });
+      static_for<0, NR>([&](auto I) { issue_w(decltype(I)::value, decltype(I)::value); });
       wait_prev_group(ctl, first ? __builtin_amdgcn_readfirstlane(ep_in) : *s_ep, d);
-      static_for<0, kRing>([&](auto I) { issue_x(decltype(I)::value, decltype(I)::value); });
+      static_for<0, NR>([&](auto I) { issue_x(decltype(I)::value, decltype(I)::value); });
     } else {
-      static_for<0, kRing>([&](auto I) { issue(decltype(I)::value, decltype(I)::value); });
+      static_for<0, NR>([&](auto I) { issue(decltype(I)::value, decltype(I)::value); });
     }
     if (first && tid == 0) {
       *s_ep = ep_in;
@@ -506,112 +516,112 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     }
     store_x(0, 0, 0);
     __syncthreads();
-    // full rings while every chunk has a successor in this split
-    int c0 = 0;
-    for (; c0 + kRing < nc; c0 += kRing) {
-      static_for<0, kRing>([&](auto I) {
+    // full rings while the chunks after them fill the end section (the last
+    // ring, or the last two when the expand's operands are prepared early)
+    const int v_end = V - (early ? 2 : 1) * NR;
+    int v0 = 0;
+    for (; v0 < v_end; v0 += NR) {
+      static_for<0, NR>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        const int c = c0 + i;
+        const int v = v0 + i;
         __builtin_amdgcn_sched_barrier(0);
-        compute(i, c & 1);
+        compute(i, v & 1);
         __builtin_amdgcn_sched_barrier(0);
-        issue(i, c + kRing);
+        issue(i, v + NR);
         __builtin_amdgcn_sched_barrier(0);
-        store_x((i + 1) % kRing, (c + 1) & 1, c + 1);
+        store_x((i + 1) % NR, (v + 1) & 1, v + 1);
         __syncthreads();
       });
     }
-    // the expand's routing is requested now and staged after the first of
-    // the last chunks; the u rows and B rows it selects are then requested,
-    // so they land while the last chunks compute
-    if (expand) route_issue();
     const uint32_t tag_r = launch_tag(*s_ep);
-    // the last 1..kRing chunks, already issued
-    static_for<0, kRing>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int c = c0 + i;
-      if (c < nc) {
+    if (early) {
+      // chunks V-6 .. V-4: the routing is requested before the weights of
+      // chunk V-3 and staged after chunk V-4; the u pieces it selects are
+      // requested before the weights of chunk V-1, so waiting for them never
+      // waits for those weights
+      static_for<0, NR>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int v = v0 + i;
         __builtin_amdgcn_sched_barrier(0);
-        compute(i, c & 1);
-        if (c + 1 < nc) store_x((i + 1) % kRing, (c + 1) & 1, c + 1);
-        if (i == 0 && expand) stage_route(tag_r);
-        __syncthreads();
-        if (i == 0 && expand) {
-          if (stage_u) u_issue();
-          if (stage_b) b_issue();
+        compute(i, v & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 0) route_issue();
+        if (i == NR - 1) {
+          stage_route(tag_r);
+          frag_zero();
+          __syncthreads();
+          u_issue();
         }
-      }
-    });
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i, v + NR);
+        __builtin_amdgcn_sched_barrier(0);
+        store_x((i + 1) % NR, (v + 1) & 1, v + 1);
+        __syncthreads();
+      });
+      v0 += NR;
+      // chunks V-3 .. V-1: B fragments are requested after chunk V-3 (their
+      // registers free by then), the u pieces land in fragment order after
+      // chunk V-2
+      static_for<0, NR>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int v = v0 + i;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, v & 1);
+        if (i == 0) b_issue();
+        if (i == NR - 2) u_scatter(tag_r);
+        if (i + 1 < NR) {
+          store_x(i + 1, (v + 1) & 1, v + 1);
+          __syncthreads();
+        }
+      });
+    } else {
+      // the last ring, already issued; an expand's routing (and B fragments)
+      // are requested now and staged after its first chunk
+      if (expand) route_issue();
+      static_for<0, NR>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int v = v0 + i;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, v & 1);
+        if (i + 1 < NR) store_x(i + 1, (v + 1) & 1, v + 1);
+        if (i == 0 && expand) {
+          stage_route(tag_r);
+          if (px) frag_zero();
+        }
+        if (i + 1 < NR) __syncthreads();
+        if (i == 0 && px) u_issue();
+      });
+    }
   }
   const int ep = *s_ep;
   int* set = ctl_set(ctl, ep);
   const uint32_t tag = launch_tag(ep);
 
-  // adapter deltas for this wave's 16 rows.  The routing of the tile's
-  // tokens (adapter and gate of every (token, slot) pair) is in LDS, and with
-  // dense u that fits, the pairs' u rows too (staged once per workgroup, not
-  // per wave).  A lane's tokens chose at most k adapters, so it needs u only
-  // for its own (token, slot) pairs, two slots per pass, scaled by the gate;
-  // the operand for adapter e is then picked in registers.  B rows are loaded
-  // eight adapters at a time.
-  if (expand) {
-    if (stage_u || stage_b) {
-      if (stage_u) u_store(tag);
-      if (stage_b) b_store();
+  if (px) {
+    if (!early) {
+      b_issue();
+      u_scatter(tag);
       __syncthreads();
     }
-    if (stage_u && stage_b) {
-      // The E rank-r blocks side by side along K (E*r <= 128 here), 32
-      // columns per MFMA step.  The token operand does not depend on the
-      // wave, so the workgroup builds it once: for token tile m, step st and
-      // lane position (row lr, group kg) -- adapter e = (32 st + 8 kg) / r,
-      // rank columns c .. c+7 -- the gated u of the token's slots that chose
-      // e, summed in slot order and split into bf16 (hi, lo), stored in MFMA
-      // fragment order where the activation chunks were.  Each wave then adds
-      // two MFMAs per step against its rows of B_e.
-      const int kcat = a.E * a.r;
-      const int nst = (kcat + 31) >> 5;
-      const int lg_r = __builtin_ctz(a.r);  // r is a power of two
-      uint4* fhi = reinterpret_cast<uint4*>(xs);
-      uint4* flo = fhi + MT * 4 * 64;
-      for (int q = tid; q < MT * nst * 64; q += kThreads) {
-        const int ln = q & 63, ms = q >> 6, m = ms / nst, st = ms % nst;
-        const int t = m * 16 + (ln & 15), kcol = st * 32 + (ln >> 4) * 8;
-        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        if (t < a.T && kcol < kcat) {
-          const int e = kcol >> lg_r, c = kcol & (a.r - 1);
-          for (int j = 0; j < a.k; ++j) {
-            const int p = t * a.k + j;
-            if (s_sel[p] == e) {
-              const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]);
-              const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] += u0[i], v[4 + i] += u1[i];
-            }
-          }
-        }
-        uint4 hi, lo;
-        split_hi_lo(v, hi, lo);
-        fhi[(m * 4 + st) * 64 + ln] = hi;
-        flo[(m * 4 + st) * 64 + ln] = lo;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {  // at most four steps
-        if (st >= nst) break;
-        const int kcol = st * 32 + kg * 8;
-        const bool colok = kcol < kcat;
-        const int e = colok ? kcol >> lg_r : 0, c = colok ? kcol & (a.r - 1) : 0;
-        const uint4 b = sel4(colok, *reinterpret_cast<const uint4*>(&s_b[((e * kTileRows + wave * 16 + lr) << lg_r) + c]));
+    for (int st = 0; st < 4; ++st) {
+      if (st * 32 < kcat) {
+        const uint4 b = sel4(st * 32 + kg * 8 < kcat, bfr[st]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           acc[m] = mfma16(fhi[(m * 4 + st) * 64 + lane], b, acc[m]);
           acc[m] = mfma16(flo[(m * 4 + st) * 64 + lane], b, acc[m]);
         }
       }
-    } else {
+    }
+  } else if (expand) {
+    // adapter deltas for this wave's 16 rows, lane by lane: the routing of
+    // the tile's tokens (adapter and gate of every (token, slot) pair) is in
+    // LDS.  A lane's tokens chose at most k adapters, so it needs u only for
+    // its own (token, slot) pairs, two slots per pass, scaled by the gate;
+    // the operand for adapter e is then picked in registers.  B rows are
+    // loaded eight adapters at a time.
+    {
       if (!d.dense) wait_geq(ctl, &set[kSetShrinkDone + 32 * d.group], d.shrink_target);
       const size_t slots = upart_slots(a, d);
       const size_t pbytes = (size_t)d.KP * slots * a.r * sizeof(float);  // pair-chunk partials (E > 32)
@@ -633,18 +643,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
               ga[m][q] = v ? s_gate[t * a.k + j] : 0.f;
             }
           f32x4_t uu[MT][2][2];
-          if (stage_u) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                const int p = (m * 16 + lr) * a.k + jp + q;
-                const bool ok = sa[m][q] >= 0 && c < a.r;
-                const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                uu[m][q][0] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c]) : z;
-                uu[m][q][1] = ok ? *reinterpret_cast<const f32x4_t*>(&s_u[p * a.r + c + 4]) : z;
-              }
-          } else if (d.dense) {
+          if (d.dense) {
             // tagged pairs [e][t][c] from this launch's A tiles, MU token tiles
             // at a time (all their loads out before any is checked)
             constexpr int MU = 1;
@@ -708,7 +707,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
           uint4 uhi[MT][2], ulo[MT][2];
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const float g0 = stage_u ? 1.f : ga[m][0], g1 = stage_u ? 1.f : ga[m][1];  // staged u is gated
+            const float g0 = ga[m][0], g1 = ga[m][1];
             float v0[8], v1[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -740,14 +739,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
             }
             if (!group) continue;
             uint4 bo[G];
-            if (stage_b) {
 #pragma unroll
-              for (int g = 0; g < G; ++g)
-                bo[g] = *reinterpret_cast<const uint4*>(&s_b[((min(e0 + g, a.E - 1) * kTileRows + wave * 16 + lr) * a.r + cc)]);
-            } else {
-#pragma unroll
-              for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
-            }
+            for (int g = 0; g < G; ++g) bo[g] = ld16(Bm + ((size_t)min(e0 + g, a.E - 1) * pd.d_out + row) * a.r + cc);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
               if (!d.dense && !any[g]) continue;
@@ -846,16 +839,25 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     return;
   }
 
-  // store: lane -> output row row0 + lane%16; accumulator v -> token m*16 + 4*(lane/16) + v
-  if (row0 + lr < pd.d_out) {
-    bf16_t* y = static_cast<bf16_t*>(pd.y);
+  // store through LDS: lane holds output row row0 + lane%16 of tokens
+  // m*16 + 4*(lane/16) + v; the tile goes to the activation buffer the last
+  // chunk did not use (free since the barrier of chunk V-2) as [token][64
+  // rows], then each thread writes 16 bytes (8 rows of one token; d_out and
+  // ld_y are multiples of 8)
+  {
+    bf16_t* ys = xs + (size_t)(V & 1) * XB * 512;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = m * 16 + 4 * kg + v;
-        if (t < a.T) y[(size_t)t * pd.ld_y + row0 + lr] = f32_to_bf16(acc[m][v]);
-      }
+      for (int v = 0; v < 4; ++v) ys[(m * 16 + 4 * kg + v) * kTileRows + wave * 16 + lr] = f32_to_bf16(acc[m][v]);
+    __syncthreads();
+    const int tile_row0 = row0 - wave * 16;
+    bf16_t* y = static_cast<bf16_t*>(pd.y);
+    for (int q = tid; q < a.T * (kTileRows / 8); q += kThreads) {
+      const int t = q / (kTileRows / 8), c8 = (q % (kTileRows / 8)) * 8;
+      if (tile_row0 + c8 < pd.d_out)
+        *reinterpret_cast<uint4*>(y + (size_t)t * pd.ld_y + tile_row0 + c8) = *reinterpret_cast<const uint4*>(&ys[t * kTileRows + c8]);
+    }
   }
   if (d.count_done) {
     // a later group of this launch waits for this tile (and, with release, reads it)
