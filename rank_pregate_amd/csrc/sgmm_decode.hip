@@ -50,7 +50,7 @@ constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
 // so the ring is no deeper than the bandwidth needs: with 64 tokens the
 // activation bytes equal the weight bytes and two chunks suffice.
 template <int MT>
-constexpr int kRingOf = MT >= 4 ? 2 : 3;
+constexpr int kRingOf = MT >= 4 ? 2 : 4;
 static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
 static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
