@@ -253,12 +253,16 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
       }
       need = std::max(need, rp::step_workspace_upper_bound(desc, ng, (int)T, (int)E, (int)r, k));
     }
+  } else if (dt == RP_BF16) {
+    // every group's u side by side (a launch pair runs several groups)
+    need = rp::kWorkspaceCounterBytes;
+    for (int g = 0; g < n_groups; ++g) need += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k);
   } else {
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
       for (int p = 0; p < gs[g].n_proj; ++p) sum += gs[g].projs[p].d_out;
-      need = std::max(need, rp::sgmm_workspace_upper_bound(dt == RP_BF16 ? rp::kBF16 : rp::kF32, gs[g].n_proj,
-                                                           (int)T, (int)gs[g].d_in, sum, (int)E, (int)r, k));
+      need = std::max(need, rp::sgmm_workspace_upper_bound(rp::kF32, gs[g].n_proj, (int)T, (int)gs[g].d_in, sum,
+                                                           (int)E, (int)r, k));
     }
   }
   return need;
@@ -303,6 +307,49 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     hipError_t e = rp::launch_pregate(pg, stream);
     if (e == hipSuccess) e = rp::launch_segment(sg, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  if (!decode && dt == RP_BF16) {
+    // groups batched into launch pairs (shrink, then GEMM); a group that reads
+    // an earlier group's output starts a new batch, so the launch boundary
+    // orders the data
+    for (int g0 = 0; g0 < n_groups;) {
+      int ng = 1;
+      while (g0 + ng < n_groups && ng < rp::kMaxGroups && !gs[g0 + ng].x_from_call) ++ng;
+      rp::PrefillStep ps{};
+      ps.n_groups = ng;
+      ps.n_tok_tiles = (int)((T + 127) / 128);
+      ps.units = rp::prefill_shrink_units((int)T, (int)E, k);
+      size_t off = rp::kWorkspaceCounterBytes;
+      int shrink_blocks = 0, gemm_blocks = 0;
+      for (int i = 0; i < ng; ++i) {
+        const rp_group& g = gs[g0 + i];
+        int d_out[RP_MAX_PROJ];
+        for (int p = 0; p < g.n_proj; ++p) d_out[p] = (int)g.projs[p].d_out;
+        const rp::SgmmPlan plan =
+            rp::plan_sgmm(rdt, g.n_proj, d_out, (int)T, (int)g.d_in, (int)E, (int)r, k, n_cu, false);
+        rp::SgmmArgs& a = ps.g[i];
+        fill_group(&a, g.projs, g.n_proj, g.x, T, g.d_in, g.ld_x, E, r, k, plan.tile_rows);
+        a.topk_idx = rt.idx;
+        a.topk_gate = rt.gate;
+        a.seg_offsets = rt.off;
+        a.pair_perm = rt.perm;
+        a.counters = reinterpret_cast<int*>(w);
+        a.u = reinterpret_cast<float*>(w + off);
+        a.partial = nullptr;
+        a.n_tiles = plan.n_tiles;
+        a.S = 1;
+        off += rp::prefill_u_bytes(g.n_proj, (int)T, (int)r, k);
+        shrink_blocks += ps.units * g.n_proj;
+        gemm_blocks += rp::prefill_group_blocks(plan.n_tiles, (int)T);
+        ps.shrink_end[i] = shrink_blocks;
+        ps.block_end[i] = gemm_blocks;
+      }
+      if (ws_bytes < off) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, off);
+      hipError_t e = rp::launch_prefill_step(ps, stream);
+      if (e != hipSuccess) return hip_fail(fn, e);
+      g0 += ng;
+    }
+    return RP_OK;
   }
   if (!decode) {
     for (int g = 0; g < n_groups; ++g) {

@@ -156,6 +156,22 @@ int fused_route_tile_tokens();                  // tokens per router tile of a f
 bool decode_fused_route_supported(int T);       // routing can run inside a decode launch of T tokens
 
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
+// Several bf16 prefill-shaped groups (T > 64) in one shrink launch and one
+// GEMM launch; group g owns blocks [end[g-1], end[g]) of each.  Groups of one
+// launch pair must not read each other's outputs.
+struct PrefillStep {
+  SgmmArgs g[kMaxGroups];
+  int n_groups;
+  int n_tok_tiles;                 // 128-token tiles
+  int units;                       // shrink units per projection (same for every group)
+  int shrink_end[kMaxGroups];      // cumulative shrink blocks
+  int block_end[kMaxGroups];       // cumulative GEMM blocks (multiples of 8)
+};
+hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s);
+constexpr size_t kWorkspaceCounterBytes = 65536;  // reserved control region at the start of every workspace
+size_t prefill_u_bytes(int n_proj, int T, int r, int k);  // one group's gated u, 256-byte aligned
+int prefill_group_blocks(int n_tiles, int T);  // GEMM blocks of one group
+int prefill_shrink_units(int T, int E, int k);  // shrink units per projection
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
                                   int k);

@@ -8,7 +8,7 @@
 namespace rp {
 
 namespace {
-constexpr size_t kCounterBytes = 65536;  // reserved control region at the start of the workspace
+constexpr size_t kCounterBytes = kWorkspaceCounterBytes;
 constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeMaxT = 64;
 constexpr int kPrefillTileRows = 128;
@@ -183,6 +183,10 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
     return step_workspace_upper_bound(&g, 1, T, E, r, k);
   }
   return align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
+}
+
+size_t prefill_u_bytes(int n_proj, int T, int r, int k) {
+  return align256((size_t)n_proj * T * k * r * sizeof(float));
 }
 
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s) {

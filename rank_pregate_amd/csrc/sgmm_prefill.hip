@@ -11,11 +11,21 @@
 namespace rp {
 namespace {
 
+// Group of block b among cumulative block counts end[0..n).
+__device__ __forceinline__ int group_of_block(const int* end, int n, int b) {
+  int g = 0;
+  while (g + 1 < n && b >= end[g]) ++g;
+  return g;
+}
+
 template <int MTR>
-__global__ __launch_bounds__(256) void shrink_bf16(SgmmArgs a, int units_per_proj) {
+__global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   __shared__ __attribute__((aligned(16))) float red[MTR * 4 * 4 * 64];
   __shared__ int s_loc[2];
-  const int proj = blockIdx.x / units_per_proj, unit = blockIdx.x % units_per_proj;
+  const int g = group_of_block(ps.shrink_end, ps.n_groups, blockIdx.x);
+  const SgmmArgs& a = ps.g[g];
+  const int b = blockIdx.x - (g > 0 ? ps.shrink_end[g - 1] : 0);
+  const int proj = b / ps.units, unit = b % ps.units;
   if (threadIdx.x < 64) {
     int e, c;
     locate_chunk(a, unit, 64, threadIdx.x, &e, &c);
@@ -32,19 +42,39 @@ __global__ __launch_bounds__(256) void shrink_bf16(SgmmArgs a, int units_per_pro
 constexpr int kPB = 128;       // tile edge (tokens and rows)
 constexpr int kPK = 32;        // K per LDS stage
 constexpr int kPLd = kPK + 8;  // padded LDS row (elements)
+constexpr int kPR = 3;         // stages whose loads are in flight ahead of the math
+constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
+constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once
+constexpr int kNoAdapter = 0x7fffffff;
+static_assert(sizeof(PrefillStep) <= 4096, "kernel argument block too large");
 
 __device__ __forceinline__ int token_at(const SgmmArgs& a, int i) {
   // top-1: walk tokens in segment order so a tile meets few adapters
   return (a.k == 1) ? a.pair_perm[i] : i;
 }
 
-__global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kPB][kPLd];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kPB][kPLd];
-  __shared__ uint32_t amask[kMaxEWords];
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Blocks b and b + 8 share an XCD (b % 8).  The n_tok_tiles token tiles of a
+// row tile are blocks q*8 + x for consecutive q, so they run on one XCD at
+// about the same time and all but the first read of the W0 tile hit its L2.
+__global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
+  // operand double buffers, reused for the output tile at the end
+  __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * 2 * kPB * kPLd];
+  auto As = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p);
+  auto Bs = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p + 2 * kPB * kPLd);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tt = blockIdx.x % n_tok_tiles, tile = blockIdx.x / n_tok_tiles;
+  const int grp = group_of_block(ps.block_end, ps.n_groups, blockIdx.x);
+  const SgmmArgs& a = ps.g[grp];
+  const int n_tok_tiles = ps.n_tok_tiles;
+  const int q = (blockIdx.x - (grp > 0 ? ps.block_end[grp - 1] : 0)) >> 3;  // groups start at multiples of 8
+  const int tile = (q / n_tok_tiles) * 8 + (blockIdx.x & 7), tt = q % n_tok_tiles;
+  if (tile >= a.n_tiles) return;
   const int proj = proj_of_tile(a, tile);
   const ProjDesc pd = proj_at(a, proj);
   const int row0 = (tile - pd.tile_begin) * kPB;
@@ -62,16 +92,16 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
   const int nkb = a.d_in / 32, n_rb = pd.d_out / 16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int q = tid + i * 256;
-    lrow[i] = q >> 2;
-    lk[i] = (q & 3) * 8;
+    const int c = tid + i * 256;
+    lrow[i] = c >> 2;
+    lk[i] = (c & 3) * 8;
     const int pos = min(i0 + lrow[i], a.T - 1);
     gA[i] = x + (size_t)token_at(a, pos) * a.ld_x;
     if (pd.tiled) {
-      tblk[i] = min(row0 / 16 + q / 64, n_rb - 1);
-      brow[i] = (q / 64) * 16 + (q % 64) % 16;
-      bk[i] = ((q % 64) / 16) * 8;
-      gB[i] = W0 + (q % 64) * 8;
+      tblk[i] = min(row0 / 16 + c / 64, n_rb - 1);
+      brow[i] = (c / 64) * 16 + (c % 64) % 16;
+      bk[i] = ((c % 64) / 16) * 8;
+      gB[i] = W0 + (c % 64) * 8;
     } else {
       brow[i] = lrow[i];
       bk[i] = lk[i];
@@ -80,25 +110,28 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
     }
   }
   const int nk = (a.d_in + kPK - 1) / kPK;
-  uint4 ra[2], rb[2];
-  auto gload = [&](int kt) {
+  // Stages go global -> registers kPR stages ahead of the math, then to the
+  // LDS double buffer one stage ahead.  Loads are never masked (stages past
+  // the end re-read the last one); columns past d_in are zeroed on the way to
+  // LDS.
+  uint4 ra[kPR][2], rb[kPR][2];
+  auto gload = [&](int slot, int kt) {
+    kt = min(kt, nk - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int k = kt * kPK + lk[i];
-      const bool ok = k < a.d_in;
-      const int kc = min(k, a.d_in - 8);
-      ra[i] = sel4(ok, ld16(gA[i] + kc));
+      ra[slot][i] = ld16(gA[i] + min(kt * kPK + lk[i], a.d_in - 8));
       if (pd.tiled)
-        rb[i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt, nkb - 1), n_rb, nkb));  // d_in % 32 == 0: whole blocks
+        rb[slot][i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt, nkb - 1), n_rb, nkb));  // d_in % 32 == 0: whole blocks
       else
-        rb[i] = sel4(k < a.d_in, ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8)));
+        rb[slot][i] = ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8));
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int slot, int buf, int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = rb[i];
+      const bool ok = kt * kPK + lk[i] < a.d_in;
+      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(ok, ra[slot][i]);
+      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = pd.tiled ? rb[slot][i] : sel4(ok, rb[slot][i]);
     }
   };
 
@@ -111,13 +144,7 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.f;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < kPK; kk += 16) {
       uint4 af[2], bfr[2];
@@ -132,93 +159,193 @@ __global__ __launch_bounds__(256) void prefill_bf16(SgmmArgs a, int n_tok_tiles)
 #pragma unroll
         for (int g = 0; g < 2; ++g) acc[f][g] = mfma32(af[f], bfr[g], acc[f][g]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // expand: the adapters met by this tile's tokens
-  if (a.k > 0) {
-    const int nw = (a.E + 31) >> 5;
-    for (int q = tid; q < nw; q += 256) amask[q] = 0u;
-    __syncthreads();
-    for (int q = tid; q < kPB * a.k; q += 256) {
-      const int pos = i0 + q / a.k;
-      if (pos < a.T) {
-        const int e = a.topk_idx[token_at(a, pos) * a.k + q % a.k];
-        if ((unsigned)e < (unsigned)a.E) atomicOr(&amask[e >> 5], 1u << (e & 31));
-      }
+  static_for<0, kPR>([&](auto I) { gload(decltype(I)::value, decltype(I)::value); });
+  lstore(0, 0, 0);
+  __syncthreads();
+  // full rings while every stage has kPR successors, ring slots by static index
+  int kt0 = 0;
+  for (; kt0 + kPR < nk; kt0 += kPR) {
+    static_for<0, kPR>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int kt = kt0 + i;
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(i, kt + kPR);
+      __builtin_amdgcn_sched_barrier(0);
+      lstore((i + 1) % kPR, (kt + 1) & 1, kt + 1);
+      __syncthreads();
+    });
+  }
+  // the last 1..kPR stages, already issued
+  static_for<0, kPR>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int kt = kt0 + i;
+    if (kt < nk) {
+      compute(kt & 1);
+      if (kt + 1 < nk) lstore((i + 1) % kPR, (kt + 1) & 1, kt + 1);
+      __syncthreads();
     }
-    __syncthreads();
+  });
+
+  // Expand: per 32-token block, the distinct adapters its tokens chose, in
+  // ascending order (found with wave minimums, no memory round trip); a lane
+  // holds its token's gated u for every slot, so an adapter's token operand is
+  // picked in registers (slots naming the same adapter summed in slot order)
+  // and split into bf16 (hi, lo).  B rows go out a batch of kPNB adapters ahead
+  // of the batch whose MFMAs run.
+  if (a.k > 0) {
     const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
     const float* ub = a.u + (size_t)proj * a.T * a.k * a.r;
-    int tok[2];
-    bool tok_ok[2];
+    const int kk = a.k;
+    int brow_g[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) brow_g[g] = min(row0 + wn * 64 + g * 32 + lr, pd.d_out - 1);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int pos = i0 + wm * 64 + f * 32 + lr;
-      tok_ok[f] = pos < a.T;
-      tok[f] = token_at(a, min(pos, a.T - 1));
-    }
-    for (int w = 0; w < nw; ++w) {
-      uint32_t bits = amask[w];
-      while (bits) {
-        const int e = w * 32 + __ffs(bits) - 1;
-        bits &= bits - 1;
+      const bool tok_ok = pos < a.T;
+      const int t = token_at(a, min(pos, a.T - 1));
+      // slots in groups of kPUJ (a token naming one adapter in two groups
+      // gets its two terms from two passes)
+      for (int j0 = 0; j0 < kk; j0 += kPUJ)
+      for (int c0 = 0; c0 < a.r; c0 += 16) {
+        int ej[kPUJ];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const bool mine = tok_ok[f] && chose(a.topk_idx, tok[f], a.k, e);
-          if (__ballot(mine) == 0) continue;
-          for (int c0 = 0; c0 < a.r; c0 += 16) {
-            const int c = c0 + kg * 8;
-            const bool cok = c < a.r;
+        for (int j = 0; j < kPUJ; ++j) {
+          const int e = (j0 + j < kk && tok_ok) ? a.topk_idx[t * kk + j0 + j] : -1;
+          ej[j] = (e >= 0 && e < a.E) ? e : kNoAdapter;
+        }
+        const int c = c0 + kg * 8;
+        const bool cok = c < a.r;
+        const int cc = min(c, a.r - 8);
+        f32x4_t uj[kPUJ][2];
+#pragma unroll
+        for (int j = 0; j < kPUJ; ++j) {
+          const bool ok = ej[j] != kNoAdapter && cok;
+          const float* p = ub + (size_t)(t * kk + min(j0 + j, kk - 1)) * a.r + cc;
+          uj[j][0] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          uj[j][1] = ok ? *reinterpret_cast<const f32x4_t*>(p + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        uint32_t todo = 0;
+#pragma unroll
+        for (int j = 0; j < kPUJ; ++j)
+          if (ej[j] != kNoAdapter) todo |= 1u << j;
+        auto next_e = [&]() -> int {
+          int cand = kNoAdapter;
+#pragma unroll
+          for (int j = 0; j < kPUJ; ++j)
+            if ((todo >> j) & 1u) cand = min(cand, ej[j]);
+          const int e = wave_min_int(cand);
+#pragma unroll
+          for (int j = 0; j < kPUJ; ++j)
+            if (ej[j] == e) todo &= ~(1u << j);
+          return e;
+        };
+        int beA[kPNB], beB[kPNB];
+        uint4 bA[kPNB][2], bB[kPNB][2];
+        auto collect = [&](int (&be)[kPNB], uint4 (&bo)[kPNB][2]) -> bool {
+#pragma unroll
+          for (int i = 0; i < kPNB; ++i) be[i] = next_e();
+#pragma unroll
+          for (int i = 0; i < kPNB; ++i) {
+            const int e = be[i] == kNoAdapter ? 0 : be[i];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) bo[i][g] = ld16(Bm + ((size_t)e * pd.d_out + brow_g[g]) * a.r + cc);
+          }
+          return be[0] != kNoAdapter;
+        };
+        auto apply = [&](const int (&be)[kPNB], const uint4 (&bo)[kPNB][2]) {
+#pragma unroll
+          for (int i = 0; i < kPNB; ++i) {
+            if (be[i] == kNoAdapter) continue;
+            float v[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) v[m] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kPUJ; ++j)
+              if (ej[j] == be[i]) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) v[m] += uj[j][0][m], v[4 + m] += uj[j][1][m];
+              }
             uint4 hi, lo;
-            u_operand(ub, a.topk_idx, a.r, tok[f], a.k, e, min(c, a.r - 8), cok && mine, hi, lo);
+            split_hi_lo(v, hi, lo);
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-              const int row = min(row0 + wn * 64 + g * 32 + lr, pd.d_out - 1);
-              const uint4 bo = sel4(cok, ld16(Bm + ((size_t)e * pd.d_out + row) * a.r + min(c, a.r - 8)));
-              acc[f][g] = mfma32(hi, bo, acc[f][g]);
-              acc[f][g] = mfma32(lo, bo, acc[f][g]);
+              const uint4 b = sel4(cok, bo[i][g]);
+              acc[f][g] = mfma32(hi, b, acc[f][g]);
+              acc[f][g] = mfma32(lo, b, acc[f][g]);
             }
           }
+        };
+        bool haveA = collect(beA, bA);
+        while (haveA) {
+          const bool haveB = collect(beB, bB);
+          apply(beA, bA);
+          if (!haveB) break;
+          haveA = collect(beA, bA);
+          apply(beB, bB);
         }
       }
     }
   }
 
-  bf16_t* y = static_cast<bf16_t*>(pd.y);
+  // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
+  // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
+  bf16_t* ys = smem_p;
+  static_assert(2 * 2 * kPB * kPLd >= kPB * kPB, "output tile must fit the operand buffers");
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int row = row0 + wn * 64 + g * 32 + lr;
-    if (row >= pd.d_out) continue;
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int pos = i0 + wm * 64 + f * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-        if (pos < a.T) y[(size_t)token_at(a, pos) * pd.ld_y + row] = f32_to_bf16(acc[f][g][v]);
-      }
+      for (int v = 0; v < 16; ++v)
+        ys[(wm * 64 + f * 32 + 8 * (v >> 2) + 4 * kg + (v & 3)) * kPB + wn * 64 + g * 32 + lr] = f32_to_bf16(acc[f][g][v]);
+  __syncthreads();
+  bf16_t* y = static_cast<bf16_t*>(pd.y);
+  for (int c = tid; c < kPB * (kPB / 8); c += 256) {
+    const int tl = c / (kPB / 8), r8 = (c % (kPB / 8)) * 8;
+    const int pos = i0 + tl;
+    if (pos < a.T && row0 + r8 < pd.d_out)
+      *reinterpret_cast<uint4*>(y + (size_t)token_at(a, pos) * pd.ld_y + row0 + r8) = *reinterpret_cast<const uint4*>(&ys[tl * kPB + r8]);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s) {
-  if (a.k > 0) {
-    const int units = a.E + (a.T * a.k + 63) / 64;
-    const dim3 g(units * a.n_proj);
-    switch ((a.r + 15) >> 4) {
-      case 1: shrink_bf16<1><<<g, 256, 0, s>>>(a, units); break;
-      case 2: shrink_bf16<2><<<g, 256, 0, s>>>(a, units); break;
-      case 4: shrink_bf16<4><<<g, 256, 0, s>>>(a, units); break;
-      default: shrink_bf16<8><<<g, 256, 0, s>>>(a, units); break;
+int prefill_group_blocks(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB - 1) / kPB); }
+int prefill_shrink_units(int T, int E, int k) { return E + (T * k + 63) / 64; }
+
+hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
+  const SgmmArgs& a0 = ps.g[0];
+  if (a0.T == 0) return hipSuccess;
+  if (a0.k > 0) {
+    const dim3 g(ps.shrink_end[ps.n_groups - 1]);
+    switch ((a0.r + 15) >> 4) {
+      case 1: shrink_bf16<1><<<g, 256, 0, s>>>(ps); break;
+      case 2: shrink_bf16<2><<<g, 256, 0, s>>>(ps); break;
+      case 4: shrink_bf16<4><<<g, 256, 0, s>>>(ps); break;
+      default: shrink_bf16<8><<<g, 256, 0, s>>>(ps); break;
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const int ntt = (a.T + kPB - 1) / kPB;
-  prefill_bf16<<<plan.n_tiles * ntt, 256, 0, s>>>(a, ntt);
+  prefill_bf16<<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s) {
+  PrefillStep ps{};
+  ps.g[0] = a;
+  ps.g[0].n_tiles = plan.n_tiles;
+  ps.n_groups = 1;
+  ps.n_tok_tiles = (a.T + kPB - 1) / kPB;
+  ps.units = prefill_shrink_units(a.T, a.E, a.k);
+  ps.shrink_end[0] = ps.units * a.n_proj;
+  ps.block_end[0] = prefill_group_blocks(plan.n_tiles, a.T);
+  return launch_prefill_step(ps, s);
 }
 
 }  // namespace rp
