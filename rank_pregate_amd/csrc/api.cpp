@@ -256,7 +256,13 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
   } else if (dt == RP_BF16) {
     // every group's u side by side (a launch pair runs several groups)
     need = rp::kWorkspaceCounterBytes;
-    for (int g = 0; g < n_groups; ++g) need += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k);
+    for (int g = 0; g < n_groups; ++g) {
+      int64_t sum = 0;
+      for (int p = 0; p < gs[g].n_proj; ++p) sum += gs[g].projs[p].d_out;
+      const int tiles_bound = (int)(sum / 128 + gs[g].n_proj);
+      need += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k) +
+              rp::prefill_partial_bytes(tiles_bound, (int)T, rp::prefill_max_splits((int)gs[g].d_in));
+    }
   } else {
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
@@ -320,7 +326,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       ps.n_tok_tiles = (int)((T + 127) / 128);
       ps.units = rp::prefill_shrink_units((int)T, (int)E, k);
       size_t off = rp::kWorkspaceCounterBytes;
-      int shrink_blocks = 0, gemm_blocks = 0;
+      int shrink_blocks = 0, gemm_blocks = 0, counters = 0;
       for (int i = 0; i < ng; ++i) {
         const rp_group& g = gs[g0 + i];
         int d_out[RP_MAX_PROJ];
@@ -333,14 +339,20 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         a.topk_gate = rt.gate;
         a.seg_offsets = rt.off;
         a.pair_perm = rt.perm;
-        a.counters = reinterpret_cast<int*>(w);
         a.u = reinterpret_cast<float*>(w + off);
-        a.partial = nullptr;
         a.n_tiles = plan.n_tiles;
-        a.S = 1;
         off += rp::prefill_u_bytes(g.n_proj, (int)T, (int)r, k);
+        // split-K needs one arrival counter per (tile, token tile)
+        int S = rp::prefill_splits((int)g.d_in, plan.n_tiles, (int)T, n_cu);
+        const int n_cnt = (plan.n_tiles + 7) / 8 * 8 * ps.n_tok_tiles;
+        if (S > 1 && counters + n_cnt > rp::kPrefillCounterWords) S = 1;
+        a.S = S;
+        a.counters = reinterpret_cast<int*>(w) + rp::kPrefillCounterWord + counters;
+        a.partial = reinterpret_cast<float*>(w + off);
+        if (S > 1) counters += n_cnt;
+        off += rp::prefill_partial_bytes(plan.n_tiles, (int)T, S);
         shrink_blocks += ps.units * g.n_proj;
-        gemm_blocks += rp::prefill_group_blocks(plan.n_tiles, (int)T);
+        gemm_blocks += rp::prefill_group_blocks(plan.n_tiles, (int)T) * S;
         ps.shrink_end[i] = shrink_blocks;
         ps.block_end[i] = gemm_blocks;
       }

@@ -169,6 +169,14 @@ struct PrefillStep {
 };
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s);
 constexpr size_t kWorkspaceCounterBytes = 65536;  // reserved control region at the start of every workspace
+// words [kPrefillCounterWord, + kPrefillCounterWords) of that region: split-K
+// arrival counters of prefill GEMM tiles (each returns to zero when its tile
+// completes); the decode control sets sit below
+constexpr int kPrefillCounterWord = 9216;
+constexpr int kPrefillCounterWords = (int)(kWorkspaceCounterBytes / 4) - kPrefillCounterWord;
+int prefill_splits(int d_in, int n_tiles, int T, int n_cu);          // K splits of one group's GEMM tiles
+size_t prefill_partial_bytes(int n_tiles, int T, int S);            // its split-K partial tiles
+int prefill_max_splits(int d_in);                                     // bound on prefill_splits for any device
 size_t prefill_u_bytes(int n_proj, int T, int r, int k);  // one group's gated u, 256-byte aligned
 int prefill_group_blocks(int n_tiles, int T);  // GEMM blocks of one group
 int prefill_shrink_units(int T, int E, int k);  // shrink units per projection

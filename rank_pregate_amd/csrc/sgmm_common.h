@@ -30,7 +30,7 @@ constexpr int kSetArrive = kSetSegDone + 32;     // + 32 * (blockIdx % 8): workg
 constexpr int kSetArriveAll = kSetArrive + 8 * 32;
 constexpr int kSetGroupDone = kSetArriveAll + 64;
 constexpr int kSetWords = kSetGroupDone + 256 * kMaxGroups;
-static_assert(kCtlSet0 + 2 * kCtlSetStride <= 65536 / 4, "control sets exceed the reserved region");
+static_assert(kCtlSet0 + 2 * kCtlSetStride <= kPrefillCounterWord, "control sets overlap the prefill counters");
 static_assert(kSetWords <= kCtlSetStride, "control set overflow");
 
 // Device-scope (sc1) loads of routing data another workgroup of the same

@@ -185,6 +185,19 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
   return align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
 }
 
+// Long K on few blocks splits the GEMM tiles along K (about 4096 columns a
+// split) so their blocks stay short next to the other groups'; a group with
+// blocks enough for the chip keeps whole tiles.
+int prefill_max_splits(int d_in) { return std::max(1, std::min(8, (d_in + 4095) / 4096)); }
+int prefill_splits(int d_in, int n_tiles, int T, int n_cu) {
+  const int blocks = (n_tiles + 7) / 8 * 8 * ((T + 127) / 128);
+  if (blocks >= 2 * n_cu) return 1;
+  return prefill_max_splits(d_in);
+}
+size_t prefill_partial_bytes(int n_tiles, int T, int S) {
+  return S > 1 ? align256((size_t)(n_tiles + 7) / 8 * 8 * ((T + 127) / 128) * S * 128 * 128 * sizeof(float)) : 0;
+}
+
 size_t prefill_u_bytes(int n_proj, int T, int r, int k) {
   return align256((size_t)n_proj * T * k * r * sizeof(float));
 }

@@ -71,9 +71,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = group_of_block(ps.block_end, ps.n_groups, blockIdx.x);
   const SgmmArgs& a = ps.g[grp];
-  const int n_tok_tiles = ps.n_tok_tiles;
+  const int n_tok_tiles = ps.n_tok_tiles, S = a.S;
+  // block q*8 + x of the group: row tile (q / (ntt*S))*8 + x, K split and
+  // token tile from q % (ntt*S), so every split and token tile of a row tile
+  // shares an XCD
   const int q = (blockIdx.x - (grp > 0 ? ps.block_end[grp - 1] : 0)) >> 3;  // groups start at multiples of 8
-  const int tile = (q / n_tok_tiles) * 8 + (blockIdx.x & 7), tt = q % n_tok_tiles;
+  const int per = n_tok_tiles * S;
+  const int tile = (q / per) * 8 + (blockIdx.x & 7);
+  const int split = (q % per) / n_tok_tiles, tt = q % n_tok_tiles;
   if (tile >= a.n_tiles) return;
   const int proj = proj_of_tile(a, tile);
   const ProjDesc pd = proj_at(a, proj);
@@ -109,14 +114,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
       gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in;
     }
   }
-  const int nk = (a.d_in + kPK - 1) / kPK;
+  const int nk_all = (a.d_in + kPK - 1) / kPK;
+  const int kb = (int)((long long)nk_all * split / S);
+  const int nk = (int)((long long)nk_all * (split + 1) / S) - kb;  // this split's stages, >= 1
   // Stages go global -> registers kPR stages ahead of the math, then to the
   // LDS double buffer one stage ahead.  Loads are never masked (stages past
   // the end re-read the last one); columns past d_in are zeroed on the way to
-  // LDS.
+  // LDS.  Stage j of the split is stage kb + j of K.
   uint4 ra[kPR][2], rb[kPR][2];
-  auto gload = [&](int slot, int kt) {
-    kt = min(kt, nk - 1);
+  auto gload = [&](int slot, int j) {
+    const int kt = kb + min(j, nk - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       ra[slot][i] = ld16(gA[i] + min(kt * kPK + lk[i], a.d_in - 8));
@@ -126,10 +133,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
         rb[slot][i] = ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8));
     }
   };
-  auto lstore = [&](int slot, int buf, int kt) {
+  auto lstore = [&](int slot, int buf, int j) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool ok = kt * kPK + lk[i] < a.d_in;
+      const bool ok = (kb + j) * kPK + lk[i] < a.d_in;
       *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(ok, ra[slot][i]);
       *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = pd.tiled ? rb[slot][i] : sel4(ok, rb[slot][i]);
     }
@@ -189,6 +196,70 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
       __syncthreads();
     }
   });
+
+  if (S > 1) {
+    // split-K: every split publishes its fp32 partial tile with device-scope
+    // stores (chunk c of lane l at ((wave*16 + c)*64 + l)*16 bytes); the last
+    // to arrive sums all S in split order, so the result does not depend on
+    // which split finishes last, and then applies the adapters
+    __shared__ int s_last;
+    const size_t tile_floats = (size_t)kPB * kPB;
+    const size_t slot0 = ((size_t)tile * n_tok_tiles + tt) * S;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        a.partial + slot0 * tile_floats, 0, (int)(S * tile_floats * sizeof(float)), 0x00020000);
+    constexpr int kSc1 = 1 << 4;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int c = (f * 2 + g) * 4 + v4;
+          const f32x4_t val = {acc[f][g][4 * v4], acc[f][g][4 * v4 + 1], acc[f][g][4 * v4 + 2], acc[f][g][4 * v4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), pr,
+                                                 (uint32_t)((split * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1);
+        }
+    __builtin_amdgcn_s_waitcnt(0);  // the partial is in memory before the arrival is counted
+    __syncthreads();
+    int* cnt = a.counters + (size_t)tile * n_tok_tiles + tt;
+    if (tid == 0) s_last = atomicAdd(cnt, 1) == S - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    f32x16_t tot[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[f][g][v] = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      if (sp == split) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) tot[f][g] += acc[f][g];
+        continue;
+      }
+      f32x4_t pv[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        pv[c] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    pr, (uint32_t)((sp * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1));
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[f][g][4 * v4 + e] += pv[(f * 2 + g) * 4 + v4][e];
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) acc[f][g] = tot[f][g];
+  }
 
   // Expand: per 32-token block, the distinct adapters its tokens chose, in
   // ascending order (found with wave minimums, no memory round trip); a lane

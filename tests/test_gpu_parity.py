@@ -279,6 +279,16 @@ def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed=T + d_in + E)
 
 
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (200, 8200, [136], 6, 16, 2),       # K split two ways, ragged last stage and tile
+    (130, 12288, [256, 64], 5, 32, 2),  # K split three ways, two projections
+])
+def test_projection_prefill_split_k(T, d_in, d_outs, E, r, k):
+    """Long K on few row tiles: the bf16 prefill GEMM splits K and sums the partial tiles in split order."""
+    say("projection split-K", T, d_in, d_outs, E, r, k)
+    _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E)
+
+
 @pytest.mark.parametrize("T,d_in,d_out,E,r,k,dt", [
     (32, 256, 128, 8, 16, 2, "bf16"),   # decode, adapters applied by row tiles of the stacked A
     (48, 256, 96, 40, 16, 3, "bf16"),   # decode, E > 32: segment-chunk shrink
