@@ -176,9 +176,10 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
  *   rp_sgmm_fused(projs, n_proj, x, ..., topk_idx, topk_gate, seg_offsets, pair_perm, ...)
  *
  * with bit-identical routing outputs, which later groups of the same step then
- * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 32) everything runs in
- * one kernel launch whose router and segmentation finish while the backbone
- * weights stream; other shapes issue the three launches in order.
+ * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 32, E <= 64)
+ * everything runs in one kernel launch whose router and segmentation finish
+ * while the backbone weights stream; other shapes issue the three launches in
+ * order.
  *
  *   Wg        [d_in, E], dense, dtype dt (the router weight)
  *   topk_idx  int32 [T, k], topk_gate fp32 [T, k], seg_offsets int32 [E+1],

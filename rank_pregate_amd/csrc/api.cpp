@@ -308,7 +308,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     sg.pair_perm = rt.perm;
     sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
   }
-  const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T);
+  const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T, (int)E);
   if (route && !fuse_route) {
     hipError_t e = rp::launch_pregate(pg, stream);
     if (e == hipSuccess) e = rp::launch_segment(sg, stream);

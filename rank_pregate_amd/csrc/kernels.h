@@ -153,7 +153,7 @@ int decode_mt(int T);       // 16-token tiles of the decode kernel
 int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
 int decode_resident_per_cu(int T, bool fused);  // workgroups of the decode kernel one CU holds at once
 int fused_route_tile_tokens();                  // tokens per router tile of a fused decode launch
-bool decode_fused_route_supported(int T);       // routing can run inside a decode launch of T tokens
+bool decode_fused_route_supported(int T, int E);  // routing can run inside a decode launch of T tokens
 
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 // Several bf16 prefill-shaped groups (T > 64) in one shrink launch and one

@@ -6,20 +6,27 @@
 namespace rp {
 namespace {
 
-template <typename Tin, int TT>
-__global__ __launch_bounds__(kRouteThreads) void pregate_kernel(PregateArgs a, RoutePlan p) {
+template <typename Tin, int TT, int NT>
+__global__ __launch_bounds__(NT) void pregate_kernel(PregateArgs a, RoutePlan p) {
   extern __shared__ float smem[];
-  route_tile<Tin, TT>(a, blockIdx.x * TT, p, smem);
+  route_tile<Tin, TT, NT>(a, blockIdx.x * TT, p, smem);
 }
 
 template <typename Tin>
 hipError_t launch_t(const PregateArgs& a, hipStream_t s) {
   const RoutePlan p = route_plan(a.E, a.d_in, (int)sizeof(Tin));
-  const size_t lds = sizeof(float) * route_lds_floats(a.E, p.TT);
-  if (p.TT == 4)
-    pregate_kernel<Tin, 4><<<(a.T + 3) / 4, kRouteThreads, lds, s>>>(a, p);
-  else
-    pregate_kernel<Tin, 2><<<(a.T + 1) / 2, kRouteThreads, lds, s>>>(a, p);
+  const size_t lds = sizeof(float) * route_lds_floats(p, a.E, p.TT);
+  if (p.NT == kRouteThreads) {
+    if (p.TT == 4)
+      pregate_kernel<Tin, 4, kRouteThreads><<<(a.T + 3) / 4, kRouteThreads, lds, s>>>(a, p);
+    else
+      pregate_kernel<Tin, 2, kRouteThreads><<<(a.T + 1) / 2, kRouteThreads, lds, s>>>(a, p);
+  } else {
+    if (p.TT == 4)
+      pregate_kernel<Tin, 4, kRouteThreadsWide><<<(a.T + 3) / 4, kRouteThreadsWide, lds, s>>>(a, p);
+    else
+      pregate_kernel<Tin, 2, kRouteThreadsWide><<<(a.T + 1) / 2, kRouteThreadsWide, lds, s>>>(a, p);
+  }
   return hipGetLastError();
 }
 

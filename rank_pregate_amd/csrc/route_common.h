@@ -29,7 +29,8 @@ __device__ __forceinline__ void stc_f32(float* p, float v) {
 // ---------------------------------------------------------------------------
 // router
 // ---------------------------------------------------------------------------
-constexpr int kRouteThreads = 128;  // threads per router tile (both launch forms)
+constexpr int kRouteThreads = 128;     // threads per router tile for E <= 64 (both launch forms)
+constexpr int kRouteThreadsWide = 512;  // threads per router tile for E > 64 (router launch only)
 constexpr int kRouteCB = 8;         // router columns per thread
 
 template <typename Tin>
@@ -98,38 +99,47 @@ struct RoutePlan {
   int slice;  // k per k-slice
   bool vec_cols;
   int TT;     // tokens per tile
+  int NT;     // threads per tile
+  int KR;     // partial sums per column left after the in-wave butterfly
 };
 
+// The k-slices (and with them the summation order of a logit) depend on E and
+// d_in only, never on T or on which launch runs the router: with E <= 64 a
+// tile has 128 threads (the decode launch runs two tiles per workgroup), with
+// more adapters 512, so a thread's k-slice stays short.
 __host__ __device__ inline RoutePlan route_plan(int E, int d_in, int elem_bytes) {
   RoutePlan p;
   const int ncb = (E + kRouteCB - 1) / kRouteCB;
   p.NCBp = 1;
   while (p.NCBp < ncb) p.NCBp <<= 1;
-  const int KS = kRouteThreads / p.NCBp > 0 ? kRouteThreads / p.NCBp : 1;
+  p.NT = E <= 64 ? kRouteThreads : kRouteThreadsWide;
+  const int KS = p.NT / p.NCBp > 0 ? p.NT / p.NCBp : 1;
   p.slice = ((d_in + KS - 1) / KS + 7) / 8 * 8;
   p.vec_cols = (E * elem_bytes) % 16 == 0;
-  p.TT = E <= 64 ? 4 : 2;
+  const int L = p.NCBp >= 64 ? 1 : 64 / p.NCBp;
+  p.KR = KS / L > 1 ? KS / L : 1;
+  p.TT = E <= 64 || (p.KR + 1) * 4 * E * 4 <= 65536 ? 4 : 2;
   return p;
 }
 
-// LDS floats a router tile needs.
-__host__ __device__ inline int route_lds_floats(int E, int TT) { return 3 * TT * E; }
+// LDS floats a router tile needs: KR partial sums and the logits per (token, column).
+__host__ __device__ inline int route_lds_floats(const RoutePlan& p, int E, int TT) { return (p.KR + 1) * TT * E; }
 
 // Score tokens [t0, t0 + TT) against all E router columns, choose the top k
 // and their softmax gates.  Threads are (block of 8 columns, k-slice); a thread
 // walks its k-slice in ascending k with one fp32 sum per (token, column); the
 // slices are combined with a fixed butterfly inside each wave and then in wave
 // order, so equal router columns give bit-equal logits.
-// NCBp <= 128 (E <= 1024).  Must be called by all kRouteThreads threads of a
+// NCBp <= 128 (E <= 1024).  Must be called by all NT threads of a
 // group (every group of a wider workgroup calls it, with its own smem and t0).
 // With `tagged` set, each (token, slot) result is also written as two tagged
 // 8-byte pairs (index, tag) and (gate bits, tag) for readers in the same launch.
-template <typename Tin, int TT>
+template <typename Tin, int TT, int NT = kRouteThreads>
 __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const RoutePlan& rp_, float* smem,
                                            unsigned long long* tagged = nullptr, uint32_t tag = 0) {
   const int NCBp = rp_.NCBp;
-  // a wider workgroup runs one tile per group of kRouteThreads threads
-  const int tid = threadIdx.x & (kRouteThreads - 1), lane = tid & 63, wave = tid >> 6;
+  // a wider workgroup runs one tile per group of NT threads
+  const int tid = threadIdx.x & (NT - 1), lane = tid & 63, wave = tid >> 6;
   const int nt = min(TT, a.T - t0);
   const int E = a.E;
   const Tin* x = static_cast<const Tin*>(a.x);
@@ -137,7 +147,7 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   const int ncb = (E + kRouteCB - 1) / kRouteCB;
   const int cb = tid % NCBp, ks = tid / NCBp;
   const int L = NCBp >= 64 ? 1 : 64 / NCBp;          // lanes of a wave sharing a column block
-  const int KR = max(1, (kRouteThreads / NCBp) / L);  // partial sums left per column after the butterfly
+  const int KR = max(1, (NT / NCBp) / L);  // partial sums left per column after the butterfly
   float* red = smem;
   float* lg = smem + (size_t)KR * TT * E;
 
@@ -147,7 +157,7 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
 #pragma unroll
     for (int c = 0; c < kRouteCB; ++c) acc[t][c] = 0.f;
   const int c0 = cb * kRouteCB;
-  const bool active = cb < ncb && ks * NCBp + cb < kRouteThreads;
+  const bool active = cb < ncb && ks * NCBp + cb < NT;
   if (active) {
     const Tin* xr[TT];
 #pragma unroll
@@ -232,7 +242,7 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
         if (c0 + c < E) red[((size_t)kr * TT + t) * E + c0 + c] = acc[t][c];
   }
   __syncthreads();
-  for (int q = tid; q < TT * E; q += kRouteThreads) {
+  for (int q = tid; q < TT * E; q += NT) {
     float s = 0.f;
     for (int j = 0; j < KR; ++j) s += red[(size_t)j * TT * E + q];
     lg[q] = s;
@@ -240,11 +250,11 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   __syncthreads();
 
   if (a.logits) {
-    for (int q = tid; q < nt * E; q += kRouteThreads) a.logits[(size_t)t0 * E + q] = lg[q];
+    for (int q = tid; q < nt * E; q += NT) a.logits[(size_t)t0 * E + q] = lg[q];
   }
 
   // top-k per token on one wave; waves take tokens w, w + 2, ...
-  for (int tt = wave; tt < nt; tt += kRouteThreads / 64) {
+  for (int tt = wave; tt < nt; tt += NT / 64) {
     const float* row = lg + tt * E;
     uint32_t taken = 0;  // bit m: this lane's m-th candidate (e = lane + 64 m) is chosen
     float selv[kMaxK];

@@ -55,6 +55,7 @@ static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations")
 static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
+constexpr int kMaxFusedE = 64;        // adapters a fused launch routes over (two partial sums per column)
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, CDNA
@@ -110,7 +111,7 @@ constexpr size_t smem_bytes() {
   // activation chunks (double-buffered), the expand's routing, its token operand (hi, lo)
   constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + MT * 4 * 64 * 16 * 2;
   constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
-  constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxE * sizeof(float) : 0;  // two router tiles
+  constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxFusedE * sizeof(float) : 0;  // two router tiles
   constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
   size_t m = xs;
   if (red > m) m = red;
@@ -926,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         const int half = tid / kRouteThreads;
         const RoutePlan rpl = route_plan(st.pg.E, st.pg.d_in, (int)sizeof(bf16_t));
         route_tile<bf16_t, kFusedRouteTokens>(st.pg, (item * 2 + half) * kFusedRouteTokens, rpl,
-                                              reinterpret_cast<float*>(smem) + half * route_lds_floats(st.pg.E, kFusedRouteTokens),
+                                              reinterpret_cast<float*>(smem) + half * route_lds_floats(rpl, st.pg.E, kFusedRouteTokens),
                                               reinterpret_cast<unsigned long long*>(st.route_tagged), launch_tag(s_ep));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1038,7 +1039,7 @@ int decode_resident_per_cu(int T, bool fused) {
   }
 }
 
-bool decode_fused_route_supported(int T) { return decode_mt(T) <= 2; }
+bool decode_fused_route_supported(int T, int E) { return decode_mt(T) <= 2 && E <= 64; }
 
 hipError_t launch_step(const StepArgs& st, const StepPlan& plan, hipStream_t s) { return launch_t(st, plan, s); }
 
