@@ -18,9 +18,11 @@ __device__ __forceinline__ int group_of_block(const int* end, int n, int b) {
   return g;
 }
 
-template <int MTR>
+// One shrink block: a chunk of 16*NCT pairs of one segment.  Small segments
+// (a few tokens each) take NCT = 1 and keep more K steps of A_e in flight.
+template <int MTR, int NCT>
 __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
-  __shared__ __attribute__((aligned(16))) float red[MTR * 4 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float red[MTR * NCT * 4 * 64];
   __shared__ int s_loc[2];
   const int g = group_of_block(ps.shrink_end, ps.n_groups, blockIdx.x);
   const SgmmArgs& a = ps.g[g];
@@ -28,12 +30,13 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   const int proj = b / ps.units, unit = b % ps.units;
   if (threadIdx.x < 64) {
     int e, c;
-    locate_chunk(a, unit, 64, threadIdx.x, &e, &c);
+    locate_chunk(a, unit, 16 * NCT, threadIdx.x, &e, &c);
     if (threadIdx.x == 0) { s_loc[0] = e; s_loc[1] = c; }
   }
   __syncthreads();
   if (s_loc[0] < 0) return;
-  shrink_unit<MTR, 4, 4, (MTR >= 4 ? 1 : 2)>(a, proj, s_loc[0], s_loc[1], red);
+  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR >= 4 ? 1 : 2);  // K steps per load batch
+  shrink_unit<MTR, NCT, 4, U>(a, proj, s_loc[0], s_loc[1], red);
 }
 
 // ============================================================================
@@ -387,18 +390,23 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
 }  // namespace
 
 int prefill_group_blocks(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB - 1) / kPB); }
-int prefill_shrink_units(int T, int E, int k) { return E + (T * k + 63) / 64; }
+int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * E ? 1 : 4; }
+int prefill_shrink_units(int T, int E, int k) {
+  const int nch = 16 * prefill_shrink_nct(T, E, k);
+  return E + (T * k + nch - 1) / nch;
+}
 
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   const SgmmArgs& a0 = ps.g[0];
   if (a0.T == 0) return hipSuccess;
   if (a0.k > 0) {
     const dim3 g(ps.shrink_end[ps.n_groups - 1]);
+    const bool small = prefill_shrink_nct(a0.T, a0.E, a0.k) == 1;
     switch ((a0.r + 15) >> 4) {
-      case 1: shrink_bf16<1><<<g, 256, 0, s>>>(ps); break;
-      case 2: shrink_bf16<2><<<g, 256, 0, s>>>(ps); break;
-      case 4: shrink_bf16<4><<<g, 256, 0, s>>>(ps); break;
-      default: shrink_bf16<8><<<g, 256, 0, s>>>(ps); break;
+      case 1: small ? shrink_bf16<1, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<1, 4><<<g, 256, 0, s>>>(ps); break;
+      case 2: small ? shrink_bf16<2, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<2, 4><<<g, 256, 0, s>>>(ps); break;
+      case 4: small ? shrink_bf16<4, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<4, 4><<<g, 256, 0, s>>>(ps); break;
+      default: small ? shrink_bf16<8, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<8, 4><<<g, 256, 0, s>>>(ps); break;
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
