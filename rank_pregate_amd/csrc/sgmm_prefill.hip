@@ -56,10 +56,17 @@ __device__ __forceinline__ int token_at(const SgmmArgs& a, int i) {
   return (a.k == 1) ? a.pair_perm[i] : i;
 }
 
+// Minimum over the 64 lanes of a wave (all lanes active), with DPP moves
+// instead of LDS permutes: within quads, half rows, rows, then row 0 into
+// row 1, row 2 into row 3, rows 0-1 into rows 2-3; lane 63 holds the result.
 __device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Blocks b and b + 8 share an XCD (b % 8).  The n_tok_tiles token tiles of a
