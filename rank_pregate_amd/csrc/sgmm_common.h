@@ -18,6 +18,7 @@ namespace rp {
 // In a control set, per group g of the launch (g < kMaxGroups):
 //   kSetShrinkDone + 32 g          pair-chunk shrink units finished
 //   kSetGroupDone + 256 g + 32 c   output tiles finished, counted per tile % 8
+//   kSetQueue                      items claimed after every workgroup's first (item = grid + count)
 constexpr int kCtlEpoch = 0;
 constexpr int kCtlWaitOverflow = 32;
 constexpr int kCtlSegErr = 64;
@@ -29,7 +30,8 @@ constexpr int kSetSegDone = kSetRouteDone + 32;  // segmentation finished
 constexpr int kSetArrive = kSetSegDone + 32;     // + 32 * (blockIdx % 8): workgroups that read the epoch
 constexpr int kSetArriveAll = kSetArrive + 8 * 32;
 constexpr int kSetGroupDone = kSetArriveAll + 64;
-constexpr int kSetWords = kSetGroupDone + 256 * kMaxGroups;
+constexpr int kSetQueue = kSetGroupDone + 256 * kMaxGroups;  // items handed out after each workgroup's first
+constexpr int kSetWords = kSetQueue + 32;
 static_assert(kCtlSet0 + 2 * kCtlSetStride <= kPrefillCounterWord, "control sets overlap the prefill counters");
 static_assert(kSetWords <= kCtlSetStride, "control set overflow");
 

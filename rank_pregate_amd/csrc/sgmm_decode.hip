@@ -910,7 +910,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
   int ep_in = 0;
   if (tid == 0) ep_in = __hip_atomic_load(&ctl[kCtlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool first = true;
-  for (int item = blockIdx.x; item < st.n_items; item += gridDim.x) {
+  // Items in claim order: a workgroup's first item is its block index, each
+  // later one comes from a launch-wide counter claimed at the start of the
+  // item before (its latency overlaps that item).  Claims are in increasing
+  // order, so every item an item waits for has been claimed by a running
+  // workgroup.
+  __shared__ int s_next[2];
+  int item = blockIdx.x;
+  for (int iter = 0; item < st.n_items; ++iter) {
+    int nxt = st.n_items;  // a launch with no more items than workgroups claims nothing
+    if (tid == 0 && st.n_items > (int)gridDim.x) nxt = (int)gridDim.x + atomicAdd(ctl_set(ctl, ep_in) + kSetQueue, 1);
     if (FUSED && item < st.n_pre) {
       if (first) {
         if (tid == 0) {
@@ -987,7 +996,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         first = false;
       }
     }
+    if (tid == 0) s_next[iter & 1] = nxt;
     __syncthreads();  // LDS is reused by the next item
+    item = s_next[iter & 1];
   }
 }
 
