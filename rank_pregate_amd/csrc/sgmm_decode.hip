@@ -56,6 +56,7 @@ static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles 
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
 constexpr int kMaxFusedE = 64;        // adapters a fused launch routes over (two partial sums per column)
+constexpr int kUPieces = 4;           // u pieces (two tagged values) a thread holds for the staged expand
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, CDNA
@@ -290,7 +291,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
 // flight.  The expand's operands (routing, u, B) are requested inside the last
 // two rings at fixed positions, each before the weights it must not wait for,
 // so only the expand's MFMAs and the stores follow the last chunk.
-template <int MT, bool TILED, bool FUSED, bool ATILE>
+template <int MT, bool TILED, bool FUSED, bool ATILE, bool LANEX>
 __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d, int bi, bf16_t* xs, int* ctl, int* s_ep,
                           bool first, int ep_in) {
   constexpr int G = 8;                          // adapters per batch of B loads
@@ -441,11 +442,11 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int kcat = a.E * a.r;
   const int half_r = a.r >> 1;
   const int lg_r = __builtin_ctz(a.r);  // r is a power of two >= 8
-  constexpr int kUP = 4;                // u pieces (two tagged values) per thread
+  constexpr int kUP = kUPieces;
   const bool px = expand && d.dense && kcat <= 128 && n_pairs * half_r <= kUP * kThreads;
   // with two rings or more, the expand's operands are requested and placed
   // while the last chunks stream, so only its MFMAs follow the last chunk
-  const bool early = MT <= 2 && px && V >= 2 * NR;
+  const bool early = !LANEX && px && V >= 2 * NR;
   uint4 bfr[4];
   auto b_issue = [&]() {
 #pragma unroll
@@ -615,7 +616,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         }
       }
     }
-  } else if (expand) {
+  } else if (LANEX && expand) {
     // adapter deltas for this wave's 16 rows, lane by lane: the routing of
     // the tile's tokens (adapter and gate of every (token, slot) pair) is in
     // LDS.  A lane's tokens chose at most k adapters, so it needs u only for
@@ -899,7 +900,11 @@ __device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
   return d;
 }
 
-template <int MT, bool FUSED>
+// LANEX: the launch has items whose expand cannot take the staged form (more
+// than 32 adapters, E*r > 128, or more u pieces than the threads hold); only
+// then is the lane-by-lane expand compiled in (its registers would otherwise
+// crowd the stream).
+template <int MT, bool FUSED, bool LANEX>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<MT, FUSED>()];
   __shared__ int s_ep, s_loc[2], s_wave_tot[kWV], s_bad;
@@ -960,7 +965,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
       const SgmmArgs& a = st.g[gi];
       const DecodeArgs d = group_view(st, gi);
       if (li < d.n_shrink && d.dense) {
-        base_item<MT, false, FUSED, true>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
+        base_item<MT, false, FUSED, true, LANEX>(a, d, li, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         first = false;
       } else if (li < d.n_shrink) {
         if (first) {
@@ -990,9 +995,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         const int bi = li - d.n_shrink;
         const int bp = proj_of_tile(a, bi / a.S);
         if (RP_PICK(a, bp, tiled))
-          base_item<MT, true, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
+          base_item<MT, true, FUSED, false, LANEX>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         else
-          base_item<MT, false, FUSED, false>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
+          base_item<MT, false, FUSED, false, LANEX>(a, d, bi, reinterpret_cast<bf16_t*>(smem), ctl, &s_ep, first, ep_in);
         first = false;
       }
     }
@@ -1009,30 +1014,41 @@ int resident_per_cu() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   if (cache[dev] > 0) return cache[dev];
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MT, FUSED>, kThreads, 0) != hipSuccess || n < 1)
+  int n2 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MT, FUSED, false>, kThreads, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, decode_kernel<MT, FUSED, true>, kThreads, 0) != hipSuccess)
     n = 1;
+  n = std::max(1, std::min(n, n2));
   cache[dev] = n;
   return n;
 }
 
-hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
+template <bool LANEX>
+hipError_t launch_lx(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
   const dim3 grid(plan.grid);
   const int T = st.g[0].T;
   if (st.fused) {
     // routing inside the launch is built for up to two token tiles (T <= 32)
     switch (decode_mt(T)) {
-      case 1: decode_kernel<1, true><<<grid, kThreads, 0, s>>>(st); break;
-      case 2: decode_kernel<2, true><<<grid, kThreads, 0, s>>>(st); break;
+      case 1: decode_kernel<1, true, LANEX><<<grid, kThreads, 0, s>>>(st); break;
+      case 2: decode_kernel<2, true, LANEX><<<grid, kThreads, 0, s>>>(st); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (decode_mt(T)) {
-      case 1: decode_kernel<1, false><<<grid, kThreads, 0, s>>>(st); break;
-      case 2: decode_kernel<2, false><<<grid, kThreads, 0, s>>>(st); break;
-      default: decode_kernel<4, false><<<grid, kThreads, 0, s>>>(st); break;
+      case 1: decode_kernel<1, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
+      case 2: decode_kernel<2, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
+      default: decode_kernel<4, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
+  // the staged expand's conditions (base_item's px), uniform over the launch
+  const SgmmArgs& a = st.g[0];
+  const bool staged = a.k == 0 || (st.dense && a.E * a.r <= 128 && a.T * a.k * (a.r / 2) <= kUPieces * kThreads);
+  return staged ? launch_lx<false>(st, plan, s) : launch_lx<true>(st, plan, s);
 }
 
 }  // namespace

@@ -268,6 +268,8 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
     (64, 256, [128, 96], 16, 8, 2),    # two projections, different widths
     (100, 128, [64, 64, 64], 9, 32, 3),
     (48, 256, [128], 100, 16, 2),      # decode, E > 32: shrink over segment chunks
+    (24, 512, [192], 12, 32, 2),       # decode, E*r > 128: lane-by-lane expand over dense u
+    (64, 256, [128], 8, 16, 4),        # decode, more u pieces than the staged expand holds
     (64, 4096, [4096], 16, 8, 2),      # decode, four token tiles, full width
     (256, 512, [256], 256, 16, 2),     # many adapters, 1-3 tokens per segment
     (257, 256, [136], 7, 64, 1),       # first prefill size, ragged
