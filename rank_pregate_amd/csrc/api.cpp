@@ -259,7 +259,7 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
       for (int p = 0; p < gs[g].n_proj; ++p) sum += gs[g].projs[p].d_out;
-      const int tiles_bound = (int)(sum / 128 + gs[g].n_proj);
+      const int tiles_bound = (int)(sum / rp::prefill_tile_rows((int)T) + gs[g].n_proj);
       need += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k) +
               rp::prefill_partial_bytes(tiles_bound, (int)T, rp::prefill_max_splits((int)gs[g].d_in));
     }
@@ -344,7 +344,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         off += rp::prefill_u_bytes(g.n_proj, (int)T, (int)r, k);
         // split-K needs one arrival counter per (tile, token tile)
         int S = rp::prefill_splits((int)g.d_in, plan.n_tiles, (int)T, n_cu);
-        const int n_cnt = (plan.n_tiles + 7) / 8 * 8 * ps.n_tok_tiles;
+        const int n_cnt = rp::prefill_units(plan.n_tiles, (int)T);
         if (S > 1 && counters + n_cnt > rp::kPrefillCounterWords) S = 1;
         a.S = S;
         a.counters = reinterpret_cast<int*>(w) + rp::kPrefillCounterWord + counters;

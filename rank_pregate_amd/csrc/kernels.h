@@ -178,7 +178,9 @@ int prefill_splits(int d_in, int n_tiles, int T, int n_cu);          // K splits
 size_t prefill_partial_bytes(int n_tiles, int T, int S);            // its split-K partial tiles
 int prefill_max_splits(int d_in);                                     // bound on prefill_splits for any device
 size_t prefill_u_bytes(int n_proj, int T, int r, int k);  // one group's gated u, 256-byte aligned
-int prefill_group_blocks(int n_tiles, int T);  // GEMM blocks of one group
+int prefill_group_blocks(int n_tiles, int T);  // GEMM blocks of one group (one K split)
+int prefill_units(int n_tiles, int T);         // (row tile, token tile) units of one group
+int prefill_tile_rows(int T);                  // output rows per GEMM tile
 int prefill_shrink_units(int T, int E, int k);  // shrink units per projection
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,

@@ -11,7 +11,6 @@ namespace {
 constexpr size_t kCounterBytes = kWorkspaceCounterBytes;
 constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeMaxT = 64;
-constexpr int kPrefillTileRows = 128;
 constexpr int kF32TileRows = 64;
 constexpr int kDenseMaxE = 32;           // decode shrink covers every token per adapter up to this many adapters
 constexpr int kMaxSplits = 8;            // decode split-K
@@ -107,7 +106,7 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
     return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, decode_tiles(n_proj, d_out), kCounterBytes);
   SgmmPlan p{};
   p.path = (dt == kF32) ? 0 : 2;
-  p.tile_rows = p.path == 0 ? kF32TileRows : kPrefillTileRows;
+  p.tile_rows = p.path == 0 ? kF32TileRows : prefill_tile_rows(T);
   p.n_tiles = 0;
   for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + p.tile_rows - 1) / p.tile_rows;
   p.S = 1;
@@ -182,7 +181,12 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
     StepGroupDesc g{n_proj, d_out, d_in, 0};
     return step_workspace_upper_bound(&g, 1, T, E, r, k);
   }
-  return align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
+  size_t b = align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
+  if (dt == kBF16) {  // the prefill GEMM's split-K partials
+    const int tiles_bound = (int)(sum_d_out / prefill_tile_rows(T) + n_proj);
+    b += prefill_partial_bytes(tiles_bound, T, prefill_max_splits(d_in));
+  }
+  return b;
 }
 
 // Long K on few blocks splits the GEMM tiles along K (about 4096 columns a
@@ -190,12 +194,11 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
 // blocks enough for the chip keeps whole tiles.
 int prefill_max_splits(int d_in) { return std::max(1, std::min(8, (d_in + 4095) / 4096)); }
 int prefill_splits(int d_in, int n_tiles, int T, int n_cu) {
-  const int blocks = (n_tiles + 7) / 8 * 8 * ((T + 127) / 128);
-  if (blocks >= 2 * n_cu) return 1;
+  if (prefill_units(n_tiles, T) >= 2 * n_cu) return 1;
   return prefill_max_splits(d_in);
 }
-size_t prefill_partial_bytes(int n_tiles, int T, int S) {
-  return S > 1 ? align256((size_t)(n_tiles + 7) / 8 * 8 * ((T + 127) / 128) * S * 128 * 128 * sizeof(float)) : 0;
+size_t prefill_partial_bytes(int n_tiles, int T, int S) {  // a tile's partial: 16384 fp32 in either tiling
+  return S > 1 ? align256((size_t)prefill_units(n_tiles, T) * S * 16384 * sizeof(float)) : 0;
 }
 
 size_t prefill_u_bytes(int n_proj, int T, int r, int k) {

@@ -69,6 +69,179 @@ __device__ __forceinline__ int wave_min_int(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Split-K hand-over of a 4-wave GEMM block whose accumulators are acc[2][2]
+// (64 floats a lane): every split publishes its fp32 partial tile with
+// device-scope stores (chunk c of lane l at ((wave*16 + c)*64 + l)*16 bytes),
+// counts its arrival, and the last to arrive sums all S in split order (the
+// result does not depend on which finishes last).  Returns false in the splits
+// that are not last.  `slot0` numbers the tile's first partial.
+__device__ __forceinline__ bool splitk_reduce(const SgmmArgs& a, size_t slot0, int split, int S, int* cnt,
+                                              f32x16_t (&acc)[2][2]) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr size_t tile_floats = 4 * 64 * 64;
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+      a.partial + slot0 * tile_floats, 0, (int)(S * tile_floats * sizeof(float)), 0x00020000);
+  constexpr int kSc1 = 1 << 4;
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int c = (f * 2 + g) * 4 + v4;
+        const f32x4_t val = {acc[f][g][4 * v4], acc[f][g][4 * v4 + 1], acc[f][g][4 * v4 + 2], acc[f][g][4 * v4 + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), pr,
+                                               (uint32_t)((split * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1);
+      }
+  __builtin_amdgcn_s_waitcnt(0);  // the partial is in memory before the arrival is counted
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(cnt, 1) == S - 1;
+  __syncthreads();
+  if (!s_last) return false;
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+  f32x16_t tot[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tot[f][g][v] = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    if (sp == split) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) tot[f][g] += acc[f][g];
+      continue;
+    }
+    f32x4_t pv[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      pv[c] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                  pr, (uint32_t)((sp * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1));
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tot[f][g][4 * v4 + e] += pv[(f * 2 + g) * 4 + v4][e];
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[f][g] = tot[f][g];
+  return true;
+}
+
+// Expand: per 32-token block, the distinct adapters its tokens chose, in
+// ascending order (found with wave minimums, no memory round trip); a lane
+// holds its token's gated u for every slot, so an adapter's token operand is
+// picked in registers (slots naming the same adapter summed in slot order)
+// and split into bf16 (hi, lo).  B rows go out a batch of kPNB adapters ahead
+// of the batch whose MFMAs run.
+// The wave's tokens are positions pos0 .. pos0+63 (two 32-token blocks), its
+// rows rowb .. rowb+63 (two 32-row blocks); acc[f][g] as the GEMM left it.
+__device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDesc& pd, int proj, int pos0, int rowb,
+                                                f32x16_t (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, lr = lane & 31, kg = lane >> 5;
+  const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
+  const float* ub = a.u + (size_t)proj * a.T * a.k * a.r;
+  const int kk = a.k;
+  int brow_g[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) brow_g[g] = min(rowb + g * 32 + lr, pd.d_out - 1);
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int pos = pos0 + f * 32 + lr;
+    const bool tok_ok = pos < a.T;
+    const int t = token_at(a, min(pos, a.T - 1));
+    // slots in groups of kPUJ (a token naming one adapter in two groups
+    // gets its two terms from two passes)
+    for (int j0 = 0; j0 < kk; j0 += kPUJ)
+    for (int c0 = 0; c0 < a.r; c0 += 16) {
+      int ej[kPUJ];
+#pragma unroll
+      for (int j = 0; j < kPUJ; ++j) {
+        const int e = (j0 + j < kk && tok_ok) ? a.topk_idx[t * kk + j0 + j] : -1;
+        ej[j] = (e >= 0 && e < a.E) ? e : kNoAdapter;
+      }
+      const int c = c0 + kg * 8;
+      const bool cok = c < a.r;
+      const int cc = min(c, a.r - 8);
+      f32x4_t uj[kPUJ][2];
+#pragma unroll
+      for (int j = 0; j < kPUJ; ++j) {
+        const bool ok = ej[j] != kNoAdapter && cok;
+        const float* p = ub + (size_t)(t * kk + min(j0 + j, kk - 1)) * a.r + cc;
+        uj[j][0] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uj[j][1] = ok ? *reinterpret_cast<const f32x4_t*>(p + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      uint32_t todo = 0;
+#pragma unroll
+      for (int j = 0; j < kPUJ; ++j)
+        if (ej[j] != kNoAdapter) todo |= 1u << j;
+      auto next_e = [&]() -> int {
+        int cand = kNoAdapter;
+#pragma unroll
+        for (int j = 0; j < kPUJ; ++j)
+          if ((todo >> j) & 1u) cand = min(cand, ej[j]);
+        const int e = wave_min_int(cand);
+#pragma unroll
+        for (int j = 0; j < kPUJ; ++j)
+          if (ej[j] == e) todo &= ~(1u << j);
+        return e;
+      };
+      int beA[kPNB], beB[kPNB];
+      uint4 bA[kPNB][2], bB[kPNB][2];
+      auto collect = [&](int (&be)[kPNB], uint4 (&bo)[kPNB][2]) -> bool {
+#pragma unroll
+        for (int i = 0; i < kPNB; ++i) be[i] = next_e();
+#pragma unroll
+        for (int i = 0; i < kPNB; ++i) {
+          const int e = be[i] == kNoAdapter ? 0 : be[i];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) bo[i][g] = ld16(Bm + ((size_t)e * pd.d_out + brow_g[g]) * a.r + cc);
+        }
+        return be[0] != kNoAdapter;
+      };
+      auto apply = [&](const int (&be)[kPNB], const uint4 (&bo)[kPNB][2]) {
+#pragma unroll
+        for (int i = 0; i < kPNB; ++i) {
+          if (be[i] == kNoAdapter) continue;
+          float v[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) v[m] = 0.f;
+#pragma unroll
+          for (int j = 0; j < kPUJ; ++j)
+            if (ej[j] == be[i]) {
+#pragma unroll
+              for (int m = 0; m < 4; ++m) v[m] += uj[j][0][m], v[4 + m] += uj[j][1][m];
+            }
+          uint4 hi, lo;
+          split_hi_lo(v, hi, lo);
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const uint4 b = sel4(cok, bo[i][g]);
+            acc[f][g] = mfma32(hi, b, acc[f][g]);
+            acc[f][g] = mfma32(lo, b, acc[f][g]);
+          }
+        }
+      };
+      bool haveA = collect(beA, bA);
+      while (haveA) {
+        const bool haveB = collect(beB, bB);
+        apply(beA, bA);
+        if (!haveB) break;
+        haveA = collect(beA, bA);
+        apply(beB, bB);
+      }
+    }
+  }
+}
+
 // Blocks b and b + 8 share an XCD (b % 8).  The n_tok_tiles token tiles of a
 // row tile are blocks q*8 + x for consecutive q, so they run on one XCD at
 // about the same time and all but the first read of the W0 tile hit its L2.
@@ -207,171 +380,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
     }
   });
 
-  if (S > 1) {
-    // split-K: every split publishes its fp32 partial tile with device-scope
-    // stores (chunk c of lane l at ((wave*16 + c)*64 + l)*16 bytes); the last
-    // to arrive sums all S in split order, so the result does not depend on
-    // which split finishes last, and then applies the adapters
-    __shared__ int s_last;
-    const size_t tile_floats = (size_t)kPB * kPB;
-    const size_t slot0 = ((size_t)tile * n_tok_tiles + tt) * S;
-    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-        a.partial + slot0 * tile_floats, 0, (int)(S * tile_floats * sizeof(float)), 0x00020000);
-    constexpr int kSc1 = 1 << 4;
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int c = (f * 2 + g) * 4 + v4;
-          const f32x4_t val = {acc[f][g][4 * v4], acc[f][g][4 * v4 + 1], acc[f][g][4 * v4 + 2], acc[f][g][4 * v4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), pr,
-                                                 (uint32_t)((split * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1);
-        }
-    __builtin_amdgcn_s_waitcnt(0);  // the partial is in memory before the arrival is counted
-    __syncthreads();
-    int* cnt = a.counters + (size_t)tile * n_tok_tiles + tt;
-    if (tid == 0) s_last = atomicAdd(cnt, 1) == S - 1;
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    f32x16_t tot[2][2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tot[f][g][v] = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-      if (sp == split) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int g = 0; g < 2; ++g) tot[f][g] += acc[f][g];
-        continue;
-      }
-      f32x4_t pv[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c)
-        pv[c] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                    pr, (uint32_t)((sp * tile_floats + ((wave * 16 + c) * 64 + lane) * 4) * 4), 0, kSc1));
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tot[f][g][4 * v4 + e] += pv[(f * 2 + g) * 4 + v4][e];
-    }
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) acc[f][g] = tot[f][g];
-  }
-
-  // Expand: per 32-token block, the distinct adapters its tokens chose, in
-  // ascending order (found with wave minimums, no memory round trip); a lane
-  // holds its token's gated u for every slot, so an adapter's token operand is
-  // picked in registers (slots naming the same adapter summed in slot order)
-  // and split into bf16 (hi, lo).  B rows go out a batch of kPNB adapters ahead
-  // of the batch whose MFMAs run.
-  if (a.k > 0) {
-    const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
-    const float* ub = a.u + (size_t)proj * a.T * a.k * a.r;
-    const int kk = a.k;
-    int brow_g[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) brow_g[g] = min(row0 + wn * 64 + g * 32 + lr, pd.d_out - 1);
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int pos = i0 + wm * 64 + f * 32 + lr;
-      const bool tok_ok = pos < a.T;
-      const int t = token_at(a, min(pos, a.T - 1));
-      // slots in groups of kPUJ (a token naming one adapter in two groups
-      // gets its two terms from two passes)
-      for (int j0 = 0; j0 < kk; j0 += kPUJ)
-      for (int c0 = 0; c0 < a.r; c0 += 16) {
-        int ej[kPUJ];
-#pragma unroll
-        for (int j = 0; j < kPUJ; ++j) {
-          const int e = (j0 + j < kk && tok_ok) ? a.topk_idx[t * kk + j0 + j] : -1;
-          ej[j] = (e >= 0 && e < a.E) ? e : kNoAdapter;
-        }
-        const int c = c0 + kg * 8;
-        const bool cok = c < a.r;
-        const int cc = min(c, a.r - 8);
-        f32x4_t uj[kPUJ][2];
-#pragma unroll
-        for (int j = 0; j < kPUJ; ++j) {
-          const bool ok = ej[j] != kNoAdapter && cok;
-          const float* p = ub + (size_t)(t * kk + min(j0 + j, kk - 1)) * a.r + cc;
-          uj[j][0] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          uj[j][1] = ok ? *reinterpret_cast<const f32x4_t*>(p + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        uint32_t todo = 0;
-#pragma unroll
-        for (int j = 0; j < kPUJ; ++j)
-          if (ej[j] != kNoAdapter) todo |= 1u << j;
-        auto next_e = [&]() -> int {
-          int cand = kNoAdapter;
-#pragma unroll
-          for (int j = 0; j < kPUJ; ++j)
-            if ((todo >> j) & 1u) cand = min(cand, ej[j]);
-          const int e = wave_min_int(cand);
-#pragma unroll
-          for (int j = 0; j < kPUJ; ++j)
-            if (ej[j] == e) todo &= ~(1u << j);
-          return e;
-        };
-        int beA[kPNB], beB[kPNB];
-        uint4 bA[kPNB][2], bB[kPNB][2];
-        auto collect = [&](int (&be)[kPNB], uint4 (&bo)[kPNB][2]) -> bool {
-#pragma unroll
-          for (int i = 0; i < kPNB; ++i) be[i] = next_e();
-#pragma unroll
-          for (int i = 0; i < kPNB; ++i) {
-            const int e = be[i] == kNoAdapter ? 0 : be[i];
-#pragma unroll
-            for (int g = 0; g < 2; ++g) bo[i][g] = ld16(Bm + ((size_t)e * pd.d_out + brow_g[g]) * a.r + cc);
-          }
-          return be[0] != kNoAdapter;
-        };
-        auto apply = [&](const int (&be)[kPNB], const uint4 (&bo)[kPNB][2]) {
-#pragma unroll
-          for (int i = 0; i < kPNB; ++i) {
-            if (be[i] == kNoAdapter) continue;
-            float v[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) v[m] = 0.f;
-#pragma unroll
-            for (int j = 0; j < kPUJ; ++j)
-              if (ej[j] == be[i]) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) v[m] += uj[j][0][m], v[4 + m] += uj[j][1][m];
-              }
-            uint4 hi, lo;
-            split_hi_lo(v, hi, lo);
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-              const uint4 b = sel4(cok, bo[i][g]);
-              acc[f][g] = mfma32(hi, b, acc[f][g]);
-              acc[f][g] = mfma32(lo, b, acc[f][g]);
-            }
-          }
-        };
-        bool haveA = collect(beA, bA);
-        while (haveA) {
-          const bool haveB = collect(beB, bB);
-          apply(beA, bA);
-          if (!haveB) break;
-          haveA = collect(beA, bA);
-          apply(beB, bB);
-        }
-      }
-    }
-  }
+  if (S > 1 && !splitk_reduce(a, ((size_t)tile * n_tok_tiles + tt) * S, split, S,
+                              a.counters + (size_t)tile * n_tok_tiles + tt, acc))
+    return;
+  if (a.k > 0) expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
 
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
@@ -396,7 +408,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
 
 }  // namespace
 
-int prefill_group_blocks(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB - 1) / kPB); }
+int prefill_tile_rows(int T) { (void)T; return kPB; }
+// (row tile, token tile) units of one group's GEMM, the blocks of one K split
+int prefill_units(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB - 1) / kPB); }
+int prefill_group_blocks(int n_tiles, int T) { return prefill_units(n_tiles, T); }
 int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * E ? 1 : 4; }
 int prefill_shrink_units(int T, int E, int k) {
   const int nch = 16 * prefill_shrink_nct(T, E, k);

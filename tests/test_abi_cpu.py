@@ -267,3 +267,21 @@ def test_step_workspace_size():
     assert ten >= one and ten <= 8 * one
     assert L.rp_sgmm_step_workspace_size(arr, 0, 32, 8, 16, 2, rp.RP_BF16) == 0
     assert L.rp_sgmm_step_workspace_size(arr, 1, 32, 8, 12, 2, rp.RP_BF16) == 0
+
+
+@pytest.mark.parametrize("T,d_in,d_outs", [(200, 8200, [136]), (256, 11008, [4096]), (130, 12288, [256, 64])])
+def test_prefill_workspace_covers_split_k(T, d_in, d_outs):
+    """A single bf16 prefill group may split K: rp_sgmm_workspace_size covers its partial tiles,
+    and agrees with the step size of the same group."""
+    L = rp.lib()
+    E, r, k = 6, 16, 2
+    n = len(d_outs)
+    proj = (rp.RpProj * n)(*[rp.RpProj(FAKE, FAKE, FAKE, FAKE, d, d, 0, 0) for d in d_outs])
+    g = rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), n, 0, FAKE, d_in, d_in)
+    single = L.rp_sgmm_workspace_size(n, T, d_in, sum(d_outs), E, r, k, rp.RP_BF16)
+    step = L.rp_sgmm_step_workspace_size((rp.RpGroup * 1)(g), 1, T, E, r, k, rp.RP_BF16)
+    u_only = 65536 + ((n * T * k * r * 4 + 255) // 256) * 256
+    tiles = sum((d + 127) // 128 for d in d_outs)
+    partials = ((tiles + 7) // 8 * 8) * ((T + 127) // 128) * 2 * 128 * 128 * 4  # at least two splits
+    assert single >= u_only + partials
+    assert step >= u_only + partials

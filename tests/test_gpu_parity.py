@@ -286,9 +286,13 @@ def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     (130, 12288, [256, 64], 5, 32, 2),  # K split three ways, two projections
 ])
 def test_projection_prefill_split_k(T, d_in, d_outs, E, r, k):
-    """Long K on few row tiles: the bf16 prefill GEMM splits K and sums the partial tiles in split order."""
+    """Long K on few row tiles: the bf16 prefill GEMM splits K and sums the partial tiles in split order.
+
+    The workspace is exactly rp_sgmm_workspace_size bytes (it must cover the partial tiles)."""
     say("projection split-K", T, d_in, d_outs, E, r, k)
-    _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E)
+    n = rp.sgmm_workspace_size(len(d_outs), T, d_in, sum(d_outs), E, r, k, rp.RP_BF16)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E, ws=ws)
 
 
 @pytest.mark.parametrize("T,d_in,d_out,E,r,k,dt", [
