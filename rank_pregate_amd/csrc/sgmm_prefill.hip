@@ -28,6 +28,17 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   const SgmmArgs& a = ps.g[g];
   const int b = blockIdx.x - (g > 0 ? ps.shrink_end[g - 1] : 0);
   const int proj = b / ps.units, unit = b % ps.units;
+  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR >= 4 ? 1 : 2);  // K steps per load batch
+  if (NCT == 1) {
+    // small segments: block e takes segment e whole, chunk by chunk (no scan
+    // over the segment table to find its work)
+    const int n = a.seg_offsets[unit + 1] - a.seg_offsets[unit];
+    for (int c = 0; c * 16 < n; ++c) {
+      shrink_unit<MTR, NCT, 4, U>(a, proj, unit, c, red);
+      __syncthreads();  // `red` is read out before the next chunk reduces into it
+    }
+    return;
+  }
   if (threadIdx.x < 64) {
     int e, c;
     locate_chunk(a, unit, 16 * NCT, threadIdx.x, &e, &c);
@@ -35,7 +46,6 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   }
   __syncthreads();
   if (s_loc[0] < 0) return;
-  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR >= 4 ? 1 : 2);  // K steps per load batch
   shrink_unit<MTR, NCT, 4, U>(a, proj, s_loc[0], s_loc[1], red);
 }
 
@@ -414,8 +424,8 @@ int prefill_units(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB
 int prefill_group_blocks(int n_tiles, int T) { return prefill_units(n_tiles, T); }
 int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * E ? 1 : 4; }
 int prefill_shrink_units(int T, int E, int k) {
-  const int nch = 16 * prefill_shrink_nct(T, E, k);
-  return E + (T * k + nch - 1) / nch;
+  if (prefill_shrink_nct(T, E, k) == 1) return E;  // one block per segment
+  return E + (T * k + 63) / 64;
 }
 
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
