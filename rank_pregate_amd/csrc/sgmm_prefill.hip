@@ -255,6 +255,11 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
 // Blocks b and b + 8 share an XCD (b % 8).  The n_tok_tiles token tiles of a
 // row tile are blocks q*8 + x for consecutive q, so they run on one XCD at
 // about the same time and all but the first read of the W0 tile hit its L2.
+// FAST: every projection of the launch is in the tiled W0 order and every
+// d_in is a multiple of 32, so a stage never reaches past d_in (no clamps or
+// selects) and a wave's W0 block row is wave-uniform: its block offsets are
+// scalar arithmetic.
+template <bool FAST>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   // operand double buffers, reused for the output tile at the end
   __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * 2 * kPB * kPLd];
@@ -315,8 +320,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   // the end re-read the last one); columns past d_in are zeroed on the way to
   // LDS.  Stage j of the split is stage kb + j of K.
   uint4 ra[kPR][2], rb[kPR][2];
+  // FAST: block row of piece i is row0/16 + wave + 4i, the same for the wave
+  int rbw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) rbw[i] = __builtin_amdgcn_readfirstlane(min(row0 / 16 + wave + 4 * i, n_rb - 1));
+  const bf16_t* gA0[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) gA0[i] = gA[i] + lk[i];
+  const bf16_t* Wl = W0 + lane * 8;
   auto gload = [&](int slot, int j) {
     const int kt = kb + min(j, nk - 1);
+    if (FAST) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ra[slot][i] = ld16(gA0[i] + kt * kPK);
+        rb[slot][i] = ld16(Wl + w0_block_offset(rbw[i], kt, n_rb, nkb));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       ra[slot][i] = ld16(gA[i] + min(kt * kPK + lk[i], a.d_in - 8));
@@ -329,9 +350,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   auto lstore = [&](int slot, int buf, int j) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool ok = (kb + j) * kPK + lk[i] < a.d_in;
+      const bool ok = FAST || (kb + j) * kPK + lk[i] < a.d_in;
       *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(ok, ra[slot][i]);
-      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = pd.tiled ? rb[slot][i] : sel4(ok, rb[slot][i]);
+      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = (FAST || pd.tiled) ? rb[slot][i] : sel4(ok, rb[slot][i]);
     }
   };
 
@@ -443,7 +464,15 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  prefill_bf16<<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
+  bool fast = true;  // every projection tiled, every d_in a multiple of 32
+  for (int g = 0; g < ps.n_groups; ++g) {
+    fast = fast && ps.g[g].d_in % 32 == 0;
+    for (int p = 0; p < ps.g[g].n_proj; ++p) fast = fast && ps.g[g].proj[p].tiled;
+  }
+  if (fast)
+    prefill_bf16<true><<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
+  else
+    prefill_bf16<false><<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
   return hipGetLastError();
 }
 
