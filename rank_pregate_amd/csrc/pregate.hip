@@ -12,21 +12,30 @@ __global__ __launch_bounds__(NT) void pregate_kernel(PregateArgs a, RoutePlan p)
   route_tile<Tin, TT, NT>(a, blockIdx.x * TT, p, smem);
 }
 
+// Fewer tokens per tile while that still leaves tiles for every CU: a tile
+// reads the whole router weight, so small batches are spread wide.  The
+// summation order of a logit does not depend on the tile size.
+constexpr int kRouteFillTiles = 256;
+
+template <typename Tin, int NT>
+void launch_nt(const PregateArgs& a, const RoutePlan& p, hipStream_t s) {
+  const int TT = a.T <= kRouteFillTiles ? 1 : a.T <= 2 * kRouteFillTiles ? 2 : p.TT;
+  const size_t lds = sizeof(float) * route_lds_floats(p, a.E, TT);
+  if (TT == 1)
+    pregate_kernel<Tin, 1, NT><<<a.T, NT, lds, s>>>(a, p);
+  else if (TT == 2)
+    pregate_kernel<Tin, 2, NT><<<(a.T + 1) / 2, NT, lds, s>>>(a, p);
+  else
+    pregate_kernel<Tin, 4, NT><<<(a.T + 3) / 4, NT, lds, s>>>(a, p);
+}
+
 template <typename Tin>
 hipError_t launch_t(const PregateArgs& a, hipStream_t s) {
   const RoutePlan p = route_plan(a.E, a.d_in, (int)sizeof(Tin));
-  const size_t lds = sizeof(float) * route_lds_floats(p, a.E, p.TT);
-  if (p.NT == kRouteThreads) {
-    if (p.TT == 4)
-      pregate_kernel<Tin, 4, kRouteThreads><<<(a.T + 3) / 4, kRouteThreads, lds, s>>>(a, p);
-    else
-      pregate_kernel<Tin, 2, kRouteThreads><<<(a.T + 1) / 2, kRouteThreads, lds, s>>>(a, p);
-  } else {
-    if (p.TT == 4)
-      pregate_kernel<Tin, 4, kRouteThreadsWide><<<(a.T + 3) / 4, kRouteThreadsWide, lds, s>>>(a, p);
-    else
-      pregate_kernel<Tin, 2, kRouteThreadsWide><<<(a.T + 1) / 2, kRouteThreadsWide, lds, s>>>(a, p);
-  }
+  if (p.NT == kRouteThreads)
+    launch_nt<Tin, kRouteThreads>(a, p, s);
+  else
+    launch_nt<Tin, kRouteThreadsWide>(a, p, s);
   return hipGetLastError();
 }
 

@@ -151,6 +151,8 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   float* red = smem;
   float* lg = smem + (size_t)KR * TT * E;
 
+  // a one-token tile has registers to spare for a deeper load batch
+  constexpr int NB = TT == 1 ? 2 * kRouteNB : kRouteNB;
   float acc[TT][kRouteCB];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
@@ -166,20 +168,20 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
     const int ke8 = kb + max(0, ke - kb) / 8 * 8;  // full groups of 8; fp32 rows may end in a group of 4
     int k0 = kb;
     if (rp_.vec_cols && c0 + kRouteCB <= E) {
-      // batches of kRouteNB groups: every load of a batch is issued before its
+      // batches of NB groups: every load of a batch is issued before its
       // arithmetic, so a batch costs one memory round trip; the sums still run
       // over k in ascending order
-      for (; k0 + 8 * kRouteNB <= ke8; k0 += 8 * kRouteNB) {
-        typename Raw8<Tin>::type xq[kRouteNB][TT], wq[kRouteNB][8];
+      for (; k0 + 8 * NB <= ke8; k0 += 8 * NB) {
+        typename Raw8<Tin>::type xq[NB][TT], wq[NB][8];
 #pragma unroll
-        for (int b = 0; b < kRouteNB; ++b) {
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
           for (int t = 0; t < TT; ++t) xq[b][t] = Raw8<Tin>::fetch(xr[t] + k0 + 8 * b);
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) wq[b][kk] = Raw8<Tin>::fetch(Wg + (size_t)(k0 + 8 * b + kk) * E + c0);
         }
 #pragma unroll
-        for (int b = 0; b < kRouteNB; ++b) {
+        for (int b = 0; b < NB; ++b) {
           float xv[TT][8], wv[8][kRouteCB];
 #pragma unroll
           for (int t = 0; t < TT; ++t) Raw8<Tin>::unpack(xq[b][t], xv[t]);

@@ -53,9 +53,11 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
 // Stage 2, prefill: 128 tokens x 128 rows per workgroup, LDS-tiled MFMA GEMM.
 // ============================================================================
 constexpr int kPB = 128;       // tile edge (tokens and rows)
-constexpr int kPK = 32;        // K per LDS stage
+constexpr int kPK = 64;        // K per LDS stage
 constexpr int kPLd = kPK + 8;  // padded LDS row (elements)
-constexpr int kPR = 3;         // stages whose loads are in flight ahead of the math
+constexpr int kPR = 2;         // stages whose loads are in flight ahead of the math
+constexpr int kPP = kPB * kPK / 8 / 256;  // 16-byte pieces per thread, operand and stage
+constexpr int kPCB = kPK / 32;            // tiled W0 block columns per stage
 constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
 constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once
 constexpr int kNoAdapter = 0x7fffffff;
@@ -256,7 +258,7 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
 // row tile are blocks q*8 + x for consecutive q, so they run on one XCD at
 // about the same time and all but the first read of the W0 tile hit its L2.
 // FAST: every projection of the launch is in the tiled W0 order and every
-// d_in is a multiple of 32, so a stage never reaches past d_in (no clamps or
+// d_in is a multiple of kPK, so a stage never reaches past d_in (no clamps or
 // selects) and a wave's W0 block row is wave-uniform: its block offsets are
 // scalar arithmetic.
 template <bool FAST>
@@ -285,31 +287,34 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* W0 = static_cast<const bf16_t*>(pd.W0);
 
-  // global -> LDS: 512 16-byte chunks per operand tile, two per thread each
-  // A (tokens): chunk q -> token row q/4, columns 8*(q%4).  B (W0 rows):
-  // row-major the same; tiled, chunk q is lane q%64 of 16-row block q/64, which
-  // holds row 16*(q/64) + (q%64)%16, columns 8*((q%64)/16).
-  const bf16_t* gA[2];
-  const bf16_t* gB[2];
-  int lrow[2], lk[2], brow[2], bk[2], tblk[2];
+  // global -> LDS: kPP 16-byte pieces per thread and operand.  A (tokens):
+  // piece c -> token row c/(kPK/8), columns 8*(c%(kPK/8)).  B (W0 rows):
+  // row-major the same; tiled, piece c is lane c%64 of block c/64 = (row block
+  // (c/64)%8, block column (c/64)/8), which holds row 16*((c/64)%8) + (c%64)%16,
+  // columns 32*((c/64)/8) + 8*((c%64)/16).  Block c/64 = wave + 4i is uniform
+  // over a wave.
+  const bf16_t* gA[kPP];
+  const bf16_t* gB[kPP];
+  int lrow[kPP], lk[kPP], brow[kPP], bk[kPP], tblk[kPP];
   const int nkb = a.d_in / 32, n_rb = pd.d_out / 16;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kPP; ++i) {
     const int c = tid + i * 256;
-    lrow[i] = c >> 2;
-    lk[i] = (c & 3) * 8;
+    lrow[i] = c / (kPK / 8);
+    lk[i] = (c % (kPK / 8)) * 8;
     const int pos = min(i0 + lrow[i], a.T - 1);
-    gA[i] = x + (size_t)token_at(a, pos) * a.ld_x;
+    gA[i] = x + (size_t)token_at(a, pos) * a.ld_x + lk[i];
     if (pd.tiled) {
-      tblk[i] = min(row0 / 16 + c / 64, n_rb - 1);
-      brow[i] = (c / 64) * 16 + (c % 64) % 16;
-      bk[i] = ((c % 64) / 16) * 8;
+      const int blk = c / 64;
+      tblk[i] = min(row0 / 16 + blk % 8, n_rb - 1);
+      brow[i] = (blk % 8) * 16 + (c % 64) % 16;
+      bk[i] = (blk / 8) * 32 + ((c % 64) / 16) * 8;
       gB[i] = W0 + (c % 64) * 8;
     } else {
       brow[i] = lrow[i];
       bk[i] = lk[i];
       tblk[i] = 0;
-      gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in;
+      gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in + lk[i];
     }
   }
   const int nk_all = (a.d_in + kPK - 1) / kPK;
@@ -319,40 +324,39 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   // LDS double buffer one stage ahead.  Loads are never masked (stages past
   // the end re-read the last one); columns past d_in are zeroed on the way to
   // LDS.  Stage j of the split is stage kb + j of K.
-  uint4 ra[kPR][2], rb[kPR][2];
-  // FAST: block row of piece i is row0/16 + wave + 4i, the same for the wave
-  int rbw[2];
+  uint4 ra[kPR][kPP], rb[kPR][kPP];
+  // FAST: tiled block row of piece i, scalar
+  int rbw[kPP];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) rbw[i] = __builtin_amdgcn_readfirstlane(min(row0 / 16 + wave + 4 * i, n_rb - 1));
-  const bf16_t* gA0[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) gA0[i] = gA[i] + lk[i];
+  for (int i = 0; i < kPP; ++i)
+    rbw[i] = __builtin_amdgcn_readfirstlane(min(row0 / 16 + (wave + 4 * i) % 8, n_rb - 1));
   const bf16_t* Wl = W0 + lane * 8;
   auto gload = [&](int slot, int j) {
     const int kt = kb + min(j, nk - 1);
     if (FAST) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        ra[slot][i] = ld16(gA0[i] + kt * kPK);
-        rb[slot][i] = ld16(Wl + w0_block_offset(rbw[i], kt, n_rb, nkb));
+      for (int i = 0; i < kPP; ++i) {
+        ra[slot][i] = ld16(gA[i] + kt * kPK);
+        rb[slot][i] = ld16(Wl + w0_block_offset(rbw[i], kt * kPCB + (4 * i) / 8, n_rb, nkb));
       }
       return;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[slot][i] = ld16(gA[i] + min(kt * kPK + lk[i], a.d_in - 8));
+    for (int i = 0; i < kPP; ++i) {
+      ra[slot][i] = ld16(gA[i] + min(kt * kPK, a.d_in - 8 - lk[i]));
       if (pd.tiled)
-        rb[slot][i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt, nkb - 1), n_rb, nkb));  // d_in % 32 == 0: whole blocks
+        rb[slot][i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt * kPCB + bk[i] / 32, nkb - 1), n_rb, nkb));
       else
-        rb[slot][i] = ld16(gB[i] + min(kt * kPK + lk[i], a.d_in - 8));
+        rb[slot][i] = ld16(gB[i] + min(kt * kPK, a.d_in - 8 - lk[i]));
     }
   };
   auto lstore = [&](int slot, int buf, int j) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = FAST || (kb + j) * kPK + lk[i] < a.d_in;
-      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(ok, ra[slot][i]);
-      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = (FAST || pd.tiled) ? rb[slot][i] : sel4(ok, rb[slot][i]);
+    for (int i = 0; i < kPP; ++i) {
+      const bool oka = FAST || (kb + j) * kPK + lk[i] < a.d_in;
+      const bool okb = FAST || (kb + j) * kPK + bk[i] < a.d_in;
+      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(oka, ra[slot][i]);
+      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = sel4(okb, rb[slot][i]);
     }
   };
 
@@ -464,9 +468,9 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  bool fast = true;  // every projection tiled, every d_in a multiple of 32
+  bool fast = true;  // every projection tiled, every d_in a multiple of kPK
   for (int g = 0; g < ps.n_groups; ++g) {
-    fast = fast && ps.g[g].d_in % 32 == 0;
+    fast = fast && ps.g[g].d_in % kPK == 0;
     for (int p = 0; p < ps.g[g].n_proj; ++p) fast = fast && ps.g[g].proj[p].tiled;
   }
   if (fast)
