@@ -323,7 +323,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       while (g0 + ng < n_groups && ng < rp::kMaxGroups && !gs[g0 + ng].x_from_call) ++ng;
       rp::PrefillStep ps{};
       ps.n_groups = ng;
-      ps.n_tok_tiles = (int)((T + 127) / 128);
+      ps.n_tok_tiles = (int)((T + rp::prefill_tile_tokens((int)T) - 1) / rp::prefill_tile_tokens((int)T));
       ps.units = rp::prefill_shrink_units((int)T, (int)E, k);
       size_t off = rp::kWorkspaceCounterBytes;
       int shrink_blocks = 0, gemm_blocks = 0, counters = 0;

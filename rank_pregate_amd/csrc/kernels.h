@@ -162,7 +162,7 @@ hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s
 struct PrefillStep {
   SgmmArgs g[kMaxGroups];
   int n_groups;
-  int n_tok_tiles;                 // 128-token tiles
+  int n_tok_tiles;                 // token tiles of prefill_tile_tokens(T) tokens
   int units;                       // shrink units per projection (same for every group)
   int shrink_end[kMaxGroups];      // cumulative shrink blocks
   int block_end[kMaxGroups];       // cumulative GEMM blocks (multiples of 8)
@@ -181,6 +181,7 @@ size_t prefill_u_bytes(int n_proj, int T, int r, int k);  // one group's gated u
 int prefill_group_blocks(int n_tiles, int T);  // GEMM blocks of one group (one K split)
 int prefill_units(int n_tiles, int T);         // (row tile, token tile) units of one group
 int prefill_tile_rows(int T);                  // output rows per GEMM tile
+int prefill_tile_tokens(int T);                // tokens per GEMM tile
 int prefill_shrink_units(int T, int E, int k);  // shrink units per projection
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,

@@ -197,8 +197,9 @@ int prefill_splits(int d_in, int n_tiles, int T, int n_cu) {
   if (prefill_units(n_tiles, T) >= 2 * n_cu) return 1;
   return prefill_max_splits(d_in);
 }
-size_t prefill_partial_bytes(int n_tiles, int T, int S) {  // a tile's partial: 16384 fp32 in either tiling
-  return S > 1 ? align256((size_t)prefill_units(n_tiles, T) * S * 16384 * sizeof(float)) : 0;
+size_t prefill_partial_bytes(int n_tiles, int T, int S) {  // a tile's partial: its fp32 outputs
+  const size_t tile_floats = (size_t)prefill_tile_tokens(T) * prefill_tile_rows(T);
+  return S > 1 ? align256((size_t)prefill_units(n_tiles, T) * S * tile_floats * sizeof(float)) : 0;
 }
 
 size_t prefill_u_bytes(int n_proj, int T, int r, int k) {

@@ -6,6 +6,8 @@
 // With top-1 the tokens are visited in segment order, so a tile meets one or
 // two adapters.  The intermediates come from a separate shrink launch, one
 // workgroup per (projection, chunk of 64 pairs of a segment).
+#include <cstdlib>
+
 #include "sgmm_common.h"
 
 namespace rp {
@@ -56,8 +58,8 @@ constexpr int kPB = 128;       // tile edge (tokens and rows)
 constexpr int kPK = 64;        // K per LDS stage
 constexpr int kPLd = kPK + 8;  // padded LDS row (elements)
 constexpr int kPR = 2;         // stages whose loads are in flight ahead of the math
-constexpr int kPP = kPB * kPK / 8 / 256;  // 16-byte pieces per thread, operand and stage
-constexpr int kPCB = kPK / 32;            // tiled W0 block columns per stage
+constexpr int kPCB = kPK / 32;  // tiled W0 block columns per stage
+constexpr int kPBigT = 1024;    // from this many tokens, 256-token tiles of eight waves
 constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
 constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once
 constexpr int kNoAdapter = 0x7fffffff;
@@ -81,17 +83,18 @@ __device__ __forceinline__ int wave_min_int(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Split-K hand-over of a 4-wave GEMM block whose accumulators are acc[2][2]
+// Split-K hand-over of an NW-wave GEMM block whose accumulators are acc[2][2]
 // (64 floats a lane): every split publishes its fp32 partial tile with
 // device-scope stores (chunk c of lane l at ((wave*16 + c)*64 + l)*16 bytes),
 // counts its arrival, and the last to arrive sums all S in split order (the
 // result does not depend on which finishes last).  Returns false in the splits
 // that are not last.  `slot0` numbers the tile's first partial.
+template <int NW>
 __device__ __forceinline__ bool splitk_reduce(const SgmmArgs& a, size_t slot0, int split, int S, int* cnt,
                                               f32x16_t (&acc)[2][2]) {
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr size_t tile_floats = 4 * 64 * 64;
+  constexpr size_t tile_floats = NW * 64 * 64;
   const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
       a.partial + slot0 * tile_floats, 0, (int)(S * tile_floats * sizeof(float)), 0x00020000);
   constexpr int kSc1 = 1 << 4;
@@ -261,12 +264,18 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
 // d_in is a multiple of kPK, so a stage never reaches past d_in (no clamps or
 // selects) and a wave's W0 block row is wave-uniform: its block offsets are
 // scalar arithmetic.
-template <bool FAST>
-__global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
+// BM: tokens per tile, 128 (four waves, two blocks a CU) or 256 (eight waves,
+// one block a CU; each W0 byte fetched serves twice the tokens).  Waves are
+// BM/64 x 2 tiles of 64 tokens x 64 rows.
+template <bool FAST, int BM>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(PrefillStep ps) {
+  constexpr int NT = 2 * BM, NW = NT / 64;
+  constexpr int kPPA = BM * kPK / 8 / NT;   // 16-byte pieces per thread and stage: A
+  constexpr int kPPB = kPB * kPK / 8 / NT;  // and B
   // operand double buffers, reused for the output tile at the end
-  __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * 2 * kPB * kPLd];
-  auto As = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p);
-  auto Bs = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p + 2 * kPB * kPLd);
+  __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * (BM + kPB) * kPLd];
+  auto As = reinterpret_cast<bf16_t(*)[BM][kPLd]>(smem_p);
+  auto Bs = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p + 2 * BM * kPLd);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = group_of_block(ps.block_end, ps.n_groups, blockIdx.x);
@@ -283,27 +292,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   const int proj = proj_of_tile(a, tile);
   const ProjDesc pd = proj_at(a, proj);
   const int row0 = (tile - pd.tile_begin) * kPB;
-  const int i0 = tt * kPB;  // position in token order
+  const int i0 = tt * BM;  // position in token order
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* W0 = static_cast<const bf16_t*>(pd.W0);
 
-  // global -> LDS: kPP 16-byte pieces per thread and operand.  A (tokens):
-  // piece c -> token row c/(kPK/8), columns 8*(c%(kPK/8)).  B (W0 rows):
-  // row-major the same; tiled, piece c is lane c%64 of block c/64 = (row block
-  // (c/64)%8, block column (c/64)/8), which holds row 16*((c/64)%8) + (c%64)%16,
-  // columns 32*((c/64)/8) + 8*((c%64)/16).  Block c/64 = wave + 4i is uniform
-  // over a wave.
-  const bf16_t* gA[kPP];
-  const bf16_t* gB[kPP];
-  int lrow[kPP], lk[kPP], brow[kPP], bk[kPP], tblk[kPP];
+  // global -> LDS, 16-byte pieces.  A (tokens): piece c -> token row
+  // c/(kPK/8), columns 8*(c%(kPK/8)).  B (W0 rows): row-major the same; tiled,
+  // piece c is lane c%64 of block c/64 = (row block (c/64)%8, block column
+  // (c/64)/8), which holds row 16*((c/64)%8) + (c%64)%16, columns
+  // 32*((c/64)/8) + 8*((c%64)/16).  Block c/64 = wave + NW*i is uniform over a
+  // wave.
+  const bf16_t* gA[kPPA];
+  const bf16_t* gB[kPPB];
+  int lrow[kPPA], lk[kPPA], brow[kPPB], bk[kPPB], tblk[kPPB];
   const int nkb = a.d_in / 32, n_rb = pd.d_out / 16;
 #pragma unroll
-  for (int i = 0; i < kPP; ++i) {
-    const int c = tid + i * 256;
+  for (int i = 0; i < kPPA; ++i) {
+    const int c = tid + i * NT;
     lrow[i] = c / (kPK / 8);
     lk[i] = (c % (kPK / 8)) * 8;
     const int pos = min(i0 + lrow[i], a.T - 1);
     gA[i] = x + (size_t)token_at(a, pos) * a.ld_x + lk[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kPPB; ++i) {
+    const int c = tid + i * NT;
     if (pd.tiled) {
       const int blk = c / 64;
       tblk[i] = min(row0 / 16 + blk % 8, n_rb - 1);
@@ -311,10 +324,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
       bk[i] = (blk / 8) * 32 + ((c % 64) / 16) * 8;
       gB[i] = W0 + (c % 64) * 8;
     } else {
-      brow[i] = lrow[i];
-      bk[i] = lk[i];
+      brow[i] = c / (kPK / 8);
+      bk[i] = (c % (kPK / 8)) * 8;
       tblk[i] = 0;
-      gB[i] = W0 + (size_t)min(row0 + lrow[i], pd.d_out - 1) * a.d_in + lk[i];
+      gB[i] = W0 + (size_t)min(row0 + brow[i], pd.d_out - 1) * a.d_in + bk[i];
     }
   }
   const int nk_all = (a.d_in + kPK - 1) / kPK;
@@ -324,43 +337,46 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   // LDS double buffer one stage ahead.  Loads are never masked (stages past
   // the end re-read the last one); columns past d_in are zeroed on the way to
   // LDS.  Stage j of the split is stage kb + j of K.
-  uint4 ra[kPR][kPP], rb[kPR][kPP];
+  uint4 ra[kPR][kPPA], rb[kPR][kPPB];
   // FAST: tiled block row of piece i, scalar
-  int rbw[kPP];
+  int rbw[kPPB];
 #pragma unroll
-  for (int i = 0; i < kPP; ++i)
-    rbw[i] = __builtin_amdgcn_readfirstlane(min(row0 / 16 + (wave + 4 * i) % 8, n_rb - 1));
+  for (int i = 0; i < kPPB; ++i)
+    rbw[i] = __builtin_amdgcn_readfirstlane(min(row0 / 16 + (wave + NW * i) % 8, n_rb - 1));
   const bf16_t* Wl = W0 + lane * 8;
   auto gload = [&](int slot, int j) {
     const int kt = kb + min(j, nk - 1);
     if (FAST) {
 #pragma unroll
-      for (int i = 0; i < kPP; ++i) {
-        ra[slot][i] = ld16(gA[i] + kt * kPK);
-        rb[slot][i] = ld16(Wl + w0_block_offset(rbw[i], kt * kPCB + (4 * i) / 8, n_rb, nkb));
-      }
+      for (int i = 0; i < kPPA; ++i) ra[slot][i] = ld16(gA[i] + kt * kPK);
+#pragma unroll
+      for (int i = 0; i < kPPB; ++i) rb[slot][i] = ld16(Wl + w0_block_offset(rbw[i], kt * kPCB + NW * i / 8, n_rb, nkb));
       return;
     }
 #pragma unroll
-    for (int i = 0; i < kPP; ++i) {
-      ra[slot][i] = ld16(gA[i] + min(kt * kPK, a.d_in - 8 - lk[i]));
+    for (int i = 0; i < kPPA; ++i) ra[slot][i] = ld16(gA[i] + min(kt * kPK, a.d_in - 8 - lk[i]));
+#pragma unroll
+    for (int i = 0; i < kPPB; ++i) {
       if (pd.tiled)
         rb[slot][i] = ld16(gB[i] + w0_block_offset(tblk[i], min(kt * kPCB + bk[i] / 32, nkb - 1), n_rb, nkb));
       else
-        rb[slot][i] = ld16(gB[i] + min(kt * kPK, a.d_in - 8 - lk[i]));
+        rb[slot][i] = ld16(gB[i] + min(kt * kPK, a.d_in - 8 - bk[i]));
     }
   };
   auto lstore = [&](int slot, int buf, int j) {
 #pragma unroll
-    for (int i = 0; i < kPP; ++i) {
-      const bool oka = FAST || (kb + j) * kPK + lk[i] < a.d_in;
-      const bool okb = FAST || (kb + j) * kPK + bk[i] < a.d_in;
-      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(oka, ra[slot][i]);
-      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = sel4(okb, rb[slot][i]);
+    for (int i = 0; i < kPPA; ++i) {
+      const bool ok = FAST || (kb + j) * kPK + lk[i] < a.d_in;
+      *reinterpret_cast<uint4*>(&As[buf][lrow[i]][lk[i]]) = sel4(ok, ra[slot][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kPPB; ++i) {
+      const bool ok = FAST || (kb + j) * kPK + bk[i] < a.d_in;
+      *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bk[i]]) = sel4(ok, rb[slot][i]);
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;  // wave tile: tokens wm*64.., rows wn*64..
+  const int wm = wave % (BM / 64), wn = wave / (BM / 64);  // wave tile: tokens wm*64.., rows wn*64..
   const int lr = lane & 31, kg = lane >> 5;
   f32x16_t acc[2][2];
 #pragma unroll
@@ -369,21 +385,25 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.f;
+  // MFMA fragments, double-buffered: those of the next 16 columns of the
+  // stage are read from LDS while the MFMAs of the current ones run
+  uint4 fa[2][2], fb[2][2];
+  auto fragload = [&](int buf, int kk, int p) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) fa[p][f] = *reinterpret_cast<const uint4*>(&As[buf][wm * 64 + f * 32 + lr][kk + kg * 8]);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) fb[p][g] = *reinterpret_cast<const uint4*>(&Bs[buf][wn * 64 + g * 32 + lr][kk + kg * 8]);
+  };
   auto compute = [&](int cur) {
-#pragma unroll
-    for (int kk = 0; kk < kPK; kk += 16) {
-      uint4 af[2], bfr[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-        af[f] = *reinterpret_cast<const uint4*>(&As[cur][wm * 64 + f * 32 + lr][kk + kg * 8]);
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-        bfr[g] = *reinterpret_cast<const uint4*>(&Bs[cur][wn * 64 + g * 32 + lr][kk + kg * 8]);
+    fragload(cur, 0, 0);
+    static_for<0, kPK / 16>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      if (q + 1 < kPK / 16) fragload(cur, (q + 1) * 16, (q + 1) & 1);
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) acc[f][g] = mfma32(af[f], bfr[g], acc[f][g]);
-    }
+        for (int g = 0; g < 2; ++g) acc[f][g] = mfma32(fa[q & 1][f], fb[q & 1][g], acc[f][g]);
+    });
   };
 
   static_for<0, kPR>([&](auto I) { gload(decltype(I)::value, decltype(I)::value); });
@@ -395,11 +415,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
     static_for<0, kPR>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int kt = kt0 + i;
-      __builtin_amdgcn_sched_barrier(0);
       compute(kt & 1);
-      __builtin_amdgcn_sched_barrier(0);
       gload(i, kt + kPR);
-      __builtin_amdgcn_sched_barrier(0);
       lstore((i + 1) % kPR, (kt + 1) & 1, kt + 1);
       __syncthreads();
     });
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
     }
   });
 
-  if (S > 1 && !splitk_reduce(a, ((size_t)tile * n_tok_tiles + tt) * S, split, S,
+  if (S > 1 && !splitk_reduce<NW>(a, ((size_t)tile * n_tok_tiles + tt) * S, split, S,
                               a.counters + (size_t)tile * n_tok_tiles + tt, acc))
     return;
   if (a.k > 0) expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
@@ -423,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
   bf16_t* ys = smem_p;
-  static_assert(2 * 2 * kPB * kPLd >= kPB * kPB, "output tile must fit the operand buffers");
+  static_assert(2 * (BM + kPB) * kPLd >= BM * kPB, "output tile must fit the operand buffers");
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -433,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
         ys[(wm * 64 + f * 32 + 8 * (v >> 2) + 4 * kg + (v & 3)) * kPB + wn * 64 + g * 32 + lr] = f32_to_bf16(acc[f][g][v]);
   __syncthreads();
   bf16_t* y = static_cast<bf16_t*>(pd.y);
-  for (int c = tid; c < kPB * (kPB / 8); c += 256) {
+  for (int c = tid; c < BM * (kPB / 8); c += NT) {
     const int tl = c / (kPB / 8), r8 = (c % (kPB / 8)) * 8;
     const int pos = i0 + tl;
     if (pos < a.T && row0 + r8 < pd.d_out)
@@ -444,8 +461,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(PrefillStep ps) {
 }  // namespace
 
 int prefill_tile_rows(int T) { (void)T; return kPB; }
+int prefill_tile_tokens(int T) {
+  if (const char* env = std::getenv("RP_PREFILL_TILE_TOKENS")) {  // tuning override
+    const int v = std::atoi(env);
+    if (v == 128 || v == 256) return v;
+  }
+  return T >= kPBigT ? 256 : 128;
+}
 // (row tile, token tile) units of one group's GEMM, the blocks of one K split
-int prefill_units(int n_tiles, int T) { return (n_tiles + 7) / 8 * 8 * ((T + kPB - 1) / kPB); }
+int prefill_units(int n_tiles, int T) {
+  const int bm = prefill_tile_tokens(T);
+  return (n_tiles + 7) / 8 * 8 * ((T + bm - 1) / bm);
+}
 int prefill_group_blocks(int n_tiles, int T) { return prefill_units(n_tiles, T); }
 int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * E ? 1 : 4; }
 int prefill_shrink_units(int T, int E, int k) {
@@ -473,10 +500,20 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
     fast = fast && ps.g[g].d_in % kPK == 0;
     for (int p = 0; p < ps.g[g].n_proj; ++p) fast = fast && ps.g[g].proj[p].tiled;
   }
-  if (fast)
-    prefill_bf16<true><<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
-  else
-    prefill_bf16<false><<<ps.block_end[ps.n_groups - 1], 256, 0, s>>>(ps);
+  const dim3 grid(ps.block_end[ps.n_groups - 1]);
+  if (ps.n_tok_tiles != (a0.T + prefill_tile_tokens(a0.T) - 1) / prefill_tile_tokens(a0.T))
+    return hipErrorInvalidValue;  // token tiles planned for another tile size
+  if (prefill_tile_tokens(a0.T) == 256) {
+    if (fast)
+      prefill_bf16<true, 256><<<grid, 512, 0, s>>>(ps);
+    else
+      prefill_bf16<false, 256><<<grid, 512, 0, s>>>(ps);
+  } else {
+    if (fast)
+      prefill_bf16<true, 128><<<grid, 256, 0, s>>>(ps);
+    else
+      prefill_bf16<false, 128><<<grid, 256, 0, s>>>(ps);
+  }
   return hipGetLastError();
 }
 
@@ -485,7 +522,7 @@ hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s
   ps.g[0] = a;
   ps.g[0].n_tiles = plan.n_tiles;
   ps.n_groups = 1;
-  ps.n_tok_tiles = (a.T + kPB - 1) / kPB;
+  ps.n_tok_tiles = (a.T + prefill_tile_tokens(a.T) - 1) / prefill_tile_tokens(a.T);
   ps.units = prefill_shrink_units(a.T, a.E, a.k);
   ps.shrink_end[0] = ps.units * a.n_proj;
   ps.block_end[0] = prefill_group_blocks(plan.n_tiles, a.T);

@@ -269,7 +269,8 @@ def test_step_workspace_size():
     assert L.rp_sgmm_step_workspace_size(arr, 1, 32, 8, 12, 2, rp.RP_BF16) == 0
 
 
-@pytest.mark.parametrize("T,d_in,d_outs", [(200, 8200, [136]), (256, 11008, [4096]), (130, 12288, [256, 64])])
+@pytest.mark.parametrize("T,d_in,d_outs", [(200, 8200, [136]), (256, 11008, [4096]), (130, 12288, [256, 64]),
+                                           (1100, 12288, [128])])
 def test_prefill_workspace_covers_split_k(T, d_in, d_outs):
     """A single bf16 prefill group may split K: rp_sgmm_workspace_size covers its partial tiles,
     and agrees with the step size of the same group."""

@@ -275,6 +275,7 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
     (257, 256, [136], 7, 64, 1),       # first prefill size, ragged
     (300, 264, [128, 40], 12, 128, 2),  # prefill, k=2, r=128
     (1000, 512, [512], 32, 64, 1),
+    (1100, 256, [200], 9, 16, 2),      # 256-token tiles of eight waves, ragged T and d_out
 ])
 def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     say("projection", dt, T, d_in, d_outs, E, r, k)
@@ -284,6 +285,7 @@ def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
 @pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
     (200, 8200, [136], 6, 16, 2),       # K split two ways, ragged last stage and tile
     (130, 12288, [256, 64], 5, 32, 2),  # K split three ways, two projections
+    (1030, 12288, [128], 6, 16, 2),     # 256-token tiles, K split three ways
 ])
 def test_projection_prefill_split_k(T, d_in, d_outs, E, r, k):
     """Long K on few row tiles: the bf16 prefill GEMM splits K and sums the partial tiles in split order.
@@ -319,6 +321,8 @@ def test_projection_duplicate_adapters(T, d_in, d_out, E, r, k, dt):
     (48, 4096, [4096], 8, 16, 2),
     (100, 128, [64, 64, 64], 9, 32, 3),  # tiled order through the prefill path
     (300, 256, [208, 48], 12, 64, 1),
+    (1024, 256, [128, 64], 12, 32, 2),  # 256-token tiles, every stage whole (no clamps)
+    (1040, 96, [208], 5, 16, 1),        # 256-token tiles, last stage half past d_in
 ])
 def test_projection_tiled_w0(T, d_in, d_outs, E, r, k):
     say("projection tiled", T, d_in, d_outs, E, r, k)
