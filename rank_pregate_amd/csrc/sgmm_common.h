@@ -171,24 +171,40 @@ __device__ __forceinline__ void shrink_unit(const SgmmArgs& a, int proj, int e, 
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = sb; s < se; s += U) {
-    uint4 av[U][MTR], bv[U][NCT];
+  // batches of U K steps, two in flight: the loads of the next batch go out
+  // before the MFMAs of the current one (batches and steps still summed in
+  // ascending K)
+  uint4 av[2][U][MTR], bv[2][U][NCT];
+  auto load = [&](int buf, int s) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = (s + u) * 32 + kg * 8;
       const bool ok = (s + u < se) && (k < a.d_in);
       const int kc = min(k, a.d_in - 8);
 #pragma unroll
-      for (int mt = 0; mt < MTR; ++mt) av[u][mt] = sel4(ok && aok[mt], ld16(ap[mt] + kc));
+      for (int mt = 0; mt < MTR; ++mt) av[buf][u][mt] = sel4(ok && aok[mt], ld16(ap[mt] + kc));
 #pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) bv[u][nt] = sel4(ok, ld16(xp[nt] + kc));
+      for (int nt = 0; nt < NCT; ++nt) bv[buf][u][nt] = sel4(ok, ld16(xp[nt] + kc));
     }
+  };
+  auto math = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) acc[mt][nt] = mfma16(av[u][mt], bv[u][nt], acc[mt][nt]);
+        for (int nt = 0; nt < NCT; ++nt) acc[mt][nt] = mfma16(av[buf][u][mt], bv[buf][u][nt], acc[mt][nt]);
+  };
+  int s = sb;
+  if (s < se) load(0, s);
+  while (s < se) {
+    if (s + U < se) load(1, s + U);
+    math(0);
+    s += U;
+    if (s >= se) break;
+    if (s + U < se) load(0, s + U);
+    math(1);
+    s += U;
   }
 
   // fixed-order sum over waves (wave 0 first), accumulated in LDS

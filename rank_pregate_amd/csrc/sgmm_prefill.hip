@@ -20,15 +20,34 @@ __device__ __forceinline__ int group_of_block(const int* end, int n, int b) {
   return g;
 }
 
+// Shrink blocks go to the groups in order of decreasing d_in (ties: lower
+// group first), so the longest blocks are dispatched first and the launch
+// does not end on them.  Returns the group; *b = the block's index in it.
+__device__ __forceinline__ int shrink_group_of_block(const PrefillStep& ps, int bid, int* b) {
+  uint32_t done = 0;
+  int g = 0;
+  for (int n = 0; n < ps.n_groups; ++n) {
+    g = -1;
+    for (int h = 0; h < ps.n_groups; ++h)
+      if (!((done >> h) & 1u) && (g < 0 || ps.g[h].d_in > ps.g[g].d_in)) g = h;
+    done |= 1u << g;
+    const int cnt = ps.shrink_end[g] - (g > 0 ? ps.shrink_end[g - 1] : 0);
+    if (bid < cnt) break;
+    bid -= cnt;
+  }
+  *b = bid;
+  return g;
+}
+
 // One shrink block: a chunk of 16*NCT pairs of one segment.  Small segments
 // (a few tokens each) take NCT = 1 and keep more K steps of A_e in flight.
 template <int MTR, int NCT>
 __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   __shared__ __attribute__((aligned(16))) float red[MTR * NCT * 4 * 64];
   __shared__ int s_loc[2];
-  const int g = group_of_block(ps.shrink_end, ps.n_groups, blockIdx.x);
+  int b;
+  const int g = shrink_group_of_block(ps, blockIdx.x, &b);
   const SgmmArgs& a = ps.g[g];
-  const int b = blockIdx.x - (g > 0 ? ps.shrink_end[g - 1] : 0);
   const int proj = b / ps.units, unit = b % ps.units;
   constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR >= 4 ? 1 : 2);  // K steps per load batch
   if (NCT == 1) {
@@ -59,7 +78,7 @@ constexpr int kPK = 64;        // K per LDS stage
 constexpr int kPLd = kPK + 8;  // padded LDS row (elements)
 constexpr int kPR = 2;         // stages whose loads are in flight ahead of the math
 constexpr int kPCB = kPK / 32;  // tiled W0 block columns per stage
-constexpr int kPBigT = 1024;    // from this many tokens, 256-token tiles of eight waves
+constexpr int kPBigT = 256;     // from this many tokens, 256-token tiles of eight waves
 constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
 constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once
 constexpr int kNoAdapter = 0x7fffffff;
