@@ -1,11 +1,12 @@
-// Prefill-shaped fused SGMM (T > 256 tokens): the base projection is a dense
-// GEMM (bf16 MFMA, 128 tokens x 128 rows per workgroup, LDS-tiled), so it is
-// bound by matrix throughput rather than HBM.  The adapter deltas (AdaFuse
-// technical summary §2.B) are folded in as extra MFMA steps: for every adapter
-// the tile's tokens chose, B_e's rows times the gathered rank-r intermediates.
-// With top-1 the tokens are visited in segment order, so a tile meets one or
-// two adapters.  The intermediates come from a separate shrink launch, one
-// workgroup per (projection, chunk of 64 pairs of a segment).
+// Prefill-shaped fused SGMM (bf16, T > 64 tokens): the base projection is a
+// dense GEMM (bf16 MFMA, 128 or 256 tokens x 128 rows per workgroup,
+// LDS-tiled), bound by matrix throughput at thousands of tokens.  The adapter
+// deltas (AdaFuse technical summary §2.B) are folded in as extra MFMA steps:
+// for every adapter the tile's tokens chose, B_e's rows times the gathered
+// rank-r intermediates.  With top-1 the tokens are visited in segment order,
+// so a tile meets one or two adapters.  The intermediates come from a separate
+// shrink launch, one workgroup per (projection, segment) when segments hold a
+// few tokens, else per (projection, chunk of 64 pairs of a segment).
 #include <cstdlib>
 
 #include "sgmm_common.h"
@@ -71,9 +72,9 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
 }
 
 // ============================================================================
-// Stage 2, prefill: 128 tokens x 128 rows per workgroup, LDS-tiled MFMA GEMM.
+// Stage 2, prefill: 128 or 256 tokens x 128 rows per workgroup, LDS-tiled MFMA GEMM.
 // ============================================================================
-constexpr int kPB = 128;       // tile edge (tokens and rows)
+constexpr int kPB = 128;       // W0 rows per tile
 constexpr int kPK = 64;        // K per LDS stage
 constexpr int kPLd = kPK + 8;  // padded LDS row (elements)
 constexpr int kPR = 2;         // stages whose loads are in flight ahead of the math
