@@ -117,7 +117,11 @@ def test_pregate_workload(name):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("T,d,E,k", [(7, 64, 6, 2), (65, 128, 200, 3), (16, 256, 1024, 8), (3, 32, 1, 1)])
+@pytest.mark.parametrize("T,d,E,k", [(7, 64, 6, 2), (65, 128, 200, 3), (16, 256, 1024, 8), (3, 32, 1, 1),
+                                     (300, 64, 200, 3),   # two-token tiles, 512 threads
+                                     (600, 64, 100, 2),   # four-token tiles, 512 threads
+                                     (400, 32, 8, 1),     # two-token tiles, 128 threads
+                                     (700, 32, 16, 2)])   # four-token tiles, 128 threads
 def test_pregate_exact_ties(dt, T, d, E, k):
     """Integer inputs give exact logits; duplicated router columns tie exactly -> lowest index."""
     say("pregate ties", dt, T, d, E, k)
@@ -134,6 +138,23 @@ def test_pregate_exact_ties(dt, T, d, E, k):
     idx_ref, gate_ref, _ = oracle.pregate(x.astype(np.float64), Wg.astype(np.float64), k)
     np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
     assert np.abs(gate.cpu().numpy() - gate_ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("T", [1, 255, 256, 257, 512, 513, 1030])
+@pytest.mark.parametrize("E", [8, 300])
+def test_pregate_tile_sizes(T, E):
+    """Router tiles of one, two or four tokens (chosen from T) give logits within the fp32
+    accumulation bound and the oracle's top-k away from near ties."""
+    say("pregate tile sizes", T, E)
+    rng = np.random.default_rng(7 * T + E)
+    d, k = 256, 2
+    x = datagen.f32_to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    Wg = datagen.f32_to_bf16_bits(rng.standard_normal((d, E), dtype=np.float32) / np.float32(16.0))
+    xd, Wgd = to_device(x, "bf16", DEV), to_device(Wg, "bf16", DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx, gate = rp.pregate(xd, Wgd, k, logits=logits)
+    torch.cuda.synchronize()
+    compare_routing(idx, gate, logits, widen(x, "bf16"), widen(Wg, "bf16"), k)
 
 
 # --------------------------------------------------------------------------- segmentation
