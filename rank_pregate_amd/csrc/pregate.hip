@@ -25,7 +25,7 @@ void launch_nt(const PregateArgs& a, const RoutePlan& p, hipStream_t s) {
     pregate_kernel<Tin, 1, NT><<<a.T, NT, lds, s>>>(a, p);
   else if (TT == 2)
     pregate_kernel<Tin, 2, NT><<<(a.T + 1) / 2, NT, lds, s>>>(a, p);
-  else
+  else if constexpr (NT <= 512)  // wider tiles hold at most two tokens
     pregate_kernel<Tin, 4, NT><<<(a.T + 3) / 4, NT, lds, s>>>(a, p);
 }
 

@@ -30,7 +30,7 @@ __device__ __forceinline__ void stc_f32(float* p, float v) {
 // router
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 128;     // threads per router tile for E <= 64 (both launch forms)
-constexpr int kRouteThreadsWide = 512;  // threads per router tile for E > 64 (router launch only)
+constexpr int kRouteThreadsWide = 1024;  // threads per router tile for E > 64 (router launch only)
 constexpr int kRouteCB = 8;         // router columns per thread
 
 template <typename Tin>
@@ -118,7 +118,7 @@ __host__ __device__ inline RoutePlan route_plan(int E, int d_in, int elem_bytes)
   p.vec_cols = (E * elem_bytes) % 16 == 0;
   const int L = p.NCBp >= 64 ? 1 : 64 / p.NCBp;
   p.KR = KS / L > 1 ? KS / L : 1;
-  p.TT = E <= 64 || (p.KR + 1) * 4 * E * 4 <= 65536 ? 4 : 2;
+  p.TT = E <= 64 || (p.NT <= 512 && (p.KR + 1) * 4 * E * 4 <= 65536) ? 4 : 2;
   return p;
 }
 
@@ -152,7 +152,7 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   float* lg = smem + (size_t)KR * TT * E;
 
   // a one-token tile has registers to spare for a deeper load batch
-  constexpr int NB = TT == 1 ? 2 * kRouteNB : kRouteNB;
+  constexpr int NB = NT <= 512 ? (TT == 1 ? 2 * kRouteNB : kRouteNB) : (TT == 1 ? kRouteNB : 1);
   float acc[TT][kRouteCB];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
