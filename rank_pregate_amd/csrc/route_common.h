@@ -106,7 +106,8 @@ struct RoutePlan {
 // The k-slices (and with them the summation order of a logit) depend on E and
 // d_in only, never on T or on which launch runs the router: with E <= 64 a
 // tile has 128 threads (the decode launch runs two tiles per workgroup), with
-// more adapters 512, so a thread's k-slice stays short.
+// more adapters 1024 (at most two tokens a tile), so a thread's k-slice stays
+// short.
 __host__ __device__ inline RoutePlan route_plan(int E, int d_in, int elem_bytes) {
   RoutePlan p;
   const int ncb = (E + kRouteCB - 1) / kRouteCB;
@@ -151,7 +152,8 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   float* red = smem;
   float* lg = smem + (size_t)KR * TT * E;
 
-  // a one-token tile has registers to spare for a deeper load batch
+  // loads per batch: as many as the registers of a thread hold (fewer threads
+  // per CU and fewer tokens per tile leave more)
   constexpr int NB = NT <= 512 ? (TT == 1 ? 2 * kRouteNB : kRouteNB) : (TT == 1 ? kRouteNB : 1);
   float acc[TT][kRouteCB];
 #pragma unroll
