@@ -42,21 +42,28 @@ __device__ __forceinline__ int shrink_group_of_block(const PrefillStep& ps, int 
 
 // One shrink block: a chunk of 16*NCT pairs of one segment.  Small segments
 // (a few tokens each) take NCT = 1 and keep more K steps of A_e in flight.
+// Waves of a shrink block: chunks of 64 pairs (long segments, few blocks)
+// split K eight ways while rank <= 64 leaves the registers for it, other
+// blocks four ways.
 template <int MTR, int NCT>
-__global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
+constexpr int kShrinkWaves = NCT == 4 && MTR <= 4 ? 8 : 4;
+
+template <int MTR, int NCT>
+__global__ __launch_bounds__(64 * (kShrinkWaves<MTR, NCT>)) void shrink_bf16(PrefillStep ps) {
   __shared__ __attribute__((aligned(16))) float red[MTR * NCT * 4 * 64];
   __shared__ int s_loc[2];
   int b;
   const int g = shrink_group_of_block(ps, blockIdx.x, &b);
   const SgmmArgs& a = ps.g[g];
   const int proj = b / ps.units, unit = b % ps.units;
-  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR >= 4 ? 1 : 2);  // K steps per load batch
+  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR <= 2 ? 2 : 1);  // K steps per load batch
+  constexpr int W = kShrinkWaves<MTR, NCT>;
   if (NCT == 1) {
     // small segments: block e takes segment e whole, chunk by chunk (no scan
     // over the segment table to find its work)
     const int n = a.seg_offsets[unit + 1] - a.seg_offsets[unit];
     for (int c = 0; c * 16 < n; ++c) {
-      shrink_unit<MTR, NCT, 4, U>(a, proj, unit, c, red);
+      shrink_unit<MTR, NCT, W, U>(a, proj, unit, c, red);
       __syncthreads();  // `red` is read out before the next chunk reduces into it
     }
     return;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(256) void shrink_bf16(PrefillStep ps) {
   }
   __syncthreads();
   if (s_loc[0] < 0) return;
-  shrink_unit<MTR, NCT, 4, U>(a, proj, s_loc[0], s_loc[1], red);
+  shrink_unit<MTR, NCT, W, U>(a, proj, s_loc[0], s_loc[1], red);
 }
 
 // ============================================================================
@@ -506,10 +513,11 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   if (a0.k > 0) {
     const dim3 g(ps.shrink_end[ps.n_groups - 1]);
     const bool small = prefill_shrink_nct(a0.T, a0.E, a0.k) == 1;
+    static_assert(kShrinkWaves<4, 4> == 8 && kShrinkWaves<8, 4> == 4 && kShrinkWaves<1, 1> == 4, "launch sizes");
     switch ((a0.r + 15) >> 4) {
-      case 1: small ? shrink_bf16<1, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<1, 4><<<g, 256, 0, s>>>(ps); break;
-      case 2: small ? shrink_bf16<2, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<2, 4><<<g, 256, 0, s>>>(ps); break;
-      case 4: small ? shrink_bf16<4, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<4, 4><<<g, 256, 0, s>>>(ps); break;
+      case 1: small ? shrink_bf16<1, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<1, 4><<<g, 512, 0, s>>>(ps); break;
+      case 2: small ? shrink_bf16<2, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<2, 4><<<g, 512, 0, s>>>(ps); break;
+      case 4: small ? shrink_bf16<4, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<4, 4><<<g, 512, 0, s>>>(ps); break;
       default: small ? shrink_bf16<8, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<8, 4><<<g, 256, 0, s>>>(ps); break;
     }
     hipError_t err = hipGetLastError();
