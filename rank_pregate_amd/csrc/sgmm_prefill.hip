@@ -40,14 +40,14 @@ __device__ __forceinline__ int shrink_group_of_block(const PrefillStep& ps, int 
   return g;
 }
 
-// One shrink block: a chunk of 16*NCT pairs of one segment.  Small segments
-// (a few tokens each) take NCT = 1 and keep more K steps of A_e in flight.
 // Waves of a shrink block: chunks of 64 pairs (long segments, few blocks)
 // split K eight ways while rank <= 64 leaves the registers for it, other
 // blocks four ways.
 template <int MTR, int NCT>
 constexpr int kShrinkWaves = NCT == 4 && MTR <= 4 ? 8 : 4;
 
+// One shrink block: a chunk of 16*NCT pairs of one segment.  Small segments
+// (a few tokens each) take NCT = 1 and keep more K steps of A_e in flight.
 template <int MTR, int NCT>
 __global__ __launch_bounds__(64 * (kShrinkWaves<MTR, NCT>)) void shrink_bf16(PrefillStep ps) {
   __shared__ __attribute__((aligned(16))) float red[MTR * NCT * 4 * 64];
