@@ -284,6 +284,92 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
   }
 }
 
+// Expand for top-1 with r <= 64 (RC = r/16 rank-column pieces): a token has
+// one adapter, so a lane loads its token's gated u for every rank column at
+// once, and for each distinct adapter of the 32-token block (ascending, by
+// wave minimums) the B rows of every rank column in one batch; the next
+// adapter's B rows are in flight while the current one's MFMAs run.  Rank
+// columns past r are zero on both sides.
+template <int RC>
+__device__ __forceinline__ void expand_top1(const SgmmArgs& a, const ProjDesc& pd, int proj, int pos0, int rowb,
+                                            f32x16_t (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, lr = lane & 31, kg = lane >> 5;
+  const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
+  const float* ub = a.u + (size_t)proj * a.T * a.r;
+  int brow_g[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) brow_g[g] = min(rowb + g * 32 + lr, pd.d_out - 1);
+  bool cok[RC];
+  int cc[RC];
+#pragma unroll
+  for (int q = 0; q < RC; ++q) {
+    const int c = q * 16 + kg * 8;
+    cok[q] = c < a.r;
+    cc[q] = min(c, a.r - 8);
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    __builtin_amdgcn_sched_barrier(0);  // keeps the second block's loads after the first's MFMAs
+    const int pos = pos0 + f * 32 + lr;
+    const int t = token_at(a, min(pos, a.T - 1));
+    const int e0 = pos < a.T ? a.topk_idx[t] : -1;
+    const int mine = (e0 >= 0 && e0 < a.E) ? e0 : kNoAdapter;
+    f32x4_t u[RC][2];
+#pragma unroll
+    for (int q = 0; q < RC; ++q) {
+      const float* p = ub + (size_t)t * a.r + cc[q];
+      u[q][0] = *reinterpret_cast<const f32x4_t*>(p);
+      u[q][1] = *reinterpret_cast<const f32x4_t*>(p + 4);
+    }
+    bool todo = mine != kNoAdapter;
+    auto next_e = [&]() -> int {
+      const int e = wave_min_int(todo ? mine : kNoAdapter);
+      if (mine == e) todo = false;
+      return e;
+    };
+    uint4 bA[RC][2], bB[RC][2];
+    auto load_b = [&](int e, uint4 (&bo)[RC][2]) {
+      const int ee = e == kNoAdapter ? 0 : e;
+#pragma unroll
+      for (int q = 0; q < RC; ++q)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) bo[q][g] = ld16(Bm + ((size_t)ee * pd.d_out + brow_g[g]) * a.r + cc[q]);
+    };
+    auto apply = [&](int e, const uint4 (&bo)[RC][2]) {
+#pragma unroll
+      for (int q = 0; q < RC; ++q) {
+        float v[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          v[m] = (mine == e && cok[q]) ? u[q][0][m] : 0.f;
+          v[4 + m] = (mine == e && cok[q]) ? u[q][1][m] : 0.f;
+        }
+        uint4 hi, lo;
+        split_hi_lo(v, hi, lo);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint4 b = sel4(cok[q], bo[q][g]);
+          acc[f][g] = mfma32(hi, b, acc[f][g]);
+          acc[f][g] = mfma32(lo, b, acc[f][g]);
+        }
+      }
+    };
+    int eA = next_e();
+    if (eA == kNoAdapter) continue;
+    load_b(eA, bA);
+    while (true) {
+      const int eB = next_e();
+      if (eB != kNoAdapter) load_b(eB, bB);
+      apply(eA, bA);
+      if (eB == kNoAdapter) break;
+      eA = next_e();
+      if (eA != kNoAdapter) load_b(eA, bA);
+      apply(eB, bB);
+      if (eA == kNoAdapter) break;
+    }
+  }
+}
+
 // Blocks b and b + 8 share an XCD (b % 8).  The n_tok_tiles token tiles of a
 // row tile are blocks q*8 + x for consecutive q, so they run on one XCD at
 // about the same time and all but the first read of the W0 tile hit its L2.
@@ -294,7 +380,8 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
 // BM: tokens per tile, 128 (four waves, two blocks a CU) or 256 (eight waves,
 // one block a CU; each W0 byte fetched serves twice the tokens).  Waves are
 // BM/64 x 2 tiles of 64 tokens x 64 rows.
-template <bool FAST, int BM>
+// TOP1: top-1 routing with r <= 64 (the expand of expand_top1).
+template <bool FAST, int BM, bool TOP1>
 __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(PrefillStep ps) {
   constexpr int NT = 2 * BM, NW = NT / 64;
   constexpr int kPPA = BM * kPK / 8 / NT;   // 16-byte pieces per thread and stage: A
@@ -462,7 +549,10 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   if (S > 1 && !splitk_reduce<NW>(a, ((size_t)tile * n_tok_tiles + tt) * S, split, S,
                               a.counters + (size_t)tile * n_tok_tiles + tt, acc))
     return;
-  if (a.k > 0) expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
+  if (TOP1)
+    expand_top1<4>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
+  else if (a.k > 0)
+    expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
 
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
@@ -531,16 +621,17 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   const dim3 grid(ps.block_end[ps.n_groups - 1]);
   if (ps.n_tok_tiles != (a0.T + prefill_tile_tokens(a0.T) - 1) / prefill_tile_tokens(a0.T))
     return hipErrorInvalidValue;  // token tiles planned for another tile size
+  const bool top1 = a0.k == 1 && a0.r <= 64;
   if (prefill_tile_tokens(a0.T) == 256) {
     if (fast)
-      prefill_bf16<true, 256><<<grid, 512, 0, s>>>(ps);
+      top1 ? prefill_bf16<true, 256, true><<<grid, 512, 0, s>>>(ps) : prefill_bf16<true, 256, false><<<grid, 512, 0, s>>>(ps);
     else
-      prefill_bf16<false, 256><<<grid, 512, 0, s>>>(ps);
+      top1 ? prefill_bf16<false, 256, true><<<grid, 512, 0, s>>>(ps) : prefill_bf16<false, 256, false><<<grid, 512, 0, s>>>(ps);
   } else {
     if (fast)
-      prefill_bf16<true, 128><<<grid, 256, 0, s>>>(ps);
+      top1 ? prefill_bf16<true, 128, true><<<grid, 256, 0, s>>>(ps) : prefill_bf16<true, 128, false><<<grid, 256, 0, s>>>(ps);
     else
-      prefill_bf16<false, 128><<<grid, 256, 0, s>>>(ps);
+      top1 ? prefill_bf16<false, 128, true><<<grid, 256, 0, s>>>(ps) : prefill_bf16<false, 128, false><<<grid, 256, 0, s>>>(ps);
   }
   return hipGetLastError();
 }
