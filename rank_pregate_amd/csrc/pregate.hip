@@ -1,6 +1,8 @@
 // Token-level pre-gating kernel (AdaFuse, technical summary §2.A; §2.B decoding
 // steps 1-2): one workgroup per tile of TT tokens; the arithmetic lives in
 // route_common.h and is shared with the fused route-and-project launch.
+#include <algorithm>
+
 #include "route_common.h"
 
 namespace rp {
@@ -19,14 +21,15 @@ constexpr int kRouteFillTiles = 256;
 
 template <typename Tin, int NT>
 void launch_nt(const PregateArgs& a, const RoutePlan& p, hipStream_t s) {
-  const int TT = a.T <= kRouteFillTiles ? 1 : a.T <= 2 * kRouteFillTiles ? 2 : p.TT;
+  constexpr int kMaxTT = NT <= 512 ? 4 : 2;  // wider tiles hold at most two tokens
+  const int TT = std::min(kMaxTT, a.T <= kRouteFillTiles ? 1 : a.T <= 2 * kRouteFillTiles ? 2 : p.TT);
   const size_t lds = sizeof(float) * route_lds_floats(p, a.E, TT);
   if (TT == 1)
     pregate_kernel<Tin, 1, NT><<<a.T, NT, lds, s>>>(a, p);
-  else if (TT == 2)
+  else if (TT == 2 || kMaxTT == 2)
     pregate_kernel<Tin, 2, NT><<<(a.T + 1) / 2, NT, lds, s>>>(a, p);
-  else if constexpr (NT <= 512)  // wider tiles hold at most two tokens
-    pregate_kernel<Tin, 4, NT><<<(a.T + 3) / 4, NT, lds, s>>>(a, p);
+  else
+    pregate_kernel<Tin, kMaxTT, NT><<<(a.T + 3) / 4, NT, lds, s>>>(a, p);
 }
 
 template <typename Tin>
