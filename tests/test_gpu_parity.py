@@ -297,6 +297,8 @@ def _run_projection_case(T, d_in, d_outs, E, r, k, dt, seed, b_scale=0.1, zero_B
     (300, 264, [128, 40], 12, 128, 2),  # prefill, k=2, r=128
     (1000, 512, [512], 32, 64, 1),
     (1100, 256, [200], 9, 16, 2),      # 256-token tiles of eight waves, ragged T and d_out
+    (300, 128, [96], 6, 8, 1),         # top-1 expand, r = 8 (rank columns past r are zero)
+    (200, 256, [128, 64], 10, 32, 1),  # top-1 expand, r = 32, 128-token tiles
 ])
 def test_projection_shapes(dt, T, d_in, d_outs, E, r, k):
     say("projection", dt, T, d_in, d_outs, E, r, k)
