@@ -187,7 +187,7 @@ __device__ __forceinline__ bool splitk_reduce(const SgmmArgs& a, size_t slot0, i
 // The wave's tokens are positions pos0 .. pos0+63 (two 32-token blocks), its
 // rows rowb .. rowb+63 (two 32-row blocks); acc[f][g] as the GEMM left it.
 __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDesc& pd, int proj, int pos0, int rowb,
-                                                f32x16_t (&acc)[2][2]) {
+                                                f32x16_t (&acc)[2][2], uint32_t* emask) {
   const int lane = threadIdx.x & 63, lr = lane & 31, kg = lane >> 5;
   const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
   const float* ub = a.u + (size_t)proj * a.T * a.k * a.r;
@@ -202,14 +202,21 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
     const int t = token_at(a, min(pos, a.T - 1));
     // slots in groups of kPUJ (a token naming one adapter in two groups
     // gets its two terms from two passes)
-    for (int j0 = 0; j0 < kk; j0 += kPUJ)
-    for (int c0 = 0; c0 < a.r; c0 += 16) {
+    for (int j0 = 0; j0 < kk; j0 += kPUJ) {
       int ej[kPUJ];
 #pragma unroll
       for (int j = 0; j < kPUJ; ++j) {
         const int e = (j0 + j < kk && tok_ok) ? a.topk_idx[t * kk + j0 + j] : -1;
         ej[j] = (e >= 0 && e < a.E) ? e : kNoAdapter;
       }
+      // the wave's distinct adapters as a bit mask in LDS (one word per 32
+      // adapters); LDS operations of one wave complete in issue order
+      const int n_words = (a.E + 31) >> 5;
+      for (int w = lane; w < n_words; w += 64) emask[w] = 0u;
+#pragma unroll
+      for (int j = 0; j < kPUJ; ++j)
+        if (ej[j] != kNoAdapter) atomicOr(&emask[ej[j] >> 5], 1u << (ej[j] & 31));
+    for (int c0 = 0; c0 < a.r; c0 += 16) {
       const int c = c0 + kg * 8;
       const bool cok = c < a.r;
       const int cc = min(c, a.r - 8);
@@ -221,19 +228,14 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
         uj[j][0] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         uj[j][1] = ok ? *reinterpret_cast<const f32x4_t*>(p + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      uint32_t todo = 0;
-#pragma unroll
-      for (int j = 0; j < kPUJ; ++j)
-        if (ej[j] != kNoAdapter) todo |= 1u << j;
+      // ascending walk over the mask (wave-uniform, scalar)
+      int wi = 0;
+      uint32_t cur = __builtin_amdgcn_readfirstlane(emask[0]);
       auto next_e = [&]() -> int {
-        int cand = kNoAdapter;
-#pragma unroll
-        for (int j = 0; j < kPUJ; ++j)
-          if ((todo >> j) & 1u) cand = min(cand, ej[j]);
-        const int e = wave_min_int(cand);
-#pragma unroll
-        for (int j = 0; j < kPUJ; ++j)
-          if (ej[j] == e) todo &= ~(1u << j);
+        while (cur == 0u && wi + 1 < n_words) cur = __builtin_amdgcn_readfirstlane(emask[++wi]);
+        if (cur == 0u) return kNoAdapter;
+        const int e = wi * 32 + __builtin_ctz(cur);
+        cur &= cur - 1u;
         return e;
       };
       int beA[kPNB], beB[kPNB];
@@ -280,6 +282,7 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
         haveA = collect(beA, bA);
         apply(beB, bB);
       }
+    }
     }
   }
 }
@@ -388,6 +391,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   constexpr int kPPB = kPB * kPK / 8 / NT;  // and B
   // operand double buffers, reused for the output tile at the end
   __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * (BM + kPB) * kPLd];
+  __shared__ uint32_t s_emask[TOP1 ? 1 : NW][TOP1 ? 1 : kMaxEWords];  // expand: a wave's adapters
   auto As = reinterpret_cast<bf16_t(*)[BM][kPLd]>(smem_p);
   auto Bs = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p + 2 * BM * kPLd);
 
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   if (TOP1)
     expand_top1<4>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
   else if (a.k > 0)
-    expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
+    expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc, s_emask[wave]);
 
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
