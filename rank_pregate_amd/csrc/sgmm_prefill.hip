@@ -88,7 +88,7 @@ constexpr int kPR = 2;         // stages whose loads are in flight ahead of the 
 constexpr int kPCB = kPK / 32;  // tiled W0 block columns per stage
 constexpr int kPBigT = 256;     // from this many tokens, 256-token tiles of eight waves
 constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
-constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once
+constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once (k > 2)
 constexpr int kNoAdapter = 0x7fffffff;
 static_assert(sizeof(PrefillStep) <= 4096, "kernel argument block too large");
 
@@ -186,6 +186,7 @@ __device__ __forceinline__ bool splitk_reduce(const SgmmArgs& a, size_t slot0, i
 // of the batch whose MFMAs run.
 // The wave's tokens are positions pos0 .. pos0+63 (two 32-token blocks), its
 // rows rowb .. rowb+63 (two 32-row blocks); acc[f][g] as the GEMM left it.
+template <int PUJ>
 __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDesc& pd, int proj, int pos0, int rowb,
                                                 f32x16_t (&acc)[2][2], uint32_t* emask) {
   const int lane = threadIdx.x & 63, lr = lane & 31, kg = lane >> 5;
@@ -200,12 +201,12 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
     const int pos = pos0 + f * 32 + lr;
     const bool tok_ok = pos < a.T;
     const int t = token_at(a, min(pos, a.T - 1));
-    // slots in groups of kPUJ (a token naming one adapter in two groups
+    // slots in groups of PUJ (a token naming one adapter in two groups
     // gets its two terms from two passes)
-    for (int j0 = 0; j0 < kk; j0 += kPUJ) {
-      int ej[kPUJ];
+    for (int j0 = 0; j0 < kk; j0 += PUJ) {
+      int ej[PUJ];
 #pragma unroll
-      for (int j = 0; j < kPUJ; ++j) {
+      for (int j = 0; j < PUJ; ++j) {
         const int e = (j0 + j < kk && tok_ok) ? a.topk_idx[t * kk + j0 + j] : -1;
         ej[j] = (e >= 0 && e < a.E) ? e : kNoAdapter;
       }
@@ -214,15 +215,15 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
       const int n_words = (a.E + 31) >> 5;
       for (int w = lane; w < n_words; w += 64) emask[w] = 0u;
 #pragma unroll
-      for (int j = 0; j < kPUJ; ++j)
+      for (int j = 0; j < PUJ; ++j)
         if (ej[j] != kNoAdapter) atomicOr(&emask[ej[j] >> 5], 1u << (ej[j] & 31));
     for (int c0 = 0; c0 < a.r; c0 += 16) {
       const int c = c0 + kg * 8;
       const bool cok = c < a.r;
       const int cc = min(c, a.r - 8);
-      f32x4_t uj[kPUJ][2];
+      f32x4_t uj[PUJ][2];
 #pragma unroll
-      for (int j = 0; j < kPUJ; ++j) {
+      for (int j = 0; j < PUJ; ++j) {
         const bool ok = ej[j] != kNoAdapter && cok;
         const float* p = ub + (size_t)(t * kk + min(j0 + j, kk - 1)) * a.r + cc;
         uj[j][0] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -259,7 +260,7 @@ __device__ __forceinline__ void expand_adapters(const SgmmArgs& a, const ProjDes
 #pragma unroll
           for (int m = 0; m < 8; ++m) v[m] = 0.f;
 #pragma unroll
-          for (int j = 0; j < kPUJ; ++j)
+          for (int j = 0; j < PUJ; ++j)
             if (ej[j] == be[i]) {
 #pragma unroll
               for (int m = 0; m < 4; ++m) v[m] += uj[j][0][m], v[4 + m] += uj[j][1][m];
@@ -383,14 +384,16 @@ __device__ __forceinline__ void expand_top1(const SgmmArgs& a, const ProjDesc& p
 // BM: tokens per tile, 128 (four waves, two blocks a CU) or 256 (eight waves,
 // one block a CU; each W0 byte fetched serves twice the tokens).  Waves are
 // BM/64 x 2 tiles of 64 tokens x 64 rows.
-// TOP1: top-1 routing with r <= 64 (the expand of expand_top1).
-template <bool FAST, int BM, bool TOP1>
+// EXP: the expand form: 1 top-1 routing with r <= 64 (expand_top1), 2 two
+// slots per token, 4 up to four slots per pass.
+template <bool FAST, int BM, int EXP>
 __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(PrefillStep ps) {
   constexpr int NT = 2 * BM, NW = NT / 64;
   constexpr int kPPA = BM * kPK / 8 / NT;   // 16-byte pieces per thread and stage: A
   constexpr int kPPB = kPB * kPK / 8 / NT;  // and B
   // operand double buffers, reused for the output tile at the end
   __shared__ __attribute__((aligned(16))) bf16_t smem_p[2 * (BM + kPB) * kPLd];
+  constexpr bool TOP1 = EXP == 1;
   __shared__ uint32_t s_emask[TOP1 ? 1 : NW][TOP1 ? 1 : kMaxEWords];  // expand: a wave's adapters
   auto As = reinterpret_cast<bf16_t(*)[BM][kPLd]>(smem_p);
   auto Bs = reinterpret_cast<bf16_t(*)[kPB][kPLd]>(smem_p + 2 * BM * kPLd);
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   if (TOP1)
     expand_top1<4>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
   else if (a.k > 0)
-    expand_adapters(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc, s_emask[wave]);
+    expand_adapters<EXP == 2 ? 2 : kPUJ>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc, s_emask[wave]);
 
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
@@ -601,6 +604,19 @@ int prefill_shrink_units(int T, int E, int k) {
   return E + (T * k + 63) / 64;
 }
 
+template <int BM>
+void launch_gemm(const PrefillStep& ps, bool fast, int exp, dim3 grid, hipStream_t s) {
+  if (fast) {
+    if (exp == 1) prefill_bf16<true, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
+    else if (exp == 2) prefill_bf16<true, BM, 2><<<grid, 2 * BM, 0, s>>>(ps);
+    else prefill_bf16<true, BM, 4><<<grid, 2 * BM, 0, s>>>(ps);
+  } else {
+    if (exp == 1) prefill_bf16<false, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
+    else if (exp == 2) prefill_bf16<false, BM, 2><<<grid, 2 * BM, 0, s>>>(ps);
+    else prefill_bf16<false, BM, 4><<<grid, 2 * BM, 0, s>>>(ps);
+  }
+}
+
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   const SgmmArgs& a0 = ps.g[0];
   if (a0.T == 0) return hipSuccess;
@@ -625,18 +641,11 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   const dim3 grid(ps.block_end[ps.n_groups - 1]);
   if (ps.n_tok_tiles != (a0.T + prefill_tile_tokens(a0.T) - 1) / prefill_tile_tokens(a0.T))
     return hipErrorInvalidValue;  // token tiles planned for another tile size
-  const bool top1 = a0.k == 1 && a0.r <= 64;
-  if (prefill_tile_tokens(a0.T) == 256) {
-    if (fast)
-      top1 ? prefill_bf16<true, 256, true><<<grid, 512, 0, s>>>(ps) : prefill_bf16<true, 256, false><<<grid, 512, 0, s>>>(ps);
-    else
-      top1 ? prefill_bf16<false, 256, true><<<grid, 512, 0, s>>>(ps) : prefill_bf16<false, 256, false><<<grid, 512, 0, s>>>(ps);
-  } else {
-    if (fast)
-      top1 ? prefill_bf16<true, 128, true><<<grid, 256, 0, s>>>(ps) : prefill_bf16<true, 128, false><<<grid, 256, 0, s>>>(ps);
-    else
-      top1 ? prefill_bf16<false, 128, true><<<grid, 256, 0, s>>>(ps) : prefill_bf16<false, 128, false><<<grid, 256, 0, s>>>(ps);
-  }
+  const int exp = a0.k == 1 && a0.r <= 64 ? 1 : a0.k <= 2 ? 2 : 4;
+  if (prefill_tile_tokens(a0.T) == 256)
+    launch_gemm<256>(ps, fast, exp, grid, s);
+  else
+    launch_gemm<128>(ps, fast, exp, grid, s);
   return hipGetLastError();
 }
 
