@@ -37,16 +37,14 @@ def router_logits(x: np.ndarray, Wg: np.ndarray) -> np.ndarray:
     return np.asarray(x, np.float64) @ np.asarray(Wg, np.float64)
 
 
-def select_topk(logits: np.ndarray, k: int, decision_dtype=np.float32) -> np.ndarray:
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """Top-k adapter choice per token, §2.B step 2.
 
-    Adapters are ranked by (logit descending, index ascending): an exact tie
-    goes to the lower index.  The decision is taken on the logits rounded to
-    `decision_dtype` (fp32, the precision the device computes them in), so
-    both sides decide in the same precision.  Returns int32 [T, k], best
-    first.
+    Adapters are ranked on the fp64 logits by (logit descending, index
+    ascending): an exact tie goes to the lower index.  Returns int32 [T, k],
+    best first.
     """
-    l = np.asarray(logits, np.float64).astype(decision_dtype)
+    l = np.asarray(logits, np.float64)
     T, E = l.shape
     if not (0 <= k <= E):
         raise ValueError("k out of range")

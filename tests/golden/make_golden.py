@@ -38,7 +38,7 @@ def make(name, seed, T, d_in, d_out, E, r, k, dtype, integer_range, tie_cols=Non
     else:
         x, Wg, W0, A, B = (v.tolist() for v in (x, Wg, W0, A, B))
     logits = brute.logits(x, Wg)
-    idx = [brute.topk([float(np.float32(v)) for v in row], k) for row in logits]
+    idx = [brute.topk([float(v) for v in row], k) for row in logits]
     gate = [brute.gates([float(v) for v in row], chosen) for row, chosen in zip(logits, idx)]
     exact = integer_range is not None and k == 1
     if exact:

@@ -53,20 +53,21 @@ def _sgmm_variant(kind):
     return sgmm
 
 
-def _topk_highest_index_wins(logits, k, decision_dtype=np.float32):
-    l = np.asarray(logits, np.float64).astype(decision_dtype)
+def _topk_highest_index_wins(logits, k):
+    l = np.asarray(logits, np.float64)
     T, E = l.shape
     e_ids = np.broadcast_to(np.arange(E)[::-1], (T, E))
     order = np.lexsort((e_ids, -l), axis=-1)
     return order[:, :k].astype(np.int32)
 
 
-def _topk_no_rounding(logits, k, decision_dtype=None):
-    return reference.select_topk(logits, k, decision_dtype=np.float64)
+def _topk_rounds_to_fp32(logits, k):
+    # ranks logits rounded to fp32: near-equal logits collapse into false ties
+    return reference.select_topk(np.asarray(logits, np.float64).astype(np.float32).astype(np.float64), k)
 
 
-def _topk_ascending(logits, k, decision_dtype=np.float32):
-    return reference.select_topk(-np.asarray(logits), k, decision_dtype)
+def _topk_ascending(logits, k):
+    return reference.select_topk(-np.asarray(logits), k)
 
 
 def _segment_unstable(idx, E):
@@ -104,7 +105,7 @@ def _logits_transposed_weight(x, Wg):
 MUTANTS = {
     "logits_weight_rows_reversed": dict(router_logits=_logits_transposed_weight),
     "topk_ties_to_highest": dict(select_topk=_topk_highest_index_wins),
-    "topk_decides_in_fp64": dict(select_topk=_topk_no_rounding),
+    "topk_decides_in_fp32": dict(select_topk=_topk_rounds_to_fp32),
     "topk_ascending": dict(select_topk=_topk_ascending),
     "gates_over_all_E": dict(softmax_gates=_gates_full_softmax),
     "gates_not_normalised_exactly": dict(softmax_gates=_gates_wrong_shift),
