@@ -20,8 +20,10 @@
  *   rp_sgmm_step  -- a decode step: many projection groups in dependency
  *                    order (q|k|v, o, gate|up, down, layer after layer), the
  *                    routing optionally computed first, as few launches as
- *                    possible (page 2 of the sources: the whole decode step
- *                    replayed as one unit).
+ *                    possible ("FlashSVD v1.5: Making Low-Rank Transformers
+ *                    Inference Actually Fast", La Solución: gate and up
+ *                    packed into one wide operation, and the per-token
+ *                    routine recorded once and replayed as a unit).
  *
  * Conventions shared by every entry point
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 5
+#define RP_ABI_VERSION 6
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
 #define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call (per group) */
@@ -58,7 +60,8 @@ typedef enum {
   RP_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, size or count out of range */
   RP_ERR_UNSUPPORTED = 2,   /* well-formed but outside what the kernels implement */
   RP_ERR_WORKSPACE = 3,     /* workspace missing, misaligned or too small */
-  RP_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+  RP_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  RP_ERR_DEVICE = 5         /* rp_workspace_status: a kernel flagged a fault in the workspace */
 } rp_status;
 
 typedef enum { RP_F32 = 0, RP_BF16 = 1 } rp_dtype;
@@ -232,9 +235,33 @@ size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int
 rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream);
 
 /* Workspace bytes rp_sgmm_fused needs for these sizes; sum_d_out is the sum of
- * the projections' d_out.  Returns 0 for sizes the call would reject. */
+ * the projections' d_out.  Returns 0 for sizes the call would reject.
+ * Besides the rank-r intermediates (T*k*r per projection), the workspace holds
+ * the split-K partial tiles of long-K or few-tile calls: their count follows
+ * the output tiles over all projections (sum_d_out) and the K splits (d_in). */
 size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t sum_d_out, int64_t E,
                               int64_t r, int32_t k, rp_dtype dt);
+
+/* Device-side health of an SGMM workspace (one used by rp_sgmm_fused,
+ * rp_route_sgmm_fused or rp_sgmm_step).  Kernels that hand data between
+ * workgroups of one launch wait for it with bounded polls; a wait that runs
+ * out (possible only if the launch's workgroups are not all resident at once,
+ * e.g. another program occupies the device's compute units) gives up and sets
+ * a sticky word in the workspace, and the outputs of that call are then not
+ * valid.  Routing computed by these calls also counts, in a second word,
+ * pairs whose adapter index was outside [0, E) (always 0 for indices the
+ * router wrote).
+ *
+ *   ws, ws_bytes     the workspace (at least 64 KiB, 256-byte aligned)
+ *   wait_overflow    host int32 out, or NULL: nonzero if a wait gave up
+ *   bad_indices      host int32 out, or NULL: out-of-range indices counted
+ *   clear            nonzero: reset both words after reading them
+ *
+ * Orders after the work queued on `stream`: queues a copy of the two words,
+ * then waits for the stream (so it cannot be recorded into a graph).  Returns
+ * RP_ERR_DEVICE when either word is nonzero, RP_OK when both are zero. */
+rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t* wait_overflow,
+                              int32_t* bad_indices, hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* rp_last_error(void);

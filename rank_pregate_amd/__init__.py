@@ -15,20 +15,22 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 from typing import List, Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librank_pregate.so")
 
-RP_OK, RP_ERR_INVALID_ARG, RP_ERR_UNSUPPORTED, RP_ERR_WORKSPACE, RP_ERR_HIP = range(5)
+RP_OK, RP_ERR_INVALID_ARG, RP_ERR_UNSUPPORTED, RP_ERR_WORKSPACE, RP_ERR_HIP, RP_ERR_DEVICE = range(6)
 RP_F32, RP_BF16 = 0, 1
 RP_MAX_K, RP_MAX_E, RP_MAX_PROJ = 8, 1024, 4
 
 _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3: "RP_ERR_WORKSPACE",
-                 4: "RP_ERR_HIP"}
+                 4: "RP_ERR_HIP", 5: "RP_ERR_DEVICE"}
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
-            "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy")
+            "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy",
+            "rp_workspace_status")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
@@ -83,7 +85,9 @@ def lib() -> ctypes.CDLL:
     L.rp_pack_w0.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
     L.rp_util_stream_read.argtypes = [vp, sz, vp, vp]
     L.rp_util_copy.argtypes = [vp, vp, sz, vp]
-    for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_pack_w0", "rp_util_stream_read", "rp_util_copy"):
+    L.rp_workspace_status.argtypes = [vp, sz, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
+    for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_route_sgmm_fused", "rp_sgmm_step", "rp_pack_w0",
+                 "rp_util_stream_read", "rp_util_copy", "rp_workspace_status"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -184,27 +188,62 @@ def sgmm_workspace_size(n_proj: int, T: int, d_in: int, sum_d_out: int, E: int, 
     return lib().rp_sgmm_workspace_size(n_proj, T, d_in, sum_d_out, E, r, k, dtype_code)
 
 
-class Workspace:
-    """A zero-initialised device buffer reused across rp_sgmm_fused calls on one stream.
+_tracked = weakref.WeakValueDictionary()
 
-    The library keeps the buffer's control region consistent between calls, so
-    a buffer only has to be zeroed when it is (re)allocated.
+
+def track_workspace(ws):
+    """Remember an SGMM workspace tensor (weakly) so check_workspaces() can read its status words."""
+    _tracked[id(ws)] = ws
+    return ws
+
+
+class Workspace:
+    """Zero-initialised device buffers reused across calls, one per (device, stream).
+
+    The library keeps a buffer's control region consistent between calls, so a
+    buffer only has to be zeroed when it is (re)allocated.  Calls on different
+    streams get different buffers (calls that may overlap in time must not
+    share one).  A new buffer is zero-filled on the current torch stream, which
+    is then waited for, so the fill is complete before the call's stream uses
+    it; pass an explicit workspace when recording a graph.
     """
 
     def __init__(self):
         self._buf = {}
 
-    def get(self, nbytes: int, device):
+    def get(self, nbytes: int, device, stream: int = 0):
         torch = _torch()
-        key = str(device)
+        key = (str(device), int(stream))
         b = self._buf.get(key)
         if b is None or b.numel() < nbytes:
-            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-            self._buf[key] = b
+            b = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+            torch.cuda.current_stream(device).synchronize()
+            self._buf[key] = track_workspace(b)
         return b
 
 
 _default_ws = Workspace()
+
+
+def workspace_status(ws, clear: bool = False, stream=None) -> Tuple[int, int]:
+    """rp_workspace_status: (wait_overflow, bad_indices) of an SGMM workspace tensor.
+
+    Waits for `stream` (default: the current one).  Raises RankPregateError
+    (RP_ERR_DEVICE) when either word is nonzero."""
+    wo, bad = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib().rp_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), int(clear), ctypes.byref(wo),
+                                   ctypes.byref(bad), _stream(stream, ws.device))
+    _check(st, "rp_workspace_status")
+    return wo.value, bad.value
+
+
+def check_workspaces(clear: bool = True) -> int:
+    """workspace_status on every tracked workspace still alive; returns how many were checked."""
+    n = 0
+    for ws in list(_tracked.values()):
+        workspace_status(ws, clear=clear)
+        n += 1
+    return n
 
 
 def _proj_array(projs: Sequence[Tuple], x):
@@ -251,11 +290,12 @@ def route_sgmm_fused(projs: Sequence[Tuple], x, Wg, E: int, r: int, k: int, topk
     if pair_perm is None:
         pair_perm = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
     arr, ys, sum_d_out = _proj_array(projs, x)
+    sh = _stream(stream, dev)
     if ws is None:
-        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), dev)
+        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), dev, sh)
     st = lib().rp_route_sgmm_fused(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), _ptr(Wg), E, r, k, dt,
                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), _ptr(ws),
-                                   ws.numel(), _stream(stream, dev))
+                                   ws.numel(), sh)
     _check(st, "rp_route_sgmm_fused")
     return ys, topk_idx, topk_gate, seg_offsets, pair_perm
 
@@ -271,11 +311,11 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
     T, d_in = x.shape
     dt = _dtype_code(x)
     arr, ys, sum_d_out = _proj_array(projs, x)
+    sh = _stream(stream, x.device)
     if ws is None:
-        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), x.device)
+        ws = _default_ws.get(sgmm_workspace_size(len(projs), T, d_in, sum_d_out, E, r, k, dt), x.device, sh)
     st = lib().rp_sgmm_fused(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), E, r, k, _ptr(topk_idx),
-                             _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(),
-                             _stream(stream, x.device))
+                             _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(), sh)
     _check(st, "rp_sgmm_fused")
     return ys
 
@@ -316,10 +356,11 @@ def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx
         ys.append(gys)
         garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(projs), from_call, _ptr(x), x.shape[1],
                           _rows(x, "x"))
+    sh = _stream(stream, dev)
     if ws is None:
-        ws = _default_ws.get(lib().rp_sgmm_step_workspace_size(garr, len(groups), T, E, r, k, dt), dev)
+        ws = _default_ws.get(lib().rp_sgmm_step_workspace_size(garr, len(groups), T, E, r, k, dt), dev, sh)
     st = lib().rp_sgmm_step(garr, len(groups), T, E, r, k, _ptr(Wg), _ptr(topk_idx), _ptr(topk_gate),
-                            _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(), _stream(stream, dev))
+                            _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(), sh)
     _check(st, "rp_sgmm_step")
     return ys, topk_idx, topk_gate, seg_offsets, pair_perm
 
@@ -366,3 +407,4 @@ def copy(dst, src, stream=None) -> None:
 # the C names, for callers that mirror the header
 rp_pregate, rp_segment, rp_sgmm_fused, rp_route_sgmm_fused = pregate, segment, sgmm_fused, route_sgmm_fused
 rp_sgmm_step = sgmm_step
+rp_workspace_status = workspace_status

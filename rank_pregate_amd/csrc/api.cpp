@@ -224,9 +224,12 @@ void fill_group(rp::SgmmArgs* a, const rp_proj* projs, int n_proj, const void* x
   a->k = k;
 }
 
-// Word of the workspace's control region that receives the count of
-// out-of-range router indices when a call computes the routing.
+// Words of the workspace's control region: the count of out-of-range router
+// indices when a call computes the routing, and the sticky flag a kernel sets
+// when a cross-workgroup wait gives up (the device side's kCtlSegErr and
+// kCtlWaitOverflow).
 constexpr size_t kSegErrWord = 64;
+constexpr size_t kWaitOverflowWord = 32;
 
 struct Routing {
   const void* Wg;  // non-null: compute the routing from the first group's x
@@ -542,6 +545,34 @@ rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int6
   const size_t need = groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
   if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   return run_groups(fn, groups, n_groups, T, E, r, k, dt, rt, ws, ws_bytes, stream);
+}
+
+rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t* wait_overflow,
+                              int32_t* bad_indices, hipStream_t stream) {
+  g_last_error.clear();
+  if (!ws || !aligned(ws, 256) || ws_bytes < rp::kWorkspaceCounterBytes)
+    return fail(RP_ERR_WORKSPACE, "rp_workspace_status: need a 256-byte aligned workspace of at least %zu bytes",
+                rp::kWorkspaceCounterBytes);
+  // the two words sit in one 256-byte span of the control region
+  static_assert(kSegErrWord > kWaitOverflowWord && kSegErrWord - kWaitOverflowWord < 64, "status span");
+  int32_t span[64];
+  int32_t* src = static_cast<int32_t*>(ws) + kWaitOverflowWord;
+  hipError_t e = hipMemcpyAsync(span, src, sizeof span, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail("rp_workspace_status", e);
+  const int32_t wo = span[0], bad = span[kSegErrWord - kWaitOverflowWord];
+  if (wait_overflow) *wait_overflow = wo;
+  if (bad_indices) *bad_indices = bad;
+  if (clear && (wo != 0 || bad != 0)) {
+    e = hipMemsetAsync(src, 0, sizeof(int32_t), stream);
+    if (e == hipSuccess) e = hipMemsetAsync(static_cast<int32_t*>(ws) + kSegErrWord, 0, sizeof(int32_t), stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail("rp_workspace_status clear", e);
+  }
+  if (wo != 0 || bad != 0)
+    return fail(RP_ERR_DEVICE, "rp_workspace_status: wait overflow flag %d, out-of-range adapter indices %d%s", wo,
+                bad, wo ? " (a cross-workgroup wait gave up: outputs since the last clear are not valid)" : "");
+  return RP_OK;
 }
 
 rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream) {

@@ -9,20 +9,25 @@
 // first (§2.A pre-gating; §2.B decoding steps 1-2), so routing overlaps the
 // weight stream instead of preceding it.
 //
-// Work items, numbered in this order; workgroup b runs items b, b + G, ...:
-//   0. (fused) router tiles, then one segmentation item.
-//   1. shrink units: for one adapter e and one of KP parts of K, either every
-//      token (`dense`, small E) or one chunk of <= 16 pairs of e's segment:
-//      unscaled partial products A_e x[t] in fp32.
-//   2. base items (32 output rows, one of S splits of K), two waves, each
-//      owning 16 rows: bf16 MFMA 16x16x32 with the tokens as M and W0 rows as
-//      N.  The tokens' activations for each 256-wide K chunk are staged in LDS
-//      with coalesced loads two chunks ahead; W0 rows stream from HBM straight
-//      into registers one chunk ahead, in a pinned issue order that keeps the
-//      loads in flight behind the math.  Then the adapter deltas: the KP
-//      partials of the lane's (token, slot) pairs are summed in part order and
-//      scaled by the gate, and each touched adapter adds a (hi, lo) pair of
-//      MFMAs on B_e's rows.
+// Work items, numbered in this order; a workgroup's first item is its block
+// index, each later one is claimed from a launch-wide counter:
+//   0. (fused) router items (two two-token tiles, one per half workgroup),
+//      then one segmentation item.
+//   1. shrink items, for every group whose input comes from the call first:
+//      with E <= 32, 64-row tiles of the stacked [A_0; ..; A_{E-1}] through
+//      the backbone's streaming loop over every token, split along K (`dense`
+//      u as tagged fp32 pairs); with more adapters, chunks of <= 16 pairs of
+//      one segment over one of KP parts of K (unscaled fp32 partials).
+//   2. backbone items: 64 output rows (16 per wave, four waves) over one of S
+//      splits of K, bf16 MFMA 16x16x32 with the tokens as M and W0 rows as N.
+//      K goes in 128-column chunks; each thread issues a chunk's activation
+//      pieces and then its wave's four 1 KB weight blocks NR chunks ahead of
+//      the math into register rings (NR = 4 for T <= 32, 2 for T = 64); the
+//      next chunk's activations move to an LDS double buffer in MFMA fragment
+//      order one chunk before use.  The last split adds the other splits'
+//      partial tiles in split order and applies the adapter deltas: the
+//      chosen adapters' gated u as a (hi, lo) bf16 token operand against B_e's
+//      rows, its operands requested inside the last two rings.
 // An item only ever waits for items with smaller numbers, and the grid never
 // exceeds what the chip holds at once, so every wait ends: the smallest
 // unfinished item always has its workgroup running and nothing to wait for.

@@ -1,7 +1,6 @@
 // Launch planning for the SGMM entry points: which kernel family serves a
 // call, output-row tiling, K splits, grid and workspace layout.
 #include <algorithm>
-#include <cstdlib>
 
 #include "kernels.h"
 
@@ -81,10 +80,6 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   // and a launch with fewer tiles than CUs splits until every CU has an item
   int S = (d_in + kSplitCols / 2) / kSplitCols;
   S = std::max(S, (n_cu + launch_tiles - 1) / std::max(1, launch_tiles));
-  if (const char* env = std::getenv("RP_DECODE_SPLITS")) {  // tuning override
-    const int v = std::atoi(env);
-    if (v > 0) S = v;
-  }
   p.S = std::max(1, std::min(S, s_max));
   p.n_shrink = n_shrink;
   p.n_items = n_shrink + p.n_tiles * p.S;

@@ -585,13 +585,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
 }  // namespace
 
 int prefill_tile_rows(int T) { (void)T; return kPB; }
-int prefill_tile_tokens(int T) {
-  if (const char* env = std::getenv("RP_PREFILL_TILE_TOKENS")) {  // tuning override
-    const int v = std::atoi(env);
-    if (v == 128 || v == 256) return v;
-  }
-  return T >= kPBigT ? 256 : 128;
-}
+int prefill_tile_tokens(int T) { return T >= kPBigT ? 256 : 128; }
 // (row tile, token tile) units of one group's GEMM, the blocks of one K split
 int prefill_units(int n_tiles, int T) {
   const int bm = prefill_tile_tokens(T);

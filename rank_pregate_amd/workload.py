@@ -23,7 +23,7 @@ import numpy as np
 from . import datagen
 from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
 from . import route_sgmm_fused as rp_route_sgmm_fused, sgmm_step as rp_sgmm_step, step_workspace_size
-from . import sgmm_workspace_size, segment_workspace_size, pack_w0, RP_BF16, RP_F32
+from . import sgmm_workspace_size, segment_workspace_size, pack_w0, track_workspace, RP_BF16, RP_F32
 
 
 def to_device(a: np.ndarray, dtype: str, device):
@@ -99,7 +99,7 @@ class DeviceWorkload:
                 for p in g.projs:
                     self.outputs[(l, p)] = torch.empty((T, g.d_out), dtype=tdt, device=self.device)
         ws_bytes = step_workspace_size(self.step_groups(0), E, wl.r, k)
-        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.ws = track_workspace(torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device))
         self.step_count = 0
 
     # -- the hot path --------------------------------------------------------

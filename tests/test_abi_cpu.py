@@ -13,6 +13,8 @@ HEADER = os.path.join(ROOT, "include", "rank_pregate.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(rp.LIB_PATH), reason="library not built")
 
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
 
 def _declared():
     text = open(HEADER).read()
@@ -29,7 +31,15 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 5
+    assert rp.abi_version() == 6
+
+
+@pytest.mark.parametrize("ws,nbytes", [(None, 1 << 16), (FAKE + 16, 1 << 16), (FAKE, 4096)])
+def test_workspace_status_rejects(ws, nbytes):
+    wo, bad = ctypes.c_int32(7), ctypes.c_int32(7)
+    st = rp.lib().rp_workspace_status(ws, nbytes, 0, ctypes.byref(wo), ctypes.byref(bad), None)
+    assert st == rp.RP_ERR_WORKSPACE and rp.last_error()
+    assert wo.value == 7 and bad.value == 7  # nothing read
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -37,9 +47,6 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(rp, "LIB_PATH", "/nonexistent/librank_pregate.so")
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         rp.lib()
-
-
-FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (validation fails first)
 
 
 def _pregate(**kw):

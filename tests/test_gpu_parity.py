@@ -320,7 +320,7 @@ def test_projection_prefill_split_k(T, d_in, d_outs, E, r, k):
     The workspace is exactly rp_sgmm_workspace_size bytes (it must cover the partial tiles)."""
     say("projection split-K", T, d_in, d_outs, E, r, k)
     n = rp.sgmm_workspace_size(len(d_outs), T, d_in, sum(d_outs), E, r, k, rp.RP_BF16)
-    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ws = rp.track_workspace(torch.zeros(n, dtype=torch.uint8, device=DEV))
     _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E, ws=ws)
 
 
@@ -478,7 +478,7 @@ def test_workspace_shared_across_call_kinds():
     """One workspace through a sequence of fused, separate and differently shaped calls: each
     call starts from the control state the previous one left."""
     say("workspace sequence")
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    ws = rp.track_workspace(torch.zeros(64 << 20, dtype=torch.uint8, device=DEV))
     shapes = [(32, 512, [256, 128], 8, 16, 2), (9, 256, [64], 40, 8, 1), (64, 256, [128], 16, 32, 2)]
     for rep in range(3):
         for i, (T, d_in, d_outs, E, r, k) in enumerate(shapes):
