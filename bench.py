@@ -62,6 +62,45 @@ def measured_traffic(kernel: str, workload: str):
     return int(d["bytes_per_launch"]) if "bytes_per_launch" in d else None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def graph_kernel_nodes(graph) -> int:
+    """Kernel nodes of a captured torch CUDAGraph (hipGraphGetNodes / hipGraphNodeGetType), or -1."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        g = ctypes.c_void_p(graph.raw_cuda_graph())
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(g, None, ctypes.byref(n)) != 0:
+            return -1
+        nodes = (ctypes.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(g, nodes, ctypes.byref(n)) != 0:
+            return -1
+        kernels = 0
+        for i in range(n.value):
+            t = ctypes.c_int(-1)
+            if hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) != 0:
+                return -1
+            kernels += t.value == 0  # hipGraphNodeTypeKernel
+        return kernels
+    except (OSError, AttributeError, RuntimeError, TypeError):
+        return -1
+
+
+def percentile(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q))
+
+
 def cpu_baseline(wl, seconds: float):
     """The CPU oracle on the same workload, timed on this host (a reported baseline only)."""
     import numpy as np
@@ -94,7 +133,7 @@ def cpu_baseline(wl, seconds: float):
     return {"value": wl.T * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full {wl.name} step(s) of the fp64 NumPy oracle (T={wl.T}, layer 0, all groups), "
                       f"{el:.1f} s, widening of bf16 inputs included, input generation excluded; "
-                      f"host {platform.processor() or platform.machine()}, "
+                      f"host {cpu_model()}, "
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
@@ -202,24 +241,42 @@ def main():
             def run(i):
                 graphs[i % copies].replay()
 
-        def run_steps(n):
+        def run_steps(n, marks=None):
+            """n steps; with `marks`, an event after every round of `copies` steps (per-step samples)."""
             if args.no_graph:
                 for i in range(n):
                     run(i)
+                    if marks is not None and (i + 1) % copies == 0:
+                        marks.append(torch.cuda.Event(enable_timing=True))
+                        marks[-1].record(stream)
                 return
             for _ in range(n // copies):
                 round_graph.replay()
+                if marks is not None:
+                    marks.append(torch.cuda.Event(enable_timing=True))
+                    marks[-1].record(stream)
             for i in range(n % copies):
                 run(i)
 
         run_steps(args.warmup)
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [ev0]
         ev0.record(stream)
-        run_steps(args.steps)
+        run_steps(args.steps, marks)
         ev1.record(stream)
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps
+        step_samples = [marks[i].elapsed_time(marks[i + 1]) / copies for i in range(len(marks) - 1)]
+        if not step_samples:
+            step_samples = [ms_per_step]
+
+        # kernel launches of one step, counted in a captured graph of it
+        cg = torch.cuda.CUDAGraph(keep_graph=True)
+        with torch.cuda.graph(cg, stream=stream):
+            dw.run(0, fused=fused)
+        launches = graph_kernel_nodes(cg)
+        del cg
 
         # the dominant launch: the step's first multi-group launch (routing
         # inside when fused, then up to eight projection groups), alone, one
@@ -255,21 +312,41 @@ def main():
         torch.cuda.synchronize()
         dom_ms = a.elapsed_time(b) / (reps * copies)
 
-        # base-only (k = 0) step for the adapter overhead
-        for i in range(3):
-            dw.project(i % copies, k=0)
+        # base-only (k = 0) step for the adapter overhead: the same projection
+        # groups without routing or adapters, a round of them per graph
+        nb = max(2, args.steps // copies)
+        if args.no_graph:
+            for i in range(copies):
+                dw.project(i, k=0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(nb * copies):
+                dw.project(i % copies, k=0)
+            e1.record(stream)
+        else:
+            bg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(bg, stream=stream):
+                for c in range(copies):
+                    dw.project(c, k=0)
+            bg.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(nb):
+                bg.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        nb = max(10, args.steps // 4)
-        for i in range(nb):
-            dw.project(i % copies, k=0)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        base_ms = e0.elapsed_time(e1) / nb
+        base_ms = e0.elapsed_time(e1) / (nb * copies)
+
+        # every wait inside the launches ended and no index was out of range
+        wait_overflow, bad_idx = rp.workspace_status(dw.ws, stream=stream)
 
     step_bytes = dw.algorithmic_bytes(n_touched)
     step_flops = dw.algorithmic_flops()
+    base_bytes = dw.algorithmic_bytes(n_touched, k=0) - dw.routing_bytes()
+    base_flops = dw.algorithmic_flops(k=0) - 2 * wl.T * wl.d * wl.E
+    med, p10, p90 = (percentile(step_samples, q) for q in (50, 10, 90))
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_per_step * 1e-3)
     dom_bytes = sum(dw.group_bytes(i, n_touched) for i in range(n_dom))
@@ -279,12 +356,17 @@ def main():
     dom_groups = [names[i % len(names)] for i in range(n_dom)]
     dom_name = f"rp_sgmm_step({'route, ' if fused else ''}{', '.join(dom_groups)})"
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_flops = sum(dw.group_flops(i) for i in range(n_dom)) + (2 * wl.T * wl.d * wl.E if fused else 0)
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    mfma_bound = wl.name == "prefill_mlp"  # ~1425 FLOP per byte: past the bf16 MFMA ridge (~312)
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, {tokens_per_s:,.0f} tokens/s, algorithmic {step_bytes / 1e6:.1f} MB "
         f"-> {gbs:,.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); {step_flops / (ms_per_step * 1e-3) / 1e12:.1f} "
         f"TFLOP/s; touched adapters {n_touched}/{wl.E}")
     log(f"[bench] dominant call {dom_name}: {dom_ms * 1e3:.1f} us for {dom_bytes / 1e6:.1f} MB "
         f"-> {dom_gbs:,.0f} GB/s")
-    log(f"[bench] base-only (k=0) projections {base_ms * 1e3:.1f} us per step (eager)")
+    log(f"[bench] base-only (k=0) projections {base_ms * 1e3:.1f} us per step; adapter overhead "
+        f"{100 * (ms_per_step / base_ms - 1):.1f}%; {launches} kernel launches per step; "
+        f"median {med * 1e3:.1f} us (p10 {p10 * 1e3:.1f}, p90 {p90 * 1e3:.1f})")
 
     line = {
         "metric": METRIC,
@@ -304,12 +386,23 @@ def main():
                    "graph": not args.no_graph, "route_fused": fused, "achieved_GBps": round(gbs, 1),
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                    "algorithmic_bytes_per_step": step_bytes, "touched_adapters": n_touched},
-        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("step", wl.name),
-                     "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
-                     "bytes_per_launch": dom_bytes},
+        "roofline": ({"bound": "mfma", "achieved": round(dom_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(dom_tflops / BF16_PEAK_TFLOPS, 4)}
+                     if mfma_bound else
+                     {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4)}),
     }
+    line["roofline"].update({"traffic": measured_traffic("step", wl.name), "kernel": dom_name,
+                             "avg_launch_us": round(dom_ms * 1e3, 2), "bytes_per_launch": dom_bytes,
+                             "flops_per_launch": dom_flops, "achieved_GBps": round(dom_gbs, 1),
+                             "achieved_TFLOPs": round(dom_tflops, 1)})
+    line["timing"] = {"median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
+                      "samples": len(step_samples), "sample": f"mean step time of each round of {copies} steps",
+                      "launches_per_step": launches, "base_only_ms": round(base_ms, 5),
+                      "adapter_overhead_pct": round(100 * (ms_per_step / base_ms - 1), 2),
+                      "adapter_byte_frac": round(1 - base_bytes / step_bytes, 4),
+                      "adapter_flop_frac": round(1 - base_flops / step_flops, 4),
+                      "device_status": {"wait_overflow": wait_overflow, "bad_indices": bad_idx}}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

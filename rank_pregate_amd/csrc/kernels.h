@@ -184,6 +184,7 @@ int prefill_tile_rows(int T);                  // output rows per GEMM tile
 int prefill_tile_tokens(int T);                // tokens per GEMM tile
 int prefill_shrink_units(int T, int E, int k);  // shrink units per projection
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
+int f32_tile_rows();  // output rows per fp32 workgroup
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,
                                   int k);
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);

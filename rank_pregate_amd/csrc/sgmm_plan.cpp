@@ -10,7 +10,6 @@ namespace {
 constexpr size_t kCounterBytes = kWorkspaceCounterBytes;
 constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeMaxT = 64;
-constexpr int kF32TileRows = 64;
 constexpr int kDenseMaxE = 32;           // decode shrink covers every token per adapter up to this many adapters
 constexpr int kMaxSplits = 8;            // decode split-K
 constexpr int kMaxKParts = 8;            // decode pair-chunk shrink K parts
@@ -101,7 +100,7 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
     return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, decode_tiles(n_proj, d_out), kCounterBytes);
   SgmmPlan p{};
   p.path = (dt == kF32) ? 0 : 2;
-  p.tile_rows = p.path == 0 ? kF32TileRows : prefill_tile_rows(T);
+  p.tile_rows = p.path == 0 ? f32_tile_rows() : prefill_tile_rows(T);
   p.n_tiles = 0;
   for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + p.tile_rows - 1) / p.tile_rows;
   p.S = 1;

@@ -169,6 +169,13 @@ class DeviceWorkload:
                 b += n_touched * wl.r * (g.d_in + g.d_out) * bpe
         return b
 
+    def group_flops(self, gi: int, k: Optional[int] = None) -> int:
+        """Algorithmic FLOPs of projection group number gi of the step."""
+        wl = self.wl
+        kk = wl.k if k is None else k
+        g = wl.groups[gi % len(wl.groups)]
+        return len(g.projs) * (2 * wl.T * g.d_in * g.d_out + 2 * wl.T * kk * wl.r * (g.d_in + g.d_out))
+
     def routing_bytes(self) -> int:
         """Router weight and input, and the routing arrays."""
         wl = self.wl
