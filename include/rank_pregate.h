@@ -234,7 +234,8 @@ size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int
  * d_out % 16 == 0, d_in % 32 == 0, src and dst 16-byte aligned and disjoint. */
 rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp_dtype dt, hipStream_t stream);
 
-/* Workspace bytes rp_sgmm_fused needs for these sizes; sum_d_out is the sum of
+/* Workspace bytes rp_sgmm_fused needs for these sizes, an upper bound valid on
+ * any device; sum_d_out is the sum of
  * the projections' d_out.  Returns 0 for sizes the call would reject.
  * Besides the rank-r intermediates (T*k*r per projection), the workspace holds
  * the split-K partial tiles of long-K or few-tile calls: their count follows

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -57,6 +58,11 @@ int cu_count(int* out) {
 constexpr int64_t kIntMax = 0x7fffffff;
 
 }  // namespace
+
+namespace rp {
+// Records a status message for rp_last_error() from another source file of the library.
+rp_status record_error(rp_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace rp
 
 extern "C" {
 
@@ -280,11 +286,19 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
 // Runs the groups of a validated call in order on `stream`.  Decode shapes go
 // through the multi-group decode kernel, up to kMaxGroups groups per launch;
 // routing to compute runs inside the first launch when T <= 32, otherwise as
-// router and segmentation launches of its own first.
+// router and segmentation launches of its own first.  With `dry_need` set it
+// only plans: *dry_need receives the workspace bytes the largest launch of the
+// call uses on the current device, and nothing is launched.
 rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
-                     rp_dtype dt, const Routing& rt, void* ws, size_t ws_bytes, hipStream_t stream) {
+                     rp_dtype dt, const Routing& rt, void* ws, size_t ws_bytes, hipStream_t stream,
+                     size_t* dry_need = nullptr) {
   int n_cu = 0;
   if (cu_count(&n_cu) != 0) return fail(RP_ERR_HIP, "%s: cannot query the current device", fn);
+  const bool dry = dry_need != nullptr;
+  if (dry) {
+    *dry_need = rp::kWorkspaceCounterBytes;
+    ws_bytes = SIZE_MAX;
+  }
   const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
   const bool decode = decode_shape(dt, T);
   char* w = static_cast<char*>(ws);
@@ -312,7 +326,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
   }
   const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T, (int)E);
-  if (route && !fuse_route) {
+  if (route && !fuse_route && !dry) {
     hipError_t e = rp::launch_pregate(pg, stream);
     if (e == hipSuccess) e = rp::launch_segment(sg, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
@@ -360,9 +374,13 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         ps.block_end[i] = gemm_blocks;
       }
       if (ws_bytes < off) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, off);
+      g0 += ng;
+      if (dry) {
+        *dry_need = std::max(*dry_need, off);
+        continue;
+      }
       hipError_t e = rp::launch_prefill_step(ps, stream);
       if (e != hipSuccess) return hip_fail(fn, e);
-      g0 += ng;
     }
     return RP_OK;
   }
@@ -374,6 +392,10 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
           rp::plan_sgmm(rdt, gs[g].n_proj, d_out, (int)T, (int)gs[g].d_in, (int)E, (int)r, k, n_cu, false);
       if (ws_bytes < plan.bytes)
         return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.bytes);
+      if (dry) {
+        *dry_need = std::max(*dry_need, plan.bytes);
+        continue;
+      }
       rp::SgmmArgs a{};
       fill_group(&a, gs[g].projs, gs[g].n_proj, gs[g].x, T, gs[g].d_in, gs[g].ld_x, E, r, k, plan.tile_rows);
       a.topk_idx = rt.idx;
@@ -404,6 +426,10 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     const rp::StepPlan sp = rp::plan_step(desc, ng, (int)T, (int)E, (int)r, k, n_cu, fused_here);
     if (ws_bytes < sp.bytes)
       return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, sp.bytes);
+    if (dry) {
+      *dry_need = std::max(*dry_need, sp.bytes);
+      continue;
+    }
     rp::StepArgs st{};
     for (int i = 0; i < ng; ++i) {
       const rp_group& g = gs[g0 + i];
@@ -458,6 +484,28 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
   return RP_OK;
 }
 
+// Workspace bytes a validated call uses on the current device (0 if the
+// device cannot be queried).
+size_t exact_need(const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k, rp_dtype dt,
+                  bool route) {
+  size_t need = 0;
+  const Routing rt{route ? reinterpret_cast<const void*>(16) : nullptr, nullptr, nullptr, nullptr, nullptr};
+  const std::string saved = g_last_error;
+  if (run_groups("plan", gs, n_groups, T, E, r, k, dt, rt, nullptr, 0, nullptr, &need) != RP_OK) need = 0;
+  g_last_error = saved;
+  return need;
+}
+
+// Checks that the workspace covers every launch of a validated call before
+// anything is queued.
+rp_status check_need(const char* fn, const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                     rp_dtype dt, bool route, size_t ws_bytes) {
+  size_t need = exact_need(gs, n_groups, T, E, r, k, dt, route);
+  if (need == 0) need = groups_workspace_bytes(gs, n_groups, T, E, r, k, dt);  // no device: the bound
+  if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  return RP_OK;
+}
+
 // Checks of a call's routing pointers; `compute` when the call writes them.
 rp_status check_routing(const char* fn, const Routing& rt, int64_t T, int64_t E, int32_t k, bool compute) {
   if (compute) {
@@ -490,6 +538,8 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
   st = check_routing(fn, rt, T, E, k, false);
   if (st != RP_OK) return st;
   const rp_group g{projs, n_proj, 0, x, d_in, ld_x};
+  st = check_need(fn, &g, 1, T, E, r, k, dt, false, ws_bytes);
+  if (st != RP_OK) return st;
   return run_groups(fn, &g, 1, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
@@ -506,6 +556,8 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
   st = check_routing(fn, rt, T, E, k, true);
   if (st != RP_OK) return st;
   const rp_group g{projs, n_proj, 0, x, d_in, ld_x};
+  st = check_need(fn, &g, 1, T, E, r, k, dt, true, ws_bytes);
+  if (st != RP_OK) return st;
   return run_groups(fn, &g, 1, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
@@ -519,31 +571,53 @@ size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int
     for (int p = 0; p < groups[g].n_proj; ++p)
       if (groups[g].projs[p].d_out < 8 || groups[g].projs[p].d_out > kIntMax) return 0;
   }
-  return groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
+  // the exact need of the call on the current device (routing computed or
+  // not needs the same bytes); the device-independent bound if it cannot be
+  // queried
+  const size_t need = exact_need(groups, n_groups, T, E, r, k, dt, k > 0);
+  return need ? need : groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
 }
 
-rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
-                       const void* Wg_or_null, int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets,
-                       int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
-  g_last_error.clear();
-  const char* fn = "rp_sgmm_step";
+}  // extern "C"
+
+namespace rp {
+// Every argument check of rp_sgmm_step except the workspace's (no device call).
+rp_status validate_step(const char* fn, const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r,
+                        int32_t k, const void* Wg_or_null, int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets,
+                        int32_t* pair_perm, rp_dtype dt) {
   if (!groups || n_groups < 1 || n_groups > RP_MAX_GROUPS)
     return fail(RP_ERR_INVALID_ARG, "%s: n_groups=%d not in [1, %d]", fn, n_groups, RP_MAX_GROUPS);
+  void* const ws_stub = reinterpret_cast<void*>(256);  // the workspace is checked by the caller
   for (int g = 0; g < n_groups; ++g) {
-    char name[64];
+    char name[96];
     snprintf(name, sizeof name, "%s: group %d", fn, g);
     rp_status st = check_sgmm(name, groups[g].projs, groups[g].n_proj, groups[g].x, T, groups[g].d_in,
-                              groups[g].ld_x, E, r, k, dt, ws);
+                              groups[g].ld_x, E, r, k, dt, ws_stub);
     if (st != RP_OK) return st;
     if (groups[g].x_from_call != 0 && groups[g].x_from_call != 1)
       return fail(RP_ERR_INVALID_ARG, "%s: x_from_call must be 0 or 1", name);
   }
   if (T == 0) return RP_OK;
   const Routing rt{Wg_or_null, topk_idx, topk_gate, seg_offsets, pair_perm};
-  rp_status st = check_routing(fn, rt, T, E, k, Wg_or_null != nullptr);
+  return check_routing(fn, rt, T, E, k, Wg_or_null != nullptr);
+}
+}  // namespace rp
+
+extern "C" {
+
+rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
+                       const void* Wg_or_null, int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets,
+                       int32_t* pair_perm, rp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_sgmm_step";
+  rp_status st = rp::validate_step(fn, groups, n_groups, T, E, r, k, Wg_or_null, topk_idx, topk_gate, seg_offsets,
+                                   pair_perm, dt);
+  if (st != RP_OK || T == 0) return st;
+  if (!ws) return fail(RP_ERR_WORKSPACE, "%s: null workspace", fn);
+  if (!aligned(ws, 256)) return fail(RP_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  st = check_need(fn, groups, n_groups, T, E, r, k, dt, Wg_or_null != nullptr, ws_bytes);
   if (st != RP_OK) return st;
-  const size_t need = groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
-  if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  const Routing rt{Wg_or_null, topk_idx, topk_gate, seg_offsets, pair_perm};
   return run_groups(fn, groups, n_groups, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
