@@ -229,6 +229,22 @@ rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int6
 size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r,
                                    int32_t k, rp_dtype dt);
 
+/* rp_sgmm_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments without ws / ws_bytes, the same kernels and results.  The
+ * workspace is a static device array of 64 MiB (64 << 20 bytes) that each GPU
+ * the library runs on holds until the process ends; a call whose
+ * rp_sgmm_step_workspace_size exceeds it returns RP_ERR_WORKSPACE and launches
+ * nothing.  The first call on a device looks up that device's array and
+ * clears its control region with a kernel on `stream`; that first call must
+ * not be recorded into a graph (RP_ERR_INVALID_ARG), later ones may be.  All
+ * calls on one GPU share the array: calls that may overlap in time on one GPU
+ * (other streams, other host threads) race and give undefined results.  No
+ * hipMalloc, hipFree or other allocating routine is called. */
+rp_status rp_sgmm_step_noalloc(const rp_group* groups, int32_t n_groups, int64_t T, int64_t E, int64_t r,
+                               int32_t k, const void* Wg_or_null, int32_t* topk_idx, float* topk_gate,
+                               int32_t* seg_offsets, int32_t* pair_perm, rp_dtype dt, hipStream_t stream);
+
 /* Repack a dense row-major bf16 W0 [d_out, d_in] into RP_W0_TILED order (a
  * one-time weight preparation; the result serves every later call).
  * d_out % 16 == 0, d_in % 32 == 0, src and dst 16-byte aligned and disjoint. */

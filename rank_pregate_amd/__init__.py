@@ -30,7 +30,7 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
             "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy",
-            "rp_workspace_status")
+            "rp_workspace_status", "rp_sgmm_step_noalloc")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
@@ -86,8 +86,10 @@ def lib() -> ctypes.CDLL:
     L.rp_util_stream_read.argtypes = [vp, sz, vp, vp]
     L.rp_util_copy.argtypes = [vp, vp, sz, vp]
     L.rp_workspace_status.argtypes = [vp, sz, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
+    L.rp_sgmm_step_noalloc.argtypes = [ctypes.POINTER(RpGroup), i32, i64, i64, i64, i32, vp, vp, vp, vp, vp,
+                                       ctypes.c_int, vp]
     for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_route_sgmm_fused", "rp_sgmm_step", "rp_pack_w0",
-                 "rp_util_stream_read", "rp_util_copy", "rp_workspace_status"):
+                 "rp_util_stream_read", "rp_util_copy", "rp_workspace_status", "rp_sgmm_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -320,14 +322,8 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
     return ys
 
 
-def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx=None, topk_gate=None,
-              seg_offsets=None, pair_perm=None, ws=None, stream=None):
-    """rp_sgmm_step on torch tensors.
-
-    groups: sequence of (projs, x) or (projs, x, x_from_call); projs as for sgmm_fused.  With Wg the routing
-    is computed from the first group's x into the four routing tensors (allocated when None); without it
-    they are inputs.  Returns (list of y lists per group, topk_idx, topk_gate, seg_offsets, pair_perm).
-    """
+def _step_args(groups, E, k, Wg, topk_idx, topk_gate, seg_offsets, pair_perm):
+    """Marshal sgmm_step's arguments: (group array, arrays to keep alive, ys, routing tensors, T, dt, dev)."""
     torch = _torch()
     x0 = groups[0][1]
     T = x0.shape[0]
@@ -356,12 +352,38 @@ def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx
         ys.append(gys)
         garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(projs), from_call, _ptr(x), x.shape[1],
                           _rows(x, "x"))
+    return garr, keep, ys, (topk_idx, topk_gate, seg_offsets, pair_perm), T, dt, dev
+
+
+def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx=None, topk_gate=None,
+              seg_offsets=None, pair_perm=None, ws=None, stream=None):
+    """rp_sgmm_step on torch tensors.
+
+    groups: sequence of (projs, x) or (projs, x, x_from_call); projs as for sgmm_fused.  With Wg the routing
+    is computed from the first group's x into the four routing tensors (allocated when None); without it
+    they are inputs.  Returns (list of y lists per group, topk_idx, topk_gate, seg_offsets, pair_perm).
+    """
+    garr, keep, ys, (topk_idx, topk_gate, seg_offsets, pair_perm), T, dt, dev = _step_args(
+        groups, E, k, Wg, topk_idx, topk_gate, seg_offsets, pair_perm)
     sh = _stream(stream, dev)
     if ws is None:
         ws = _default_ws.get(lib().rp_sgmm_step_workspace_size(garr, len(groups), T, E, r, k, dt), dev, sh)
     st = lib().rp_sgmm_step(garr, len(groups), T, E, r, k, _ptr(Wg), _ptr(topk_idx), _ptr(topk_gate),
                             _ptr(seg_offsets), _ptr(pair_perm), dt, _ptr(ws), ws.numel(), sh)
     _check(st, "rp_sgmm_step")
+    return ys, topk_idx, topk_gate, seg_offsets, pair_perm
+
+
+def sgmm_step_noalloc(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx=None, topk_gate=None,
+                      seg_offsets=None, pair_perm=None, stream=None):
+    """rp_sgmm_step_noalloc on torch tensors: sgmm_step without a workspace argument (the library's
+    static one serves).  Outputs and routing tensors that are None are allocated here by torch; pass
+    them all to keep the call free of allocation."""
+    garr, keep, ys, (topk_idx, topk_gate, seg_offsets, pair_perm), T, dt, dev = _step_args(
+        groups, E, k, Wg, topk_idx, topk_gate, seg_offsets, pair_perm)
+    st = lib().rp_sgmm_step_noalloc(garr, len(groups), T, E, r, k, _ptr(Wg), _ptr(topk_idx), _ptr(topk_gate),
+                                    _ptr(seg_offsets), _ptr(pair_perm), dt, _stream(stream, dev))
+    _check(st, "rp_sgmm_step_noalloc")
     return ys, topk_idx, topk_gate, seg_offsets, pair_perm
 
 
@@ -408,3 +430,4 @@ def copy(dst, src, stream=None) -> None:
 rp_pregate, rp_segment, rp_sgmm_fused, rp_route_sgmm_fused = pregate, segment, sgmm_fused, route_sgmm_fused
 rp_sgmm_step = sgmm_step
 rp_workspace_status = workspace_status
+rp_sgmm_step_noalloc = sgmm_step_noalloc

@@ -293,3 +293,37 @@ def test_prefill_workspace_covers_split_k(T, d_in, d_outs):
     partials = ((tiles + 7) // 8 * 8) * ((T + 127) // 128) * 2 * 128 * 128 * 4  # at least two splits
     assert single >= u_only + partials
     assert step >= u_only + partials
+
+
+def _noalloc(groups=None, **kw):
+    a = dict(T=32, E=8, r=16, k=2, Wg=None, idx=FAKE, gate=FAKE, off=FAKE, perm=FAKE, dt=rp.RP_BF16)
+    a.update(kw)
+    proj = (rp.RpProj * 1)(rp.RpProj(FAKE, FAKE, FAKE, FAKE, 128, 128, 0, 0))
+    if groups is None:
+        groups = [rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), 1, 0, FAKE, 256, 256)]
+    arr = (rp.RpGroup * len(groups))(*groups)
+    return rp.lib().rp_sgmm_step_noalloc(arr, len(groups), a["T"], a["E"], a["r"], a["k"], a["Wg"], a["idx"],
+                                         a["gate"], a["off"], a["perm"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=12), rp.RP_ERR_UNSUPPORTED),
+    (dict(k=9), rp.RP_ERR_INVALID_ARG),
+    (dict(idx=None), rp.RP_ERR_INVALID_ARG),
+    (dict(Wg=FAKE, k=0), rp.RP_ERR_INVALID_ARG),
+])
+def test_noalloc_rejects(kw, status):
+    """The static-workspace variant validates like rp_sgmm_step, before any device call."""
+    assert _noalloc(**kw) == status
+    assert rp.last_error()
+
+
+def test_noalloc_rejects_beyond_static_workspace_cpu():
+    proj = (rp.RpProj * 4)(*[rp.RpProj(FAKE, FAKE, FAKE, FAKE, 256, 256, 0, 0)] * 4)
+    g = rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), 4, 0, FAKE, 256, 256)
+    assert _noalloc(groups=[g], T=4096, E=16, r=128, k=8) == rp.RP_ERR_WORKSPACE
+    assert "static" in rp.last_error()
+
+
+def test_noalloc_T0_is_noop():
+    assert _noalloc(T=0, idx=None, gate=None, off=None, perm=None) == rp.RP_OK
