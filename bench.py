@@ -177,6 +177,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--separate-route", action="store_true",
                     help="run rp_pregate and rp_segment as launches of their own instead of inside the first group")
+    ap.add_argument("--ablation", default="auto",
+                    help="comma list of baselines timed next to the fused step on the same kernels: unfused "
+                         "(a base launch and one launch per adapter), per_layer_routing (the router re-run at "
+                         "every layer); 'auto': unfused, plus per_layer_routing for multi-layer workloads; "
+                         "'none' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
@@ -209,7 +214,14 @@ def main():
         copies = max(1, min(16, -(-1_200_000_000 // per_copy)))
     log(f"[bench] workload {wl.name}: {wl.description}; weight copies {copies}")
     t_gen = time.perf_counter()
-    dw = DeviceWorkload(wl, dev, copies=copies)
+    if args.ablation == "auto":
+        variants = [] if wl.assignment != "router" else (
+            ["unfused"] + (["per_layer_routing"] if wl.layers > 1 else []) + ["token_fused", "token_merge_unmerge"])
+    elif args.ablation == "none":
+        variants = []
+    else:
+        variants = [v for v in args.ablation.split(",") if v]
+    dw = DeviceWorkload(wl, dev, copies=copies, per_layer_router="per_layer_routing" in variants)
     log(f"[bench] data generated and uploaded in {time.perf_counter() - t_gen:.1f} s")
 
     stream = torch.cuda.Stream(device=dev)  # default priority
@@ -339,6 +351,77 @@ def main():
         torch.cuda.synchronize()
         base_ms = e0.elapsed_time(e1) / (nb * copies)
 
+        # baselines on the same kernels: a round of steps per graph, rotating copies
+        ablation = {}
+        drift_ref = None
+        if "token_merge_unmerge" in variants:
+            # copy 0's layer-0 backbone weights before any merge, for the unmerge drift
+            drift_ref = {key: v.W0.clone() for key, v in dw.weights[0].items() if key[0] == dw.layers[0]}
+        for variant in variants:
+            if args.no_graph:
+                for c in range(copies):
+                    dw.run_variant(variant, c)
+                torch.cuda.synchronize()
+                va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                va.record(stream)
+                for i in range(nb * copies):
+                    dw.run_variant(variant, i % copies)
+                vb.record(stream)
+            else:
+                vg = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(vg, stream=stream):
+                    for c in range(copies):
+                        dw.run_variant(variant, c)
+                vg.replay()
+                torch.cuda.synchronize()
+                va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                va.record(stream)
+                for _ in range(nb):
+                    vg.replay()
+                vb.record(stream)
+            torch.cuda.synchronize()
+            v_ms = va.elapsed_time(vb) / (nb * copies)
+            lg = torch.cuda.CUDAGraph(keep_graph=True)
+            with torch.cuda.graph(lg, stream=stream):
+                dw.run_variant(variant, 0)
+            v_launches = graph_kernel_nodes(lg)
+            del lg
+            if not args.no_graph:
+                del vg
+            if variant.startswith("token_"):
+                ablation[variant] = {"ms_per_token": round(v_ms, 5), "launches_per_token": v_launches}
+                log(f"[bench] one token, {variant}: {v_ms * 1e3:.1f} us, {v_launches} launches")
+                continue
+            ablation[variant] = {"ms_per_step": round(v_ms, 5), "vs_fused": round(v_ms / ms_per_step, 3),
+                                 "vs_base_only": round(v_ms / base_ms, 3), "launches_per_step": v_launches}
+            log(f"[bench] baseline {variant}: {v_ms * 1e3:.1f} us per step ({v_ms / ms_per_step:.2f}x the fused step, "
+                f"{v_ms / base_ms:.2f}x base-only), {v_launches} launches")
+        if "token_fused" in ablation and "token_merge_unmerge" in ablation:
+            tf, tm = ablation["token_fused"]["ms_per_token"], ablation["token_merge_unmerge"]["ms_per_token"]
+            w0_bytes = sum(v.W0.numel() * v.W0.element_size() for v in dw.weights[0].values())
+            ablation["token_merge_unmerge"]["vs_token_fused"] = round(tm / tf, 3)
+            # merge and unmerge each read and write every W0, the backbone reads it once more
+            ablation["token_merge_unmerge"]["w0_bytes_moved"] = 5 * w0_bytes
+            ablation["token_fused"]["w0_bytes_moved"] = w0_bytes
+        if drift_ref is not None:
+            torch.cuda.synchronize()
+            changed = total = 0
+            max_abs = max_w = 0.0
+            for key, ref in drift_ref.items():
+                now = dw.weights[0][key].W0
+                diff = (now.float() - ref.float()).abs()
+                changed += int((diff > 0).sum().item())
+                total += now.numel()
+                max_abs = max(max_abs, float(diff.max().item()))
+                max_w = max(max_w, float(ref.float().abs().max().item()))
+            cycles = nb + 1
+            ablation["token_merge_unmerge"]["unmerge_drift"] = {
+                "merge_unmerge_cycles": cycles, "elements_changed_frac": round(changed / total, 6),
+                "max_abs_change": max_abs, "max_abs_change_over_max_w0": max_abs / max_w,
+                "scope": f"layer {dw.layers[0]} backbone weights of weight copy 0"}
+            log(f"[bench] unmerge drift after {cycles} merge/unmerge cycles: {100 * changed / total:.3f}% of "
+                f"layer-{dw.layers[0]} W0 elements changed, max |change| {max_abs:.2e} ({max_abs / max_w:.2e} of max|W0|)")
+
         # every wait inside the launches ended and no index was out of range
         wait_overflow, bad_idx = rp.workspace_status(dw.ws, stream=stream)
 
@@ -403,6 +486,8 @@ def main():
                       "adapter_byte_frac": round(1 - base_bytes / step_bytes, 4),
                       "adapter_flop_frac": round(1 - base_flops / step_flops, 4),
                       "device_status": {"wait_overflow": wait_overflow, "bad_indices": bad_idx}}
+    if ablation:
+        line["ablation"] = ablation
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

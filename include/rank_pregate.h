@@ -259,6 +259,52 @@ rp_status rp_pack_w0(const void* src, void* dst, int64_t d_out, int64_t d_in, rp
 size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t sum_d_out, int64_t E,
                               int64_t r, int32_t k, rp_dtype dt);
 
+/* One adapter's gated low-rank delta added in place to the outputs of the
+ * tokens in its segment, for every projection of a group (the unfused form:
+ * a base projection, e.g. rp_sgmm_fused with k = 0, then one call per adapter;
+ * the "simple fusion" that AdaFuse's ablation, technical summary §4, measures
+ * against SGMM, and the per-adapter launches its §1 blames for latency):
+ *
+ *   y[t,:] += topk_gate[t,j] * B_e (A_e x[t,:])   for every pair p = t*k + j
+ *                                                 in pair_perm[seg_offsets[e] ..
+ *                                                 seg_offsets[e+1]),  e = adapter
+ *
+ * y is read and written (it must already hold the base projection); each
+ * pair's delta is accumulated in fp32 and added with one rounding to dt, pairs
+ * of the segment in order.  W0 is not read.  projs, x, T, d_in, ld_x, E, r, k,
+ * dt as for rp_sgmm_fused; 0 <= adapter < E; k >= 1; seg_offsets / pair_perm
+ * as rp_segment writes them, topk_gate as rp_pregate writes it.  No workspace.
+ * The segment's size is read on the device, so a call can be recorded into a
+ * graph before the routing is known; an empty segment launches a no-op. */
+rp_status rp_adapter_apply(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                           int64_t ld_x, int64_t E, int64_t r, int32_t k, int32_t adapter, const float* topk_gate,
+                           const int32_t* seg_offsets, const int32_t* pair_perm, rp_dtype dt, hipStream_t stream);
+
+/* In-place merge of weighted adapters into a backbone weight, or its inverse
+ * (AdaFuse technical summary §2.B, decoding steps 3 and 5: the selected
+ * experts are folded into the backbone, the backbone runs, and they are
+ * unfolded for the next token):
+ *
+ *   W0[o,i] <- round_dt(W0[o,i] + sign * sum_{j<n_sel} weights[j] * sum_c B[e_j,o,c] A[e_j,c,i]),
+ *   e_j = sel[j]
+ *
+ * The rank sum runs in fp32 in (j, c) order and is added to W0 in fp32, then
+ * rounded to dt.  With bf16 a merge followed by an unmerge does not in general
+ * restore W0 bit for bit (each rounds): the factorised path (rp_sgmm_fused)
+ * never writes W0.
+ *
+ *   W0       [d_out, d_in] in w0_layout order (read and written)
+ *   A, B     [E, r, d_in], [E, d_out, r], dtype dt
+ *   sel      device int32 [n_sel]: adapter indices (e.g. one token's topk_idx
+ *            row); an index outside [0, E) contributes nothing
+ *   weights  device fp32 [n_sel] (e.g. that token's topk_gate row)
+ *   sign     +1 to merge, -1 to unmerge (any finite value scales the delta)
+ * Limits: d_in a multiple of 8; RP_W0_TILED as for rp_proj; r in
+ * {8,16,32,64,128}; 0 <= n_sel <= RP_MAX_K (0 is a no-op).  No workspace. */
+rp_status rp_merge_adapters(void* W0, int32_t w0_layout, int64_t d_out, int64_t d_in, const void* A, const void* B,
+                            int64_t E, int64_t r, const int32_t* sel, const float* weights, int32_t n_sel, float sign,
+                            rp_dtype dt, hipStream_t stream);
+
 /* Device-side health of an SGMM workspace (one used by rp_sgmm_fused,
  * rp_route_sgmm_fused or rp_sgmm_step).  Kernels that hand data between
  * workgroups of one launch wait for it with bounded polls; a wait that runs

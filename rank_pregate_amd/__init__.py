@@ -30,7 +30,7 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
             "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy",
-            "rp_workspace_status", "rp_sgmm_step_noalloc")
+            "rp_workspace_status", "rp_sgmm_step_noalloc", "rp_adapter_apply", "rp_merge_adapters")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
 
 
@@ -86,10 +86,15 @@ def lib() -> ctypes.CDLL:
     L.rp_util_stream_read.argtypes = [vp, sz, vp, vp]
     L.rp_util_copy.argtypes = [vp, vp, sz, vp]
     L.rp_workspace_status.argtypes = [vp, sz, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
+    L.rp_adapter_apply.argtypes = [ctypes.POINTER(RpProj), i32, vp, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp,
+                                   ctypes.c_int, vp]
+    L.rp_merge_adapters.argtypes = [vp, i32, i64, i64, vp, vp, i64, i64, vp, vp, i32, ctypes.c_float, ctypes.c_int,
+                                    vp]
     L.rp_sgmm_step_noalloc.argtypes = [ctypes.POINTER(RpGroup), i32, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                        ctypes.c_int, vp]
     for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_route_sgmm_fused", "rp_sgmm_step", "rp_pack_w0",
-                 "rp_util_stream_read", "rp_util_copy", "rp_workspace_status", "rp_sgmm_step_noalloc"):
+                 "rp_util_stream_read", "rp_util_copy", "rp_workspace_status", "rp_sgmm_step_noalloc",
+                 "rp_adapter_apply", "rp_merge_adapters"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -322,6 +327,36 @@ def sgmm_fused(projs: Sequence[Tuple], x, E: int, r: int, k: int, topk_idx=None,
     return ys
 
 
+def adapter_apply(projs: Sequence[Tuple], x, E: int, r: int, k: int, adapter: int, topk_gate, seg_offsets,
+                  pair_perm, stream=None) -> None:
+    """rp_adapter_apply on torch tensors: adds adapter `adapter`'s gated delta into each projection's y
+    (projs as for sgmm_fused, with y given and already holding the base projection)."""
+    T, d_in = x.shape
+    if any(len(pr) < 4 or pr[3] is None for pr in projs):
+        raise ValueError("adapter_apply updates y in place: every projection needs its y")
+    arr, _, _ = _proj_array(projs, x)
+    st = lib().rp_adapter_apply(arr, len(projs), _ptr(x), T, d_in, _rows(x, "x"), E, r, k, adapter,
+                                _ptr(topk_gate), _ptr(seg_offsets), _ptr(pair_perm), _dtype_code(x),
+                                _stream(stream, x.device))
+    _check(st, "rp_adapter_apply")
+
+
+def merge_adapters(W0, A, B, sel, weights, sign: float = 1.0, stream=None) -> None:
+    """rp_merge_adapters: W0 += sign * sum_j weights[j] B[sel[j]] A[sel[j]] in place.
+
+    W0: dense [d_out, d_in] or the 4-D tiled tensor pack_w0 returns; A [E, r, d_in]; B [E, d_out, r];
+    sel int32 and weights float32 device tensors of n_sel entries."""
+    tiled = W0.dim() == 4
+    d_out = W0.shape[0] * 16 if tiled else W0.shape[0]
+    E, r, d_in = A.shape
+    if sel.dtype != _torch().int32 or weights.dtype != _torch().float32 or sel.numel() != weights.numel():
+        raise ValueError("sel must be int32 and weights float32, with as many entries")
+    st = lib().rp_merge_adapters(_ptr(W0), RP_W0_TILED if tiled else RP_W0_ROWS, d_out, d_in, _ptr(A), _ptr(B), E, r,
+                                 _ptr(sel), _ptr(weights), sel.numel(), float(sign), _dtype_code(W0),
+                                 _stream(stream, W0.device))
+    _check(st, "rp_merge_adapters")
+
+
 def _step_args(groups, E, k, Wg, topk_idx, topk_gate, seg_offsets, pair_perm):
     """Marshal sgmm_step's arguments: (group array, arrays to keep alive, ys, routing tensors, T, dt, dev)."""
     torch = _torch()
@@ -431,3 +466,5 @@ rp_pregate, rp_segment, rp_sgmm_fused, rp_route_sgmm_fused = pregate, segment, s
 rp_sgmm_step = sgmm_step
 rp_workspace_status = workspace_status
 rp_sgmm_step_noalloc = sgmm_step_noalloc
+rp_adapter_apply = adapter_apply
+rp_merge_adapters = merge_adapters

@@ -621,6 +621,73 @@ rp_status rp_sgmm_step(const rp_group* groups, int32_t n_groups, int64_t T, int6
   return run_groups(fn, groups, n_groups, T, E, r, k, dt, rt, ws, ws_bytes, stream);
 }
 
+rp_status rp_adapter_apply(const rp_proj* projs, int32_t n_proj, const void* x, int64_t T, int64_t d_in,
+                           int64_t ld_x, int64_t E, int64_t r, int32_t k, int32_t adapter, const float* topk_gate,
+                           const int32_t* seg_offsets, const int32_t* pair_perm, rp_dtype dt, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_adapter_apply";
+  // the projection checks of rp_sgmm_fused (W0 is not read; no workspace is used)
+  rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, reinterpret_cast<void*>(256));
+  if (st != RP_OK) return st;
+  if (k < 1) return fail(RP_ERR_INVALID_ARG, "%s: k=%d, an adapter delta needs k >= 1", fn, k);
+  if (adapter < 0 || adapter >= E) return fail(RP_ERR_INVALID_ARG, "%s: adapter %d not in [0, E)", fn, adapter);
+  if (T == 0) return RP_OK;
+  if (!topk_gate || !seg_offsets || !pair_perm || !aligned(topk_gate, 4) || !aligned(seg_offsets, 4) ||
+      !aligned(pair_perm, 4))
+    return fail(RP_ERR_INVALID_ARG, "%s: topk_gate, seg_offsets and pair_perm must be non-null and 4-byte aligned", fn);
+  rp::SgmmArgs a{};
+  fill_group(&a, projs, n_proj, x, T, d_in, ld_x, E, r, k, rp::adapter_apply_tile_rows());
+  int tiles = 0;
+  for (int p = 0; p < n_proj; ++p)
+    tiles += (int)((projs[p].d_out + rp::adapter_apply_tile_rows() - 1) / rp::adapter_apply_tile_rows());
+  a.n_tiles = tiles;
+  a.topk_gate = topk_gate;
+  a.seg_offsets = seg_offsets;
+  a.pair_perm = pair_perm;
+  hipError_t e = rp::launch_adapter_apply(a, adapter, dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_adapter_apply launch", e);
+}
+
+rp_status rp_merge_adapters(void* W0, int32_t w0_layout, int64_t d_out, int64_t d_in, const void* A, const void* B,
+                            int64_t E, int64_t r, const int32_t* sel, const float* weights, int32_t n_sel, float sign,
+                            rp_dtype dt, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_merge_adapters";
+  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (w0_layout != RP_W0_ROWS && w0_layout != RP_W0_TILED)
+    return fail(RP_ERR_INVALID_ARG, "%s: unknown w0_layout %d", fn, w0_layout);
+  if (d_out < 1 || d_in < 8 || d_in % 8 != 0 || d_out > kIntMax || d_in > kIntMax || d_out * d_in > ((int64_t)1 << 40))
+    return fail(RP_ERR_INVALID_ARG, "%s: need d_out >= 1 and d_in a positive multiple of 8 (got %lld x %lld)", fn,
+                (long long)d_out, (long long)d_in);
+  if (w0_layout == RP_W0_TILED && (dt != RP_BF16 || d_out % 16 != 0 || d_in % 32 != 0))
+    return fail(RP_ERR_UNSUPPORTED, "%s: the tiled W0 layout needs bf16, d_out %% 16 == 0 and d_in %% 32 == 0", fn);
+  if (E < 1 || E > RP_MAX_E) return fail(RP_ERR_INVALID_ARG, "%s: E=%lld not in [1, %d]", fn, (long long)E, RP_MAX_E);
+  if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128))
+    return fail(RP_ERR_UNSUPPORTED, "%s: rank r=%lld not in {8,16,32,64,128}", fn, (long long)r);
+  if (n_sel < 0 || n_sel > RP_MAX_K) return fail(RP_ERR_INVALID_ARG, "%s: n_sel=%d not in [0, %d]", fn, n_sel, RP_MAX_K);
+  if (E * r * std::max(d_in, d_out) > ((int64_t)1 << 40)) return fail(RP_ERR_INVALID_ARG, "%s: sizes too large", fn);
+  if (n_sel == 0) return RP_OK;
+  if (!W0 || !A || !B || !aligned(W0, 16) || !aligned(A, 16) || !aligned(B, 16))
+    return fail(RP_ERR_INVALID_ARG, "%s: W0, A, B must be non-null and 16-byte aligned", fn);
+  if (!sel || !weights || !aligned(sel, 4) || !aligned(weights, 4))
+    return fail(RP_ERR_INVALID_ARG, "%s: sel and weights must be non-null and 4-byte aligned", fn);
+  rp::MergeArgs m;
+  m.W0 = W0;
+  m.tiled = w0_layout == RP_W0_TILED;
+  m.d_out = (int)d_out;
+  m.d_in = (int)d_in;
+  m.A = A;
+  m.B = B;
+  m.E = (int)E;
+  m.r = (int)r;
+  m.sel = sel;
+  m.weights = weights;
+  m.n_sel = n_sel;
+  m.sign = sign;
+  hipError_t e = rp::launch_merge(m, dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
+  return e == hipSuccess ? RP_OK : hip_fail("rp_merge_adapters launch", e);
+}
+
 rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t* wait_overflow,
                               int32_t* bad_indices, hipStream_t stream) {
   g_last_error.clear();

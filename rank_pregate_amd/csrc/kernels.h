@@ -190,6 +190,26 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
 hipError_t launch_sgmm(const SgmmArgs& a, const SgmmPlan& plan, Dtype dt, hipStream_t s);
 
 
+// One adapter's gated delta added in place to its segment's outputs (tiles of
+// adapter_apply_tile_rows() rows over the group's projections).
+hipError_t launch_adapter_apply(const SgmmArgs& a, int e, Dtype dt, hipStream_t s);
+int adapter_apply_tile_rows();
+
+// In-place merge (sign +1) or unmerge (sign -1) of n_sel weighted adapters into W0.
+struct MergeArgs {
+  void* W0;
+  int tiled;  // W0 in the rp_pack_w0 order
+  int d_out, d_in;
+  const void* A;  // [E, r, d_in]
+  const void* B;  // [E, d_out, r]
+  int E, r;
+  const int* sel;        // device: n_sel adapter indices
+  const float* weights;  // device: n_sel weights
+  int n_sel;
+  float sign;
+};
+hipError_t launch_merge(const MergeArgs& m, Dtype dt, hipStream_t s);
+
 hipError_t launch_pack_w0(const void* src, void* dst, int d_out, int d_in, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t n_bytes, hipStream_t s);

@@ -175,9 +175,10 @@ def router_input(wl: Workload) -> np.ndarray:
     return layer_input(wl, 0, wl.groups[0].x_name)
 
 
-def router_weight(wl: Workload) -> np.ndarray:
-    """Wg[d, E], N(0, 1/d)."""
-    return _fmt(wl, _normal(_seed(wl, 0, "Wg"), (wl.d, wl.E), 1.0 / np.sqrt(wl.d)))
+def router_weight(wl: Workload, layer: int = 0) -> np.ndarray:
+    """Wg[d, E], N(0, 1/d): the pre-gating router (layer 0), or the router of `layer` when every
+    layer routes on its own (the per-layer routing baseline)."""
+    return _fmt(wl, _normal(_seed(wl, layer, "Wg"), (wl.d, wl.E), 1.0 / np.sqrt(wl.d)))
 
 
 def layer_input(wl: Workload, layer: int, x_name: str) -> np.ndarray:

@@ -24,6 +24,7 @@ from . import datagen
 from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgmm_fused
 from . import route_sgmm_fused as rp_route_sgmm_fused, sgmm_step as rp_sgmm_step, step_workspace_size
 from . import sgmm_workspace_size, segment_workspace_size, pack_w0, track_workspace, RP_BF16, RP_F32
+from . import adapter_apply as rp_adapter_apply, merge_adapters as rp_merge_adapters
 
 
 def to_device(a: np.ndarray, dtype: str, device):
@@ -52,7 +53,7 @@ class DevProj:
 
 class DeviceWorkload:
     def __init__(self, wl: datagen.Workload, device="cuda:0", layers: Optional[List[int]] = None,
-                 b_scale: float = 0.1, copies: int = 1, packed: bool = True):
+                 b_scale: float = 0.1, copies: int = 1, packed: bool = True, per_layer_router: bool = False):
         import torch
         self.wl = wl
         self.device = torch.device(device)
@@ -98,9 +99,28 @@ class DeviceWorkload:
             for l in self.layers:
                 for p in g.projs:
                     self.outputs[(l, p)] = torch.empty((T, g.d_out), dtype=tdt, device=self.device)
-        ws_bytes = step_workspace_size(self.step_groups(0), E, wl.r, k)
-        self.ws = track_workspace(torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device))
+        # one workspace for every call kind made here: the whole step, each group on its own without
+        # adapters (the unfused baseline), and one token's step with and without adapters (fewer
+        # tiles per launch split K further, so a smaller call can need more)
+        groups0 = self.step_groups(0)
+        sizes = [step_workspace_size(groups0, E, wl.r, k)]
+        sizes += [step_workspace_size([g], E, wl.r, 0) for g in groups0]
+        if dt == "bf16":
+            tok = self.token_groups(0)
+            sizes += [step_workspace_size(tok, E, wl.r, k), step_workspace_size(tok, E, wl.r, 0)]
+        self.ws = track_workspace(torch.zeros(max(sizes), dtype=torch.uint8, device=self.device))
         self.step_count = 0
+        # per-layer routing baseline: a router per layer on that layer's first input
+        self.layer_routing: Dict[int, Tuple] = {}
+        self.Wg_layer: Dict[int, object] = {}
+        if per_layer_router:
+            for l in self.layers:
+                self.Wg_layer[l] = up(datagen.router_weight(wl, l))
+                self.layer_routing[l] = (
+                    torch.empty((T, k), dtype=torch.int32, device=self.device),
+                    torch.empty((T, k), dtype=torch.float32, device=self.device),
+                    torch.empty(E + 1, dtype=torch.int32, device=self.device),
+                    torch.empty(max(1, T * k), dtype=torch.int32, device=self.device))
 
     # -- the hot path --------------------------------------------------------
     def route(self, stream=None):
@@ -151,6 +171,89 @@ class DeviceWorkload:
         rp_sgmm_step(self.step_groups(copy), wl.E, wl.r, kk, topk_idx=self.sel_idx if kk else None,
                      topk_gate=self.sel_gate if kk else None, seg_offsets=self.seg_offsets if kk else None,
                      pair_perm=self.pair_perm if kk else None, ws=self.ws, stream=stream)
+
+    # -- baselines on the same kernels (AdaFuse technical summary §1 and §4) ---
+    def run_per_layer_routing(self, copy: int = 0, stream=None):
+        """The router re-run at every layer (per-layer dynamic adapters): each layer's groups in one
+        rp_sgmm_step call that first routes that layer's input with that layer's router."""
+        wl = self.wl
+        if not self.layer_routing:
+            raise RuntimeError("build the workload with per_layer_router=True")
+        groups = self.step_groups(copy)
+        n = len(wl.groups)
+        for i, l in enumerate(self.layers):
+            idx, gate, off, perm = self.layer_routing[l]
+            rp_sgmm_step(groups[i * n:(i + 1) * n], wl.E, wl.r, wl.k, Wg=self.Wg_layer[l], topk_idx=idx,
+                         topk_gate=gate, seg_offsets=off, pair_perm=perm, ws=self.ws, stream=stream)
+
+    def run_unfused(self, copy: int = 0, stream=None):
+        """Pre-gating once, then per projection group a base launch (k = 0) followed by one launch
+        per adapter adding its gated delta (the unfused "simple fusion" form)."""
+        wl = self.wl
+        self.route(stream)
+        for projs, x in self.step_groups(copy):
+            rp_sgmm_fused(projs, x, wl.E, wl.r, 0, ws=self.ws, stream=stream)
+            for e in range(wl.E):
+                rp_adapter_apply(projs, x, wl.E, wl.r, wl.k, e, self.sel_gate, self.seg_offsets, self.pair_perm,
+                                 stream=stream)
+
+    # -- one token: the pages' literal merge -> infer -> unmerge, and the factorised form
+    def _token_buffers(self):
+        import torch
+        if not hasattr(self, "tok_idx"):
+            wl, dev = self.wl, self.device
+            self.tok_idx = torch.empty((1, wl.k), dtype=torch.int32, device=dev)
+            self.tok_gate = torch.empty((1, wl.k), dtype=torch.float32, device=dev)
+            self.tok_off = torch.empty(wl.E + 1, dtype=torch.int32, device=dev)
+            self.tok_perm = torch.empty(max(1, wl.k), dtype=torch.int32, device=dev)
+            tdt = self.outputs[next(iter(self.outputs))].dtype
+            self.tok_out = {key: torch.empty((1, y.shape[1]), dtype=tdt, device=dev) for key, y in self.outputs.items()}
+
+    def token_groups(self, copy: int = 0, token: int = 0):
+        """The step's groups for one token (row `token` of every input), writing tok_out."""
+        self._token_buffers()
+        W = self.weights[copy]
+        groups = []
+        for l in self.layers:
+            for g in self.wl.groups:
+                x = self.inputs[(l, g.x_name)][token:token + 1]
+                groups.append(([(W[(l, p)].W0, W[(l, p)].A, W[(l, p)].B, self.tok_out[(l, p)]) for p in g.projs], x))
+        return groups
+
+    def run_token_fused(self, copy: int = 0, token: int = 0, stream=None):
+        """One token through the factorised fused path (routing inside the step)."""
+        wl = self.wl
+        groups = self.token_groups(copy, token)
+        rp_sgmm_step(groups, wl.E, wl.r, wl.k, Wg=self.Wg, topk_idx=self.tok_idx, topk_gate=self.tok_gate,
+                     seg_offsets=self.tok_off, pair_perm=self.tok_perm, ws=self.ws, stream=stream)
+
+    def run_token_merged(self, copy: int = 0, token: int = 0, stream=None):
+        """AdaFuse's literal decoding steps 1-5 for one token: route it, merge its k adapters into every
+        W0 of the step, run the backbone alone (k = 0), unmerge them."""
+        wl = self.wl
+        groups = self.token_groups(copy, token)
+        rp_pregate(self.x_router[token:token + 1], self.Wg, wl.k, self.tok_idx, self.tok_gate, stream=stream)
+        sel, w = self.tok_idx[0], self.tok_gate[0]
+        W = self.weights[copy]
+        for pw in W.values():
+            rp_merge_adapters(pw.W0, pw.A, pw.B, sel, w, 1.0, stream=stream)
+        rp_sgmm_step(groups, wl.E, wl.r, 0, ws=self.ws, stream=stream)
+        for pw in W.values():
+            rp_merge_adapters(pw.W0, pw.A, pw.B, sel, w, -1.0, stream=stream)
+
+    def run_variant(self, variant: str, copy: int = 0, stream=None):
+        if variant == "fused":
+            self.run(copy, stream=stream)
+        elif variant == "per_layer_routing":
+            self.run_per_layer_routing(copy, stream=stream)
+        elif variant == "unfused":
+            self.run_unfused(copy, stream=stream)
+        elif variant == "token_fused":
+            self.run_token_fused(copy, stream=stream)
+        elif variant == "token_merge_unmerge":
+            self.run_token_merged(copy, stream=stream)
+        else:
+            raise ValueError(variant)
 
     def step(self, stream=None, fused: bool = True):
         self.run(self.step_count % self.copies, fused=fused, stream=stream)

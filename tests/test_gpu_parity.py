@@ -656,7 +656,8 @@ def _device_workload(name):
     """The full-size workload on the device (every layer), built once per test session (all five
     together hold about 15 GB of device memory)."""
     if name not in _WL_CACHE:
-        _WL_CACHE[name] = DeviceWorkload(datagen.WORKLOADS[name], DEV)
+        wl = datagen.WORKLOADS[name]
+        _WL_CACHE[name] = DeviceWorkload(wl, DEV, per_layer_router=wl.layers > 1)
     return _WL_CACHE[name]
 
 
@@ -712,3 +713,186 @@ def test_determinism_repeat(name):
                 f"{name}: step {rep} output {key} differs from step 0"
         for a, b in zip((dw.topk_idx, dw.topk_gate, dw.seg_offsets, dw.pair_perm), route0):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name}: step {rep} routing differs"
+
+
+# --------------------------------------------------------------------------- baselines on the same kernels
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (32, 256, [256, 128], 8, 16, 2),
+    (9, 512, [320], 5, 128, 3),          # r = 128, ragged rows
+    (100, 128, [64], 3, 8, 1),           # segments longer than one 16-pair chunk
+    (20, 64, [512], 40, 32, 2),          # most segments empty
+])
+def test_adapter_apply(dt, T, d_in, d_outs, E, r, k):
+    """rp_adapter_apply: a base launch (k = 0) then one launch per adapter equals the fused projection
+    (the oracle), including tokens that name one adapter in two slots."""
+    say("adapter apply", dt, T, d_in, d_outs, E, r, k)
+    rng = np.random.default_rng(T + E + r)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    hw, dev = [], []
+    for d_out in d_outs:
+        W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+        B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) / np.float32(np.sqrt(r)))
+        hw.append((W0, A, B))
+        dev.append(tuple(to_device(a, dt, DEV) for a in (W0, A, B)) + (torch.empty((T, d_out), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV),))
+    idx = datagen.uniform_indices(T + 1, T, E, k)
+    if k > 1:
+        idx[::4, 1] = idx[::4, 0]
+    gate = datagen.random_gates(T + 1, T, k)
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    xd = to_device(x, dt, DEV)
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    rp.sgmm_fused(dev, xd, E, r, 0)
+    for e in range(E):
+        rp.adapter_apply(dev, xd, E, r, k, e, gate_d, off, perm)
+    torch.cuda.synchronize()
+    x64 = widen(x, dt)
+    for (W0, A, B), d in zip(hw, dev):
+        ref = oracle.sgmm(x64, widen(W0, dt), widen(A, dt), widen(B, dt), idx, gate.astype(np.float64))
+        check_y(d[3], ref, dt, "adapter apply")
+
+
+@pytest.mark.timeout(900)
+def test_ablation_per_layer_routing():
+    """The router re-run at every layer of the 32-layer step (each layer on its own router and
+    input): every layer's routing bit-exact and every output against the oracle."""
+    name = "decode_32layer"
+    wl = datagen.WORKLOADS[name]
+    dw = _device_workload(name)
+    say("per-layer routing", name)
+    dw.run_per_layer_routing()
+    torch.cuda.synchronize()
+    for l in dw.layers:
+        x_r = datagen.layer_input(wl, l, wl.groups[0].x_name)
+        Wg_l = datagen.router_weight(wl, l)
+        idx_d, gate_d, off_d, perm_d = dw.layer_routing[l]
+        same, idx_ref, gate_ref = compare_routing(idx_d, gate_d, None, widen(x_r, wl.dtype), widen(Wg_l, wl.dtype),
+                                                  wl.k)
+        assert same.all(), f"layer {l}: near ties"
+        off_ref, perm_ref = oracle.segment(idx_ref, wl.E)
+        np.testing.assert_array_equal(off_d.cpu().numpy(), off_ref)
+        np.testing.assert_array_equal(perm_d.cpu().numpy()[: wl.T * wl.k], perm_ref)
+        worst = 0.0
+        for g in wl.groups:
+            x64 = widen(datagen.layer_input(wl, l, g.x_name), wl.dtype)
+            for p in g.projs:
+                w = datagen.proj_weights(wl, l, g, p)
+                ref = oracle.sgmm(x64, widen(w.W0, wl.dtype), widen(w.A, wl.dtype), widen(w.B, wl.dtype),
+                                  idx_ref, gate_ref)
+                worst = max(worst, check_y(dw.outputs[(l, p)], ref, wl.dtype, f"per-layer L{l} {p}"))
+        say(f"per-layer routing layer {l}: worst {worst:.2e}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode_qkvo", "decode_many_adapters", "decode_32layer"])
+def test_ablation_unfused(name):
+    """Pre-gating once, then a base launch and one launch per adapter for every group: every output
+    against the oracle."""
+    wl = datagen.WORKLOADS[name]
+    dw = _device_workload(name)
+    say("unfused", name)
+    for y in dw.outputs.values():
+        y.zero_()
+    dw.run_unfused()
+    torch.cuda.synchronize()
+    idx_ref, gate_ref = _oracle_routing(wl)
+    for l in dw.layers:
+        worst = 0.0
+        for g in wl.groups:
+            x64 = widen(datagen.layer_input(wl, l, g.x_name), wl.dtype)
+            for p in g.projs:
+                w = datagen.proj_weights(wl, l, g, p)
+                ref = oracle.sgmm(x64, widen(w.W0, wl.dtype), widen(w.A, wl.dtype), widen(w.B, wl.dtype),
+                                  idx_ref, gate_ref)
+                worst = max(worst, check_y(dw.outputs[(l, p)], ref, wl.dtype, f"unfused {name} L{l} {p}"))
+        say(f"unfused {name} layer {l}: worst {worst:.2e}")
+
+
+def _unpack_tiled(packed, d_out, d_in):
+    """Row-major [d_out, d_in] from the tiled order (chunks of four 16x32 blocks, each chunk's blocks
+    row block by row block; a block's 64 groups of 8 columns, group q = row q%16, columns 8*(q//16)+)."""
+    flat = np.asarray(packed).reshape(-1)
+    out = np.empty((d_out, d_in), flat.dtype)
+    nb, n_rb = d_in // 32, d_out // 16
+    for rb in range(n_rb):
+        for cb in range(nb):
+            g = cb // 4
+            nbg = min(4, nb - 4 * g)
+            o = (4 * g * n_rb + rb * nbg + cb - 4 * g) * 512
+            blk = flat[o:o + 512].reshape(4, 16, 8)  # [column group][row][8 columns]
+            out[rb * 16:rb * 16 + 16, cb * 32:cb * 32 + 32] = blk.transpose(1, 0, 2).reshape(16, 32)
+    return out
+
+
+def _ulp_bf16(v):
+    """Spacing of bfloat16 numbers at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+@pytest.mark.parametrize("dt,tiled", [("bf16", False), ("bf16", True), ("f32", False)])
+@pytest.mark.parametrize("d_out,d_in,E,r,sel", [
+    (256, 512, 6, 16, [2, 5]),
+    (96, 1024, 4, 128, [3]),            # r = 128: several LDS stages of rank columns
+    (160, 4096, 8, 8, [7, 0, 7]),       # an adapter named twice; ragged row tile
+])
+def test_merge_infer_unmerge(dt, tiled, d_out, d_in, E, r, sel):
+    """The pages' literal decoding steps for one token: merging its adapters into W0 gives
+    W0 + sum_j g_j B_j A_j to one rounding of W0's type; the backbone alone on the merged W0 equals
+    the factorised fused projection (and the oracle); unmerging restores W0 up to rounding."""
+    if tiled and dt != "bf16":
+        pytest.skip("the tiled order is bf16 only")
+    say("merge", dt, tiled, d_out, d_in, E, r, sel)
+    rng = np.random.default_rng(d_out + d_in + r)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) / np.float32(np.sqrt(r)))
+    x = conv(rng.standard_normal((1, d_in), dtype=np.float32))
+    g = datagen.random_gates(d_in, 1, len(sel))[0]
+    W0d = to_device(W0, dt, DEV)
+    W0t = rp.pack_w0(W0d) if tiled else W0d.clone()
+    Ad, Bd, xd = (to_device(a, dt, DEV) for a in (A, B, x))
+    sel_d = torch.tensor(sel, dtype=torch.int32, device=DEV)
+    g_d = torch.from_numpy(g).to(DEV)
+    # merge
+    rp.merge_adapters(W0t, Ad, Bd, sel_d, g_d, 1.0)
+    W0_64, A64, B64 = widen(W0, dt), widen(A, dt), widen(B, dt)
+    exact = W0_64 + sum(float(gj) * (B64[e] @ A64[e]) for e, gj in zip(sel, g))
+    (y_merged,) = rp.sgmm_fused([(W0t, Ad, Bd)], xd, E, r, 0)
+    torch.cuda.synchronize()
+    if not tiled:
+        got = widen(to_host(W0t), dt)
+        if dt == "bf16":
+            slack = 2.0 ** -20 * np.abs(exact).max()  # the fp32 rank sum where W0 and the delta cancel
+            assert np.all(np.abs(got - exact) <= _ulp_bf16(exact) + slack), "merged W0 beyond one bf16 ulp"
+        else:
+            assert np.abs(got - exact).max() <= 1e-5 * np.abs(exact).max()
+    # the backbone on the merged W0 = x (W0 + sum g B A)^T = the factorised projection
+    ref = widen(x, dt)
+    ref_y = ref @ exact.T
+    check_y(y_merged, ref_y, dt, "backbone on the merged weight")
+    idx = torch.tensor([sel], dtype=torch.int32, device=DEV)
+    gate = torch.from_numpy(g[None, :].copy()).to(DEV)
+    off, perm = rp.segment(idx, E)
+    (y_fact,) = rp.sgmm_fused([(W0d, Ad, Bd)], xd, E, r, len(sel), idx, gate, off, perm)
+    torch.cuda.synchronize()
+    check_y(y_fact, oracle.sgmm(ref, W0_64, A64, B64, np.array([sel], np.int32), g[None, :].astype(np.float64)),
+            dt, "factorised")
+    # unmerge: W0 back up to the two roundings
+    rp.merge_adapters(W0t, Ad, Bd, sel_d, g_d, -1.0)
+    torch.cuda.synchronize()
+    after = to_host(W0t)
+    a64 = widen(_unpack_tiled(after, d_out, d_in) if tiled else after, dt)
+    drift = np.abs(a64 - W0_64)
+    changed = float((drift > 0).mean())
+    if dt == "bf16":
+        # the merge rounds at the merged value's scale, the unmerge at the original's
+        bound = 0.5 * _ulp_bf16(exact) + 0.5 * _ulp_bf16(W0_64) + 2.0 ** -19 * np.abs(exact).max()
+        assert np.all(drift <= bound), "unmerge drift beyond the two roundings"
+    else:
+        assert drift.max() <= 1e-5 * np.abs(exact).max()
+    say(f"unmerge: {100 * changed:.2f}% of W0 elements differ from the original (max {drift.max():.2e})")
