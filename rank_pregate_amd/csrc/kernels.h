@@ -150,6 +150,7 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
 size_t step_workspace_upper_bound(const StepGroupDesc* groups, int n_groups, int T, int E, int r, int k);
 hipError_t launch_step(const StepArgs& st, const StepPlan& plan, hipStream_t s);
 int decode_mt(int T);       // 16-token tiles of the decode kernel
+int decode_tile_rows(int T);  // output rows per decode item (16 per wave)
 int decode_chunk_k(int T);  // K per LDS chunk of the decode kernel
 int decode_resident_per_cu(int T, bool fused);  // workgroups of the decode kernel one CU holds at once
 int fused_route_tile_tokens();                  // tokens per router tile of a fused decode launch

@@ -18,8 +18,8 @@
 //      the backbone's streaming loop over every token, split along K (`dense`
 //      u as tagged fp32 pairs); with more adapters, chunks of <= 16 pairs of
 //      one segment over one of KP parts of K (unscaled fp32 partials).
-//   2. backbone items: 64 output rows (16 per wave, four waves) over one of S
-//      splits of K, bf16 MFMA 16x16x32 with the tokens as M and W0 rows as N.
+//   2. backbone items: 16 output rows per wave (four waves, or eight for 64
+//      tokens) over one of S splits of K, bf16 MFMA 16x16x32 with the tokens as M and W0 rows as N.
 //      K goes in 128-column chunks; each thread issues a chunk's activation
 //      pieces and then its wave's four 1 KB weight blocks NR chunks ahead of
 //      the math into register rings (NR = 4 for T <= 32, 2 for T = 64); the
@@ -45,23 +45,32 @@ namespace rp {
 namespace {
 
 constexpr int kSpinLimit = 1 << 22;  // ~seconds; a wait this long flags kCtlWaitOverflow and gives up
-constexpr int kWV = 4;               // waves per item
-constexpr int kThreads = 64 * kWV;
-constexpr int kTileRows = 16 * kWV;  // output rows per item, 16 per wave
 constexpr int kKC = 128;             // K per chunk
 constexpr int kKS = kKC / 32;        // MFMA k-steps per chunk
+// Waves per item (16 output rows each).  A workgroup stages each chunk's
+// activations once for all its waves, so the activation bytes per weight byte
+// of a workgroup are T / (16 * waves): with 64 tokens, eight waves (128-row
+// tiles) halve them against four (measured with a stream probe of this loop on
+// 128 MiB: 4.6 -> 5.9 TB/s); with 32 tokens or fewer four waves stream as fast.
+template <int MT>
+constexpr int kWavesOf = MT >= 4 ? 8 : 4;
+template <int MT>
+constexpr int kThreadsOf = 64 * kWavesOf<MT>;
+template <int MT>
+constexpr int kTileRowsOf = 16 * kWavesOf<MT>;
+template <int MT>
+constexpr int kBlocksPerCuOf = kWavesOf<MT> == 8 ? 1 : 2;  // launch bound: workgroups one CU holds
 // Chunks whose loads are in flight ahead of the math.  A load returns about
 // that many chunk times after issue (returns are in order behind the stream),
 // so the ring is no deeper than the bandwidth needs: with 64 tokens the
 // activation bytes equal the weight bytes and two chunks suffice.
 template <int MT>
 constexpr int kRingOf = MT >= 4 ? 2 : 4;
-static_assert(kKS == kWV, "wave w stages k-step w of every chunk's activations");
-static_assert(kThreads == 2 * kRouteThreads, "a workgroup runs two router tiles side by side");
+static_assert(kThreadsOf<2> == 2 * kRouteThreads, "a fused workgroup runs two router tiles side by side");
 static_assert(sizeof(StepArgs) <= 4096, "kernel argument block too large");
 constexpr int kFusedRouteTokens = 2;  // tokens per router tile of a fused launch
 constexpr int kMaxFusedE = 64;        // adapters a fused launch routes over (two partial sums per column)
-constexpr int kUPieces = 4;           // u pieces (two tagged values) a thread holds for the staged expand
+constexpr int kUPiecesPerItem = 1024;  // u pieces (two tagged values each) the staged expand holds per item
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, CDNA
@@ -114,11 +123,12 @@ __device__ __forceinline__ bool retry_tagged(int* ctl, bool lane_ok, int* spins)
 
 template <int MT, bool FUSED>
 constexpr size_t smem_bytes() {
+  constexpr size_t WV = kWavesOf<MT>;
   // activation chunks (double-buffered), the expand's routing, its token operand (hi, lo)
   constexpr size_t xs = 2ull * MT * kKS * 512 * sizeof(bf16_t) + 16ull * MT * kMaxK * 8 + MT * 4 * 64 * 16 * 2;
-  constexpr size_t red = (kWV - 1ull) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
+  constexpr size_t red = (WV - 1) * 8 * 64 * 4 * sizeof(float);         // pair shrink: waves 1.., 8 rank tiles
   constexpr size_t route = FUSED ? 2ull * 3 * kFusedRouteTokens * kMaxFusedE * sizeof(float) : 0;  // two router tiles
-  constexpr size_t seg = FUSED ? (size_t)kWV * kMaxE * sizeof(int) : 0;       // segmentation histograms
+  constexpr size_t seg = FUSED ? WV * kMaxE * sizeof(int) : 0;           // segmentation histograms
   size_t m = xs;
   if (red > m) m = red;
   if (route > m) m = route;
@@ -196,7 +206,7 @@ __device__ __forceinline__ size_t upart_slots(const SgmmArgs& a, const DecodeArg
 // 16) against one chunk of <= 16 pairs of e's segment, over K part kp; the
 // two waves split the part and are added in wave order.  COH: the segments
 // were written by this launch.
-template <int MTR, bool COH>
+template <int MTR, bool COH, int WV>
 __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs& d, int proj, int unit, int kp,
                                             float* red, int* s_loc, int* ctl, int ep) {
   // k-steps per batch: all loads of a batch are issued before its MFMAs, so a
@@ -230,7 +240,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
   }
   const int nsteps = (a.d_in + 31) >> 5;
   const int pb = nsteps * kp / d.KP, pe = nsteps * (kp + 1) / d.KP;
-  const int sb = pb + (pe - pb) * wave / kWV, se = pb + (pe - pb) * (wave + 1) / kWV;
+  const int sb = pb + (pe - pb) * wave / WV, se = pb + (pe - pb) * (wave + 1) / WV;
   f32x4_t acc[MTR];
 #pragma unroll
   for (int mt = 0; mt < MTR; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -260,7 +270,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int w = 1; w < kWV; ++w)
+    for (int w = 1; w < WV; ++w)
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) acc[mt] += *reinterpret_cast<const f32x4_t*>(&red[(((w - 1) * 8 + mt) * 64 + lane) * 4]);
     const size_t slots = upart_slots(a, d);
@@ -303,6 +313,11 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   constexpr uint32_t kOob = 0x80000000u;        // past any buffer: a buffer load returns zero
   constexpr int XB = MT * kKS;                  // 1 KB activation fragment blocks per chunk
   constexpr int NR = kRingOf<MT>;               // chunks in flight ahead of the math
+  constexpr int WV = kWavesOf<MT>;              // waves of the item, 16 output rows each
+  constexpr int NTH = 64 * WV;
+  constexpr int TR = 16 * WV;                   // output rows of the item
+  constexpr int MP = XB / WV;                   // activation fragment blocks a thread stages per chunk
+  static_assert(XB % WV == 0, "every wave stages the same number of fragment blocks");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = ATILE ? d.SA : a.S;
   const int tile = bi / S, split = bi % S;
@@ -311,7 +326,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int proj = ATILE ? tile / d.atiles_per_proj : proj_of_tile(a, tile);
   const ProjDesc pd = proj_at(a, proj);
   const int n_rows = ATILE ? a.E * a.r : pd.d_out;
-  const int row0 = (ATILE ? tile % d.atiles_per_proj : tile - pd.tile_begin) * kTileRows + wave * 16;
+  const int row0 = (ATILE ? tile % d.atiles_per_proj : tile - pd.tile_begin) * TR + wave * 16;
   const int lr = lane & 15, kg = lane >> 4;
   const int row = min(row0 + lr, n_rows - 1);
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
@@ -324,18 +339,19 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int nch = (a.d_in + kKC - 1) / kKC;
   const int cbeg = (int)((long long)nch * split / S);
   const int nc = (int)((long long)nch * (split + 1) / S) - cbeg;  // >= 1: the plan keeps S <= nch
-  // activation piece m of this thread: token m*16 + lane%16, columns
-  // 32*wave + 8*kg .. +7 of the chunk (k-step `wave` of token tile m)
-  const int xcol = wave * 32 + kg * 8;
-  const bf16_t* xq[MT];
+  // activation piece p of this thread: fragment block b = wave + WV*p of the
+  // chunk, i.e. token tile b / 4 (token (b/4)*16 + lane%16) and k-step b % 4
+  // = wave % 4 (columns 32*(wave%4) + 8*kg .. +7 of the chunk)
+  const int xcol = (wave & 3) * 32 + kg * 8;
+  const bf16_t* xq[MP];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) xq[m] = x + (size_t)min(m * 16 + lr, a.T - 1) * a.ld_x;
+  for (int p = 0; p < MP; ++p) xq[p] = x + (size_t)min(((wave + WV * p) >> 2) * 16 + lr, a.T - 1) * a.ld_x;
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint4 wr[NR][kKS];
-  uint4 xr[NR][MT];
+  uint4 xr[NR][MP];
 
   // The split's nc chunks are preceded by `pad` empty ones so that their count
   // V is a multiple of NR: chunk v then always sits in ring slot v % NR
@@ -364,18 +380,19 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   auto issue_x = [&](int slot, int v) {
     const int col = min((cbeg + max(v - pad, 0)) * kKC + xcol, a.d_in - 8);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xr[slot][m] = ld16(xq[m] + col);
+    for (int p = 0; p < MP; ++p) xr[slot][p] = ld16(xq[p] + col);
   };
   auto issue = [&](int slot, int v) {  // activations first, then weights
     issue_x(slot, v);
     issue_w(slot, v);
   };
-  // piece m of thread tid goes to fragment block m*kKS + wave, lane `lane`
+  // piece p of thread tid goes to fragment block wave + WV*p, lane `lane`
   auto store_x = [&](int slot, int buf, int v) {
     const int c = v - pad;
     const bool ok = c >= 0 && (cbeg + c) * kKC + xcol < a.d_in;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) *reinterpret_cast<uint4*>(&xs[(buf * XB + m * kKS) * 512 + tid * 8]) = sel4(ok, xr[slot][m]);
+    for (int p = 0; p < MP; ++p)
+      *reinterpret_cast<uint4*>(&xs[(buf * XB + WV * p) * 512 + tid * 8]) = sel4(ok, xr[slot][p]);
   };
   auto compute = [&](int slot, int buf) {
 #pragma unroll
@@ -396,15 +413,15 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     for (int i = 0; i < 4; ++i)
       w[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off == kOob ? kOob : off + 16 * i, 0, kSc1);
   };
-  // routing of the tile's tokens for the expand: pair p = tid + j * kThreads
+  // routing of the tile's tokens for the expand: pair p = tid + j * NTH
   // as (index, tag, gate bits, tag) when this launch's router tiles wrote it,
   // else (index, -, gate bits, -) from the inputs
-  constexpr int kRP = (16 * MT * kMaxK + kThreads - 1) / kThreads;
+  constexpr int kRP = (16 * MT * kMaxK + NTH - 1) / NTH;
   const int n_pairs = a.T * a.k;
   const __amdgpu_buffer_rsrc_t rt = rsrc(d.route_tagged, (uint32_t)((size_t)n_pairs * 16));
   u32x4_v rraw[kRP];
   auto route_load = [&](int j) {
-    const int p = tid + j * kThreads;
+    const int p = tid + j * NTH;
     if (FUSED) {
       rraw[j] = __builtin_amdgcn_raw_buffer_load_b128(rt, p < n_pairs ? (uint32_t)(p * 16) : kOob, 0, kSc1);
     } else {
@@ -425,7 +442,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   auto stage_route = [&](uint32_t tg) {
 #pragma unroll
     for (int j = 0; j < kRP; ++j) {
-      const int p = tid + j * kThreads;
+      const int p = tid + j * NTH;
       if (FUSED) {
         // written by this launch's router tiles, validated by tag
         int spins = 0;
@@ -447,8 +464,8 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int kcat = a.E * a.r;
   const int half_r = a.r >> 1;
   const int lg_r = __builtin_ctz(a.r);  // r is a power of two >= 8
-  constexpr int kUP = kUPieces;
-  const bool px = expand && d.dense && kcat <= 128 && n_pairs * half_r <= kUP * kThreads;
+  constexpr int kUP = kUPiecesPerItem / NTH;  // per thread
+  const bool px = expand && d.dense && kcat <= 128 && n_pairs * half_r <= kUP * NTH;
   // with two rings or more, the expand's operands are requested and placed
   // while the last chunks stream, so only its MFMAs follow the last chunk
   const bool early = !LANEX && px && V >= 2 * NR;
@@ -469,16 +486,16 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   };
   auto u_issue = [&]() {
 #pragma unroll
-    for (int i = 0; i < kUP; ++i) uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, u_piece(tid + i * kThreads), 0, kSc1);
+    for (int i = 0; i < kUP; ++i) uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, u_piece(tid + i * NTH), 0, kSc1);
   };
   auto frag_zero = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2 * MT; ++i) fhi[tid + i * kThreads] = zero4();  // fhi and flo, MT * 512 entries
+    for (int i = 0; i < 512 * MT / NTH; ++i) fhi[tid + i * NTH] = zero4();  // fhi and flo, MT * 512 entries
   };
   auto u_scatter = [&](uint32_t tg) {
 #pragma unroll
     for (int i = 0; i < kUP; ++i) {
-      const int q = tid + i * kThreads;
+      const int q = tid + i * NTH;
       const uint32_t off = u_piece(q);
       int spins = 0;
       while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins))
@@ -774,13 +791,13 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     // split-K: splits 0..S-2 publish their partial tiles as tagged pairs; the
     // last split reads them as they land and sums all S in split order
     constexpr int kWaveBytes = MT * 64 * 32;
-    const size_t tile_bytes = (size_t)S * kWV * kWaveBytes;
+    const size_t tile_bytes = (size_t)S * WV * kWaveBytes;
     const __amdgpu_buffer_rsrc_t pr =
         rsrc(reinterpret_cast<char*>(ATILE ? d.partial_a : a.partial) + tile * tile_bytes, (uint32_t)tile_bytes);
     if (!last) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        st_tagged4(pr, (uint32_t)((split * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32), acc[m], tag);
+        st_tagged4(pr, (uint32_t)((split * WV + wave) * kWaveBytes + (m * 64 + lane) * 32), acc[m], tag);
       return;
     }
     // SU splits at a time: all their loads go out before any is checked (a
@@ -800,7 +817,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             const int s = s0 + i;
-            const uint32_t off = s < S && s != split ? (uint32_t)((s * kWV + wave) * kWaveBytes + (m * 64 + lane) * 32) : kOob;
+            const uint32_t off = s < S && s != split ? (uint32_t)((s * WV + wave) * kWaveBytes + (m * 64 + lane) * 32) : kOob;
             raw[i][m][0] = __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kSc1);
             raw[i][m][1] = __builtin_amdgcn_raw_buffer_load_b128(pr, off == kOob ? kOob : off + 16, 0, kSc1);
           }
@@ -856,14 +873,14 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ys[(m * 16 + 4 * kg + v) * kTileRows + wave * 16 + lr] = f32_to_bf16(acc[m][v]);
+      for (int v = 0; v < 4; ++v) ys[(m * 16 + 4 * kg + v) * TR + wave * 16 + lr] = f32_to_bf16(acc[m][v]);
     __syncthreads();
     const int tile_row0 = row0 - wave * 16;
     bf16_t* y = static_cast<bf16_t*>(pd.y);
-    for (int q = tid; q < a.T * (kTileRows / 8); q += kThreads) {
-      const int t = q / (kTileRows / 8), c8 = (q % (kTileRows / 8)) * 8;
+    for (int q = tid; q < a.T * (TR / 8); q += NTH) {
+      const int t = q / (TR / 8), c8 = (q % (TR / 8)) * 8;
       if (tile_row0 + c8 < pd.d_out)
-        *reinterpret_cast<uint4*>(y + (size_t)t * pd.ld_y + tile_row0 + c8) = *reinterpret_cast<const uint4*>(&ys[t * kTileRows + c8]);
+        *reinterpret_cast<uint4*>(y + (size_t)t * pd.ld_y + tile_row0 + c8) = *reinterpret_cast<const uint4*>(&ys[t * TR + c8]);
     }
   }
   if (d.count_done) {
@@ -910,9 +927,10 @@ __device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
 // then is the lane-by-lane expand compiled in (its registers would otherwise
 // crowd the stream).
 template <int MT, bool FUSED, bool LANEX>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
+__global__ __launch_bounds__(kThreadsOf<MT>, kBlocksPerCuOf<MT>) void decode_kernel(StepArgs st) {
+  constexpr int WV = kWavesOf<MT>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<MT, FUSED>()];
-  __shared__ int s_ep, s_loc[2], s_wave_tot[kWV], s_bad;
+  __shared__ int s_ep, s_loc[2], s_wave_tot[WV], s_bad;
   int* ctl = st.g[0].counters;
   const int tid = threadIdx.x;
   // the epoch is read once per workgroup; backbone items publish it after
@@ -953,7 +971,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         if (tid == 0) atomicAdd(&set[kSetRouteDone], 1);
       } else {
         wait_geq(ctl, &set[kSetRouteDone], st.n_route);
-        segment_block<kWV>(st.sg, reinterpret_cast<int*>(smem), s_wave_tot, &s_bad);
+        segment_block<WV>(st.sg, reinterpret_cast<int*>(smem), s_wave_tot, &s_bad);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) atomicAdd(&set[kSetSegDone], 1);
@@ -987,10 +1005,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(StepArgs st) {
         float* red = reinterpret_cast<float*>(smem);
         if (FUSED) wait_geq(ctl, &set[kSetSegDone], 1);
         switch ((a.r + 15) >> 4) {
-          case 1: shrink_item<1, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
-          case 2: shrink_item<2, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
-          case 4: shrink_item<4, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
-          default: shrink_item<8, FUSED>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          case 1: shrink_item<1, FUSED, WV>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          case 2: shrink_item<2, FUSED, WV>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          case 4: shrink_item<4, FUSED, WV>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
+          default: shrink_item<8, FUSED, WV>(a, d, proj, unit, kp, red, s_loc, ctl, s_ep); break;
         }
         // the u stores are device-coherent; wait for them before counting this unit done
         __builtin_amdgcn_s_waitcnt(0);
@@ -1020,8 +1038,8 @@ int resident_per_cu() {
   if (cache[dev] > 0) return cache[dev];
   int n = 0;
   int n2 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MT, FUSED, false>, kThreads, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, decode_kernel<MT, FUSED, true>, kThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MT, FUSED, false>, kThreadsOf<MT>, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, decode_kernel<MT, FUSED, true>, kThreadsOf<MT>, 0) != hipSuccess)
     n = 1;
   n = std::max(1, std::min(n, n2));
   cache[dev] = n;
@@ -1035,15 +1053,15 @@ hipError_t launch_lx(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
   if (st.fused) {
     // routing inside the launch is built for up to two token tiles (T <= 32)
     switch (decode_mt(T)) {
-      case 1: decode_kernel<1, true, LANEX><<<grid, kThreads, 0, s>>>(st); break;
-      case 2: decode_kernel<2, true, LANEX><<<grid, kThreads, 0, s>>>(st); break;
+      case 1: decode_kernel<1, true, LANEX><<<grid, kThreadsOf<1>, 0, s>>>(st); break;
+      case 2: decode_kernel<2, true, LANEX><<<grid, kThreadsOf<2>, 0, s>>>(st); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (decode_mt(T)) {
-      case 1: decode_kernel<1, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
-      case 2: decode_kernel<2, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
-      default: decode_kernel<4, false, LANEX><<<grid, kThreads, 0, s>>>(st); break;
+      case 1: decode_kernel<1, false, LANEX><<<grid, kThreadsOf<1>, 0, s>>>(st); break;
+      case 2: decode_kernel<2, false, LANEX><<<grid, kThreadsOf<2>, 0, s>>>(st); break;
+      default: decode_kernel<4, false, LANEX><<<grid, kThreadsOf<4>, 0, s>>>(st); break;
     }
   }
   return hipGetLastError();
@@ -1052,7 +1070,7 @@ hipError_t launch_lx(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
 hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
   // the staged expand's conditions (base_item's px), uniform over the launch
   const SgmmArgs& a = st.g[0];
-  const bool staged = a.k == 0 || (st.dense && a.E * a.r <= 128 && a.T * a.k * (a.r / 2) <= kUPieces * kThreads);
+  const bool staged = a.k == 0 || (st.dense && a.E * a.r <= 128 && a.T * a.k * (a.r / 2) <= kUPiecesPerItem);
   return staged ? launch_lx<false>(st, plan, s) : launch_lx<true>(st, plan, s);
 }
 
@@ -1060,7 +1078,7 @@ hipError_t launch_t(const StepArgs& st, const StepPlan& plan, hipStream_t s) {
 
 int decode_mt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 int decode_chunk_k(int T) { (void)T; return kKC; }
-int decode_tile_rows() { return kTileRows; }
+int decode_tile_rows(int T) { return decode_mt(T) >= 4 ? kTileRowsOf<4> : kTileRowsOf<1>; }
 int fused_route_tile_tokens() { return 2 * kFusedRouteTokens; }  // tokens per router item
 
 int decode_resident_per_cu(int T, bool fused) {

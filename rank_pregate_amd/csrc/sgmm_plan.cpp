@@ -8,7 +8,6 @@ namespace rp {
 
 namespace {
 constexpr size_t kCounterBytes = kWorkspaceCounterBytes;
-constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeMaxT = 64;
 constexpr int kDenseMaxE = 32;           // decode shrink covers every token per adapter up to this many adapters
 constexpr int kMaxSplits = 8;            // decode split-K
@@ -35,14 +34,14 @@ size_t decode_u_bytes(int n_proj, int T, int E, int r, int k, int KP, bool dense
 }
 
 size_t decode_partial_bytes(int n_tiles, int S, int T) {
-  return S > 1 ? (size_t)n_tiles * S * 16 * decode_mt(T) * kDecodeTileRows * 8 : 0;
+  return S > 1 ? (size_t)n_tiles * S * 16 * decode_mt(T) * decode_tile_rows(T) * 8 : 0;
 }
 
-int a_tiles_per_proj(int E, int r) { return (E * r + kDecodeTileRows - 1) / kDecodeTileRows; }
+int a_tiles_per_proj(int E, int r, int T) { return (E * r + decode_tile_rows(T) - 1) / decode_tile_rows(T); }
 
-int decode_tiles(int n_proj, const int* d_out) {
+int decode_tiles(int n_proj, const int* d_out, int T) {
   int n = 0;
-  for (int i = 0; i < n_proj; ++i) n += (d_out[i] + kDecodeTileRows - 1) / kDecodeTileRows;
+  for (int i = 0; i < n_proj; ++i) n += (d_out[i] + decode_tile_rows(T) - 1) / decode_tile_rows(T);
   return n;
 }
 
@@ -52,9 +51,8 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
                            int launch_tiles, size_t off) {
   SgmmPlan p{};
   p.path = 1;
-  p.tile_rows = kDecodeTileRows;
-  p.n_tiles = 0;
-  for (int i = 0; i < n_proj; ++i) p.n_tiles += (d_out[i] + kDecodeTileRows - 1) / kDecodeTileRows;
+  p.tile_rows = decode_tile_rows(T);
+  p.n_tiles = decode_tiles(n_proj, d_out, T);
   p.t_pad = 16 * decode_mt(T);
   p.dense = E <= kDenseMaxE;
   const int nchunks = (d_in + decode_chunk_k(T) - 1) / decode_chunk_k(T);
@@ -65,7 +63,7 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   if (k > 0 && p.dense) {
     // the shrink as row tiles of [A_0; ..; A_{E-1}], split along K more finely
     // than the backbone so its results are ready before the backbone's
-    p.atiles_per_proj = a_tiles_per_proj(E, r);
+    p.atiles_per_proj = a_tiles_per_proj(E, r, T);
     p.n_atiles = p.atiles_per_proj * n_proj;
     p.SA = s_max;
     n_shrink = p.n_atiles * p.SA;
@@ -97,7 +95,7 @@ SgmmPlan plan_sgmm(Dtype dt, int n_proj, const int* d_out, int T, int d_in, int 
                    bool fused_route) {
   (void)fused_route;
   if (dt == kBF16 && T <= kDecodeMaxT)
-    return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, decode_tiles(n_proj, d_out), kCounterBytes);
+    return plan_decode_group(n_proj, d_out, T, d_in, E, r, k, n_cu, decode_tiles(n_proj, d_out, T), kCounterBytes);
   SgmmPlan p{};
   p.path = (dt == kF32) ? 0 : 2;
   p.tile_rows = p.path == 0 ? f32_tile_rows() : prefill_tile_rows(T);
@@ -119,7 +117,7 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
   size_t off = kCounterBytes;
   int items = sp.n_pre;
   int launch_tiles = 0;
-  for (int g = 0; g < n_groups; ++g) launch_tiles += decode_tiles(groups[g].n_proj, groups[g].d_out);
+  for (int g = 0; g < n_groups; ++g) launch_tiles += decode_tiles(groups[g].n_proj, groups[g].d_out, T);
   for (int g = 0; g < n_groups; ++g) {
     sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
                                  off);
@@ -160,9 +158,9 @@ size_t step_workspace_upper_bound(const StepGroupDesc* groups, int n_groups, int
     const bool dense = E <= kDenseMaxE;
     const int KP = (k > 0 && !dense) ? shrink_kparts(groups[g].d_in, r) : 1;
     b = align256(b + decode_u_bytes(groups[g].n_proj, T, E, r, k, KP, dense));
-    const int tiles = (int)(sum_d_out / kDecodeTileRows + groups[g].n_proj);
+    const int tiles = (int)(sum_d_out / decode_tile_rows(T) + groups[g].n_proj);
     b = align256(b + decode_partial_bytes(tiles, kMaxSplits, T));
-    if (k > 0 && dense) b = align256(b + decode_partial_bytes(a_tiles_per_proj(E, r) * groups[g].n_proj, kMaxSplits, T));
+    if (k > 0 && dense) b = align256(b + decode_partial_bytes(a_tiles_per_proj(E, r, T) * groups[g].n_proj, kMaxSplits, T));
   }
   return align256(b + (size_t)T * k * 16);
 }

@@ -896,3 +896,44 @@ def test_merge_infer_unmerge(dt, tiled, d_out, d_in, E, r, sel):
     else:
         assert drift.max() <= 1e-5 * np.abs(exact).max()
     say(f"unmerge: {100 * changed:.2f}% of W0 elements differ from the original (max {drift.max():.2e})")
+
+
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (20, 8000, [4096, 520], 8, 16, 2),   # ragged last chunk, ragged row tile, split K
+    (64, 2000, [4096, 4096], 16, 8, 2),  # 64 tokens (eight-wave, 128-row tiles), ragged K
+    (32, 4096, [4096], 40, 16, 2),       # pair-chunk shrink items (E * r beyond the dense form)
+    (32, 4096, [4096], 8, 16, 0),        # base only
+])
+def test_decode_shapes_repeat(T, d_in, d_outs, E, r, k):
+    """Decode-kernel shapes at the edges of its item kinds (ragged K chunk and row tile, both tile
+    heights, both shrink forms, no adapters): outputs against the oracle, and bit-identical on a
+    second call."""
+    say("decode shape", T, d_in, d_outs, E, r, k)
+    _, ys = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E, b_scale=1.0)
+    first = [y.clone() for y in ys]
+    _, ys2 = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + E, b_scale=1.0)
+    for a, b in zip(first, ys2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "decode result changed between calls"
+
+
+def test_fused_step_two_groups():
+    """Routing inside the decode launch feeding two groups (three projections, then one)."""
+    say("fused step, two groups")
+    T, E, r, k, d = 9, 8, 16, 2, 2048
+    rng = np.random.default_rng(99)
+    conv = datagen.f32_to_bf16_bits
+    hw0, dev0 = _group_weights(rng, d, [d, d, d], E, r, "bf16")
+    hw1, dev1 = _group_weights(rng, d, [d], E, r, "bf16")
+    x0 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    x1 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    Wg = conv(rng.standard_normal((d, E), dtype=np.float32) / np.float32(np.sqrt(d)))
+    groups = [(dev0, to_device(x0, "bf16", DEV)), (dev1, to_device(x1, "bf16", DEV))]
+    ys, idx, gate, off, perm = rp.sgmm_step(groups, E, r, k, Wg=to_device(Wg, "bf16", DEV))
+    torch.cuda.synchronize()
+    same, idx_ref, gate_ref = compare_routing(idx, gate, None, widen(x0, "bf16"), widen(Wg, "bf16"), k)
+    assert same.all()
+    for hw, xin, gys in ((hw0, x0, ys[0]), (hw1, x1, ys[1])):
+        for (W0, A, B), y in zip(hw, gys):
+            ref = oracle.sgmm(widen(xin, "bf16"), widen(W0, "bf16"), widen(A, "bf16"), widen(B, "bf16"), idx_ref,
+                              gate_ref)
+            check_y(y, ref, "bf16", "fused step, two groups")
