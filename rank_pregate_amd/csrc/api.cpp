@@ -146,8 +146,12 @@ size_t rp_sgmm_workspace_size(int32_t n_proj, int64_t T, int64_t d_in, int64_t s
     return 0;
   if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128)) return 0;
   if (T * k * r * n_proj > ((int64_t)1 << 34)) return 0;
-  return rp::sgmm_workspace_upper_bound(dt == RP_BF16 ? rp::kBF16 : rp::kF32, n_proj, (int)T, (int)d_in,
-                                        (long long)sum_d_out, (int)E, (int)r, k);
+  const rp::Dtype rdt = dt == RP_BF16 ? rp::kBF16 : rp::kF32;
+  size_t b = rp::sgmm_workspace_upper_bound(rdt, n_proj, (int)T, (int)d_in, (long long)sum_d_out, (int)E, (int)r, k);
+  // routing computed by the call (rp_route_sgmm_fused) may run the split-form router first
+  if (rp::mfma_router_supported(rdt, (int)E) && rp::route_split_tiles((int)T) + 1 <= rp::kRouteCounterWords)
+    b = std::max(b, rp::kWorkspaceCounterBytes + rp::route_split_bytes((int)T, (int)E));
+  return b;
 }
 
 }  // extern "C"
@@ -247,10 +251,20 @@ struct Routing {
 
 bool decode_shape(rp_dtype dt, int64_t T) { return dt == RP_BF16 && T <= 64; }
 
+// Routing computed in a step by the split-form matrix-core router (routing and
+// segmentation in one launch); its workspace need, 0 if it does not apply.
+bool split_router(rp_dtype dt, int64_t T, int64_t E) {
+  return rp::mfma_router_supported(dt == RP_BF16 ? rp::kBF16 : rp::kF32, (int)E) &&
+         rp::route_split_tiles((int)T) + 1 <= rp::kRouteCounterWords;
+}
+size_t split_router_bytes(rp_dtype dt, int64_t T, int64_t E) {
+  return split_router(dt, T, E) ? rp::kWorkspaceCounterBytes + rp::route_split_bytes((int)T, (int)E) : 0;
+}
+
 // Workspace bytes a validated call needs.
 size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
                               rp_dtype dt) {
-  size_t need = 0;
+  size_t need = split_router_bytes(dt, T, E);  // routing, if the call computes it (before any group runs)
   if (decode_shape(dt, T)) {
     for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
       const int ng = std::min(rp::kMaxGroups, n_groups - g0);
@@ -264,14 +278,15 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
     }
   } else if (dt == RP_BF16) {
     // every group's u side by side (a launch pair runs several groups)
-    need = rp::kWorkspaceCounterBytes;
+    size_t b = rp::kWorkspaceCounterBytes;
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
       for (int p = 0; p < gs[g].n_proj; ++p) sum += gs[g].projs[p].d_out;
       const int tiles_bound = (int)(sum / rp::prefill_tile_rows((int)T) + gs[g].n_proj);
-      need += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k) +
-              rp::prefill_partial_bytes(tiles_bound, (int)T, rp::prefill_max_splits((int)gs[g].d_in));
+      b += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k) +
+           rp::prefill_partial_bytes(tiles_bound, (int)T, rp::prefill_max_splits((int)gs[g].d_in));
     }
+    need = std::max(need, b);
   } else {
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
@@ -326,7 +341,19 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
   }
   const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T, (int)E);
-  if (route && !fuse_route && !dry) {
+  if (route && !fuse_route && split_router(dt, T, E)) {
+    // router and segmentation in one launch; its partial sums sit where the
+    // groups' buffers go (the groups' launches are queued after it)
+    const size_t need = split_router_bytes(dt, T, E);
+    if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+    if (dry) {
+      *dry_need = std::max(*dry_need, need);
+    } else {
+      hipError_t e = rp::launch_route_segment_mfma(pg, sg, w + rp::kWorkspaceCounterBytes,
+                                                   reinterpret_cast<int*>(w) + rp::kRouteCounterWord, stream);
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+  } else if (route && !fuse_route && !dry) {
     hipError_t e = rp::launch_pregate(pg, stream);
     if (e == hipSuccess) e = rp::launch_segment(sg, stream);
     if (e != hipSuccess) return hip_fail(fn, e);

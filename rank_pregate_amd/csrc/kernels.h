@@ -22,6 +22,15 @@ struct PregateArgs {
 };
 hipError_t launch_pregate(const PregateArgs& a, hipStream_t s);
 
+// Router on the matrix cores (bf16, 64 < E <= kMaxE, E % 8 == 0).  The tile
+// form needs no workspace (rp_pregate); the split form also runs the
+// segmentation, with route_split_bytes(T, E) of workspace for its partial sums
+// and 1 + route_split_tiles(T) arrival counters (zero before, zero after).
+bool mfma_router_supported(Dtype dt, int E);
+int route_split_tiles(int T);
+size_t route_split_bytes(int T, int E);
+hipError_t launch_route_mfma(const PregateArgs& a, hipStream_t s);
+
 struct SegmentArgs {
   const int* topk_idx;
   int n_pairs;  // T * k
@@ -32,6 +41,8 @@ struct SegmentArgs {
   int* err_count;  // first word of the workspace
 };
 hipError_t launch_segment(const SegmentArgs& a, hipStream_t s);
+hipError_t launch_route_segment_mfma(const PregateArgs& a, const SegmentArgs& sg, void* sums, int* counters,
+                                     hipStream_t s);
 
 constexpr int kMaxProj = 4;
 
@@ -174,6 +185,10 @@ constexpr size_t kWorkspaceCounterBytes = 65536;  // reserved control region at 
 // arrival counters of prefill GEMM tiles (each returns to zero when its tile
 // completes); the decode control sets sit below
 constexpr int kPrefillCounterWord = 9216;
+// words [kRouteCounterWord, + kRouteCounterWords) of that region: arrival
+// counters of the split-form router (below the decode control sets)
+constexpr int kRouteCounterWord = 128;
+constexpr int kRouteCounterWords = 1024 - kRouteCounterWord;
 constexpr int kPrefillCounterWords = (int)(kWorkspaceCounterBytes / 4) - kPrefillCounterWord;
 int prefill_splits(int d_in, int n_tiles, int T, int n_cu);          // K splits of one group's GEMM tiles
 size_t prefill_partial_bytes(int n_tiles, int T, int S);            // its split-K partial tiles

@@ -1,6 +1,8 @@
 // Token-level pre-gating kernel (AdaFuse, technical summary §2.A; §2.B decoding
 // steps 1-2): one workgroup per tile of TT tokens; the arithmetic lives in
-// route_common.h and is shared with the fused route-and-project launch.
+// route_common.h and is shared with the fused route-and-project launch.  bf16
+// routers with more than 64 columns (a multiple of 8) run on the matrix cores
+// instead (route_mfma.hip).
 #include <algorithm>
 
 #include "route_common.h"
@@ -46,6 +48,7 @@ hipError_t launch_t(const PregateArgs& a, hipStream_t s) {
 
 hipError_t launch_pregate(const PregateArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (mfma_router_supported(a.dt, a.E)) return launch_route_mfma(a, s);
   return a.dt == kBF16 ? launch_t<bf16_t>(a, s) : launch_t<float>(a, s);
 }
 

@@ -103,6 +103,66 @@ struct RoutePlan {
   int KR;     // partial sums per column left after the in-wave butterfly
 };
 
+// Top-k of tokens [t0, t0 + nt) from their logits lg[t][E] (LDS, t relative
+// to t0) and the softmax gates over the chosen logits: one wave per token,
+// waves w, w + n_waves, ... of the caller's thread group.  Larger logit first,
+// lower index on ties.  Results go out with device-scope stores (and as tagged
+// pairs when `tagged` is set).
+__device__ __forceinline__ void route_select(const PregateArgs& a, const float* lg, int t0, int nt, int wave,
+                                             int n_waves, unsigned long long* tagged, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E;
+  for (int tt = wave; tt < nt; tt += n_waves) {
+    const float* row = lg + tt * E;
+    uint32_t taken = 0;  // bit m: this lane's m-th candidate (e = lane + 64 m) is chosen
+    float selv[kMaxK];
+    int seli[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= a.k) break;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int m = 0, e = lane; e < E; ++m, e += 64) {
+        if (!((taken >> m) & 1u)) {
+          const float v = row[e];
+          if (bi == 0x7fffffff || route_better(v, e, bv, bi)) { bv = v; bi = e; }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      selv[j] = bv;
+      seli[j] = bi;
+    }
+    if (lane < a.k) {
+      // softmax over the chosen logits, shifted by the largest
+      float s = 0.f, mine = 0.f;
+      int mine_i = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= a.k) break;
+        const float z = expf(selv[j] - selv[0]);
+        s += z;
+        if (j == lane) { mine = z; mine_i = seli[j]; }
+      }
+      const size_t base = (size_t)(t0 + tt) * a.k;
+      const float g = mine / s;
+      stc_i32(&a.topk_idx[base + lane], mine_i);
+      stc_f32(&a.topk_gate[base + lane], g);
+      if (tagged) {
+        const unsigned long long hi = (unsigned long long)tag << 32;
+        __hip_atomic_store(&tagged[(base + lane) * 2], hi | (uint32_t)mine_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&tagged[(base + lane) * 2 + 1], hi | __float_as_uint(g), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
 // The k-slices (and with them the summation order of a logit) depend on E and
 // d_in only, never on T or on which launch runs the router: with E <= 64 a
 // tile has 128 threads (the decode launch runs two tiles per workgroup), with
@@ -256,57 +316,7 @@ __device__ __forceinline__ void route_tile(const PregateArgs& a, int t0, const R
   if (a.logits) {
     for (int q = tid; q < nt * E; q += NT) a.logits[(size_t)t0 * E + q] = lg[q];
   }
-
-  // top-k per token on one wave; waves take tokens w, w + 2, ...
-  for (int tt = wave; tt < nt; tt += NT / 64) {
-    const float* row = lg + tt * E;
-    uint32_t taken = 0;  // bit m: this lane's m-th candidate (e = lane + 64 m) is chosen
-    float selv[kMaxK];
-    int seli[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= a.k) break;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int m = 0, e = lane; e < E; ++m, e += 64) {
-        if (!((taken >> m) & 1u)) {
-          const float v = row[e];
-          if (bi == 0x7fffffff || route_better(v, e, bv, bi)) { bv = v; bi = e; }
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      selv[j] = bv;
-      seli[j] = bi;
-    }
-    if (lane < a.k) {
-      // softmax over the chosen logits, shifted by the largest
-      float s = 0.f, mine = 0.f;
-      int mine_i = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j >= a.k) break;
-        const float z = expf(selv[j] - selv[0]);
-        s += z;
-        if (j == lane) { mine = z; mine_i = seli[j]; }
-      }
-      const size_t base = (size_t)(t0 + tt) * a.k;
-      const float g = mine / s;
-      stc_i32(&a.topk_idx[base + lane], mine_i);
-      stc_f32(&a.topk_gate[base + lane], g);
-      if (tagged) {
-        const unsigned long long hi = (unsigned long long)tag << 32;
-        __hip_atomic_store(&tagged[(base + lane) * 2], hi | (uint32_t)mine_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&tagged[(base + lane) * 2 + 1], hi | __float_as_uint(g), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  route_select(a, lg, t0, nt, wave, NT / 64, tagged, tag);
 }
 
 // ---------------------------------------------------------------------------

@@ -33,6 +33,8 @@ constexpr int kSetGroupDone = kSetArriveAll + 64;
 constexpr int kSetQueue = kSetGroupDone + 256 * kMaxGroups;  // items handed out after each workgroup's first
 constexpr int kSetWords = kSetQueue + 32;
 static_assert(kCtlSet0 + 2 * kCtlSetStride <= kPrefillCounterWord, "control sets overlap the prefill counters");
+static_assert(kCtlSegErr < kRouteCounterWord && kRouteCounterWord + kRouteCounterWords <= kCtlSet0,
+              "router counters overlap the control words");
 static_assert(kSetWords <= kCtlSetStride, "control set overflow");
 
 // Device-scope (sc1) loads of routing data another workgroup of the same

@@ -145,10 +145,11 @@ def test_pregate_exact_ties(dt, T, d, E, k):
 
 
 @pytest.mark.parametrize("T", [1, 255, 256, 257, 512, 513, 1030])
-@pytest.mark.parametrize("E", [8, 300])
+@pytest.mark.parametrize("E", [8, 296, 300])
 def test_pregate_tile_sizes(T, E):
-    """Router tiles of one, two or four tokens (chosen from T) give logits within the fp32
-    accumulation bound and the oracle's top-k away from near ties."""
+    """Router tiles of one, two or four tokens (chosen from T; E = 8, 300) and the matrix-core
+    router's 16-token tiles (E = 296) give logits within the fp32 accumulation bound and the
+    oracle's top-k away from near ties."""
     say("pregate tile sizes", T, E)
     rng = np.random.default_rng(7 * T + E)
     d, k = 256, 2
@@ -464,6 +465,8 @@ def _fused_case(T, d_in, d_outs, E, r, k, dt, seed, tiled=False, ws=None):
     (48, 1024, [512], 1024, 32, 8, "bf16"),           # E = 1024: two-token router tiles, k = 8
     (5, 128, [128], 3, 128, 3, "bf16"),               # r = 128
     (100, 256, [128], 8, 16, 2, "bf16"),              # prefill shape: three launches
+    (100, 200, [64], 200, 8, 3, "bf16"),              # matrix-core router, split form: ragged K, two column chunks
+    (257, 4096, [128], 256, 16, 2, "bf16"),           # matrix-core router, split form: 17 token tiles, ragged last
     (16, 128, [64], 4, 8, 1, "f32"),                  # fp32: three launches
 ])
 def test_route_fused(T, d_in, d_outs, E, r, k, dt):
