@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 6
+#define RP_ABI_VERSION 7
 #define RP_MAX_K 8          /* largest top-k */
 #define RP_MAX_E 1024       /* largest adapter count */
 #define RP_MAX_PROJ 4       /* projections per rp_sgmm_fused call (per group) */
@@ -86,7 +86,11 @@ typedef enum { RP_W0_ROWS = 0, RP_W0_TILED = 1 } rp_w0_layout;
  *   A  [E, r, d_in]      adapter down-projections, dense, one block per adapter
  *   B  [E, d_out, r]     adapter up-projections, dense, one block per adapter
  *   y  [T, d_out]        output, leading dimension ld_y (>= d_out)
- * All four have the call's dtype.  y must not alias any input.
+ *   residual [T, d_out]  NULL, or a tensor added to the output before its one
+ *                        rounding (a decoder layer's residual stream), with the
+ *                        leading dimension ld_y; it may be y itself (updated
+ *                        in place) but must not otherwise overlap y
+ * All have the call's dtype.  y must not alias any other input.
  * RP_W0_TILED needs bf16, d_out % 16 == 0 and d_in % 32 == 0; reserved must be 0. */
 typedef struct {
   const void* W0;
@@ -97,6 +101,7 @@ typedef struct {
   int64_t ld_y;
   int32_t w0_layout;
   int32_t reserved;
+  const void* residual;
 } rp_proj;
 
 /* Token-level pre-gating (AdaFuse §2.A; §2.B decoding steps 1-2).
@@ -194,6 +199,17 @@ rp_status rp_route_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* 
                               int32_t* topk_idx, float* topk_gate, int32_t* seg_offsets, int32_t* pair_perm,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Activation a group applies to its outputs (rp_group.act).
+ *   RP_ACT_NONE       the projections' outputs as they are
+ *   RP_ACT_SILU_MUL   gated MLP input: the group has two projections of equal
+ *                     d_out (gate, then up; packed as in "FlashSVD v1.5", La
+ *                     Solución) and projs[0].y receives
+ *                        m = round(silu(g) * u),  silu(g) = g / (1 + exp(-g)),
+ *                     from the rounded outputs g (projection 0) and u
+ *                     (projection 1), in fp32 -- the values rp_silu_mul gives
+ *                     on them -- while projs[1].y keeps u. */
+typedef enum { RP_ACT_NONE = 0, RP_ACT_SILU_MUL = 1 } rp_act;
+
 /* One group of projections that share their input x (see rp_sgmm_fused). */
 typedef struct {
   const rp_proj* projs;  /* host array of n_proj (1..RP_MAX_PROJ) descriptors */
@@ -202,6 +218,8 @@ typedef struct {
   const void* x;         /* [T, d_in], leading dimension ld_x */
   int64_t d_in;
   int64_t ld_x;
+  int32_t act;           /* rp_act */
+  int32_t reserved;      /* must be 0 */
 } rp_group;
 
 /* A decode step (AdaFuse §2.B decoding steps 1-3 over every adapted layer).
@@ -325,6 +343,28 @@ rp_status rp_merge_adapters(void* W0, int32_t w0_layout, int64_t d_out, int64_t 
  * RP_ERR_DEVICE when either word is nonzero, RP_OK when both are zero. */
 rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t* wait_overflow,
                               int32_t* bad_indices, hipStream_t stream);
+
+/* RMSNorm of each token row: the normalisation in front of the attention and
+ * MLP projections of a Llama-style decoder layer (the 7B models AdaFuse
+ * measures latency on, technical summary §4), part of the base model's
+ * standard inference that decoding step 4 of §2.B runs between the adapted
+ * projections:
+ *
+ *   y[t,i] = round(x[t,i] * inv[t] * gamma[i]),
+ *   inv[t] = 1 / sqrt(sum_i x[t,i]^2 / d + eps)      fp32, fixed summation order
+ *
+ *   x [T, d] (ld_x), gamma [d], y [T, d] (ld_y), dtype dt; y may be x.
+ * Limits: d a multiple of 8 (bf16) / 4 (fp32), d <= 65536; pointers 16-byte
+ * aligned, ld*sizeof(dt) multiples of 16; eps >= 0 finite; T = 0 is a no-op. */
+rp_status rp_rmsnorm(const void* x, int64_t T, int64_t d, int64_t ld_x, const void* gamma, float eps, void* y,
+                     int64_t ld_y, rp_dtype dt, hipStream_t stream);
+
+/* Gated MLP activation as its own launch (what RP_ACT_SILU_MUL fuses):
+ *   m[t,i] = round(silu(g[t,i]) * u[t,i]),  silu(g) = g / (1 + exp(-g)), fp32.
+ *   g, u, m [T, d] with leading dimensions ld_g, ld_u, ld_m; m may be g or u.
+ * Limits as for rp_rmsnorm. */
+rp_status rp_silu_mul(const void* g, int64_t ld_g, const void* u, int64_t ld_u, int64_t T, int64_t d, void* m,
+                      int64_t ld_m, rp_dtype dt, hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* rp_last_error(void);

@@ -12,6 +12,10 @@ Token-Level Pre-Gating and Fused Kernel Optimization", technical summary §2):
   * §2.A token-level pre-gating: one light linear router scores each token once
     (logits = x . Wg), the top-k adapters are chosen, and that choice is held
     for every later layer and projection.
+  * the decoder layer around the projections (§2.B decoding step 4 runs the
+    base model; §4 measures Llama-family 7B models): RMSNorm, residual adds and
+    the silu(gate) * up MLP activation, with bf16 rounding at each operation's
+    output (decoder_layer).
   * §2.B SGMM / decoding procedure: the chosen LoRA experts are applied together
     with the backbone projection in one pass.  In factorised form
         y[t] = W0 x[t] + sum_j g[t,j] * B_{e(t,j)} (A_{e(t,j)} x[t]),
@@ -28,4 +32,5 @@ closed forms and invariants; none is "parity unpinned".
 from . import reference, brute  # noqa: F401
 from .reference import (  # noqa: F401
     widen, router_logits, select_topk, topk_margin, softmax_gates, pregate, segment, sgmm,
+    round_bf16, rmsnorm, silu_mul, decoder_layer,
 )

@@ -107,3 +107,58 @@ def projection(x, W0, A, B, idx, gate) -> List[List[float]]:
             row.append(s)
         y.append(row)
     return y
+
+
+def bf16_grid_nearest(v: float) -> float:
+    """Nearest bfloat16 value by walking the representable grid (ties: even last significand bit).
+
+    A bfloat16 is the float32 whose upper 16 bits are the pattern; the two
+    patterns around v are found from v's float32 bits and compared directly.
+    """
+    import struct
+    if v == 0.0:
+        return 0.0
+    bits = struct.unpack("<I", struct.pack("<f", v))[0] & 0xFFFF0000  # a pattern at or toward zero from v
+    lo = struct.unpack("<f", struct.pack("<I", bits))[0]
+    hi = struct.unpack("<f", struct.pack("<I", bits + 0x10000))[0]  # next pattern away from zero
+    if abs(lo) > abs(v):  # float32 rounding of v went past it: step back one pattern
+        lo, hi = struct.unpack("<f", struct.pack("<I", bits - 0x10000))[0], lo
+        bits -= 0x10000
+    dl, dh = abs(v - lo), abs(hi - v)
+    if dl < dh:
+        return lo
+    if dh < dl:
+        return hi
+    return lo if (bits >> 16) % 2 == 0 else hi
+
+
+def decoder_layer(h, w, idx, gate, eps: float):
+    """The decoder layer of oracle.reference.decoder_layer without the bf16 rounding, in loops.
+
+    n1 = rmsnorm(h, gamma1); v = proj_v(n1); h1 = h + proj_o(v);
+    n2 = rmsnorm(h1, gamma2); m = silu(proj_gate(n2)) * proj_up(n2); h2 = h1 + proj_down(m).
+    """
+    h = [list(map(float, r)) for r in _tolist(h)]
+
+    def norm(x, gamma):
+        gamma = _tolist(gamma)
+        out = []
+        for row in x:
+            ms = sum(v * v for v in row) / len(row)
+            inv = 1.0 / math.sqrt(ms + eps)
+            out.append([row[i] * inv * gamma[i] for i in range(len(row))])
+        return out
+
+    def proj(x, name):
+        W0, A, B = w[name]
+        return projection(x, W0, A, B, idx, gate)
+
+    def add(a, b):
+        return [[a[t][i] + b[t][i] for i in range(len(a[t]))] for t in range(len(a))]
+
+    n1 = norm(h, w["gamma1"])
+    h1 = add(h, proj(proj(n1, "v"), "o"))
+    n2 = norm(h1, w["gamma2"])
+    g, u = proj(n2, "gate"), proj(n2, "up")
+    m = [[g[t][i] / (1.0 + math.exp(-g[t][i])) * u[t][i] for i in range(len(g[t]))] for t in range(len(g))]
+    return add(h1, proj(m, "down"))

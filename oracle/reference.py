@@ -136,3 +136,82 @@ def sgmm(x: np.ndarray, W0: np.ndarray, A: np.ndarray, B: np.ndarray, idx: np.nd
             u = A[e] @ x[t]                 # rank-r intermediate
             y[out_row] += gate[t, j] * (B[e] @ u)
     return y
+
+
+# ----------------------------------------------------------------------------- decoder layer
+# Whole-step chaining around the adapted projections.  Decoding step 4 of the
+# AdaFuse page (technical summary §2.B) runs the base model's standard
+# inference between the projections; §4 measures Llama2-7B / Mistral-7B, whose
+# decoder layer normalises with RMSNorm, adds residuals and gates its MLP with
+# silu(gate) * up (gate and up packed into one wide operation on the
+# "FlashSVD v1.5" page, La Solución).  Reading: the activations that cross
+# from one operation to the next are bf16 tensors (the interface dtype), so
+# each operation's output is rounded once to bf16, round-to-nearest-even.
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each element (ties to the even significand), as fp64.
+
+    bfloat16 keeps 8 significant bits: for |a| in [2^e, 2^(e+1)) the spacing is
+    2^(e-7); a is divided by that spacing, rounded half-to-even, and scaled back.
+    Finite normal-range inputs only.
+    """
+    a = np.asarray(a, np.float64)
+    out = np.zeros_like(a)
+    nz = a != 0
+    e = np.floor(np.log2(np.abs(a[nz])))
+    step = np.exp2(e - 7)
+    q = a[nz] / step
+    # guard the exponent against log2 landing one off at powers of two
+    big = np.abs(q) >= 256
+    step = np.where(big, step * 2, step)
+    q = a[nz] / step
+    small = np.abs(q) < 128
+    step = np.where(small, step / 2, step)
+    out[nz] = np.round(a[nz] / step) * step  # np.round: half to even
+    return out
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row: x[t] * gamma / sqrt(mean_i x[t,i]^2 + eps).  fp64."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, np.float64)[None, :]
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Gated MLP activation: silu(g) * u with silu(g) = g / (1 + exp(-g)).  fp64."""
+    g = np.asarray(g, np.float64)
+    return g / (1.0 + np.exp(-g)) * np.asarray(u, np.float64)
+
+
+def decoder_layer(h: np.ndarray, w: dict, idx: np.ndarray, gate: np.ndarray, eps: float,
+                  rnd=round_bf16) -> np.ndarray:
+    """One decode-step layer around the adapted projections; returns the next residual stream.
+
+    w maps "gamma1", "gamma2" to [d] and "q","k","v","o","gate","up","down" to
+    (W0, A, B) triples.  Every projection applies the step's routing (idx,
+    gate) through `sgmm`.  Reading (attention is outside the method): the
+    token attends to a single cached position, whose softmax weight is 1, so
+    the attention output equals v.  Each operation's output passes through
+    `rnd` (bf16 rounding by default):
+
+        n1 = rnd(rmsnorm(h, gamma1))
+        q, k, v = rnd(proj(n1))                  (q and k feed only the attention)
+        h1 = rnd(h + proj_o(v))                  residual inside the one rounding
+        n2 = rnd(rmsnorm(h1, gamma2))
+        g, u = rnd(proj_gate(n2)), rnd(proj_up(n2))
+        m = rnd(silu(g) * u)
+        h2 = rnd(h1 + proj_down(m))
+    """
+    def proj(x, name):
+        W0, A, B = w[name]
+        return sgmm(x, W0, A, B, idx, gate)
+
+    n1 = rnd(rmsnorm(h, w["gamma1"], eps))
+    v = rnd(proj(n1, "v"))
+    h1 = rnd(np.asarray(h, np.float64) + proj(v, "o"))
+    n2 = rnd(rmsnorm(h1, w["gamma2"], eps))
+    g = rnd(proj(n2, "gate"))
+    u = rnd(proj(n2, "up"))
+    m = rnd(silu_mul(g, u))
+    return rnd(h1 + proj(m, "down"))

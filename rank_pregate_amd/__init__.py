@@ -30,8 +30,10 @@ _STATUS_NAMES = {0: "RP_OK", 1: "RP_ERR_INVALID_ARG", 2: "RP_ERR_UNSUPPORTED", 3
 
 EXPORTED = ("rp_pregate", "rp_segment", "rp_segment_workspace_size", "rp_sgmm_fused", "rp_sgmm_workspace_size",
             "rp_route_sgmm_fused", "rp_sgmm_step", "rp_sgmm_step_workspace_size", "rp_pack_w0", "rp_last_error", "rp_abi_version", "rp_util_stream_read", "rp_util_copy",
-            "rp_workspace_status", "rp_sgmm_step_noalloc", "rp_adapter_apply", "rp_merge_adapters")
+            "rp_workspace_status", "rp_sgmm_step_noalloc", "rp_adapter_apply", "rp_merge_adapters", "rp_rmsnorm",
+            "rp_silu_mul")
 RP_W0_ROWS, RP_W0_TILED = 0, 1
+RP_ACT_NONE, RP_ACT_SILU_MUL = 0, 1
 
 
 class RankPregateError(RuntimeError):
@@ -43,12 +45,13 @@ class RankPregateError(RuntimeError):
 class RpProj(ctypes.Structure):
     _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("d_out", ctypes.c_int64), ("ld_y", ctypes.c_int64), ("w0_layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("residual", ctypes.c_void_p)]
 
 
 class RpGroup(ctypes.Structure):
     _fields_ = [("projs", ctypes.POINTER(RpProj)), ("n_proj", ctypes.c_int32), ("x_from_call", ctypes.c_int32),
-                ("x", ctypes.c_void_p), ("d_in", ctypes.c_int64), ("ld_x", ctypes.c_int64)]
+                ("x", ctypes.c_void_p), ("d_in", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("act", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,9 +95,11 @@ def lib() -> ctypes.CDLL:
                                     vp]
     L.rp_sgmm_step_noalloc.argtypes = [ctypes.POINTER(RpGroup), i32, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                        ctypes.c_int, vp]
+    L.rp_rmsnorm.argtypes = [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64, ctypes.c_int, vp]
+    L.rp_silu_mul.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, ctypes.c_int, vp]
     for name in ("rp_pregate", "rp_segment", "rp_sgmm_fused", "rp_route_sgmm_fused", "rp_sgmm_step", "rp_pack_w0",
                  "rp_util_stream_read", "rp_util_copy", "rp_workspace_status", "rp_sgmm_step_noalloc",
-                 "rp_adapter_apply", "rp_merge_adapters"):
+                 "rp_adapter_apply", "rp_merge_adapters", "rp_rmsnorm", "rp_silu_mul"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -262,6 +267,7 @@ def _proj_array(projs: Sequence[Tuple], x):
     for i, pr in enumerate(projs):
         W0, A, B = pr[0], pr[1], pr[2]
         y = pr[3] if len(pr) > 3 else None
+        res = pr[4] if len(pr) > 4 else None
         tiled = W0.dim() == 4
         d_out = W0.shape[0] * 16 if tiled else W0.shape[0]
         for name, t in (("W0", W0), ("A", A), ("B", B)):
@@ -270,8 +276,11 @@ def _proj_array(projs: Sequence[Tuple], x):
         if y is None:
             y = torch.empty((T, d_out), dtype=x.dtype, device=x.device)
         ys.append(y)
+        if res is not None and (res.dtype != x.dtype or tuple(res.shape) != tuple(y.shape)
+                                or _rows(res, "residual") != _rows(y, "y")):
+            raise ValueError(f"projection {i}: residual must have y's dtype, shape and row stride")
         arr[i] = RpProj(_ptr(W0), _ptr(A), _ptr(B), _ptr(y), d_out, _rows(y, "y"),
-                        RP_W0_TILED if tiled else RP_W0_ROWS, 0)
+                        RP_W0_TILED if tiled else RP_W0_ROWS, 0, _ptr(res))
         sum_d_out += d_out
     return arr, ys, sum_d_out
 
@@ -380,13 +389,14 @@ def _step_args(groups, E, k, Wg, topk_idx, topk_gate, seg_offsets, pair_perm):
     for i, g in enumerate(groups):
         projs, x = g[0], g[1]
         from_call = int(g[2]) if len(g) > 2 else 0
+        act = int(g[3]) if len(g) > 3 else RP_ACT_NONE
         if x.shape[0] != T or x.dtype != x0.dtype:
             raise ValueError(f"group {i}: x must have T rows and the first group's dtype")
         arr, gys, _ = _proj_array(projs, x)
         keep.append(arr)
         ys.append(gys)
         garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(projs), from_call, _ptr(x), x.shape[1],
-                          _rows(x, "x"))
+                          _rows(x, "x"), act, 0)
     return garr, keep, ys, (topk_idx, topk_gate, seg_offsets, pair_perm), T, dt, dev
 
 
@@ -394,7 +404,8 @@ def sgmm_step(groups: Sequence[Tuple], E: int, r: int, k: int, Wg=None, topk_idx
               seg_offsets=None, pair_perm=None, ws=None, stream=None):
     """rp_sgmm_step on torch tensors.
 
-    groups: sequence of (projs, x) or (projs, x, x_from_call); projs as for sgmm_fused.  With Wg the routing
+    groups: sequence of (projs, x), (projs, x, x_from_call) or (projs, x, x_from_call, act); projs as for
+    sgmm_fused, each (W0, A, B[, y[, residual]]); act RP_ACT_SILU_MUL writes silu(y0) * y1 over y0.  With Wg the routing
     is computed from the first group's x into the four routing tensors (allocated when None); without it
     they are inputs.  Returns (list of y lists per group, topk_idx, topk_gate, seg_offsets, pair_perm).
     """
@@ -431,8 +442,34 @@ def step_workspace_size(groups: Sequence[Tuple], E: int, r: int, k: int) -> int:
         arr, _, _ = _proj_array(g[0], g[1])
         keep.append(arr)
         garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(g[0]), 0, _ptr(g[1]), g[1].shape[1],
-                          _rows(g[1], "x"))
+                          _rows(g[1], "x"), int(g[3]) if len(g) > 3 else RP_ACT_NONE, 0)
     return lib().rp_sgmm_step_workspace_size(garr, len(groups), x0.shape[0], E, r, k, _dtype_code(x0))
+
+
+def rmsnorm(x, gamma, eps: float = 1e-5, out=None, stream=None):
+    """rp_rmsnorm: out[t] = round(x[t] * gamma / sqrt(mean(x[t]^2) + eps)); out may be x."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    if gamma.dtype != x.dtype or not gamma.is_contiguous() or gamma.numel() != x.shape[1]:
+        raise ValueError("gamma must be a dense [d] tensor with x's dtype")
+    st = lib().rp_rmsnorm(_ptr(x), x.shape[0], x.shape[1], _rows(x, "x"), _ptr(gamma), float(eps), _ptr(out),
+                          _rows(out, "out"), _dtype_code(x), _stream(stream, x.device))
+    _check(st, "rp_rmsnorm")
+    return out
+
+
+def silu_mul(g, u, out=None, stream=None):
+    """rp_silu_mul: out = round(silu(g) * u) elementwise in fp32; out may be g or u."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(g)
+    if u.shape != g.shape or u.dtype != g.dtype:
+        raise ValueError("g and u must have one shape and dtype")
+    st = lib().rp_silu_mul(_ptr(g), _rows(g, "g"), _ptr(u), _rows(u, "u"), g.shape[0], g.shape[1], _ptr(out),
+                           _rows(out, "out"), _dtype_code(g), _stream(stream, g.device))
+    _check(st, "rp_silu_mul")
+    return out
 
 
 def pack_w0(W0, out=None, stream=None):

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librank_pregate.so")
 
 SOURCES = ["api.cpp", "pregate.hip", "segment.hip", "sgmm_plan.cpp", "sgmm_decode.hip", "sgmm_prefill.hip",
-           "sgmm_f32.hip", "util.hip", "noalloc.hip", "adapter_apply.hip", "merge.hip", "route_mfma.hip"]
+           "sgmm_f32.hip", "util.hip", "noalloc.hip", "adapter_apply.hip", "merge.hip", "route_mfma.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
 

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -189,8 +190,8 @@ rp_status check_sgmm(const char* fn, const rp_proj* projs, int32_t n_proj, const
                   "multiple of 16 bytes", fn, p, (long long)q.ld_y);
     if (T > 0 && (!q.W0 || !q.y || (k > 0 && (!q.A || !q.B))))
       return fail(RP_ERR_INVALID_ARG, "%s: projection %d: null pointer", fn, p);
-    if (!aligned(q.W0, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.y, 16))
-      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: W0, A, B, y must be 16-byte aligned", fn, p);
+    if (!aligned(q.W0, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.y, 16) || !aligned(q.residual, 16))
+      return fail(RP_ERR_INVALID_ARG, "%s: projection %d: W0, A, B, y, residual must be 16-byte aligned", fn, p);
     if ((int64_t)q.d_out * d_in > ((int64_t)1 << 40) || E * r * std::max<int64_t>(d_in, q.d_out) > ((int64_t)1 << 40))
       return fail(RP_ERR_INVALID_ARG, "%s: projection %d too large", fn, p);
     if (q.reserved != 0 || (q.w0_layout != RP_W0_ROWS && q.w0_layout != RP_W0_TILED))
@@ -222,6 +223,7 @@ void fill_group(rp::SgmmArgs* a, const rp_proj* projs, int n_proj, const void* x
     a->proj[p].ld_y = (int)projs[q].ld_y;
     a->proj[p].tile_begin = tile;
     a->proj[p].tiled = projs[q].w0_layout == RP_W0_TILED;
+    a->proj[p].residual = projs[q].residual;
     if (p < n_proj) tile += ((int)projs[p].d_out + tile_rows - 1) / tile_rows;
   }
   a->n_proj = n_proj;
@@ -296,6 +298,13 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
     }
   }
   return need;
+}
+
+// A group's activation as its own launch after the group (paths without the
+// fused epilogue): projs[0].y <- silu(projs[0].y) * projs[1].y.
+hipError_t launch_act(const rp_group& g, int64_t T, rp::Dtype dt, hipStream_t stream) {
+  return rp::launch_silu_mul(g.projs[0].y, (int)g.projs[0].ld_y, g.projs[1].y, (int)g.projs[1].ld_y, (int)T,
+                             (int)g.projs[0].d_out, g.projs[0].y, (int)g.projs[0].ld_y, dt, stream);
 }
 
 // Runs the groups of a validated call in order on `stream`.  Decode shapes go
@@ -407,6 +416,8 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         continue;
       }
       hipError_t e = rp::launch_prefill_step(ps, stream);
+      for (int i = 0; e == hipSuccess && i < ng; ++i)
+        if (gs[g0 - ng + i].act == RP_ACT_SILU_MUL) e = launch_act(gs[g0 - ng + i], T, rdt, stream);
       if (e != hipSuccess) return hip_fail(fn, e);
     }
     return RP_OK;
@@ -435,6 +446,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       a.n_tiles = plan.n_tiles;
       a.S = plan.S;
       hipError_t e = rp::launch_sgmm(a, plan, rdt, stream);
+      if (e == hipSuccess && gs[g].act == RP_ACT_SILU_MUL) e = launch_act(gs[g], T, rdt, stream);
       if (e != hipSuccess) return hip_fail(fn, e);
     }
     return RP_OK;
@@ -494,6 +506,11 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       if (desc[i].x_acquire)
         for (int j = 0; j < i; ++j) q.wait_target += sp.gp[j].n_tiles;
       q.partial_a = reinterpret_cast<float*>(w + gp.off_partial_a);
+      q.act = g.act;
+      q.pair_cnt = reinterpret_cast<int*>(w) + rp::kPrefillCounterWord + i * rp::kActPairWords;
+      if (g.act == RP_ACT_SILU_MUL && (g.projs[0].d_out + gp.tile_rows - 1) / gp.tile_rows > rp::kActPairWords)
+        return fail(RP_ERR_UNSUPPORTED, "%s: group %d: RP_ACT_SILU_MUL supports at most %d output tiles", fn,
+                    g0 + i, rp::kActPairWords);
     }
     st.n_groups = ng;
     st.n_items = sp.n_items;
@@ -598,9 +615,10 @@ size_t rp_sgmm_step_workspace_size(const rp_group* groups, int32_t n_groups, int
     for (int p = 0; p < groups[g].n_proj; ++p)
       if (groups[g].projs[p].d_out < 8 || groups[g].projs[p].d_out > kIntMax) return 0;
   }
-  // the exact need of the call on the current device (routing computed or
-  // not needs the same bytes); the device-independent bound if it cannot be
-  // queried
+  // the exact need of the call on the current device, taking the routing as
+  // computed when k > 0 (its split-form router may need more than the
+  // groups; given routing never needs more); the device-independent bound if
+  // the device cannot be queried
   const size_t need = exact_need(groups, n_groups, T, E, r, k, dt, k > 0);
   return need ? need : groups_workspace_bytes(groups, n_groups, T, E, r, k, dt);
 }
@@ -623,6 +641,11 @@ rp_status validate_step(const char* fn, const rp_group* groups, int32_t n_groups
     if (st != RP_OK) return st;
     if (groups[g].x_from_call != 0 && groups[g].x_from_call != 1)
       return fail(RP_ERR_INVALID_ARG, "%s: x_from_call must be 0 or 1", name);
+    if (groups[g].reserved != 0 || (groups[g].act != RP_ACT_NONE && groups[g].act != RP_ACT_SILU_MUL))
+      return fail(RP_ERR_INVALID_ARG, "%s: unknown act %d / reserved %d", name, groups[g].act, groups[g].reserved);
+    if (groups[g].act == RP_ACT_SILU_MUL &&
+        (groups[g].n_proj != 2 || groups[g].projs[0].d_out != groups[g].projs[1].d_out))
+      return fail(RP_ERR_INVALID_ARG, "%s: RP_ACT_SILU_MUL needs two projections of equal d_out", name);
   }
   if (T == 0) return RP_OK;
   const Routing rt{Wg_or_null, topk_idx, topk_gate, seg_offsets, pair_perm};
@@ -655,6 +678,10 @@ rp_status rp_adapter_apply(const rp_proj* projs, int32_t n_proj, const void* x, 
   const char* fn = "rp_adapter_apply";
   // the projection checks of rp_sgmm_fused (W0 is not read; no workspace is used)
   rp_status st = check_sgmm(fn, projs, n_proj, x, T, d_in, ld_x, E, r, k, dt, reinterpret_cast<void*>(256));
+  for (int p = 0; st == RP_OK && p < n_proj; ++p)
+    if (projs[p].residual)
+      st = fail(RP_ERR_INVALID_ARG, "%s: projection %d: residual must be NULL (y already holds the base projection)",
+                fn, p);
   if (st != RP_OK) return st;
   if (k < 1) return fail(RP_ERR_INVALID_ARG, "%s: k=%d, an adapter delta needs k >= 1", fn, k);
   if (adapter < 0 || adapter >= E) return fail(RP_ERR_INVALID_ARG, "%s: adapter %d not in [0, E)", fn, adapter);
@@ -713,6 +740,54 @@ rp_status rp_merge_adapters(void* W0, int32_t w0_layout, int64_t d_out, int64_t 
   m.sign = sign;
   hipError_t e = rp::launch_merge(m, dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
   return e == hipSuccess ? RP_OK : hip_fail("rp_merge_adapters launch", e);
+}
+
+// Shared checks of the per-token elementwise calls: rows of d elements with
+// leading dimensions `lds` (n of them), pointers `ps`.
+static rp_status check_rows(const char* fn, int64_t T, int64_t d, const int64_t* lds, const void* const* ps, int n,
+                            rp_dtype dt) {
+  if (!valid_dtype(dt)) return fail(RP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (T < 0 || T > kIntMax) return fail(RP_ERR_INVALID_ARG, "%s: T=%lld out of range", fn, (long long)T);
+  const int64_t vec = dt == RP_BF16 ? 8 : 4, es = (int64_t)dsize(dt);
+  if (d < vec || d % vec != 0 || d > 65536)
+    return fail(RP_ERR_INVALID_ARG, "%s: d=%lld must be a positive multiple of %lld, at most 65536", fn, (long long)d,
+                (long long)vec);
+  for (int i = 0; i < n; ++i)
+    if (lds[i] < d || (lds[i] * es) % 16 != 0 || lds[i] > kIntMax)
+      return fail(RP_ERR_INVALID_ARG, "%s: leading dimension %lld must be >= d with ld*elem a multiple of 16 bytes",
+                  fn, (long long)lds[i]);
+  if (T == 0) return RP_OK;
+  for (int i = 0; i < n; ++i)
+    if (!ps[i] || !aligned(ps[i], 16)) return fail(RP_ERR_INVALID_ARG, "%s: pointers must be non-null and 16-byte aligned", fn);
+  if (T * std::max(lds[0], d) > ((int64_t)1 << 40)) return fail(RP_ERR_INVALID_ARG, "%s: T*d too large", fn);
+  return RP_OK;
+}
+
+rp_status rp_rmsnorm(const void* x, int64_t T, int64_t d, int64_t ld_x, const void* gamma, float eps, void* y,
+                     int64_t ld_y, rp_dtype dt, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_rmsnorm";
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(RP_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  const int64_t lds[3] = {ld_x, ld_y, d};
+  const void* ps[3] = {x, y, gamma};
+  rp_status st = check_rows(fn, T, d, lds, ps, 3, dt);
+  if (st != RP_OK || T == 0) return st;
+  hipError_t e = rp::launch_rmsnorm(x, (int)T, (int)d, (int)ld_x, gamma, eps, y, (int)ld_y,
+                                    dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
+  return e == hipSuccess ? RP_OK : hip_fail(fn, e);
+}
+
+rp_status rp_silu_mul(const void* g, int64_t ld_g, const void* u, int64_t ld_u, int64_t T, int64_t d, void* m,
+                      int64_t ld_m, rp_dtype dt, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "rp_silu_mul";
+  const int64_t lds[3] = {ld_g, ld_u, ld_m};
+  const void* ps[3] = {g, u, m};
+  rp_status st = check_rows(fn, T, d, lds, ps, 3, dt);
+  if (st != RP_OK || T == 0) return st;
+  hipError_t e = rp::launch_silu_mul(g, (int)ld_g, u, (int)ld_u, (int)T, (int)d, m, (int)ld_m,
+                                     dt == RP_BF16 ? rp::kBF16 : rp::kF32, stream);
+  return e == hipSuccess ? RP_OK : hip_fail(fn, e);
 }
 
 rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t* wait_overflow,

@@ -96,6 +96,10 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Gated MLP activation on one element: silu(g) * u in fp32 (the fused epilogue
+// and the separate launch both use this, so they give the same bits).
+__device__ __forceinline__ float silu_mul_f32(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);

@@ -55,6 +55,7 @@ struct ProjDesc {
   int ld_y;
   int tile_begin;  // first output-row tile of this projection in the packed row space
   int tiled;       // W0 in the 16x32-block order of rp_pack_w0
+  const void* residual;  // null, or [T, d_out] (leading dimension ld_y) added before the output rounding
 };
 
 struct SgmmArgs {
@@ -96,6 +97,8 @@ struct DecodeArgs {
   int count_done;                     // a later group waits for this one: count finished tiles
   int release;                        // ... and reads what this one wrote: release before counting
   float* partial_a;                   // dense: split-K partial tiles of the A tiles
+  int act;                            // rp_act of the group (RP_ACT_SILU_MUL: projections 0, 1 pair up)
+  int* pair_cnt;                      // act: arrival counter per output tile of projection 0
   unsigned int* route_tagged;         // fused: (index, tag, gate, tag) per (token, slot)
   PregateArgs pg;                     // fused: router arguments (outputs topk_idx, topk_gate)
   SegmentArgs sg;                     // fused: segmentation arguments
@@ -111,6 +114,8 @@ struct GroupPlan {
   int x_acquire, count_done, release;
   int wait_target;  // x_acquire: output tiles of every earlier group of the launch, else 0
   float* partial_a;
+  int act;          // rp_act: with RP_ACT_SILU_MUL the second tile of a (gate, up) pair writes silu(g)*u
+  int* pair_cnt;    // act: one arrival counter per output tile of projection 0 (zero before and after)
 };
 struct StepArgs {
   SgmmArgs g[kMaxGroups];
@@ -189,6 +194,10 @@ constexpr int kPrefillCounterWord = 9216;
 // counters of the split-form router (below the decode control sets)
 constexpr int kRouteCounterWord = 128;
 constexpr int kRouteCounterWords = 1024 - kRouteCounterWord;
+// decode launches leave the prefill counters unused: the (gate, up) tile-pair
+// counters of groups with an activation take kActPairWords words per group
+// there (each returns to zero when its pair completes)
+constexpr int kActPairWords = 896;
 constexpr int kPrefillCounterWords = (int)(kWorkspaceCounterBytes / 4) - kPrefillCounterWord;
 int prefill_splits(int d_in, int n_tiles, int T, int n_cu);          // K splits of one group's GEMM tiles
 size_t prefill_partial_bytes(int n_tiles, int T, int S);            // its split-K partial tiles
@@ -227,6 +236,10 @@ struct MergeArgs {
 hipError_t launch_merge(const MergeArgs& m, Dtype dt, hipStream_t s);
 
 hipError_t launch_pack_w0(const void* src, void* dst, int d_out, int d_in, hipStream_t s);
+hipError_t launch_rmsnorm(const void* x, int T, int d, int ld_x, const void* gamma, float eps, void* y, int ld_y,
+                          Dtype dt, hipStream_t s);
+hipError_t launch_silu_mul(const void* g, int ld_g, const void* u, int ld_u, int T, int d, void* m, int ld_m,
+                           Dtype dt, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t n_bytes, float* sink, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t n_bytes, hipStream_t s);
 

@@ -36,6 +36,7 @@ static_assert(kCtlSet0 + 2 * kCtlSetStride <= kPrefillCounterWord, "control sets
 static_assert(kCtlSegErr < kRouteCounterWord && kRouteCounterWord + kRouteCounterWords <= kCtlSet0,
               "router counters overlap the control words");
 static_assert(kSetWords <= kCtlSetStride, "control set overflow");
+static_assert(kActPairWords * kMaxGroups <= kPrefillCounterWords, "activation pair counters overflow");
 
 // Device-scope (sc1) loads of routing data another workgroup of the same
 // launch may have written; plain loads when it was written by an earlier launch.
@@ -77,6 +78,7 @@ __device__ __forceinline__ ProjDesc proj_at(const SgmmArgs& a, int p) {
   d.ld_y = RP_PICK(a, p, ld_y);
   d.tile_begin = RP_PICK(a, p, tile_begin);
   d.tiled = RP_PICK(a, p, tiled);
+  d.residual = RP_PICK(a, p, residual);
   return d;
 }
 

@@ -355,26 +355,32 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 
   // The split's nc chunks are preceded by `pad` empty ones so that their count
   // V is a multiple of NR: chunk v then always sits in ring slot v % NR
-  // and the last chunks at fixed positions of the code.  An empty chunk loads
-  // activation bytes (cache-resident) in place of weights and stages zero
-  // activations.  Loads are never masked (a select would force a wait right
-  // after them); weight blocks past d_in are clamped to a real block and meet
-  // activations that store_x wrote as zero.
+  // and the last chunks at fixed positions of the code.  An empty chunk stages
+  // zero activations; its weight slot loads activation bytes (cache-resident)
+  // in place of weights, except in a group whose x an earlier group of the
+  // launch writes: there the weight slots fill before the wait, when x may
+  // still hold anything (a NaN times the zero activations would poison the
+  // sums), so they load the split's first weight block instead.  Loads are
+  // never masked (a select would force a wait right after them); weight
+  // blocks past d_in are clamped to a real block and meet activations that
+  // store_x wrote as zero.
   const int pad = (NR - nc % NR) % NR;
   const int V = nc + pad;
+  const bool pad_reads_w = d.prev_target > 0;
   auto issue_w = [&](int slot, int v) {
     const int c = v - pad;
     const int cc = cbeg + max(c, 0);
     const bf16_t* xa = xq[0] + min(cc * kKC + xcol, a.d_in - 8);
+    const bool real = c >= 0 || pad_reads_w;
     if (TILED) {
       const int nbg = min(4, nb - 4 * cc);
       const bf16_t* blk = w0 + ((size_t)cc * 4 * n_rb + (size_t)rblk * nbg) * 512 + lane * 8;
 #pragma unroll
-      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(c >= 0 ? blk + (size_t)min(s, nbg - 1) * 512 : xa);
+      for (int s = 0; s < kKS; ++s) wr[slot][s] = ld16_stream(real ? blk + (size_t)min(s, nbg - 1) * 512 : xa);
     } else {
 #pragma unroll
       for (int s = 0; s < kKS; ++s)
-        wr[slot][s] = ld16_stream(c >= 0 ? wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8) : xa);
+        wr[slot][s] = ld16_stream(real ? wrow + min(cc * kKC + s * 32, a.d_in - 8 - kg * 8) : xa);
     }
   };
   auto issue_x = [&](int slot, int v) {
@@ -865,30 +871,103 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 
   // store through LDS: lane holds output row row0 + lane%16 of tokens
   // m*16 + 4*(lane/16) + v; the tile goes to the activation buffer the last
-  // chunk did not use (free since the barrier of chunk V-2) as [token][64
+  // chunk did not use (free since the barrier of chunk V-2) as [token][TR
   // rows], then each thread writes 16 bytes (8 rows of one token; d_out and
-  // ld_y are multiples of 8)
-  {
+  // ld_y are multiples of 8).  With a residual the tile stays fp32 (both
+  // activation buffers, once every wave is done with them) and the residual
+  // is added before the one rounding.  A group with an activation stores its
+  // tiles device-coherent: the partner tile's item reads them.
+  const int tile_row0 = row0 - wave * 16;
+  bf16_t* y = static_cast<bf16_t*>(pd.y);
+  auto put16 = [&](bf16_t* p, uint4 v) {
+    if (d.act) {
+      unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+      __hip_atomic_store(q, (unsigned long long)v.x | ((unsigned long long)v.y << 32), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, (unsigned long long)v.z | ((unsigned long long)v.w << 32), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *reinterpret_cast<uint4*>(p) = v;
+    }
+  };
+  if (pd.residual) {
+    static_assert(16 * MT * TR * 4 <= 2 * XB * 512 * 2, "an fp32 output tile fits both activation buffers");
+    float* yf = reinterpret_cast<float*>(xs);
+    const bf16_t* res = static_cast<const bf16_t*>(pd.residual);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yf[(m * 16 + 4 * kg + v) * TR + wave * 16 + lr] = acc[m][v];
+    __syncthreads();
+    for (int q = tid; q < a.T * (TR / 8); q += NTH) {
+      const int t = q / (TR / 8), c8 = (q % (TR / 8)) * 8;
+      if (tile_row0 + c8 < pd.d_out) {
+        const uint4 rv = ld16(res + (size_t)t * pd.ld_y + tile_row0 + c8);
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+        const float* f = &yf[t * TR + c8];
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = f32x2_to_bf16x2(f[2 * i] + __uint_as_float(rw[i] << 16), f[2 * i + 1] + __uint_as_float(rw[i] & 0xffff0000u));
+        put16(y + (size_t)t * pd.ld_y + tile_row0 + c8, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    }
+  } else {
     bf16_t* ys = xs + (size_t)(V & 1) * XB * 512;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int v = 0; v < 4; ++v) ys[(m * 16 + 4 * kg + v) * TR + wave * 16 + lr] = f32_to_bf16(acc[m][v]);
     __syncthreads();
-    const int tile_row0 = row0 - wave * 16;
-    bf16_t* y = static_cast<bf16_t*>(pd.y);
     for (int q = tid; q < a.T * (TR / 8); q += NTH) {
       const int t = q / (TR / 8), c8 = (q % (TR / 8)) * 8;
       if (tile_row0 + c8 < pd.d_out)
-        *reinterpret_cast<uint4*>(y + (size_t)t * pd.ld_y + tile_row0 + c8) = *reinterpret_cast<const uint4*>(&ys[t * TR + c8]);
+        put16(y + (size_t)t * pd.ld_y + tile_row0 + c8, *reinterpret_cast<const uint4*>(&ys[t * TR + c8]));
     }
+  }
+  int n_done = 1;  // output tiles this item completes
+  if (d.act) {
+    // (gate, up) pair: the item that finishes second computes m = silu(g) * u
+    // for the tile from both rounded tiles and writes it over the gate tile
+    __builtin_amdgcn_s_waitcnt(0);  // this tile is at the coherence point before the arrival
+    __syncthreads();
+    __shared__ int s_pair;
+    const int lt = tile - pd.tile_begin;
+    if (tid == 0) s_pair = atomicAdd(&d.pair_cnt[lt], 1);
+    __syncthreads();
+    if (s_pair == 0) return;  // the partner's item completes the pair
+    if (tid == 0) __hip_atomic_store(&d.pair_cnt[lt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const ProjDesc pg = proj_at(a, 0), pu = proj_at(a, 1);
+    bf16_t* gy = static_cast<bf16_t*>(pg.y);
+    const bf16_t* uy = static_cast<const bf16_t*>(pu.y);
+    for (int q = tid; q < a.T * (TR / 8); q += NTH) {
+      const int t = q / (TR / 8), c8 = (q % (TR / 8)) * 8;
+      if (tile_row0 + c8 < pd.d_out) {
+        const unsigned long long* gp = reinterpret_cast<const unsigned long long*>(gy + (size_t)t * pg.ld_y + tile_row0 + c8);
+        const unsigned long long* up = reinterpret_cast<const unsigned long long*>(uy + (size_t)t * pu.ld_y + tile_row0 + c8);
+        const unsigned long long g0 = __hip_atomic_load(gp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long g1 = __hip_atomic_load(gp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long u0 = __hip_atomic_load(up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long u1 = __hip_atomic_load(up + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t gw[4] = {(uint32_t)g0, (uint32_t)(g0 >> 32), (uint32_t)g1, (uint32_t)(g1 >> 32)};
+        const uint32_t uw[4] = {(uint32_t)u0, (uint32_t)(u0 >> 32), (uint32_t)u1, (uint32_t)(u1 >> 32)};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = f32x2_to_bf16x2(silu_mul_f32(__uint_as_float(gw[i] << 16), __uint_as_float(uw[i] << 16)),
+                                 silu_mul_f32(__uint_as_float(gw[i] & 0xffff0000u), __uint_as_float(uw[i] & 0xffff0000u)));
+        *reinterpret_cast<uint4*>(gy + (size_t)t * pg.ld_y + tile_row0 + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    n_done = 2;  // both tiles of the pair are final now
   }
   if (d.count_done) {
     // a later group of this launch waits for this tile (and, with release, reads it)
     if (d.release) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) atomicAdd(&set[kSetGroupDone + 256 * d.group + 32 * (tile & 7)], 1);
+    if (tid == 0) atomicAdd(&set[kSetGroupDone + 256 * d.group + 32 * (tile & 7)], n_done);
   }
 }
 
@@ -918,6 +997,8 @@ __device__ __forceinline__ DecodeArgs group_view(const StepArgs& st, int gi) {
   d.count_done = gp.count_done;
   d.release = gp.release;
   d.partial_a = gp.partial_a;
+  d.act = gp.act;
+  d.pair_cnt = gp.pair_cnt;
   d.route_tagged = st.route_tagged;
   return d;
 }

@@ -130,6 +130,12 @@ __global__ __launch_bounds__(256) void base_expand_f32(SgmmArgs a, int n_tok_til
 #pragma unroll
     for (int i = 0; i < 8; ++i) tot[i] += d[i];
   }
+  if (pd.residual) {  // added before the output is stored (the one rounding of fp32 is the last add)
+    const float* rr = static_cast<const float*>(pd.residual) + (size_t)t * pd.ld_y + row0;
+    const float4 r0 = ld4(rr), r1 = ld4(rr + 4);
+    tot[0] += r0.x; tot[1] += r0.y; tot[2] += r0.z; tot[3] += r0.w;
+    tot[4] += r1.x; tot[5] += r1.y; tot[6] += r1.z; tot[7] += r1.w;
+  }
   float* y = static_cast<float*>(pd.y) + (size_t)t * pd.ld_y + row0;
   *reinterpret_cast<float4*>(y) = make_float4(tot[0], tot[1], tot[2], tot[3]);
   *reinterpret_cast<float4*>(y + 4) = make_float4(tot[4], tot[5], tot[6], tot[7]);

@@ -561,6 +561,24 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   else if (a.k > 0)
     expand_adapters<EXP == 2 ? 2 : kPUJ>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc, s_emask[wave]);
 
+  // a residual is added in fp32 before the one rounding: lane entry v of
+  // acc[f][g] is token position wm*64 + f*32 + 8*(v/4) + 4*kg + v%4, row
+  // wn*64 + g*32 + lr of the tile
+  if (pd.residual) {
+    const bf16_t* res = static_cast<const bf16_t*>(pd.residual);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int row = row0 + wn * 64 + g * 32 + lr;
+      if (row >= pd.d_out) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int pos = i0 + wm * 64 + f * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+          if (pos < a.T) acc[f][g][v] += bf16_to_f32(res[(size_t)token_at(a, pos) * pd.ld_y + row]);
+        }
+    }
+  }
   // store through LDS: the tile as [token][128 rows] bf16, then 16-byte row
   // pieces per (token, 8 rows); d_out and ld_y are multiples of 8
   bf16_t* ys = smem_p;

@@ -36,7 +36,7 @@ import numpy as np
 
 PROJ_CODES = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "single": 7}
 TENSOR_CODES = {"x": 0, "W0": 1, "A": 2, "B": 3, "Wg": 4, "x_router": 5, "zipf": 6,
-                "x_attn": 7, "x_o": 8, "x_d": 9}
+                "x_attn": 7, "x_o": 8, "x_d": 9, "h0": 10, "gamma1": 11, "gamma2": 12}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -184,6 +184,18 @@ def router_weight(wl: Workload, layer: int = 0) -> np.ndarray:
 def layer_input(wl: Workload, layer: int, x_name: str) -> np.ndarray:
     width = {g.x_name: g.d_in for g in wl.groups}[x_name]
     return _fmt(wl, _normal(_seed(wl, layer, x_name), (wl.T, width), 1.0))
+
+
+def residual_input(wl: Workload) -> np.ndarray:
+    """h0 [T, d], N(0, 1): the residual stream entering layer 0 of the chained decoder layers."""
+    return _fmt(wl, _normal(_seed(wl, 0, "h0"), (wl.T, wl.d), 1.0))
+
+
+def norm_weight(wl: Workload, layer: int, which: str) -> np.ndarray:
+    """RMSNorm weight gamma [d] of `layer` ("gamma1" before attention, "gamma2" before the MLP):
+    1 + N(0, 0.1^2)."""
+    g = 1.0 + _normal(_seed(wl, layer, which), (wl.d,), 0.1)
+    return _fmt(wl, g.astype(np.float32))
 
 
 @dataclasses.dataclass

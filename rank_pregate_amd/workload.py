@@ -25,6 +25,7 @@ from . import pregate as rp_pregate, segment as rp_segment, sgmm_fused as rp_sgm
 from . import route_sgmm_fused as rp_route_sgmm_fused, sgmm_step as rp_sgmm_step, step_workspace_size
 from . import sgmm_workspace_size, segment_workspace_size, pack_w0, track_workspace, RP_BF16, RP_F32
 from . import adapter_apply as rp_adapter_apply, merge_adapters as rp_merge_adapters
+from . import rmsnorm as rp_rmsnorm, silu_mul as rp_silu_mul, RP_ACT_SILU_MUL
 
 
 def to_device(a: np.ndarray, dtype: str, device):
@@ -49,6 +50,9 @@ class DevProj:
     W0: object
     A: object
     B: object
+
+
+CHAIN_EPS = 1e-5  # RMSNorm epsilon of the chained decoder layers
 
 
 class DeviceWorkload:
@@ -241,6 +245,66 @@ class DeviceWorkload:
         for pw in W.values():
             rp_merge_adapters(pw.W0, pw.A, pw.B, sel, w, -1.0, stream=stream)
 
+    # -- whole decoder layers around the projections (chained inputs) --------
+    def _chain_buffers(self):
+        """Residual stream, norm output and per-layer RMSNorm weights of the chained layers."""
+        import torch
+        if hasattr(self, "chain_h"):
+            return
+        wl, dev = self.wl, self.device
+        names = [g.name for g in wl.groups]
+        if names != ["qkv", "o", "gate_up", "down"]:
+            raise RuntimeError("chained layers need the q|k|v, o, gate|up, down groups")
+        up = lambda a: to_device(a, wl.dtype, dev)  # noqa: E731
+        self.chain_h0 = up(datagen.residual_input(wl))
+        self.chain_h = torch.empty_like(self.chain_h0)
+        self.chain_n = torch.empty_like(self.chain_h0)
+        self.chain_gamma = {(l, w): up(datagen.norm_weight(wl, l, w)) for l in self.layers
+                            for w in ("gamma1", "gamma2")}
+        attn, mlp = self.chain_groups(0)[0]
+        need = max(step_workspace_size(attn, wl.E, wl.r, wl.k), step_workspace_size(mlp, wl.E, wl.r, wl.k))
+        if need > self.ws.numel():
+            self.ws = track_workspace(torch.zeros(need, dtype=torch.uint8, device=dev))
+
+    def chain_groups(self, copy: int = 0):
+        """Per layer, the two launches' groups of a chained decoder layer:
+        ([q|k|v on n1, o on v with residual h -> h], [gate|up on n2 with silu(g)*u, down on m with residual h -> h]).
+        Layer 0's o reads the residual from h0 (so every step starts from the same stream)."""
+        W, wl = self.weights[copy], self.wl
+        out = []
+        for i, l in enumerate(self.layers):
+            P = lambda p: (W[(l, p)].W0, W[(l, p)].A, W[(l, p)].B)  # noqa: E731
+            res = self.chain_h0 if i == 0 else self.chain_h
+            v = self.outputs[(l, "v")]
+            qkv = ([P("q") + (self.outputs[(l, "q")],), P("k") + (self.outputs[(l, "k")],), P("v") + (v,)],
+                   self.chain_n)
+            o = ([P("o") + (self.chain_h, res)], v, 1)
+            g_out = self.outputs[(l, "gate")]
+            gate_up = ([P("gate") + (g_out,), P("up") + (self.outputs[(l, "up")],)], self.chain_n, 0,
+                       RP_ACT_SILU_MUL)
+            down = ([P("down") + (self.chain_h, self.chain_h)], g_out, 1)
+            out.append(([qkv, o], [gate_up, down]))
+        return out
+
+    def run_chained(self, copy: int = 0, stream=None):
+        """Every layer as a whole decoder layer (RMSNorm, q|k|v, o + residual, RMSNorm, gate|up with the
+        fused silu(g)*u, down + residual), inputs chained from the outputs before them; the routing runs
+        inside the first launch, on layer 0's normalised input.  The residual stream ends in chain_h."""
+        self._chain_buffers()
+        wl = self.wl
+        for i, (l, (attn, mlp)) in enumerate(zip(self.layers, self.chain_groups(copy))):
+            rp_rmsnorm(self.chain_h0 if i == 0 else self.chain_h, self.chain_gamma[(l, "gamma1")], CHAIN_EPS,
+                       out=self.chain_n, stream=stream)
+            if i == 0:
+                rp_sgmm_step(attn, wl.E, wl.r, wl.k, Wg=self.Wg, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
+                             seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+            else:
+                rp_sgmm_step(attn, wl.E, wl.r, wl.k, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
+                             seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+            rp_rmsnorm(self.chain_h, self.chain_gamma[(l, "gamma2")], CHAIN_EPS, out=self.chain_n, stream=stream)
+            rp_sgmm_step(mlp, wl.E, wl.r, wl.k, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
+                         seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+
     def run_variant(self, variant: str, copy: int = 0, stream=None):
         if variant == "fused":
             self.run(copy, stream=stream)
@@ -252,6 +316,8 @@ class DeviceWorkload:
             self.run_token_fused(copy, stream=stream)
         elif variant == "token_merge_unmerge":
             self.run_token_merged(copy, stream=stream)
+        elif variant == "chained_layers":
+            self.run_chained(copy, stream=stream)
         else:
             raise ValueError(variant)
 

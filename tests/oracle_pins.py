@@ -257,4 +257,100 @@ def check_sgmm_token_subset(impl):
     np.testing.assert_allclose(impl.sgmm(x, W0, A, B, idx, gate, tokens=[5, 1, 7]), y[[5, 1, 7]], rtol=1e-14)
 
 
+# ----------------------------------------------------------------------------- decoder layer
+
+def check_round_bf16_grid(impl):
+    # against the representable grid walked pattern by pattern, and hand-made ties
+    g = _rng(30)
+    x = g.standard_normal(3000) * 10.0 ** g.integers(-6, 6, 3000)
+    want = np.array([brute.bf16_grid_nearest(float(v)) for v in x])
+    assert np.array_equal(impl.round_bf16(x), want)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 255.5, -(1 + 2.0 ** -8), 3 * 2.0 ** -9 + 2.0 ** -1])
+    assert np.array_equal(impl.round_bf16(ties), [1.0, 1 + 2.0 ** -6, 256.0, -1.0, 0.5078125])
+    exact = np.array([1.0, -0.5, 3.0, 2.0 ** -20, 1 + 2.0 ** -7])
+    assert np.array_equal(impl.round_bf16(exact), exact)
+
+
+def check_rmsnorm_closed_forms(impl):
+    g = _rng(31)
+    gamma = g.uniform(0.5, 2.0, 6)
+    # a constant row c normalises to sign(c) * gamma (eps = 0)
+    x = np.array([[3.0] * 6, [-0.25] * 6])
+    np.testing.assert_allclose(impl.rmsnorm(x, gamma, 0.0), np.array([gamma, -gamma]), rtol=1e-14)
+    # [3, 4]: mean square 12.5
+    np.testing.assert_allclose(impl.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), 0.0),
+                               [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=1e-14)
+    # scale invariance and unit mean square (eps = 0, gamma = 1)
+    x = g.standard_normal((4, 10))
+    y = impl.rmsnorm(x, np.ones(10), 0.0)
+    np.testing.assert_allclose(impl.rmsnorm(7.5 * x, np.ones(10), 0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)
+    # eps enters under the square root: a zero row stays zero, a tiny row is damped
+    assert np.array_equal(impl.rmsnorm(np.zeros((1, 4)), np.ones(4), 1e-5), np.zeros((1, 4)))
+    np.testing.assert_allclose(impl.rmsnorm(np.array([[1e-3, 1e-3]]), np.ones(2), 1e-6),
+                               [[1e-3 / math.sqrt(2e-6)] * 2], rtol=1e-13)
+
+
+def check_silu_mul_values(impl):
+    # sigma(x) = (1 + tanh(x / 2)) / 2: silu(g) = g * sigma(g)
+    g = np.array([[0.0, 1.0, -1.0, 2.0, -3.5]])
+    want = g * (1 + np.tanh(g / 2)) / 2
+    np.testing.assert_allclose(impl.silu_mul(g, np.ones_like(g)), want, rtol=1e-14, atol=1e-300)
+    # odd part: silu(x) - silu(-x) = x; linear in u; the gate is the argument of silu
+    x = _rng(32).standard_normal((3, 7))
+    one = np.ones_like(x)
+    np.testing.assert_allclose(impl.silu_mul(x, one) - impl.silu_mul(-x, one), x, rtol=1e-13, atol=1e-14)
+    u = _rng(33).standard_normal((3, 7))
+    np.testing.assert_allclose(impl.silu_mul(x, 2.0 * u), 2.0 * impl.silu_mul(x, u), rtol=1e-14)
+    assert np.array_equal(impl.silu_mul(np.zeros((1, 3)), np.array([[5.0, -1.0, 2.0]])), np.zeros((1, 3)))
+
+
+def _layer_case(seed, T=3, d=8, ff=12, E=3, r=2, k=2):
+    g = _rng(seed)
+    w = {"gamma1": g.uniform(0.5, 1.5, d), "gamma2": g.uniform(0.5, 1.5, d)}
+    for name, (o, i) in {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d), "gate": (ff, d), "up": (ff, d),
+                         "down": (d, ff)}.items():
+        w[name] = (g.standard_normal((o, i)) / math.sqrt(i), g.standard_normal((E, r, i)) / math.sqrt(i),
+                   0.3 * g.standard_normal((E, o, r)))
+    h = g.standard_normal((T, d))
+    idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = g.uniform(0.1, 1.0, (T, k))
+    return h, w, idx, gate
+
+
+def _zero(w, name):
+    W0, A, B = w[name]
+    return (np.zeros_like(W0), A, np.zeros_like(B))
+
+
+def check_decoder_layer_brute(impl):
+    ident = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    for seed in (40, 41):
+        h, w, idx, gate = _layer_case(seed)
+        np.testing.assert_allclose(impl.decoder_layer(h, w, idx, gate, 1e-5, rnd=ident),
+                                   np.array(brute.decoder_layer(h, w, idx, gate, 1e-5)), rtol=1e-11, atol=1e-12)
+
+
+def check_decoder_layer_passthrough(impl):
+    h, w, idx, gate = _layer_case(42)
+    h = impl.round_bf16(h)
+    # o and down zero: both residual adds pass h through unchanged
+    w2 = dict(w, o=_zero(w, "o"), down=_zero(w, "down"))
+    assert np.array_equal(impl.decoder_layer(h, w2, idx, gate, 1e-5), h)
+    # up zero: the MLP adds silu(g) * 0 = 0, so the layer is h + o(v) alone (o still live)
+    w3 = dict(w, up=_zero(w, "up"))
+    w4 = dict(w, up=_zero(w, "up"), down=_zero(w, "down"))
+    assert np.array_equal(impl.decoder_layer(h, w3, idx, gate, 1e-5), impl.decoder_layer(h, w4, idx, gate, 1e-5))
+    # ... while a zero gate projection makes silu(0) = 0 as well, but a live up alone must not
+    w5 = dict(w, gate=_zero(w, "gate"))
+    assert np.array_equal(impl.decoder_layer(h, w5, idx, gate, 1e-5), impl.decoder_layer(h, w4, idx, gate, 1e-5))
+
+
+def check_decoder_layer_token_permutation(impl):
+    h, w, idx, gate = _layer_case(43, T=6)
+    p = _rng(44).permutation(6)
+    y = impl.decoder_layer(h, w, idx, gate, 1e-5)
+    assert np.array_equal(impl.decoder_layer(h[p], w, idx[p], gate[p], 1e-5), y[p])
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

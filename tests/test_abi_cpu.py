@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert rp.abi_version() == 6
+    assert rp.abi_version() == 7
 
 
 @pytest.mark.parametrize("ws,nbytes", [(None, 1 << 16), (FAKE + 16, 1 << 16), (FAKE, 4096)])

@@ -571,9 +571,9 @@ def test_step_chained(T):
     groups = [([dev0[0] + (y0,), dev0[1]], to_device(x0, dt, DEV)),
               ([dev1[0] + (y1,)], y0, 1),
               ([dev2[0]], y1, 1)]
-    for rep in range(3):  # fresh outputs each time: a stale read would show
-        y0.zero_()
-        y1.zero_()
+    for rep in range(3):  # NaN-filled outputs each time: a read before the write would show
+        y0.fill_(float("nan"))
+        y1.fill_(float("nan"))
         ys, *_ = rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
         torch.cuda.synchronize()
         g64 = gate.astype(np.float64)
@@ -583,6 +583,33 @@ def test_step_chained(T):
         check_y(y1, ref1, dt, "chained group 1")
         ref2 = oracle.sgmm(dl_widen(y1, dt), *(widen(a, dt) for a in hw2[0]), idx, g64)
         check_y(ys[2][0], ref2, dt, "chained group 2")
+
+
+@pytest.mark.parametrize("T,d,ff", [(9, 512, 2048), (9, 512, 11008), (64, 512, 11008), (64, 4096, 11008)])
+def test_step_chained_wide(T, d, ff):
+    """gate|up -> down chained in one launch at widths whose K splits are padded to the load ring: the
+    dependent group's weight slots fill before its wait, while its input still holds NaN."""
+    say("step chained wide", T, d, ff)
+    rng = np.random.default_rng(T + ff + d)
+    dt, E, r, k = "bf16", 16, 8, 2
+    conv = datagen.f32_to_bf16_bits
+    hw0, dev0 = _group_weights(rng, d, [ff, ff], E, r, dt)
+    hw1, dev1 = _group_weights(rng, ff, [d], E, r, dt)
+    x0 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    g = torch.full((T, ff), float("nan"), dtype=torch.bfloat16, device=DEV)
+    u = torch.full((T, ff), float("nan"), dtype=torch.bfloat16, device=DEV)
+    idx = datagen.uniform_indices(T + 7, T, E, k)
+    gate = datagen.random_gates(T + 7, T, k)
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    groups = [([dev0[0] + (g,), dev0[1] + (u,)], to_device(x0, dt, DEV)), ([dev1[0]], u, 1)]
+    ys, *_ = rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+    torch.cuda.synchronize()
+    g64 = gate.astype(np.float64)
+    ref_u = oracle.sgmm(widen(x0, dt), *(widen(a, dt) for a in hw0[1]), idx, g64)
+    check_y(u, ref_u, dt, "chained wide: up")
+    ref = oracle.sgmm(dl_widen(u, dt), *(widen(a, dt) for a in hw1[0]), idx, g64)
+    check_y(ys[1][0], ref, dt, "chained wide: down")
 
 
 @pytest.mark.parametrize("T", [32, 64])
@@ -940,3 +967,156 @@ def test_fused_step_two_groups():
             ref = oracle.sgmm(widen(xin, "bf16"), widen(W0, "bf16"), widen(A, "bf16"), widen(B, "bf16"), idx_ref,
                               gate_ref)
             check_y(y, ref, "bf16", "fused step, two groups")
+
+
+# --------------------------------------------------------------------------- whole decoder layers
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d", [(1, 64), (9, 256), (64, 4096), (130, 11008)])
+def test_rmsnorm(dt, T, d):
+    """rp_rmsnorm against the oracle's fp64 RMSNorm rounded to the output dtype, in place too."""
+    say("rmsnorm", dt, T, d)
+    rng = np.random.default_rng(T + d)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    x = conv(rng.standard_normal((T, d), dtype=np.float32) * np.float32(3.0))
+    g = conv((1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32))
+    xd, gd = to_device(x, dt, DEV), to_device(g, dt, DEV)
+    y = rp.rmsnorm(xd, gd, 1e-5)
+    x2 = xd.clone()
+    rp.rmsnorm(x2, gd, 1e-5, out=x2)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(widen(x, dt), widen(g, dt), 1e-5)
+    got = dl_widen(y, dt)
+    if dt == "bf16":
+        # one rounding of an fp32 value within a few ulp of the fp64 one: at most one bf16 step apart
+        step = np.abs(oracle.round_bf16(ref)) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(got - ref) <= step), f"max err {np.abs(got - ref).max():.3e}"
+    else:
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6)
+    assert torch.equal(x2.view(torch.int16) if dt == "bf16" else x2, y.view(torch.int16) if dt == "bf16" else y)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_silu_mul(dt):
+    say("silu_mul", dt)
+    rng = np.random.default_rng(5)
+    T, d = 33, 1000 if dt == "f32" else 1024
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    g = conv(rng.standard_normal((T, d), dtype=np.float32) * np.float32(4.0))
+    u = conv(rng.standard_normal((T, d), dtype=np.float32))
+    m = rp.silu_mul(to_device(g, dt, DEV), to_device(u, dt, DEV))
+    torch.cuda.synchronize()
+    ref = oracle.silu_mul(widen(g, dt), widen(u, dt))
+    got = dl_widen(m, dt)
+    tol = (np.abs(ref) * (2.0 ** -7 if dt == "bf16" else 4e-6)) + 1e-30
+    assert np.all(np.abs(got - ref) <= tol), f"max err {np.abs(got - ref).max():.3e}"
+
+
+@pytest.mark.parametrize("dt,T,d_in,d_out", [("bf16", 9, 256, 192), ("bf16", 64, 512, 256), ("bf16", 300, 256, 384),
+                                             ("f32", 16, 128, 64)])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_projection_residual(dt, T, d_in, d_out, in_place):
+    """y = residual + W0 x + adapters, one rounding; the residual may be y itself (updated in place)."""
+    say("residual", dt, T, d_in, d_out, in_place)
+    rng = np.random.default_rng(T + d_out)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    E, r, k = 8, 16, 2
+    x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+    W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    B = conv(rng.standard_normal((E, d_out, r), dtype=np.float32) / np.float32(np.sqrt(r)))
+    res = conv(rng.standard_normal((T, d_out), dtype=np.float32) * np.float32(2.0))
+    idx, gate = datagen.uniform_indices(T, T, E, k), datagen.random_gates(T, T, k)
+    idx_d = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    gate_d = torch.from_numpy(gate.astype(np.float32)).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    res_d = to_device(res, dt, DEV)
+    y = res_d if in_place else torch.empty_like(res_d)
+    groups = [([(to_device(W0, dt, DEV), to_device(A, dt, DEV), to_device(B, dt, DEV), y, res_d)],
+               to_device(x, dt, DEV))]
+    rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+    torch.cuda.synchronize()
+    ref = widen(res, dt) + oracle.sgmm(widen(x, dt), widen(W0, dt), widen(A, dt), widen(B, dt), idx,
+                                       gate.astype(np.float64))
+    check_y(y, ref, dt, "residual")
+
+
+def _act_case(dt, T, d_in, d_ff, seed):
+    rng = np.random.default_rng(seed)
+    conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
+    E, r, k = 8, 16, 2
+    x = to_device(conv(rng.standard_normal((T, d_in), dtype=np.float32)), dt, DEV)
+    projs = []
+    for _ in range(2):
+        projs.append(tuple(to_device(conv(a), dt, DEV) for a in (
+            rng.standard_normal((d_ff, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)),
+            rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)),
+            rng.standard_normal((E, d_ff, r), dtype=np.float32) / np.float32(np.sqrt(r)))))
+    idx_d = torch.from_numpy(datagen.uniform_indices(seed, T, E, k).astype(np.int32)).to(DEV)
+    gate_d = torch.from_numpy(datagen.random_gates(seed, T, k).astype(np.float32)).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    return x, projs, (E, r, k), (idx_d, gate_d, off, perm)
+
+
+@pytest.mark.parametrize("dt,T,d_in,d_ff", [("bf16", 9, 256, 512), ("bf16", 64, 512, 1024), ("bf16", 32, 4096, 11008),
+                                            ("bf16", 100, 256, 384), ("f32", 16, 128, 256)])
+def test_act_matches_separate(dt, T, d_in, d_ff):
+    """A (gate, up) group with RP_ACT_SILU_MUL gives, bit for bit, rp_silu_mul of the group's own outputs
+    (fused epilogue for decode shapes, a separate launch otherwise), and up is left as it was."""
+    say("act", dt, T, d_in, d_ff)
+    x, projs, (E, r, k), rt = _act_case(dt, T, d_in, d_ff, seed=T + d_ff)
+    idx_d, gate_d, off, perm = rt
+    plain, _, _, _, _ = rp.sgmm_step([(list(projs), x)], E, r, k, topk_idx=idx_d, topk_gate=gate_d,
+                                     seg_offsets=off, pair_perm=perm)
+    m_sep = rp.silu_mul(plain[0][0], plain[0][1])
+    fused, _, _, _, _ = rp.sgmm_step([(list(projs), x, 0, rp.RP_ACT_SILU_MUL)], E, r, k, topk_idx=idx_d,
+                                     topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+    torch.cuda.synchronize()
+    as_bits = (lambda t: t.view(torch.int16)) if dt == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(as_bits(fused[0][1]), as_bits(plain[0][1])), "up output changed"
+    assert torch.equal(as_bits(fused[0][0]), as_bits(m_sep)), "fused activation differs from rp_silu_mul"
+
+
+def _chain_workload(name_idx, dt, T, d, ff, E, r, k, layers):
+    G = datagen.Group
+    groups = (G("qkv", ("q", "k", "v"), d, d, "x_attn"), G("o", ("o",), d, d, "x_o"),
+              G("gate_up", ("gate", "up"), d, ff, "x_attn"), G("down", ("down",), ff, d, "x_d"))
+    return datagen.Workload(f"chain_{name_idx}", name_idx, dt, T=T, d=d, E=E, r=r, k=k, layers=layers,
+                            groups=groups, assignment="router")
+
+
+@pytest.mark.parametrize("index,dt,T,d,ff,E,r,k,layers", [
+    (61, "bf16", 9, 256, 512, 8, 8, 2, 2),        # small decode, routing inside the first launch
+    (62, "bf16", 64, 4096, 11008, 16, 8, 2, 2),   # the 32-layer decode step's shapes, two layers
+    (63, "bf16", 100, 256, 384, 40, 16, 2, 2),    # prefill shapes: residual in the GEMM, activation as a launch
+    (64, "f32", 16, 128, 256, 4, 8, 1, 2),        # fp32
+])
+def test_decoder_layer_chain(index, dt, T, d, ff, E, r, k, layers):
+    """Whole decoder layers around the adapted projections, inputs chained (RMSNorm -> q|k|v -> o + residual ->
+    RMSNorm -> gate|up with silu(g)*u -> down + residual), routing once on layer 0's normalised input:
+    the residual stream after every layer against the oracle's decoder_layer (bf16 rounding at each
+    operation's output for bf16)."""
+    say("chain", dt, T, d, ff, E, r, k, layers)
+    wl = _chain_workload(index, dt, T, d, ff, E, r, k, layers)
+    dw = DeviceWorkload(wl, DEV, b_scale=1.0)
+    dw.run_chained()
+    torch.cuda.synchronize()
+    rnd = oracle.round_bf16 if dt == "bf16" else (lambda a: np.asarray(a, np.float64))
+    h0 = widen(datagen.residual_input(wl), dt)
+    Wg = widen(datagen.router_weight(wl), dt)
+    ws = []
+    for l in range(layers):
+        w = {g: widen(datagen.norm_weight(wl, l, g), dt) for g in ("gamma1", "gamma2")}
+        for g in wl.groups:
+            for p in g.projs:
+                pw = datagen.proj_weights(wl, l, g, p, b_scale=1.0)
+                w[p] = (widen(pw.W0, dt), widen(pw.A, dt), widen(pw.B, dt))
+        ws.append(w)
+    n1 = rnd(oracle.rmsnorm(h0, ws[0]["gamma1"], 1e-5))
+    same, idx_ref, gate_ref = compare_routing(dw.topk_idx, dw.topk_gate, None, n1, Wg, k)
+    assert same.all(), "seeds are chosen free of near ties"
+    h = h0
+    for l in range(layers):
+        h = oracle.decoder_layer(h, ws[l], idx_ref, gate_ref, 1e-5, rnd=rnd)
+    err = check_y(dw.chain_h, h, dt, f"chain after {layers} layers")
+    say(f"chain: max error {err:.2e} of max|h|")

@@ -10,7 +10,8 @@ from tests import oracle_pins
 
 def _mutant(**overrides):
     ns = types.SimpleNamespace(**{n: getattr(reference, n) for n in (
-        "router_logits", "select_topk", "topk_margin", "softmax_gates", "pregate", "segment", "sgmm")})
+        "router_logits", "select_topk", "topk_margin", "softmax_gates", "pregate", "segment", "sgmm",
+        "round_bf16", "rmsnorm", "silu_mul", "decoder_layer")})
     for k, v in overrides.items():
         setattr(ns, k, v)
     # keep pregate composed from the (possibly mutated) parts
@@ -20,7 +21,67 @@ def _mutant(**overrides):
             idx = ns.select_topk(l, k)
             return idx, ns.softmax_gates(l, idx), l
         ns.pregate = pregate
+    # and the decoder layer from the (possibly mutated) elementwise parts
+    if "decoder_layer" not in overrides:
+        ns.decoder_layer = _layer_variant(None, ns)
     return ns
+
+
+def _layer_variant(kind, ns=None):
+    def layer(h, w, idx, gate, eps, rnd=None):
+        parts = ns if ns is not None else reference
+        rnd = rnd or parts.round_bf16
+
+        def proj(x, name):
+            return parts.sgmm(x, *w[name], idx, gate)
+        n1 = rnd(parts.rmsnorm(h, w["gamma1"], eps))
+        attn = rnd(proj(n1, "q" if kind == "attention_from_q" else "v"))
+        h1 = rnd((0 if kind == "no_residual_o" else np.asarray(h, np.float64)) + proj(attn, "o"))
+        n2 = rnd(parts.rmsnorm(h1, w["gamma1" if kind == "gamma1_twice" else "gamma2"], eps))
+        g, u = rnd(proj(n2, "gate")), rnd(proj(n2, "up"))
+        m = rnd(parts.silu_mul(g, u))
+        return rnd((0 if kind == "no_residual_down" else h1) + proj(m, "down"))
+    return layer
+
+
+def _round_toward_zero(a):
+    a = np.asarray(a, np.float64)
+    r = reference.round_bf16(a)
+    step = np.exp2(np.floor(np.log2(np.abs(np.where(a == 0, 1, a)))) - 7)
+    return np.where(np.abs(r) > np.abs(a), r - np.sign(a) * step, r)
+
+
+def _round_ties_away(a):
+    a = np.asarray(a, np.float64)
+    r = reference.round_bf16(a)
+    e = np.floor(np.log2(np.abs(np.where(a == 0, 1, a))))
+    step = np.exp2(e - 7)
+    tie = np.abs(a / step - np.trunc(a / step)) == 0.5
+    return np.where(tie, np.sign(a) * (np.abs(np.trunc(a / step)) + 1) * step, r)
+
+
+def _rmsnorm_no_sqrt(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.mean(x * x, axis=1, keepdims=True) + eps) * gamma
+
+
+def _rmsnorm_eps_outside(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=1, keepdims=True)) + eps) * gamma
+
+
+def _rmsnorm_sum(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=1, keepdims=True) + eps) * gamma
+
+
+def _silu_on_up(g, u):
+    return reference.silu_mul(u, g)
+
+
+def _silu_sign(g, u):
+    g = np.asarray(g, np.float64)
+    return g / (1.0 + np.exp(g)) * u
 
 
 def _sgmm_variant(kind):
@@ -117,6 +178,17 @@ MUTANTS = {
     "sgmm_sign": dict(sgmm=_sgmm_variant("sign")),
     "sgmm_A_misindexed": dict(sgmm=_sgmm_variant("A_transposed_use")),
     "sgmm_last_slot_dropped": dict(sgmm=_sgmm_variant("delta_dropped_for_last_slot")),
+    "round_bf16_toward_zero": dict(round_bf16=_round_toward_zero),
+    "round_bf16_ties_away": dict(round_bf16=_round_ties_away),
+    "rmsnorm_no_sqrt": dict(rmsnorm=_rmsnorm_no_sqrt),
+    "rmsnorm_eps_outside_sqrt": dict(rmsnorm=_rmsnorm_eps_outside),
+    "rmsnorm_sum_not_mean": dict(rmsnorm=_rmsnorm_sum),
+    "silu_on_up": dict(silu_mul=_silu_on_up),
+    "silu_sign": dict(silu_mul=_silu_sign),
+    "layer_no_residual_o": dict(decoder_layer=_layer_variant("no_residual_o")),
+    "layer_no_residual_down": dict(decoder_layer=_layer_variant("no_residual_down")),
+    "layer_attention_from_q": dict(decoder_layer=_layer_variant("attention_from_q")),
+    "layer_gamma1_twice": dict(decoder_layer=_layer_variant("gamma1_twice")),
 }
 
 
