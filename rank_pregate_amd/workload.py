@@ -246,8 +246,9 @@ class DeviceWorkload:
             rp_merge_adapters(pw.W0, pw.A, pw.B, sel, w, -1.0, stream=stream)
 
     # -- whole decoder layers around the projections (chained inputs) --------
-    def _chain_buffers(self):
-        """Residual stream, norm output and per-layer RMSNorm weights of the chained layers."""
+    def prepare_chain(self):
+        """Residual stream, norm output and per-layer RMSNorm weights of the chained layers (uploads and
+        allocates: call before recording run_chained into a graph)."""
         import torch
         if hasattr(self, "chain_h"):
             return
@@ -290,7 +291,7 @@ class DeviceWorkload:
         """Every layer as a whole decoder layer (RMSNorm, q|k|v, o + residual, RMSNorm, gate|up with the
         fused silu(g)*u, down + residual), inputs chained from the outputs before them; the routing runs
         inside the first launch, on layer 0's normalised input.  The residual stream ends in chain_h."""
-        self._chain_buffers()
+        self.prepare_chain()
         wl = self.wl
         for i, (l, (attn, mlp)) in enumerate(zip(self.layers, self.chain_groups(copy))):
             rp_rmsnorm(self.chain_h0 if i == 0 else self.chain_h, self.chain_gamma[(l, "gamma1")], CHAIN_EPS,
