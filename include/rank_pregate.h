@@ -186,8 +186,10 @@ rp_status rp_sgmm_fused(const rp_proj* projs, int32_t n_proj, const void* x, int
  * with bit-identical routing outputs, which later groups of the same step then
  * pass to rp_sgmm_fused.  For decode shapes (bf16, T <= 32, E <= 64)
  * everything runs in one kernel launch whose router and segmentation finish
- * while the backbone weights stream; other shapes issue the three launches in
- * order.
+ * while the backbone weights stream; bf16 with 64 < E (E a multiple of 8)
+ * routes and segments in one launch of its own on the matrix cores (the
+ * routing is bit-identical to rp_pregate's); other shapes issue the three
+ * launches in order.
  *
  *   Wg        [d_in, E], dense, dtype dt (the router weight)
  *   topk_idx  int32 [T, k], topk_gate fp32 [T, k], seg_offsets int32 [E+1],
