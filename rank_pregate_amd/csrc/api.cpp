@@ -58,6 +58,29 @@ int cu_count(int* out) {
 
 constexpr int64_t kIntMax = 0x7fffffff;
 
+// A second stream per device, with the events that fork work from a caller's
+// stream onto it and join it back; created on first use outside stream
+// capture (default priority), kept until the process ends.  Callers hold
+// side_mu from the fork to the join, so the records and waits of calls from
+// several host threads do not interleave.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex side_mu;
+SideStream* side_stream(bool may_create) {
+  static SideStream cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = cache[dev];
+  if (ss.join) return &ss;
+  if (!may_create) return nullptr;
+  if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) ss.s = nullptr;
+  if (ss.s && !ss.fork && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) ss.fork = nullptr;
+  if (ss.fork && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) ss.join = nullptr;
+  return ss.join ? &ss : nullptr;
+}
+
 }  // namespace
 
 namespace rp {
@@ -263,6 +286,17 @@ size_t split_router_bytes(rp_dtype dt, int64_t T, int64_t E) {
   return split_router(dt, T, E) ? rp::kWorkspaceCounterBytes + rp::route_split_bytes((int)T, (int)E) : 0;
 }
 
+// Prefill batches whose shrink (and routing) can run beside the base GEMM:
+// bf16, the expand as a launch of its own, every group in one launch pair.
+bool overlap_shrink(const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k, rp_dtype dt) {
+  if (decode_shape(dt, T) || dt != RP_BF16 || n_groups > rp::kMaxGroups ||
+      !rp::prefill_split_expand((int)T, (int)E, (int)r, k))
+    return false;
+  for (int g = 1; g < n_groups; ++g)
+    if (gs[g].x_from_call) return false;
+  return true;
+}
+
 // Workspace bytes a validated call needs.
 size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64_t E, int64_t r, int32_t k,
                               rp_dtype dt) {
@@ -287,8 +321,10 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
       const int tiles_bound = (int)(sum / rp::prefill_tile_rows((int)T) + gs[g].n_proj);
       b += rp::prefill_u_bytes(gs[g].n_proj, (int)T, (int)r, k) +
            rp::prefill_partial_bytes(tiles_bound, (int)T, rp::prefill_max_splits((int)gs[g].d_in));
+      if (rp::prefill_split_expand((int)T, (int)E, (int)r, k)) b += rp::prefill_base_bytes(tiles_bound, (int)T);
     }
-    need = std::max(need, b);
+    // routing beside the groups: its partial sums after their buffers
+    need = overlap_shrink(gs, n_groups, T, E, r, k, dt) ? b + 256 + split_router_bytes(dt, T, E) : std::max(need, b);
   } else {
     for (int g = 0; g < n_groups; ++g) {
       int64_t sum = 0;
@@ -350,7 +386,13 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     sg.err_count = reinterpret_cast<int*>(ws) + kSegErrWord;
   }
   const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T, (int)E);
-  if (route && !fuse_route && split_router(dt, T, E)) {
+  // prefill with the expand in a launch of its own and every group in one
+  // batch: the routing and the shrink run on a second stream beside the base
+  // GEMM, which needs neither
+  const bool overlap = overlap_shrink(gs, n_groups, T, E, r, k, dt);
+  if (overlap) {
+    // launched with the groups below
+  } else if (route && !fuse_route && split_router(dt, T, E)) {
     // router and segmentation in one launch; its partial sums sit where the
     // groups' buffers go (the groups' launches are queued after it)
     const size_t need = split_router_bytes(dt, T, E);
@@ -378,8 +420,9 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       ps.n_groups = ng;
       ps.n_tok_tiles = (int)((T + rp::prefill_tile_tokens((int)T) - 1) / rp::prefill_tile_tokens((int)T));
       ps.units = rp::prefill_shrink_units((int)T, (int)E, k);
+      ps.split_expand = rp::prefill_split_expand((int)T, (int)E, (int)r, k) ? 1 : 0;
       size_t off = rp::kWorkspaceCounterBytes;
-      int shrink_blocks = 0, gemm_blocks = 0, counters = 0;
+      int shrink_blocks = 0, gemm_blocks = 0, counters = 0, expand_blocks = 0;
       for (int i = 0; i < ng; ++i) {
         const rp_group& g = gs[g0 + i];
         int d_out[RP_MAX_PROJ];
@@ -404,18 +447,51 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         a.partial = reinterpret_cast<float*>(w + off);
         if (S > 1) counters += n_cnt;
         off += rp::prefill_partial_bytes(plan.n_tiles, (int)T, S);
+        if (ps.split_expand) {
+          a.base = reinterpret_cast<float*>(w + off);
+          off += rp::prefill_base_bytes(plan.n_tiles, (int)T);
+          expand_blocks += rp::prefill_expand_blocks(plan.n_tiles, (int)T);
+          ps.expand_end[i] = expand_blocks;
+        }
         shrink_blocks += ps.units * g.n_proj;
         gemm_blocks += rp::prefill_group_blocks(plan.n_tiles, (int)T) * S;
         ps.shrink_end[i] = shrink_blocks;
         ps.block_end[i] = gemm_blocks;
       }
-      if (ws_bytes < off) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, off);
+      // the split-form router's partial sums go after the groups' buffers
+      // when it runs beside the GEMM
+      const bool split_rt = overlap && route && split_router(dt, T, E);
+      const size_t rbase = (off + 255) & ~(size_t)255;
+      const size_t need = split_rt ? rbase + rp::route_split_bytes((int)T, (int)E) : off;
+      if (ws_bytes < need) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
       g0 += ng;
       if (dry) {
-        *dry_need = std::max(*dry_need, off);
+        *dry_need = std::max(*dry_need, need);
         continue;
       }
-      hipError_t e = rp::launch_prefill_step(ps, stream);
+      hipError_t e = hipSuccess;
+      if (overlap) {
+        std::lock_guard<std::mutex> lock(side_mu);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        SideStream* ss = e == hipSuccess ? side_stream(cs == hipStreamCaptureStatusNone) : nullptr;
+        const hipStream_t side = ss ? ss->s : stream;  // without one, the same order on the caller's stream
+        if (e == hipSuccess && ss) e = hipEventRecord(ss->fork, stream);
+        if (e == hipSuccess && ss) e = hipStreamWaitEvent(side, ss->fork, 0);
+        if (e == hipSuccess && split_rt)
+          e = rp::launch_route_segment_mfma(pg, sg, w + rbase, reinterpret_cast<int*>(w) + rp::kRouteCounterWord,
+                                            side);
+        else if (e == hipSuccess && route)
+          e = rp::launch_pregate(pg, side);
+        if (e == hipSuccess && route && !split_rt) e = rp::launch_segment(sg, side);
+        if (e == hipSuccess) e = rp::launch_prefill_shrink(ps, side);
+        if (e == hipSuccess && ss) e = hipEventRecord(ss->join, side);
+        if (e == hipSuccess) e = rp::launch_prefill_gemm(ps, stream);
+        if (e == hipSuccess && ss) e = hipStreamWaitEvent(stream, ss->join, 0);
+        if (e == hipSuccess) e = rp::launch_prefill_expand(ps, stream);
+      } else {
+        e = rp::launch_prefill_step(ps, stream);
+      }
       for (int i = 0; e == hipSuccess && i < ng; ++i)
         if (gs[g0 - ng + i].act == RP_ACT_SILU_MUL) e = launch_act(gs[g0 - ng + i], T, rdt, stream);
       if (e != hipSuccess) return hip_fail(fn, e);

@@ -54,8 +54,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rm_rsrc(const void* base, uint
 __device__ __forceinline__ void logit_part(const PregateArgs& a, int t0, int chunk, int q, f32x4_t (&acc)[8]) {
   const int lane = threadIdx.x & 63, n = lane & 15, kg = lane >> 4;
   const bf16_t* xr = static_cast<const bf16_t*>(a.x) + (size_t)min(t0 + n, a.T - 1) * a.ld_x;
-  const int col = chunk * kRmCols + 8 * n;
-  const bool col_ok = col < a.E;  // E % 8 == 0: the lane's eight columns are all in or all out
+  const int col = chunk * kRmCols + 8 * n;  // E % 8 == 0: the lane's eight columns are all in or all out
   const bf16_t* wc = static_cast<const bf16_t*>(a.Wg) + min(col, a.E - 8);
   const int nks = (a.d_in + 31) >> 5;
   const int s0 = (int)((long long)nks * q / kRmParts), s1 = (int)((long long)nks * (q + 1) / kRmParts);
@@ -66,15 +65,19 @@ __device__ __forceinline__ void logit_part(const PregateArgs& a, int t0, int chu
   // k-step s: columns k = 32 s + 8 kg .. +7 of x (this lane's token) and router
   // rows k .. k+7 (this lane's columns); d_in % 8 == 0, so a group of eight is
   // all in or all out
+  // loads go to clamped addresses and are masked where they are used, not as
+  // they arrive (a select on loaded data waits for the load right there)
   auto issue = [&](int slot, int s) {
-    const int k = s * 32 + 8 * kg;
-    const int kk = min(k, a.d_in - 8);
-    const bool ok = k < a.d_in;
-    xa[slot] = pick4(ok, ld16(xr + kk));
+    const int kk = min(s * 32 + 8 * kg, a.d_in - 8);
+    xa[slot] = ld16(xr + kk);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wr[slot][i] = pick4(ok && col_ok, ld16(wc + (size_t)(kk + i) * a.E));
+    for (int i = 0; i < 8; ++i) wr[slot][i] = ld16(wc + (size_t)(kk + i) * a.E);
   };
-  auto consume = [&](int slot) {
+  auto consume = [&](int slot, int s) {
+    // K columns past d_in contribute zero (the token operand is zeroed there);
+    // router columns past E read a real column and are never stored
+    const bool ok = s * 32 + 8 * kg < a.d_in;
+    xa[slot] = pick4(ok, xa[slot]);
     // bt[c] = column col + c at rows k .. k+7 (element i = row k + i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -97,13 +100,13 @@ __device__ __forceinline__ void logit_part(const PregateArgs& a, int t0, int chu
   for (; s + kRmRing <= s1; s += kRmRing) {
     static_for<0, kRmRing>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      consume(i);
+      consume(i, s + i);
       if (s + i + kRmRing < s1) issue(i, s + i + kRmRing);
     });
   }
   static_for<0, kRmRing>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    if (s + i < s1) consume(i);
+    if (s + i < s1) consume(i, s + i);
   });
 }
 

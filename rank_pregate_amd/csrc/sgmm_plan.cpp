@@ -174,9 +174,10 @@ size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long lo
     return step_workspace_upper_bound(&g, 1, T, E, r, k);
   }
   size_t b = align256(kCounterBytes + (size_t)n_proj * T * k * r * sizeof(float));
-  if (dt == kBF16) {  // the prefill GEMM's split-K partials
+  if (dt == kBF16) {  // the prefill GEMM's split-K partials (and fp32 base tiles when the expand runs apart)
     const int tiles_bound = (int)(sum_d_out / prefill_tile_rows(T) + n_proj);
     b += prefill_partial_bytes(tiles_bound, T, prefill_max_splits(d_in));
+    if (prefill_split_expand(T, E, r, k)) b += prefill_base_bytes(tiles_bound, T);
   }
   return b;
 }

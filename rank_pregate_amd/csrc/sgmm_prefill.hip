@@ -90,6 +90,11 @@ constexpr int kPBigT = 256;     // from this many tokens, 256-token tiles of eig
 constexpr int kPNB = 4;        // adapters per batch of B loads in the expand
 constexpr int kPUJ = 4;        // slots of a token whose u a lane holds at once (k > 2)
 constexpr int kNoAdapter = 0x7fffffff;
+// expand as a launch of its own (expand_gather_bf16)
+constexpr int kGRows = 64;  // output rows per block
+constexpr int kGWaves = 4;
+constexpr int kGTok = 64;   // tokens per block
+constexpr int kGMaxK = 4;   // top-k the launch serves
 static_assert(sizeof(PrefillStep) <= 4096, "kernel argument block too large");
 
 __device__ __forceinline__ int token_at(const SgmmArgs& a, int i) {
@@ -574,6 +579,21 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void prefill_bf16(Prefil
   if (S > 1 && !splitk_reduce<NW>(a, ((size_t)tile * n_tok_tiles + tt) * S, split, S,
                               a.counters + (size_t)tile * n_tok_tiles + tt, acc))
     return;
+  if (EXP == 0) {
+    // the expand runs as a launch of its own: store the fp32 base tile as
+    // [token][128 rows] (token positions in the tile's order, T <= BM)
+    float* bt = a.base + (size_t)tile * a.T * kPB;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int pos = i0 + wm * 64 + f * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+          if (pos < a.T) bt[(size_t)pos * kPB + wn * 64 + g * 32 + lr] = acc[f][g][v];
+        }
+    return;
+  }
   if (TOP1)
     expand_top1<4>(a, pd, proj, i0 + wm * 64, row0 + wn * 64, acc);
   else if (a.k > 0)
@@ -629,6 +649,14 @@ int prefill_units(int n_tiles, int T) {
 }
 int prefill_group_blocks(int n_tiles, int T) { return prefill_units(n_tiles, T); }
 int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * E ? 1 : 4; }
+bool prefill_split_expand(int T, int E, int r, int k) {
+  return k >= 2 && k <= kGMaxK && r <= 32 && T <= kPBigT && prefill_shrink_nct(T, E, k) == 1;
+}
+size_t prefill_base_bytes(int n_tiles, int T) { return (size_t)n_tiles * T * kPB * sizeof(float); }
+int prefill_expand_blocks(int n_tiles, int T) {
+  // 64-row blocks rounded up to whole sets of 8 (one per XCD), times the token blocks
+  return (2 * n_tiles + 7) / 8 * 8 * ((T + kGTok - 1) / kGTok);
+}
 int prefill_shrink_units(int T, int E, int k) {
   if (prefill_shrink_nct(T, E, k) == 1) return E;  // one block per segment
   return E + (T * k + 63) / 64;
@@ -637,17 +665,124 @@ int prefill_shrink_units(int T, int E, int k) {
 template <int BM>
 void launch_gemm(const PrefillStep& ps, bool fast, int exp, dim3 grid, hipStream_t s) {
   if (fast) {
-    if (exp == 1) prefill_bf16<true, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
+    if (exp == 0) prefill_bf16<true, BM, 0><<<grid, 2 * BM, 0, s>>>(ps);
+    else if (exp == 1) prefill_bf16<true, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
     else if (exp == 2) prefill_bf16<true, BM, 2><<<grid, 2 * BM, 0, s>>>(ps);
     else prefill_bf16<true, BM, 4><<<grid, 2 * BM, 0, s>>>(ps);
   } else {
-    if (exp == 1) prefill_bf16<false, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
+    if (exp == 0) prefill_bf16<false, BM, 0><<<grid, 2 * BM, 0, s>>>(ps);
+    else if (exp == 1) prefill_bf16<false, BM, 1><<<grid, 2 * BM, 0, s>>>(ps);
     else if (exp == 2) prefill_bf16<false, BM, 2><<<grid, 2 * BM, 0, s>>>(ps);
     else prefill_bf16<false, BM, 4><<<grid, 2 * BM, 0, s>>>(ps);
   }
 }
 
-hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
+// ----------------------------------------------------------------------------
+// The expand as a launch of its own, for top-k >= 2 over many adapters (most
+// segments one to three tokens long): per token, not per segment.  A block
+// takes 64 output rows (lane = row) of one projection and kGTok tokens; each
+// of its waves walks its own tokens and, for token t, adds the k terms
+// B_e(t,j)[rows, :] . u[t*k + j, :] (u already carries the gate; slots in
+// order j = 0..k-1, each rank sum in rank order) to the fp32 base the GEMM
+// stored, then the residual, then rounds once to bf16.  There is no segment
+// walk, no staging and no barrier after the first: a pair's 64 B rows are 64
+// x r contiguous bf16 that its wave reads straight from memory, G tokens'
+// worth at a time.  The kGTok-token blocks of one 64-row block run on one XCD
+// one after another (blockIdx % 8 picks the XCD), so a B chunk that several
+// of them read comes from that XCD's L2 after the first.  Every output has
+// one owner, so the result does not depend on timing.
+// ----------------------------------------------------------------------------
+
+template <int R, int KK>
+__global__ __launch_bounds__(64 * kGWaves) void expand_gather_bf16(PrefillStep ps) {
+  constexpr int TW = kGTok / kGWaves;                       // tokens per wave
+  constexpr int G = 128 / (KK * R) > 0 ? 128 / (KK * R) : 1;  // tokens whose B rows are in flight at once
+  static_assert(TW % G == 0, "token groups must tile a wave's tokens");
+  __shared__ __attribute__((aligned(16))) float U[kGTok * KK * R];
+  __shared__ int I[kGTok * KK];
+  const int tid = threadIdx.x, rr = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = group_of_block(ps.expand_end, ps.n_groups, blockIdx.x);
+  const SgmmArgs& a = ps.g[grp];
+  const int b = blockIdx.x - (grp > 0 ? ps.expand_end[grp - 1] : 0);
+  const int T = a.T, k = a.k;
+  const int n_tc = (T + kGTok - 1) / kGTok;
+  const int tc = (b >> 3) % n_tc, rb = ((b >> 3) / n_tc) * 8 + (b & 7);
+  if (rb >= 2 * a.n_tiles) return;
+  const int tile = rb >> 1;
+  const int proj = proj_of_tile(a, tile);
+  const ProjDesc pd = proj_at(a, proj);
+  const int row0 = (tile - pd.tile_begin) * kPB + (rb & 1) * kGRows;
+  if (row0 >= pd.d_out) return;  // the second half of a ragged last tile
+  const int row = row0 + rr, prow = min(row, pd.d_out - 1);
+  const int t0 = tc * kGTok, nt = min(kGTok, T - t0);
+
+  // gated u and adapter indices of the block's tokens
+  const float4* ug = reinterpret_cast<const float4*>(a.u + ((size_t)proj * T + t0) * k * R);
+  for (int i = tid; i < nt * k * R / 4; i += 64 * kGWaves) reinterpret_cast<float4*>(U)[i] = ug[i];
+  for (int i = tid; i < nt * k; i += 64 * kGWaves) I[i] = a.topk_idx[(size_t)t0 * k + i];
+  __syncthreads();
+
+  const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
+  const float* bt = a.base + (size_t)tile * T * kPB + (rb & 1) * kGRows + rr;
+  const bf16_t* res = static_cast<const bf16_t*>(pd.residual);
+  bf16_t* y = static_cast<bf16_t*>(pd.y);
+  const int tw_end = min((w + 1) * TW, nt);
+  for (int g0 = w * TW; g0 < tw_end; g0 += G) {
+    // loads of G tokens first (a token past the wave's last repeats its last,
+    // and is never stored), then their sums
+    float base_v[G], res_v[G];
+    int ev[G][KK];
+    uint4 bq[G][KK][R / 8];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int tl = min(g0 + i, tw_end - 1);
+      base_v[i] = bt[(size_t)(t0 + tl) * kPB];
+      res_v[i] = res ? bf16_to_f32(res[(size_t)(t0 + tl) * pd.ld_y + prow]) : 0.f;
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        ev[i][j] = -1;
+        if (j < k) {
+          const int e = __builtin_amdgcn_readfirstlane(I[tl * k + j]);
+          if (e >= 0 && e < a.E) {  // out-of-range indices add nothing (no segment holds them)
+            ev[i][j] = e;
+            const bf16_t* src = Bm + ((size_t)e * pd.d_out + prow) * R;
+#pragma unroll
+            for (int c = 0; c < R / 8; ++c) bq[i][j][c] = ld16(src + 8 * c);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int tl = g0 + i;
+      if (tl >= tw_end) break;
+      float v = base_v[i];
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        if (ev[i][j] < 0) continue;
+        const float4* up = reinterpret_cast<const float4*>(&U[(tl * k + j) * R]);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < R / 8; ++c) {
+          const uint32_t wv[4] = {bq[i][j][c].x, bq[i][j][c].y, bq[i][j][c].z, bq[i][j][c].w};
+          const float4 u0 = up[2 * c], u1 = up[2 * c + 1];
+          const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc = fmaf(__uint_as_float(wv[q] << 16), uv[2 * q], acc);
+            acc = fmaf(__uint_as_float(wv[q] & 0xffff0000u), uv[2 * q + 1], acc);
+          }
+        }
+        v += acc;
+      }
+      v += res_v[i];
+      if (row < pd.d_out) y[(size_t)(t0 + tl) * pd.ld_y + row] = f32_to_bf16(v);
+    }
+  }
+}
+
+hipError_t launch_prefill_shrink(const PrefillStep& ps, hipStream_t s) {
   const SgmmArgs& a0 = ps.g[0];
   if (a0.T == 0) return hipSuccess;
   if (a0.k > 0) {
@@ -660,9 +795,13 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
       case 4: small ? shrink_bf16<4, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<4, 4><<<g, 512, 0, s>>>(ps); break;
       default: small ? shrink_bf16<8, 1><<<g, 256, 0, s>>>(ps) : shrink_bf16<8, 4><<<g, 256, 0, s>>>(ps); break;
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_gemm(const PrefillStep& ps, hipStream_t s) {
+  const SgmmArgs& a0 = ps.g[0];
+  if (a0.T == 0) return hipSuccess;
   bool fast = true;  // every projection tiled, every d_in a multiple of kPK
   for (int g = 0; g < ps.n_groups; ++g) {
     fast = fast && ps.g[g].d_in % kPK == 0;
@@ -671,12 +810,34 @@ hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   const dim3 grid(ps.block_end[ps.n_groups - 1]);
   if (ps.n_tok_tiles != (a0.T + prefill_tile_tokens(a0.T) - 1) / prefill_tile_tokens(a0.T))
     return hipErrorInvalidValue;  // token tiles planned for another tile size
-  const int exp = a0.k == 1 && a0.r <= 64 ? 1 : a0.k <= 2 ? 2 : 4;
+  const int exp = ps.split_expand ? 0 : a0.k == 1 && a0.r <= 64 ? 1 : a0.k <= 2 ? 2 : 4;
   if (prefill_tile_tokens(a0.T) == 256)
     launch_gemm<256>(ps, fast, exp, grid, s);
   else
     launch_gemm<128>(ps, fast, exp, grid, s);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_expand(const PrefillStep& ps, hipStream_t s) {
+  const SgmmArgs& a0 = ps.g[0];
+  if (a0.T == 0) return hipSuccess;
+  if (ps.split_expand) {
+    const dim3 xg(ps.expand_end[ps.n_groups - 1]);
+    const bool k2 = a0.k <= 2;  // k <= kGMaxK (prefill_split_expand)
+    switch (a0.r) {             // r in {8, 16, 32} (prefill_split_expand)
+      case 8: k2 ? expand_gather_bf16<8, 2><<<xg, 64 * kGWaves, 0, s>>>(ps) : expand_gather_bf16<8, 4><<<xg, 64 * kGWaves, 0, s>>>(ps); break;
+      case 16: k2 ? expand_gather_bf16<16, 2><<<xg, 64 * kGWaves, 0, s>>>(ps) : expand_gather_bf16<16, 4><<<xg, 64 * kGWaves, 0, s>>>(ps); break;
+      default: k2 ? expand_gather_bf16<32, 2><<<xg, 64 * kGWaves, 0, s>>>(ps) : expand_gather_bf16<32, 4><<<xg, 64 * kGWaves, 0, s>>>(ps); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
+  hipError_t e = launch_prefill_shrink(ps, s);
+  if (e == hipSuccess) e = launch_prefill_gemm(ps, s);
+  if (e == hipSuccess) e = launch_prefill_expand(ps, s);
+  return e;
 }
 
 hipError_t launch_prefill(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s) {

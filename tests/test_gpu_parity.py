@@ -359,6 +359,25 @@ def test_projection_tiled_w0(T, d_in, d_outs, E, r, k):
     _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + 7 * d_in + E, tiled=True)
 
 
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (256, 4096, [4096, 1024], 256, 16, 2),   # many adapters, one token tile of 256
+    (65, 512, [520, 128], 64, 8, 3),         # 128-token tile, ragged output tile (second half past d_out)
+    (200, 12288, [256], 96, 16, 2),          # long K on few tiles: split-K partials, then the fp32 base
+    (130, 256, [192, 64, 320], 40, 8, 4),    # four slots, three projections
+    (100, 1024, [384, 136], 48, 32, 2),      # rank 32, two token blocks, ragged 64-row block
+])
+def test_prefill_split_expand(T, d_in, d_outs, E, r, k):
+    """Prefill shapes with many small segments: the GEMM stores fp32 base tiles and the expand runs as a
+    launch of its own (per token, each slot's adapter rows read directly); outputs against the oracle,
+    bit-identical on a second call."""
+    say("split expand", T, d_in, d_outs, E, r, k)
+    _, ys = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + E + k, b_scale=1.0)
+    first = [y.clone() for y in ys]
+    _, ys2 = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + E + k, b_scale=1.0)
+    for a, b in zip(first, ys2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "split expand changed between calls"
+
+
 @pytest.mark.parametrize("T", [32, 300])
 def test_projection_zero_B_is_base(T):
     say("zero B", T)
@@ -969,6 +988,60 @@ def test_fused_step_two_groups():
             check_y(y, ref, "bf16", "fused step, two groups")
 
 
+def test_step_split_expand_routed_graph():
+    """Routed prefill-sized step with many small segments: routing and shrink run on the library's second
+    stream beside the base GEMM, joined before the expand.  Outputs against the oracle; a HIP graph of
+    the call, replayed three times with eager work between the replays, reproduces the eager outputs
+    bit for bit."""
+    say("split expand, routed, graph")
+    T, E, r, k = 256, 96, 16, 2
+    rng = np.random.default_rng(123)
+    conv = datagen.f32_to_bf16_bits
+    specs = [(1024, [1024, 512]), (768, [640])]
+    hws, groups, xs = [], [], []
+    for d_in, d_outs in specs:
+        hw, dv = _group_weights(rng, d_in, d_outs, E, r, "bf16", b_scale=1.0)
+        x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
+        ys = [torch.empty((T, d), dtype=torch.bfloat16, device=DEV) for d in d_outs]
+        hws.append(hw)
+        xs.append(x)
+        groups.append(([p + (y,) for p, y in zip(dv, ys)], to_device(x, "bf16", DEV)))
+    Wg = conv(rng.standard_normal((specs[0][0], E), dtype=np.float32) / np.float32(np.sqrt(specs[0][0])))
+    Wg_d = to_device(Wg, "bf16", DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(rp.step_workspace_size(groups, E, r, k), dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.Stream(device=DEV)
+    outs = [y for g in groups for (_, _, _, y) in g[0]]
+    with torch.cuda.stream(stream):
+        rp.sgmm_step(groups, E, r, k, Wg=Wg_d, topk_idx=idx, topk_gate=gate, seg_offsets=off, pair_perm=perm,
+                     ws=ws, stream=stream)
+        stream.synchronize()
+        eager = [y.clone() for y in outs]
+        same, idx_ref, gate_ref = compare_routing(idx, gate, None, widen(xs[0], "bf16"), widen(Wg, "bf16"), k)
+        assert same.all()
+        for hw, x, (projs, _) in zip(hws, xs, groups):
+            for (W0, A, B), (_, _, _, y) in zip(hw, projs):
+                ref = oracle.sgmm(widen(x, "bf16"), widen(W0, "bf16"), widen(A, "bf16"), widen(B, "bf16"), idx_ref,
+                                  gate_ref)
+                check_y(y, ref, "bf16", "split expand, routed")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            rp.sgmm_step(groups, E, r, k, Wg=Wg_d, topk_idx=idx, topk_gate=gate, seg_offsets=off, pair_perm=perm,
+                         ws=ws, stream=stream)
+        for rep in range(3):
+            for y in outs:
+                y.fill_(float("nan"))
+            idx.fill_(-1)
+            stream.synchronize()
+            g.replay()
+            stream.synchronize()
+            for a, b in zip(eager, outs):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"graph replay {rep} differs"
+
+
 # --------------------------------------------------------------------------- whole decoder layers
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -1012,15 +1085,17 @@ def test_silu_mul(dt):
     assert np.all(np.abs(got - ref) <= tol), f"max err {np.abs(got - ref).max():.3e}"
 
 
-@pytest.mark.parametrize("dt,T,d_in,d_out", [("bf16", 9, 256, 192), ("bf16", 64, 512, 256), ("bf16", 300, 256, 384),
-                                             ("f32", 16, 128, 64)])
+@pytest.mark.parametrize("dt,T,d_in,d_out,E", [("bf16", 9, 256, 192, 8), ("bf16", 64, 512, 256, 8),
+                                               ("bf16", 300, 256, 384, 8), ("bf16", 160, 256, 384, 64),
+                                               ("f32", 16, 128, 64, 8)])
 @pytest.mark.parametrize("in_place", [False, True])
-def test_projection_residual(dt, T, d_in, d_out, in_place):
-    """y = residual + W0 x + adapters, one rounding; the residual may be y itself (updated in place)."""
-    say("residual", dt, T, d_in, d_out, in_place)
+def test_projection_residual(dt, T, d_in, d_out, E, in_place):
+    """y = residual + W0 x + adapters, one rounding; the residual may be y itself (updated in place).
+    (160 tokens over 64 adapters takes the prefill path whose expand is a launch of its own.)"""
+    say("residual", dt, T, d_in, d_out, E, in_place)
     rng = np.random.default_rng(T + d_out)
     conv = datagen.f32_to_bf16_bits if dt == "bf16" else (lambda a: a.astype(np.float32))
-    E, r, k = 8, 16, 2
+    r, k = 16, 2
     x = conv(rng.standard_normal((T, d_in), dtype=np.float32))
     W0 = conv(rng.standard_normal((d_out, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
     A = conv(rng.standard_normal((E, r, d_in), dtype=np.float32) / np.float32(np.sqrt(d_in)))
