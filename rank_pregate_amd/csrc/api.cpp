@@ -387,8 +387,9 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
   }
   const bool fuse_route = route && decode && rp::decode_fused_route_supported((int)T, (int)E);
   // prefill with the expand in a launch of its own and every group in one
-  // batch: the routing and the shrink run on a second stream beside the base
-  // GEMM, which needs neither
+  // batch: the routing, the shrink and the expand run on a second stream
+  // beside the base GEMM, which needs none of them; a last launch adds the
+  // two
   const bool overlap = overlap_shrink(gs, n_groups, T, E, r, k, dt);
   if (overlap) {
     // launched with the groups below
@@ -422,7 +423,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       ps.units = rp::prefill_shrink_units((int)T, (int)E, k);
       ps.split_expand = rp::prefill_split_expand((int)T, (int)E, (int)r, k) ? 1 : 0;
       size_t off = rp::kWorkspaceCounterBytes;
-      int shrink_blocks = 0, gemm_blocks = 0, counters = 0, expand_blocks = 0;
+      int shrink_blocks = 0, gemm_blocks = 0, counters = 0, expand_blocks = 0, combine_blocks = 0;
       for (int i = 0; i < ng; ++i) {
         const rp_group& g = gs[g0 + i];
         int d_out[RP_MAX_PROJ];
@@ -449,9 +450,12 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         off += rp::prefill_partial_bytes(plan.n_tiles, (int)T, S);
         if (ps.split_expand) {
           a.base = reinterpret_cast<float*>(w + off);
+          a.delta = a.base + (size_t)plan.n_tiles * T * rp::prefill_tile_rows((int)T);
           off += rp::prefill_base_bytes(plan.n_tiles, (int)T);
           expand_blocks += rp::prefill_expand_blocks(plan.n_tiles, (int)T);
+          combine_blocks += rp::prefill_combine_blocks(plan.n_tiles, (int)T);
           ps.expand_end[i] = expand_blocks;
+          ps.combine_end[i] = combine_blocks;
         }
         shrink_blocks += ps.units * g.n_proj;
         gemm_blocks += rp::prefill_group_blocks(plan.n_tiles, (int)T) * S;
@@ -485,10 +489,11 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
           e = rp::launch_pregate(pg, side);
         if (e == hipSuccess && route && !split_rt) e = rp::launch_segment(sg, side);
         if (e == hipSuccess) e = rp::launch_prefill_shrink(ps, side);
+        if (e == hipSuccess) e = rp::launch_prefill_expand(ps, side);
         if (e == hipSuccess && ss) e = hipEventRecord(ss->join, side);
         if (e == hipSuccess) e = rp::launch_prefill_gemm(ps, stream);
         if (e == hipSuccess && ss) e = hipStreamWaitEvent(stream, ss->join, 0);
-        if (e == hipSuccess) e = rp::launch_prefill_expand(ps, stream);
+        if (e == hipSuccess) e = rp::launch_prefill_combine(ps, stream);
       } else {
         e = rp::launch_prefill_step(ps, stream);
       }

@@ -75,6 +75,7 @@ struct SgmmArgs {
   int n_tiles;       // output-row tiles over all projections
   int S;             // K splits per output tile (decode path)
   float* base;       // prefill with the expand in its own launch: fp32 base tiles [tile][T][128 rows]
+  float* delta;      // ... and the adapter terms' sums, same layout
 };
 
 // Per-group launch constants of the decode kernel (the view its item
@@ -186,11 +187,13 @@ struct PrefillStep {
   int block_end[kMaxGroups];       // cumulative GEMM blocks (multiples of 8)
   int split_expand;                // 1: the GEMM stores fp32 base tiles and the expand runs as a launch of its own
   int expand_end[kMaxGroups];      // cumulative blocks of that expand launch
+  int combine_end[kMaxGroups];     // cumulative blocks of the launch that adds base, delta and residual
 };
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s);  // the three below, in order
 hipError_t launch_prefill_shrink(const PrefillStep& ps, hipStream_t s);  // u of every group (needs the routing)
 hipError_t launch_prefill_gemm(const PrefillStep& ps, hipStream_t s);    // W0 x (+ the expand unless split_expand)
-hipError_t launch_prefill_expand(const PrefillStep& ps, hipStream_t s);  // split_expand: base + B u (+ residual)
+hipError_t launch_prefill_expand(const PrefillStep& ps, hipStream_t s);  // split_expand: delta = B u (needs u)
+hipError_t launch_prefill_combine(const PrefillStep& ps, hipStream_t s);  // split_expand: y = base + delta (+ residual)
 constexpr size_t kWorkspaceCounterBytes = 65536;  // reserved control region at the start of every workspace
 // words [kPrefillCounterWord, + kPrefillCounterWords) of that region: split-K
 // arrival counters of prefill GEMM tiles (each returns to zero when its tile
@@ -217,8 +220,9 @@ int prefill_shrink_units(int T, int E, int k);  // shrink units per projection
 // Many small segments (top-k >= 2 over many adapters, T <= 256): the GEMM stores
 // its fp32 base tiles and a separate expand launch adds the adapters' deltas.
 bool prefill_split_expand(int T, int E, int r, int k);
-size_t prefill_base_bytes(int n_tiles, int T);  // one group's fp32 base tiles
+size_t prefill_base_bytes(int n_tiles, int T);  // one group's fp32 base and delta tiles
 int prefill_expand_blocks(int n_tiles, int T);  // expand blocks of one group (a multiple of 8)
+int prefill_combine_blocks(int n_tiles, int T); // combine blocks of one group
 hipError_t launch_f32(const SgmmArgs& a, const SgmmPlan& plan, hipStream_t s);
 int f32_tile_rows();  // output rows per fp32 workgroup
 size_t sgmm_workspace_upper_bound(Dtype dt, int n_proj, int T, int d_in, long long sum_d_out, int E, int r,

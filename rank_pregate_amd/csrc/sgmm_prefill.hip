@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * (kShrinkWaves<MTR, NCT>)) void shrink_bf16(Pre
   const int g = shrink_group_of_block(ps, blockIdx.x, &b);
   const SgmmArgs& a = ps.g[g];
   const int proj = b / ps.units, unit = b % ps.units;
-  constexpr int U = NCT == 1 ? (MTR == 1 ? 8 : MTR == 2 ? 4 : 2) : (MTR <= 2 ? 2 : 1);  // K steps per load batch
+  constexpr int U = NCT == 1 ? (MTR == 1 ? 4 : MTR == 2 ? 4 : 2) : (MTR <= 2 ? 2 : 1);  // K steps per load batch
   constexpr int W = kShrinkWaves<MTR, NCT>;
   if (NCT == 1) {
     // small segments: block e takes segment e whole, chunk by chunk (no scan
@@ -95,6 +95,8 @@ constexpr int kGRows = 64;  // output rows per block
 constexpr int kGWaves = 4;
 constexpr int kGTok = 64;   // tokens per block
 constexpr int kGMaxK = 4;   // top-k the launch serves
+constexpr int kCThreads = 256;  // combine: threads per block
+constexpr int kCRowsPerBlock = kCThreads / (kPB / 8);  // ... and the (tile, token) rows it takes
 static_assert(sizeof(PrefillStep) <= 4096, "kernel argument block too large");
 
 __device__ __forceinline__ int token_at(const SgmmArgs& a, int i) {
@@ -652,10 +654,13 @@ int prefill_shrink_nct(int T, int E, int k) { return (long long)T * k <= 16LL * 
 bool prefill_split_expand(int T, int E, int r, int k) {
   return k >= 2 && k <= kGMaxK && r <= 32 && T <= kPBigT && prefill_shrink_nct(T, E, k) == 1;
 }
-size_t prefill_base_bytes(int n_tiles, int T) { return (size_t)n_tiles * T * kPB * sizeof(float); }
+size_t prefill_base_bytes(int n_tiles, int T) { return 2 * (size_t)n_tiles * T * kPB * sizeof(float); }
 int prefill_expand_blocks(int n_tiles, int T) {
   // 64-row blocks rounded up to whole sets of 8 (one per XCD), times the token blocks
   return (2 * n_tiles + 7) / 8 * 8 * ((T + kGTok - 1) / kGTok);
+}
+int prefill_combine_blocks(int n_tiles, int T) {
+  return (int)(((long long)n_tiles * T + kCRowsPerBlock - 1) / kCRowsPerBlock);
 }
 int prefill_shrink_units(int T, int E, int k) {
   if (prefill_shrink_nct(T, E, k) == 1) return E;  // one block per segment
@@ -681,18 +686,19 @@ void launch_gemm(const PrefillStep& ps, bool fast, int exp, dim3 grid, hipStream
 // The expand as a launch of its own, for top-k >= 2 over many adapters (most
 // segments one to three tokens long): per token, not per segment.  A block
 // takes 64 output rows (lane = row) of one projection and kGTok tokens; each
-// of its waves walks its own tokens and, for token t, adds the k terms
+// of its waves walks its own tokens and, for token t, sums the k terms
 // B_e(t,j)[rows, :] . u[t*k + j, :] (u already carries the gate; slots in
-// order j = 0..k-1, each rank sum in rank order) to the fp32 base the GEMM
-// stored, then the residual, then rounds once to bf16.  There is no segment
-// walk, no staging and no barrier after the first: a pair's 64 B rows are 64
-// x r contiguous bf16 that its wave reads straight from memory, G tokens'
-// worth at a time.  The kGTok-token blocks of one 64-row block run on one XCD
-// one after another (blockIdx % 8 picks the XCD), so a B chunk that several
-// of them read comes from that XCD's L2 after the first.  Every output has
-// one owner, so the result does not depend on timing.
+// order j = 0..k-1, each rank sum in rank order) into the fp32 delta tile,
+// laid out as the GEMM's base tile.  It needs the routing and u but not the
+// GEMM, so it can run beside it; combine_bf16 then rounds base + delta
+// (+ residual) once to bf16.  There is no segment walk, no staging and no
+// barrier after the first: a pair's 64 B rows are 64 x r contiguous bf16 that
+// its wave reads straight from memory, G tokens' worth at a time.  The
+// kGTok-token blocks of one 64-row block run on one XCD one after another
+// (blockIdx % 8 picks the XCD), so a B chunk that several of them read comes
+// from that XCD's L2 after the first.  Every output has one owner, so the
+// result does not depend on timing.
 // ----------------------------------------------------------------------------
-
 template <int R, int KK>
 __global__ __launch_bounds__(64 * kGWaves) void expand_gather_bf16(PrefillStep ps) {
   constexpr int TW = kGTok / kGWaves;                       // tokens per wave
@@ -724,21 +730,16 @@ __global__ __launch_bounds__(64 * kGWaves) void expand_gather_bf16(PrefillStep p
   __syncthreads();
 
   const bf16_t* Bm = static_cast<const bf16_t*>(pd.B);
-  const float* bt = a.base + (size_t)tile * T * kPB + (rb & 1) * kGRows + rr;
-  const bf16_t* res = static_cast<const bf16_t*>(pd.residual);
-  bf16_t* y = static_cast<bf16_t*>(pd.y);
+  float* dt = a.delta + (size_t)tile * T * kPB + (rb & 1) * kGRows + rr;
   const int tw_end = min((w + 1) * TW, nt);
   for (int g0 = w * TW; g0 < tw_end; g0 += G) {
     // loads of G tokens first (a token past the wave's last repeats its last,
     // and is never stored), then their sums
-    float base_v[G], res_v[G];
     int ev[G][KK];
     uint4 bq[G][KK][R / 8];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int tl = min(g0 + i, tw_end - 1);
-      base_v[i] = bt[(size_t)(t0 + tl) * kPB];
-      res_v[i] = res ? bf16_to_f32(res[(size_t)(t0 + tl) * pd.ld_y + prow]) : 0.f;
 #pragma unroll
       for (int j = 0; j < KK; ++j) {
         ev[i][j] = -1;
@@ -757,7 +758,7 @@ __global__ __launch_bounds__(64 * kGWaves) void expand_gather_bf16(PrefillStep p
     for (int i = 0; i < G; ++i) {
       const int tl = g0 + i;
       if (tl >= tw_end) break;
-      float v = base_v[i];
+      float v = 0.f;
 #pragma unroll
       for (int j = 0; j < KK; ++j) {
         if (ev[i][j] < 0) continue;
@@ -776,10 +777,45 @@ __global__ __launch_bounds__(64 * kGWaves) void expand_gather_bf16(PrefillStep p
         }
         v += acc;
       }
-      v += res_v[i];
-      if (row < pd.d_out) y[(size_t)(t0 + tl) * pd.ld_y + row] = f32_to_bf16(v);
+      dt[(size_t)(t0 + tl) * kPB] = v;
     }
   }
+}
+
+// y[t, rows] = bf16(base + delta (+ residual)) for the tiles of the split
+// expand: a thread takes 8 rows of one (tile, token), 16-byte loads and stores.
+__global__ __launch_bounds__(kCThreads) void combine_bf16(PrefillStep ps) {
+  const int grp = group_of_block(ps.combine_end, ps.n_groups, blockIdx.x);
+  const SgmmArgs& a = ps.g[grp];
+  const int b = blockIdx.x - (grp > 0 ? ps.combine_end[grp - 1] : 0);
+  const int q = b * kCRowsPerBlock + (int)threadIdx.x / (kPB / 8);  // tile * T + token
+  if (q >= a.n_tiles * a.T) return;
+  const int tile = q / a.T, t = q % a.T;
+  const int proj = proj_of_tile(a, tile);
+  const ProjDesc pd = proj_at(a, proj);
+  const int c = ((int)threadIdx.x % (kPB / 8)) * 8;
+  const int row = (tile - pd.tile_begin) * kPB + c;
+  if (row >= pd.d_out) return;  // d_out % 8 == 0: a thread's 8 rows are all in or all out
+  const float* bp = a.base + (size_t)q * kPB + c;
+  const float* dp = a.delta + (size_t)q * kPB + c;
+  const float4 b0 = *reinterpret_cast<const float4*>(bp), b1 = *reinterpret_cast<const float4*>(bp + 4);
+  const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+  float v[8] = {b0.x + d0.x, b0.y + d0.y, b0.z + d0.z, b0.w + d0.w, b1.x + d1.x, b1.y + d1.y, b1.z + d1.z, b1.w + d1.w};
+  const size_t o = (size_t)t * pd.ld_y + row;
+  if (pd.residual) {
+    const uint4 rq = ld16(static_cast<const bf16_t*>(pd.residual) + o);
+    const uint32_t rw[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] += __uint_as_float(rw[i] << 16);
+      v[2 * i + 1] += __uint_as_float(rw[i] & 0xffff0000u);
+    }
+  }
+  uint32_t ow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ow[i] = f32x2_to_bf16x2(v[2 * i], v[2 * i + 1]);
+  *reinterpret_cast<uint4*>(static_cast<bf16_t*>(pd.y) + o) = uint4{ow[0], ow[1], ow[2], ow[3]};
 }
 
 hipError_t launch_prefill_shrink(const PrefillStep& ps, hipStream_t s) {
@@ -833,10 +869,17 @@ hipError_t launch_prefill_expand(const PrefillStep& ps, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_prefill_combine(const PrefillStep& ps, hipStream_t s) {
+  if (ps.g[0].T == 0 || !ps.split_expand) return hipSuccess;
+  combine_bf16<<<dim3(ps.combine_end[ps.n_groups - 1]), kCThreads, 0, s>>>(ps);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_step(const PrefillStep& ps, hipStream_t s) {
   hipError_t e = launch_prefill_shrink(ps, s);
   if (e == hipSuccess) e = launch_prefill_gemm(ps, s);
   if (e == hipSuccess) e = launch_prefill_expand(ps, s);
+  if (e == hipSuccess) e = launch_prefill_combine(ps, s);
   return e;
 }
 
