@@ -302,6 +302,11 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
                               rp_dtype dt) {
   size_t need = split_router_bytes(dt, T, E);  // routing, if the call computes it (before any group runs)
   if (decode_shape(dt, T)) {
+    // launches alternate between two workspace halves when no group reads
+    // another's output and there are more than two (see run_groups)
+    bool alt = n_groups > 2 * rp::kMaxGroups;
+    for (int g = 0; g < n_groups; ++g) alt = alt && !gs[g].x_from_call;
+    size_t m = 0;
     for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
       const int ng = std::min(rp::kMaxGroups, n_groups - g0);
       rp::StepGroupDesc desc[rp::kMaxGroups];
@@ -310,8 +315,10 @@ size_t groups_workspace_bytes(const rp_group* gs, int n_groups, int64_t T, int64
         for (int p = 0; p < gs[g0 + i].n_proj; ++p) d_out[i][p] = (int)gs[g0 + i].projs[p].d_out;
         desc[i] = rp::StepGroupDesc{gs[g0 + i].n_proj, d_out[i], (int)gs[g0 + i].d_in, 0};
       }
-      need = std::max(need, rp::step_workspace_upper_bound(desc, ng, (int)T, (int)E, (int)r, k));
+      m = std::max(m, rp::step_workspace_upper_bound(desc, ng, (int)T, (int)E, (int)r, k));
     }
+    m = (m + 255) & ~(size_t)255;
+    need = std::max(need, alt ? 2 * m : m);
   } else if (dt == RP_BF16) {
     // every group's u side by side (a launch pair runs several groups)
     size_t b = rp::kWorkspaceCounterBytes;
@@ -532,24 +539,57 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     }
     return RP_OK;
   }
-  for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
+  // Launches of kMaxGroups groups.  When no group reads another group's
+  // output, launches after the first (which writes the routing when it runs
+  // inside) depend on nothing but it: odd launches then go to the second
+  // stream with the second half of the workspace, so the last items of one
+  // launch run beside the first items of the next instead of leaving CUs idle.
+  const int n_batches = (n_groups + rp::kMaxGroups - 1) / rp::kMaxGroups;
+  bool alt = n_batches > 2;
+  for (int g = 0; g < n_groups; ++g) alt = alt && !gs[g].x_from_call;
+  auto batch_plan = [&](int g0, rp::StepGroupDesc* desc, int (*d_out)[RP_MAX_PROJ]) {
     const int ng = std::min(rp::kMaxGroups, n_groups - g0);
-    rp::StepGroupDesc desc[rp::kMaxGroups];
-    int d_out[rp::kMaxGroups][RP_MAX_PROJ];
     for (int i = 0; i < ng; ++i) {
       const rp_group& g = gs[g0 + i];
       for (int p = 0; p < g.n_proj; ++p) d_out[i][p] = (int)g.projs[p].d_out;
       // across launches the kernel boundary orders the data already
       desc[i] = rp::StepGroupDesc{g.n_proj, d_out[i], (int)g.d_in, i > 0 && g.x_from_call ? 1 : 0};
     }
+    return rp::plan_step(desc, ng, (int)T, (int)E, (int)r, k, n_cu, fuse_route && g0 == 0);
+  };
+  size_t half = 0;  // workspace bytes of one launch (the largest)
+  for (int g0 = 0; g0 < n_groups; g0 += rp::kMaxGroups) {
+    rp::StepGroupDesc desc[rp::kMaxGroups];
+    int d_out[rp::kMaxGroups][RP_MAX_PROJ];
+    half = std::max(half, batch_plan(g0, desc, d_out).bytes);
+  }
+  half = (half + 255) & ~(size_t)255;
+  const size_t need_all = alt ? 2 * half : half;
+  if (ws_bytes < need_all) return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need_all);
+  if (dry) {
+    *dry_need = std::max(*dry_need, need_all);
+    return RP_OK;
+  }
+  std::unique_lock<std::mutex> side_lock(side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
+  if (alt) {
+    side_lock.lock();
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return hip_fail(fn, hipGetLastError());
+    ss = side_stream(cs == hipStreamCaptureStatusNone);
+    if (!ss) alt = false;  // no second stream: every launch in order on the caller's
+  }
+  char* const w_main = w;
+  for (int g0 = 0, b = 0; g0 < n_groups; g0 += rp::kMaxGroups, ++b) {
+    const int ng = std::min(rp::kMaxGroups, n_groups - g0);
+    rp::StepGroupDesc desc[rp::kMaxGroups];
+    int d_out[rp::kMaxGroups][RP_MAX_PROJ];
     const bool fused_here = fuse_route && g0 == 0;
-    const rp::StepPlan sp = rp::plan_step(desc, ng, (int)T, (int)E, (int)r, k, n_cu, fused_here);
-    if (ws_bytes < sp.bytes)
-      return fail(RP_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, sp.bytes);
-    if (dry) {
-      *dry_need = std::max(*dry_need, sp.bytes);
-      continue;
-    }
+    const rp::StepPlan sp = batch_plan(g0, desc, d_out);
+    const bool on_side = alt && (b & 1);
+    w = on_side ? w_main + half : w_main;
+    int* const ctl = reinterpret_cast<int*>(w_main + (on_side ? rp::kCounterBlockBytes : 0));
+    const hipStream_t bs = on_side ? ss->s : stream;
     rp::StepArgs st{};
     for (int i = 0; i < ng; ++i) {
       const rp_group& g = gs[g0 + i];
@@ -560,7 +600,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       a.topk_gate = rt.gate;
       a.seg_offsets = rt.off;
       a.pair_perm = rt.perm;
-      a.counters = reinterpret_cast<int*>(w);
+      a.counters = ctl;
       a.u = reinterpret_cast<float*>(w + gp.off_u);
       a.partial = reinterpret_cast<float*>(w + gp.off_partial);
       a.n_tiles = gp.n_tiles;
@@ -588,7 +628,7 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
         for (int j = 0; j < i; ++j) q.wait_target += sp.gp[j].n_tiles;
       q.partial_a = reinterpret_cast<float*>(w + gp.off_partial_a);
       q.act = g.act;
-      q.pair_cnt = reinterpret_cast<int*>(w) + rp::kPrefillCounterWord + i * rp::kActPairWords;
+      q.pair_cnt = ctl + rp::kPrefillCounterWord + i * rp::kActPairWords;
       if (g.act == RP_ACT_SILU_MUL && (g.projs[0].d_out + gp.tile_rows - 1) / gp.tile_rows > rp::kActPairWords)
         return fail(RP_ERR_UNSUPPORTED, "%s: group %d: RP_ACT_SILU_MUL supports at most %d output tiles", fn,
                     g0 + i, rp::kActPairWords);
@@ -598,12 +638,23 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
     st.n_route = sp.n_route;
     st.n_pre = sp.n_pre;
     st.fused = fused_here;
+    st.claim_all = alt ? 1 : 0;
     st.dense = sp.gp[0].dense;
     st.t_pad = sp.gp[0].t_pad;
     st.route_tagged = reinterpret_cast<unsigned int*>(w + sp.off_route);
     st.pg = pg;
     st.sg = sg;
-    hipError_t e = rp::launch_step(st, sp, stream);
+    hipError_t e = rp::launch_step(st, sp, bs);
+    if (e == hipSuccess && alt && b == 0) {
+      // the second stream starts after the first launch
+      e = hipEventRecord(ss->fork, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  if (alt) {
+    hipError_t e = hipEventRecord(ss->join, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return RP_OK;
@@ -879,17 +930,28 @@ rp_status rp_workspace_status(void* ws, size_t ws_bytes, int32_t clear, int32_t*
                 rp::kWorkspaceCounterBytes);
   // the two words sit in one 256-byte span of the control region
   static_assert(kSegErrWord > kWaitOverflowWord && kSegErrWord - kWaitOverflowWord < 64, "status span");
-  int32_t span[64];
-  int32_t* src = static_cast<int32_t*>(ws) + kWaitOverflowWord;
-  hipError_t e = hipMemcpyAsync(span, src, sizeof span, hipMemcpyDeviceToHost, stream);
+  // both control blocks (launches on the second stream flag theirs)
+  constexpr int kBlockWords = (int)(rp::kCounterBlockBytes / 4);
+  int32_t span[2][64];
+  int32_t wo = 0, bad = 0;
+  hipError_t e = hipSuccess;
+  for (int blk = 0; blk < 2 && e == hipSuccess; ++blk)
+    e = hipMemcpyAsync(span[blk], static_cast<int32_t*>(ws) + blk * kBlockWords + kWaitOverflowWord, sizeof span[blk],
+                       hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail("rp_workspace_status", e);
-  const int32_t wo = span[0], bad = span[kSegErrWord - kWaitOverflowWord];
+  for (int blk = 0; blk < 2; ++blk) {
+    wo |= span[blk][0];
+    bad += span[blk][kSegErrWord - kWaitOverflowWord];
+  }
   if (wait_overflow) *wait_overflow = wo;
   if (bad_indices) *bad_indices = bad;
   if (clear && (wo != 0 || bad != 0)) {
-    e = hipMemsetAsync(src, 0, sizeof(int32_t), stream);
-    if (e == hipSuccess) e = hipMemsetAsync(static_cast<int32_t*>(ws) + kSegErrWord, 0, sizeof(int32_t), stream);
+    for (int blk = 0; blk < 2 && e == hipSuccess; ++blk) {
+      int32_t* b0 = static_cast<int32_t*>(ws) + blk * kBlockWords;
+      e = hipMemsetAsync(b0 + kWaitOverflowWord, 0, sizeof(int32_t), stream);
+      if (e == hipSuccess) e = hipMemsetAsync(b0 + kSegErrWord, 0, sizeof(int32_t), stream);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail("rp_workspace_status clear", e);
   }

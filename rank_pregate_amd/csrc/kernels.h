@@ -124,6 +124,8 @@ struct StepArgs {
   GroupPlan gp[kMaxGroups];
   int n_groups, n_items;  // groups and items of the launch (routing items included)
   int n_route, n_pre, fused, dense, t_pad;
+  int claim_all;  // every item, a workgroup's first too, is claimed from the launch's queue (launches that may
+                  // run beside another: a waited-on item then always belongs to a running workgroup)
   unsigned int* route_tagged;
   PregateArgs pg;
   SegmentArgs sg;
@@ -194,8 +196,12 @@ hipError_t launch_prefill_shrink(const PrefillStep& ps, hipStream_t s);  // u of
 hipError_t launch_prefill_gemm(const PrefillStep& ps, hipStream_t s);    // W0 x (+ the expand unless split_expand)
 hipError_t launch_prefill_expand(const PrefillStep& ps, hipStream_t s);  // split_expand: delta = B u (needs u)
 hipError_t launch_prefill_combine(const PrefillStep& ps, hipStream_t s);  // split_expand: y = base + delta (+ residual)
-constexpr size_t kWorkspaceCounterBytes = 65536;  // reserved control region at the start of every workspace
-// words [kPrefillCounterWord, + kPrefillCounterWords) of that region: split-K
+// Reserved control region at the start of every workspace: two control blocks
+// of kCounterBlockBytes; the second serves decode launches queued on the
+// library's second stream.  Word offsets below are within a block.
+constexpr size_t kCounterBlockBytes = 65536;
+constexpr size_t kWorkspaceCounterBytes = 2 * kCounterBlockBytes;
+// words [kPrefillCounterWord, + kPrefillCounterWords) of a block: split-K
 // arrival counters of prefill GEMM tiles (each returns to zero when its tile
 // completes); the decode control sets sit below
 constexpr int kPrefillCounterWord = 9216;
@@ -207,7 +213,7 @@ constexpr int kRouteCounterWords = 1024 - kRouteCounterWord;
 // counters of groups with an activation take kActPairWords words per group
 // there (each returns to zero when its pair completes)
 constexpr int kActPairWords = 896;
-constexpr int kPrefillCounterWords = (int)(kWorkspaceCounterBytes / 4) - kPrefillCounterWord;
+constexpr int kPrefillCounterWords = (int)(kCounterBlockBytes / 4) - kPrefillCounterWord;
 int prefill_splits(int d_in, int n_tiles, int T, int n_cu);          // K splits of one group's GEMM tiles
 size_t prefill_partial_bytes(int n_tiles, int T, int S);            // its split-K partial tiles
 int prefill_max_splits(int d_in);                                     // bound on prefill_splits for any device

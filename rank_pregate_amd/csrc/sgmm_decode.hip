@@ -1023,12 +1023,28 @@ __global__ __launch_bounds__(kThreadsOf<MT>, kBlocksPerCuOf<MT>) void decode_ker
   // later one comes from a launch-wide counter claimed at the start of the
   // item before (its latency overlaps that item).  Claims are in increasing
   // order, so every item an item waits for has been claimed by a running
-  // workgroup.
+  // workgroup -- with static first items, as long as every workgroup of the
+  // launch is running, which a launch sharing the GPU with another cannot
+  // count on (workgroups go to the XCDs by index, and one XCD may be full);
+  // such launches claim every item (claim_all).
   __shared__ int s_next[2];
   int item = blockIdx.x;
+  if (st.claim_all) {
+    // the workgroup may start after later-numbered ones (another launch holds
+    // CUs): it reads the epoch and arrives now, then claims its first item
+    if (tid == 0) {
+      s_ep = ep_in;
+      arrive(ctl, ep_in);
+      s_next[1] = atomicAdd(ctl_set(ctl, ep_in) + kSetQueue, 1);
+    }
+    __syncthreads();
+    item = s_next[1];
+    first = false;
+  }
   for (int iter = 0; item < st.n_items; ++iter) {
     int nxt = st.n_items;  // a launch with no more items than workgroups claims nothing
-    if (tid == 0 && st.n_items > (int)gridDim.x) nxt = (int)gridDim.x + atomicAdd(ctl_set(ctl, ep_in) + kSetQueue, 1);
+    if (tid == 0 && (st.claim_all || st.n_items > (int)gridDim.x))
+      nxt = (st.claim_all ? 0 : (int)gridDim.x) + atomicAdd(ctl_set(ctl, ep_in) + kSetQueue, 1);
     if (FUSED && item < st.n_pre) {
       if (first) {
         if (tid == 0) {

@@ -48,7 +48,7 @@ int decode_tiles(int n_proj, const int* d_out, int T) {
 // One decode group: tiling, splits, items, and its workspace starting at `off`.
 // `launch_tiles` counts the backbone tiles of every group sharing the launch.
 SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
-                           int launch_tiles, size_t off) {
+                           int launch_tiles, size_t off, int s_mult = 1) {
   SgmmPlan p{};
   p.path = 1;
   p.tile_rows = decode_tile_rows(T);
@@ -77,7 +77,7 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   // and a launch with fewer tiles than CUs splits until every CU has an item
   int S = (d_in + kSplitCols / 2) / kSplitCols;
   S = std::max(S, (n_cu + launch_tiles - 1) / std::max(1, launch_tiles));
-  p.S = std::max(1, std::min(S, s_max));
+  p.S = std::max(1, std::min(S * s_mult, s_max));
   p.n_shrink = n_shrink;
   p.n_items = n_shrink + p.n_tiles * p.S;
   p.off_u = off;
@@ -118,9 +118,19 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
   int items = sp.n_pre;
   int launch_tiles = 0;
   for (int g = 0; g < n_groups; ++g) launch_tiles += decode_tiles(groups[g].n_proj, groups[g].d_out, T);
+  // A launch with more items than its workgroups hands them out in item
+  // order, so it ends on the last group's items: that group's K splits are
+  // doubled, so the workgroups that run out of work first wait for items of
+  // half the length.
+  int n_all = sp.n_pre;
+  for (int g = 0; g < n_groups; ++g)
+    n_all += plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
+                               off).n_items;
+  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
   for (int g = 0; g < n_groups; ++g) {
+    const int s_mult = (n_groups > 1 && g == n_groups - 1 && n_all > cap) ? 2 : 1;
     sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
-                                 off);
+                                 off, s_mult);
     off = sp.gp[g].bytes;
   }
   // Item order: routing; the shrink items of every group whose input comes
@@ -145,7 +155,6 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
   if (fused_route) off = align256(off + (size_t)T * k * 16);
   sp.bytes = off;
   sp.n_items = items;
-  const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
   sp.grid = std::min(sp.n_items, cap);
   return sp;
 }

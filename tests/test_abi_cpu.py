@@ -288,7 +288,7 @@ def test_prefill_workspace_covers_split_k(T, d_in, d_outs):
     g = rp.RpGroup(ctypes.cast(proj, ctypes.POINTER(rp.RpProj)), n, 0, FAKE, d_in, d_in)
     single = L.rp_sgmm_workspace_size(n, T, d_in, sum(d_outs), E, r, k, rp.RP_BF16)
     step = L.rp_sgmm_step_workspace_size((rp.RpGroup * 1)(g), 1, T, E, r, k, rp.RP_BF16)
-    u_only = 65536 + ((n * T * k * r * 4 + 255) // 256) * 256
+    u_only = 131072 + ((n * T * k * r * 4 + 255) // 256) * 256  # two 64 KiB control blocks, then u
     tiles = sum((d + 127) // 128 for d in d_outs)
     partials = ((tiles + 7) // 8 * 8) * ((T + 127) // 128) * 2 * 128 * 128 * 4  # at least two splits
     assert single >= u_only + partials
