@@ -451,8 +451,13 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
       const int p = tid + j * NTH;
       if (FUSED) {
         // written by this launch's router tiles, validated by tag
+        // first check outside the retry loop: waiting for this load then
+        // leaves the weight loads issued after it in flight (a loop header
+        // would wait for every load)
         int spins = 0;
-        while (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tg && rraw[j].w == tg), &spins)) route_load(j);
+        if (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tg && rraw[j].w == tg), &spins)) do
+            route_load(j);
+          while (retry_tagged(ctl, p >= n_pairs || (rraw[j].y == tg && rraw[j].w == tg), &spins));
       }
       if (p < n_pairs) {
         s_sel[p] = (int)rraw[j].x;
@@ -503,9 +508,10 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
     for (int i = 0; i < kUP; ++i) {
       const int q = tid + i * NTH;
       const uint32_t off = u_piece(q);
-      int spins = 0;
-      while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins))
-        uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, kSc1);
+      int spins = 0;  // first check outside the retry loop (as in stage_route)
+      if (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins)) do
+          uraw[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, kSc1);
+        while (retry_tagged(ctl, off == kOob || (uraw[i].y == tg && uraw[i].w == tg), &spins));
       if (off != kOob) {
         const int p = q / half_r, c = 2 * (q % half_r);
         const int t = p / a.k, j = p - t * a.k, e = s_sel[p];
