@@ -217,7 +217,8 @@ def main():
     if args.ablation == "auto":
         variants = [] if wl.assignment != "router" else (
             ["unfused"] + (["per_layer_routing"] if wl.layers > 1 else []) + ["token_fused", "token_merge_unmerge"]
-            + (["chained_layers"] if [g.name for g in wl.groups] == ["qkv", "o", "gate_up", "down"] else []))
+            + (["chained_layers", "chained_layers_dependent"]
+               if [g.name for g in wl.groups] == ["qkv", "o", "gate_up", "down"] else []))
     elif args.ablation == "none":
         variants = []
     else:
@@ -359,7 +360,7 @@ def main():
             # copy 0's layer-0 backbone weights before any merge, for the unmerge drift
             drift_ref = {key: v.W0.clone() for key, v in dw.weights[0].items() if key[0] == dw.layers[0]}
         for variant in variants:
-            if variant == "chained_layers":
+            if variant.startswith("chained_layers"):
                 dw.prepare_chain()  # uploads and allocates: not inside a graph
             if args.no_graph:
                 for c in range(copies):

@@ -441,8 +441,8 @@ def step_workspace_size(groups: Sequence[Tuple], E: int, r: int, k: int) -> int:
     for i, g in enumerate(groups):
         arr, _, _ = _proj_array(g[0], g[1])
         keep.append(arr)
-        garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(g[0]), 0, _ptr(g[1]), g[1].shape[1],
-                          _rows(g[1], "x"), int(g[3]) if len(g) > 3 else RP_ACT_NONE, 0)
+        garr[i] = RpGroup(ctypes.cast(arr, ctypes.POINTER(RpProj)), len(g[0]), int(g[2]) if len(g) > 2 else 0,
+                          _ptr(g[1]), g[1].shape[1], _rows(g[1], "x"), int(g[3]) if len(g) > 3 else RP_ACT_NONE, 0)
     return lib().rp_sgmm_step_workspace_size(garr, len(groups), x0.shape[0], E, r, k, _dtype_code(x0))
 
 

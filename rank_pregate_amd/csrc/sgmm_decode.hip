@@ -154,7 +154,10 @@ __device__ __forceinline__ int* ctl_set(int* ctl, int ep) { return ctl + kCtlSet
 // group g waits until every output tile of groups 0..g-1 is written (tiles are
 // counted per group and tile % 8, so no single counter takes every workgroup;
 // lane 8*h + c reads group h's class c); wave 0 polls, the workgroup then
-// proceeds.
+// proceeds.  No cache-wide fence follows: those tiles were stored
+// device-coherent before they were counted, and the group reads its input with
+// device-coherent loads (an agent-scope acquire would wait for the weight
+// loads already in flight and invalidate the XCD's L2).
 __device__ __forceinline__ void wait_prev_group(int* ctl, int ep, const DecodeArgs& d) {
   static_assert(8 * kMaxGroups <= 64, "one counter per lane");
   if ((threadIdx.x >> 6) == 0) {
@@ -173,7 +176,6 @@ __device__ __forceinline__ void wait_prev_group(int* ctl, int ep, const DecodeAr
     }
   }
   __syncthreads();
-  if (d.x_acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Thread 0, once per workgroup, after reading the epoch: count in per
@@ -230,6 +232,7 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
   const bf16_t* Ae = static_cast<const bf16_t*>(pd.A) + (size_t)e * a.r * a.d_in;
   const int lr = lane & 15, kg = lane >> 4;
   const bf16_t* xp = x + (size_t)(ld_route<COH>(&a.pair_perm[min(slot0 + lr, slot_end - 1)]) / a.k) * a.ld_x;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)((size_t)a.T * a.ld_x * sizeof(bf16_t)));
   const bf16_t* ap[MTR];
   bool aok[MTR];
 #pragma unroll
@@ -253,7 +256,10 @@ __device__ __forceinline__ void shrink_item(const SgmmArgs& a, const DecodeArgs&
       const int kc = min(k, a.d_in - 8);
 #pragma unroll
       for (int mt = 0; mt < MTR; ++mt) av[u][mt] = sel4(ok && aok[mt], ld16(ap[mt] + kc));
-      bv[u] = sel4(ok, ld16(xp + kc));
+      // an input written earlier in this launch is read device-coherent
+      bv[u] = sel4(ok, d.x_acquire ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rx, (uint32_t)((xp + kc - x) * sizeof(bf16_t)), 0, kSc1))
+                                   : ld16(xp + kc));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -346,6 +352,9 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const bf16_t* xq[MP];
 #pragma unroll
   for (int p = 0; p < MP; ++p) xq[p] = x + (size_t)min(((wave + WV * p) >> 2) * 16 + lr, a.T - 1) * a.ld_x;
+  // an input written earlier in this launch is read device-coherent
+  const bool x_coh = d.x_acquire != 0;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)((size_t)a.T * a.ld_x * sizeof(bf16_t)));
 
   f32x4_t acc[MT];
 #pragma unroll
@@ -385,8 +394,15 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   };
   auto issue_x = [&](int slot, int v) {
     const int col = min((cbeg + max(v - pad, 0)) * kKC + xcol, a.d_in - 8);
+    if (x_coh) {
 #pragma unroll
-    for (int p = 0; p < MP; ++p) xr[slot][p] = ld16(xq[p] + col);
+      for (int p = 0; p < MP; ++p)
+        xr[slot][p] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((xq[p] + col - x) * sizeof(bf16_t)), 0, kSc1));
+    } else {
+#pragma unroll
+      for (int p = 0; p < MP; ++p) xr[slot][p] = ld16(xq[p] + col);
+    }
   };
   auto issue = [&](int slot, int v) {  // activations first, then weights
     issue_x(slot, v);
@@ -886,7 +902,7 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
   const int tile_row0 = row0 - wave * 16;
   bf16_t* y = static_cast<bf16_t*>(pd.y);
   auto put16 = [&](bf16_t* p, uint4 v) {
-    if (d.act) {
+    if (d.act || d.release) {
       unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
       __hip_atomic_store(q, (unsigned long long)v.x | ((unsigned long long)v.y << 32), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -963,14 +979,15 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
         for (int i = 0; i < 4; ++i)
           o[i] = f32x2_to_bf16x2(silu_mul_f32(__uint_as_float(gw[i] << 16), __uint_as_float(uw[i] << 16)),
                                  silu_mul_f32(__uint_as_float(gw[i] & 0xffff0000u), __uint_as_float(uw[i] & 0xffff0000u)));
-        *reinterpret_cast<uint4*>(gy + (size_t)t * pg.ld_y + tile_row0 + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+        put16(gy + (size_t)t * pg.ld_y + tile_row0 + c8, make_uint4(o[0], o[1], o[2], o[3]));
       }
     }
     n_done = 2;  // both tiles of the pair are final now
   }
   if (d.count_done) {
-    // a later group of this launch waits for this tile (and, with release, reads it)
-    if (d.release) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // a later group of this launch waits for this tile (and, with release, reads
+    // it: then the tile was stored device-coherent, and waiting for the stores
+    // puts it at the coherence point before it is counted -- no L2 write-back)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) atomicAdd(&set[kSetGroupDone + 256 * d.group + 32 * (tile & 7)], n_done);

@@ -1,6 +1,9 @@
 // Launch planning for the SGMM entry points: which kernel family serves a
 // call, output-row tiling, K splits, grid and workspace layout.
 #include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
 
 #include "kernels.h"
 
@@ -14,6 +17,9 @@ constexpr int kMaxSplits = 8;            // decode split-K
 constexpr int kMaxKParts = 8;            // decode pair-chunk shrink K parts
 constexpr int kShrinkPartBytes = 16384;  // target A bytes per decode pair-chunk shrink unit
 constexpr int kSplitCols = 4096;         // decode backbone: about this many K columns per item
+constexpr int kMaxSplitsWide = 4;        // decode split-K of 128-row tiles (T > 32): their partial tiles are
+                                         // summed two splits per round trip, so more splits cost more than
+                                         // their shorter streams save
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -48,7 +54,7 @@ int decode_tiles(int n_proj, const int* d_out, int T) {
 // One decode group: tiling, splits, items, and its workspace starting at `off`.
 // `launch_tiles` counts the backbone tiles of every group sharing the launch.
 SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E, int r, int k, int n_cu,
-                           int launch_tiles, size_t off, int s_mult = 1) {
+                           int launch_tiles, size_t off, int s_mult = 1, int s_fill = 0) {
   SgmmPlan p{};
   p.path = 1;
   p.tile_rows = decode_tile_rows(T);
@@ -56,7 +62,7 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   p.t_pad = 16 * decode_mt(T);
   p.dense = E <= kDenseMaxE;
   const int nchunks = (d_in + decode_chunk_k(T) - 1) / decode_chunk_k(T);
-  const int s_max = std::max(1, std::min(kMaxSplits, nchunks / 2));
+  const int s_max = std::max(1, std::min(decode_tile_rows(T) >= 128 ? kMaxSplitsWide : kMaxSplits, nchunks / 2));
   p.KP = 1;
   p.SA = 1;
   int n_shrink = 0;
@@ -77,6 +83,7 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   // and a launch with fewer tiles than CUs splits until every CU has an item
   int S = (d_in + kSplitCols / 2) / kSplitCols;
   S = std::max(S, (n_cu + launch_tiles - 1) / std::max(1, launch_tiles));
+  if (s_fill > 0) S = s_fill;
   p.S = std::max(1, std::min(S * s_mult, s_max));
   p.n_shrink = n_shrink;
   p.n_items = n_shrink + p.n_tiles * p.S;
@@ -88,6 +95,49 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
   off = align256(off + decode_partial_bytes(p.n_atiles, p.SA, T));
   p.bytes = off;
   return p;
+}
+// Estimated duration of one phase of a launch of 128-row tiles, in chunk times
+// (one CU streaming one 128 x 128 weight chunk alone): the phase's items handed
+// out in claim order to `cap` workgroups, each to the first one free (the
+// launch's counter does the same), stretched when more workgroups stream at
+// once than the chip's bandwidth feeds at one CU's rate.  Constants from
+// single-group launches at 64 tokens, in chunk times: starting an item costs
+// about 2, each partial tile its last split reads 2.5, the adapter expand 2,
+// and the chip streams about 156 chunks while one CU streams one.
+constexpr double kItemStart = 2.0, kPerPartial = 2.5, kExpand = 2.0, kChipChunks = 156.0;
+
+struct PhaseGroup {
+  int tiles, nch, S, SA, n_atiles, n_pair_units, KP;
+  bool dense, expand;
+};
+
+double phase_estimate(const PhaseGroup* pg, int n, int cap) {
+  std::vector<double> items;
+  double total = 0;
+  auto splits = [&](int count, int nch, int S, double last_extra) {
+    for (int t = 0; t < count; ++t)
+      for (int s = 0; s < S; ++s) {
+        const int nc = (int)((long long)nch * (s + 1) / S - (long long)nch * s / S);
+        items.push_back(kItemStart + nc + (s == S - 1 ? kPerPartial * (S - 1) + last_extra : 0.0));
+        total += nc;
+      }
+  };
+  for (int g = 0; g < n; ++g) {  // shrink items are claimed first
+    if (pg[g].dense) splits(pg[g].n_atiles, pg[g].nch, pg[g].SA, 0.0);
+    for (int u = 0; u < pg[g].n_pair_units; ++u) items.push_back(kItemStart + 0.25 * pg[g].nch / pg[g].KP);
+  }
+  for (int g = 0; g < n; ++g) splits(pg[g].tiles, pg[g].nch, pg[g].S, pg[g].expand ? kExpand : 0.0);
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < cap; ++i) free_at.push(0.0);
+  double end = 0;
+  for (double d : items) {
+    const double t = free_at.top() + d;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  const double busy = (double)std::min<size_t>(items.size(), (size_t)cap);
+  return std::max(end * std::max(1.0, busy / kChipChunks), total / kChipChunks);
 }
 }  // namespace
 
@@ -127,10 +177,49 @@ StepPlan plan_step(const StepGroupDesc* groups, int n_groups, int T, int E, int 
     n_all += plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
                                off).n_items;
   const int cap = std::max(1, decode_resident_per_cu(T, fused_route) * n_cu);
+  // 128-row tiles (T > 32, one workgroup per CU): a phase -- a group that
+  // reads an earlier group's output and the independent groups after it --
+  // runs by itself.  When its tiles leave CUs free, its K splits are the
+  // candidate with the shortest estimated phase (a few items past the grid
+  // would add a round; many splits add partial tiles to sum): group g splits
+  // max(its long-K count, m) ways for m = 1 .. the cap, the same m for the
+  // whole phase, the fewest splits on a tie.
+  int s_fill[kMaxGroups] = {0};
+  if (decode_tile_rows(T) >= 128) {
+    for (int g0 = 0; g0 < n_groups;) {
+      int g1 = g0 + 1;
+      while (g1 < n_groups && !groups[g1].x_acquire) ++g1;
+      int tiles = 0;
+      PhaseGroup pg[kMaxGroups];
+      int s_cols[kMaxGroups], s_top[kMaxGroups], m_max = 1;
+      for (int g = g0; g < g1; ++g) {
+        const SgmmPlan q = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu,
+                                             launch_tiles, off, 1, 1);
+        const int nch = (groups[g].d_in + decode_chunk_k(T) - 1) / decode_chunk_k(T);
+        tiles += q.n_tiles;
+        s_top[g] = std::max(1, std::min(kMaxSplitsWide, nch / 2));
+        s_cols[g] = std::min(s_top[g], std::max(1, (groups[g].d_in + kSplitCols / 2) / kSplitCols));
+        m_max = std::max(m_max, s_top[g]);
+        pg[g - g0] = PhaseGroup{q.n_tiles, nch, 1, q.SA, q.dense ? q.n_atiles : 0,
+                                q.dense ? 0 : q.n_shrink, q.KP, q.dense && k > 0, k > 0};
+      }
+      if (tiles < n_cu) {
+        double best = 0;
+        int best_m = 0;
+        for (int m = 1; m <= m_max; ++m) {
+          for (int g = g0; g < g1; ++g) pg[g - g0].S = std::min(s_top[g], std::max(s_cols[g], m));
+          const double est = phase_estimate(pg, g1 - g0, cap);
+          if (best_m == 0 || est < best) best = est, best_m = m;
+        }
+        for (int g = g0; g < g1; ++g) s_fill[g] = std::min(s_top[g], std::max(s_cols[g], best_m));
+      }
+      g0 = g1;
+    }
+  }
   for (int g = 0; g < n_groups; ++g) {
-    const int s_mult = (n_groups > 1 && g == n_groups - 1 && n_all > cap) ? 2 : 1;
+    const int s_mult = (s_fill[g] == 0 && n_groups > 1 && g == n_groups - 1 && n_all > cap) ? 2 : 1;
     sp.gp[g] = plan_decode_group(groups[g].n_proj, groups[g].d_out, T, groups[g].d_in, E, r, k, n_cu, launch_tiles,
-                                 off, s_mult);
+                                 off, s_mult, s_fill[g]);
     off = sp.gp[g].bytes;
   }
   // Item order: routing; the shrink items of every group whose input comes

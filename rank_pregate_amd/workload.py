@@ -263,7 +263,7 @@ class DeviceWorkload:
         self.chain_gamma = {(l, w): up(datagen.norm_weight(wl, l, w)) for l in self.layers
                             for w in ("gamma1", "gamma2")}
         attn, mlp = self.chain_groups(0)[0]
-        need = max(step_workspace_size(attn, wl.E, wl.r, wl.k), step_workspace_size(mlp, wl.E, wl.r, wl.k))
+        need = max(step_workspace_size(part, wl.E, wl.r, wl.k) for part in [attn, mlp] + [[g] for g in attn + mlp])
         if need > self.ws.numel():
             self.ws = track_workspace(torch.zeros(need, dtype=torch.uint8, device=dev))
 
@@ -287,24 +287,33 @@ class DeviceWorkload:
             out.append(([qkv, o], [gate_up, down]))
         return out
 
-    def run_chained(self, copy: int = 0, stream=None):
+    def run_chained(self, copy: int = 0, stream=None, dependent: bool = False):
         """Every layer as a whole decoder layer (RMSNorm, q|k|v, o + residual, RMSNorm, gate|up with the
         fused silu(g)*u, down + residual), inputs chained from the outputs before them; the routing runs
-        inside the first launch, on layer 0's normalised input.  The residual stream ends in chain_h."""
+        inside the first launch, on layer 0's normalised input.  The residual stream ends in chain_h.
+
+        Each projection group is a launch of its own; with `dependent` a group that reads the group before
+        it shares that group's launch instead (it waits there for every tile of it).  Both give the same
+        bits."""
         self.prepare_chain()
         wl = self.wl
+        first = True
+
+        def launch(groups):
+            nonlocal first
+            route = dict(Wg=self.Wg) if first else {}
+            first = False
+            rp_sgmm_step(groups, wl.E, wl.r, wl.k, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
+                         seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream, **route)
+
         for i, (l, (attn, mlp)) in enumerate(zip(self.layers, self.chain_groups(copy))):
             rp_rmsnorm(self.chain_h0 if i == 0 else self.chain_h, self.chain_gamma[(l, "gamma1")], CHAIN_EPS,
                        out=self.chain_n, stream=stream)
-            if i == 0:
-                rp_sgmm_step(attn, wl.E, wl.r, wl.k, Wg=self.Wg, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
-                             seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
-            else:
-                rp_sgmm_step(attn, wl.E, wl.r, wl.k, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
-                             seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+            for part in ([attn] if dependent else [[g] for g in attn]):
+                launch(part)
             rp_rmsnorm(self.chain_h, self.chain_gamma[(l, "gamma2")], CHAIN_EPS, out=self.chain_n, stream=stream)
-            rp_sgmm_step(mlp, wl.E, wl.r, wl.k, topk_idx=self.topk_idx, topk_gate=self.topk_gate,
-                         seg_offsets=self.seg_offsets, pair_perm=self.pair_perm, ws=self.ws, stream=stream)
+            for part in ([mlp] if dependent else [[g] for g in mlp]):
+                launch(part)
 
     def run_variant(self, variant: str, copy: int = 0, stream=None):
         if variant == "fused":
@@ -319,6 +328,8 @@ class DeviceWorkload:
             self.run_token_merged(copy, stream=stream)
         elif variant == "chained_layers":
             self.run_chained(copy, stream=stream)
+        elif variant == "chained_layers_dependent":
+            self.run_chained(copy, stream=stream, dependent=True)
         else:
             raise ValueError(variant)
 

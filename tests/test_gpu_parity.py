@@ -1195,3 +1195,9 @@ def test_decoder_layer_chain(index, dt, T, d, ff, E, r, k, layers):
         h = oracle.decoder_layer(h, ws[l], idx_ref, gate_ref, 1e-5, rnd=rnd)
     err = check_y(dw.chain_h, h, dt, f"chain after {layers} layers")
     say(f"chain: max error {err:.2e} of max|h|")
+    # a dependent group in the launch of the group it reads: the same splits, so the same bits
+    separate = dw.chain_h.clone()
+    dw.chain_h.zero_()
+    dw.run_chained(dependent=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.chain_h, separate), "dependent launches differ from one launch per group"
