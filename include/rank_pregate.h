@@ -225,10 +225,11 @@ typedef struct {
 } rp_group;
 
 /* A decode step (AdaFuse §2.B decoding steps 1-3 over every adapted layer).
- * A group marked x_from_call reads its x only after every output of the
- * groups before it is written, so its x may be any earlier group's y.  A
- * group without the mark does not wait and may run concurrently with earlier
- * groups: its x must not be written by this call.  No y may overlap another
+ * A group marked x_from_call reads its x (and its projections' residuals)
+ * only after every output of the groups before it is written, so its x and
+ * residuals may be any earlier group's y.  A group without the mark does not
+ * wait and may run concurrently with earlier groups: neither its x nor its
+ * residuals may be written by this call.  No y may overlap another
  * y or any group's x.  All groups use one routing:
  *
  *   Wg_or_null non-null: the routing is computed first from groups[0].x, as

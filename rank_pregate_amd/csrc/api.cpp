@@ -629,9 +629,11 @@ rp_status run_groups(const char* fn, const rp_group* gs, int n_groups, int64_t T
       q.partial_a = reinterpret_cast<float*>(w + gp.off_partial_a);
       q.act = g.act;
       q.pair_cnt = ctl + rp::kPrefillCounterWord + i * rp::kActPairWords;
-      // such a group reads x through a buffer resource: a 32-bit byte range
-      if (desc[i].x_acquire && (uint64_t)T * (uint64_t)g.ld_x * 2u > 0xFFFFFFFFull)
-        return fail(RP_ERR_UNSUPPORTED, "%s: group %d reads an earlier group's output of more than 4 GiB (T * ld_x)",
+      // such a group reads x and its residuals through buffer resources: 32-bit byte ranges
+      bool wide = (uint64_t)T * (uint64_t)g.ld_x * 2u > 0xFFFFFFFFull;
+      for (int p = 0; p < g.n_proj; ++p) wide = wide || (uint64_t)T * (uint64_t)g.projs[p].ld_y * 2u > 0xFFFFFFFFull;
+      if (desc[i].x_acquire && wide)
+        return fail(RP_ERR_UNSUPPORTED, "%s: group %d reads an earlier group's output of more than 4 GiB (T * ld)",
                     fn, g0 + i);
       if (g.act == RP_ACT_SILU_MUL && (g.projs[0].d_out + gp.tile_rows - 1) / gp.tile_rows > rp::kActPairWords)
         return fail(RP_ERR_UNSUPPORTED, "%s: group %d: RP_ACT_SILU_MUL supports at most %d output tiles", fn,

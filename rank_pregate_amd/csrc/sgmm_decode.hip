@@ -922,10 +922,16 @@ __device__ __forceinline__ void base_item(const SgmmArgs& a, const DecodeArgs& d
 #pragma unroll
       for (int v = 0; v < 4; ++v) yf[(m * 16 + 4 * kg + v) * TR + wave * 16 + lr] = acc[m][v];
     __syncthreads();
+    // a group that waited for earlier groups may add one of their outputs:
+    // read device-coherent, as its x
+    const __amdgpu_buffer_rsrc_t rres = rsrc(res, (uint32_t)((size_t)a.T * pd.ld_y * sizeof(bf16_t)));
     for (int q = tid; q < a.T * (TR / 8); q += NTH) {
       const int t = q / (TR / 8), c8 = (q % (TR / 8)) * 8;
       if (tile_row0 + c8 < pd.d_out) {
-        const uint4 rv = ld16(res + (size_t)t * pd.ld_y + tile_row0 + c8);
+        const size_t ro = (size_t)t * pd.ld_y + tile_row0 + c8;
+        const uint4 rv = x_coh ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                     rres, (uint32_t)(ro * sizeof(bf16_t)), 0, kSc1))
+                               : ld16(res + ro);
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
         const float* f = &yf[t * TR + c8];
         uint32_t o[4];

@@ -365,6 +365,8 @@ def test_projection_tiled_w0(T, d_in, d_outs, E, r, k):
     (200, 12288, [256], 96, 16, 2),          # long K on few tiles: split-K partials, then the fp32 base
     (130, 256, [192, 64, 320], 40, 8, 4),    # four slots, three projections
     (100, 1024, [384, 136], 48, 32, 2),      # rank 32, two token blocks, ragged 64-row block
+    (90, 256, [136], 45, 16, 2),             # odd E, two token blocks, one ragged 64-row block
+    (70, 512, [200], 30, 32, 2),             # rank 32, T just past the decode path
 ])
 def test_prefill_split_expand(T, d_in, d_outs, E, r, k):
     """Prefill shapes with many small segments: the GEMM stores fp32 base tiles and the expand runs as a
@@ -602,6 +604,38 @@ def test_step_chained(T):
         check_y(y1, ref1, dt, "chained group 1")
         ref2 = oracle.sgmm(dl_widen(y1, dt), *(widen(a, dt) for a in hw2[0]), idx, g64)
         check_y(ys[2][0], ref2, dt, "chained group 2")
+
+
+@pytest.mark.parametrize("T", [20, 64])
+def test_step_chained_residual(T):
+    """A dependent group whose residual is the earlier group's output: y1 = W1 x + adapters, then
+    y2 = y1 + W2 y1 + adapters in the same call, read only after y1 is written (NaN-filled before)."""
+    say("step chained residual", T)
+    rng = np.random.default_rng(900 + T)
+    dt, E, r, k = "bf16", 8, 16, 2
+    conv = datagen.f32_to_bf16_bits
+    d = 512
+    hw0, dev0 = _group_weights(rng, d, [d], E, r, dt)
+    hw1, dev1 = _group_weights(rng, d, [d], E, r, dt)
+    x0 = conv(rng.standard_normal((T, d), dtype=np.float32))
+    y0 = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    y1 = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    idx = datagen.uniform_indices(T + 3, T, E, k)
+    gate = datagen.random_gates(T + 3, T, k)
+    idx_d, gate_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(gate).to(DEV)
+    off, perm = rp.segment(idx_d, E)
+    groups = [([dev0[0] + (y0,)], to_device(x0, dt, DEV)), ([dev1[0] + (y1, y0)], y0, 1)]
+    for rep in range(2):
+        y0.fill_(float("nan"))
+        y1.fill_(float("nan"))
+        rp.sgmm_step(groups, E, r, k, topk_idx=idx_d, topk_gate=gate_d, seg_offsets=off, pair_perm=perm)
+        torch.cuda.synchronize()
+        g64 = gate.astype(np.float64)
+        ref0 = oracle.sgmm(widen(x0, dt), *(widen(a, dt) for a in hw0[0]), idx, g64)
+        check_y(y0, ref0, dt, "residual chain: group 0")
+        got0 = dl_widen(y0, dt)
+        ref1 = oracle.sgmm(got0, *(widen(a, dt) for a in hw1[0]), idx, g64) + got0
+        check_y(y1, ref1, dt, "residual chain: group 1")
 
 
 @pytest.mark.parametrize("T,d,ff", [(9, 512, 2048), (9, 512, 11008), (64, 512, 11008), (64, 4096, 11008)])
@@ -1045,7 +1079,7 @@ def test_step_split_expand_routed_graph():
 # --------------------------------------------------------------------------- whole decoder layers
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("T,d", [(1, 64), (9, 256), (64, 4096), (130, 11008)])
+@pytest.mark.parametrize("T,d", [(1, 64), (9, 256), (64, 4096), (130, 11008), (3, 65536)])
 def test_rmsnorm(dt, T, d):
     """rp_rmsnorm against the oracle's fp64 RMSNorm rounded to the output dtype, in place too."""
     say("rmsnorm", dt, T, d)
