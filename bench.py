@@ -137,6 +137,27 @@ def cpu_baseline(wl, seconds: float):
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
+def stream_read_ceiling(dev, nbytes: int = 1 << 30) -> float:
+    """GB/s of rp_util_stream_read over a fresh `nbytes` buffer (past the Infinity Cache), mean of 5."""
+    import torch
+
+    import rank_pregate_amd as rp
+    big = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1024, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        rp.stream_read(big, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        rp.stream_read(big, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 5
+    del big
+    return nbytes / (us * 1e-6) / 1e9
+
+
 def calibrate():
     """Known-traffic kernels: a 1 GiB copy (reads 1 GiB, writes 1 GiB) for scaling the
     FETCH_SIZE / WRITE_SIZE counters, and a 4 GiB stream read for the achievable read bandwidth."""
@@ -483,6 +504,12 @@ def main():
                              "avg_launch_us": round(dom_ms * 1e3, 2), "bytes_per_launch": dom_bytes,
                              "flops_per_launch": dom_flops, "achieved_GBps": round(dom_gbs, 1),
                              "achieved_TFLOPs": round(dom_tflops, 1)})
+    if not mfma_bound:
+        # the achievable read rate on this GPU, measured after the timed work: the
+        # dominant call's algorithmic GB/s against it as well as against the peak
+        sr = stream_read_ceiling(dev)
+        line["roofline"].update({"stream_read_GBps": round(sr, 1), "frac_of_stream_read": round(dom_gbs / sr, 4)})
+        log(f"[bench] stream-read ceiling {sr:,.0f} GB/s; dominant call at {100 * dom_gbs / sr:.1f}% of it")
     line["timing"] = {"median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
                       "samples": len(step_samples), "sample": f"mean step time of each round of {copies} steps",
                       "launches_per_step": launches, "base_only_ms": round(base_ms, 5),
