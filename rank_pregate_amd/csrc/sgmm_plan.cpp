@@ -71,7 +71,9 @@ SgmmPlan plan_decode_group(int n_proj, const int* d_out, int T, int d_in, int E,
     // than the backbone so its results are ready before the backbone's
     p.atiles_per_proj = a_tiles_per_proj(E, r, T);
     p.n_atiles = p.atiles_per_proj * n_proj;
-    p.SA = s_max;
+    // (up to eight splits at every T: the backbone's cap for 128-row tiles does
+    // not apply, the shrink is what the expand waits for)
+    p.SA = std::max(1, std::min(kMaxSplits, nchunks / 2));
     n_shrink = p.n_atiles * p.SA;
   } else if (k > 0) {
     p.KP = shrink_kparts(d_in, r);
