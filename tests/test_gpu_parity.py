@@ -360,6 +360,25 @@ def test_projection_tiled_w0(T, d_in, d_outs, E, r, k):
 
 
 @pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
+    (64, 4096, [512], 16, 8, 2),             # 4 tiles of 128 rows: the most K splits a phase takes
+    (40, 1000, [1200], 12, 16, 2),           # ragged K (8 chunks, the last partial) and a ragged last tile
+    (64, 11008, [256], 16, 8, 2),            # long K: at least the long-K split count
+    (50, 2048, [4096, 4096, 1024], 8, 16, 2),  # 72 tiles over three projections
+    (64, 4096, [11008], 16, 8, 2),           # 86 tiles: few splits, several items past the CUs' count
+])
+def test_decode_phase_splits(T, d_in, d_outs, E, r, k):
+    """Decode launches of 128-row tiles that leave CUs free: the K splits come from the planner's
+    estimate of the phase (1 to 4 backbone splits, up to 8 for the shrink); outputs against the oracle
+    and bit-identical on a second call."""
+    say("phase splits", T, d_in, d_outs, E, r, k)
+    _, ys = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + len(d_outs), b_scale=1.0)
+    first = [y.clone() for y in ys]
+    _, ys2 = _run_projection_case(T, d_in, d_outs, E, r, k, "bf16", seed=T + d_in + len(d_outs), b_scale=1.0)
+    for a, b in zip(first, ys2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "phase splits changed between calls"
+
+
+@pytest.mark.parametrize("T,d_in,d_outs,E,r,k", [
     (256, 4096, [4096, 1024], 256, 16, 2),   # many adapters, one token tile of 256
     (65, 512, [520, 128], 64, 8, 3),         # 128-token tile, ragged output tile (second half past d_out)
     (200, 12288, [256], 96, 16, 2),          # long K on few tiles: split-K partials, then the fp32 base
